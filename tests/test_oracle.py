@@ -1,0 +1,356 @@
+"""Pins for the CPU oracle: brute force, closed forms, invariants, a library
+cross-check and the byte figures the pages print.  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _tolist(a):
+    return np.asarray(a, dtype=np.float64).tolist()
+
+
+# ---- brute force ----------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(6))
+def test_attention_matches_brute_force(seed):
+    r = _rng(seed)
+    B, H = int(r.integers(1, 3)), int(r.integers(1, 3))
+    Tq, Tk, D = int(r.integers(1, 10)), int(r.integers(1, 10)), int(r.integers(1, 9))
+    q = r.standard_normal((B, H, Tq, D)) * 1.5
+    k = r.standard_normal((B, H, Tk, D))
+    v = r.standard_normal((B, H, Tk, D))
+    mask = (r.random((B, Tk)) < 0.35).astype(np.uint8)
+    if seed == 3:
+        mask[0, :] = 1                      # one sequence with every key padded
+    scale = float(r.uniform(0.2, 1.5))
+    O, L = oracle.attention(q, k, v, mask, scale)
+    bO, bL = brute.attention(_tolist(q), _tolist(k), _tolist(v), mask.tolist(), scale)
+    for b in range(B):
+        for h in range(H):
+            for i in range(Tq):
+                if bL[b][h][i] == -math.inf:
+                    assert L[b, h, i] == -np.inf
+                    assert np.all(O[b, h, i] == 0.0)
+                else:
+                    assert abs(L[b, h, i] - bL[b][h][i]) <= 1e-12
+                    assert np.max(np.abs(O[b, h, i] - np.array(bO[b][h][i]))) <= 1e-12
+
+
+def test_attention_rows_subset_equals_full():
+    w = workloads.make_prefill(2, 2, 11, 13, 8, torch.float32, valid=[13, 7], seed=5)
+    O, L = oracle.attention(w.q, w.k, w.v, w.mask, w.scale)
+    rows = [0, 4, 10, 3]
+    Os, Ls = oracle.attention(w.q, w.k, w.v, w.mask, w.scale, rows=rows)
+    assert np.array_equal(Os, O[:, :, rows]) and np.array_equal(Ls, L[:, :, rows])
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_merge_matches_brute_force(seed):
+    r = _rng(100 + seed)
+    n, R, D = int(r.integers(1, 5)), 6, 5
+    outs = [r.standard_normal((R, D)) for _ in range(n)]
+    lses = [r.standard_normal(R) * 3 for _ in range(n)]
+    lses[0][2] = -np.inf                     # an empty chunk for one row
+    if n > 1:
+        for i in range(n):
+            lses[i][4] = -np.inf             # a row empty in every chunk
+    O, L = oracle.merge_lse(outs, lses)
+    bO, bL = brute.merge([o.tolist() for o in outs], [l.tolist() for l in lses])
+    for i in range(R):
+        if bL[i] == -math.inf:
+            assert L[i] == -np.inf and np.all(O[i] == 0)
+        else:
+            assert abs(L[i] - bL[i]) <= 1e-12
+            assert np.max(np.abs(O[i] - np.array(bO[i]))) <= 1e-12
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_decode_matches_brute_force(seed):
+    r = _rng(200 + seed)
+    B, Hkv, G, D, T = 2, 2, int(r.integers(1, 4)), 4, 9
+    Hq = Hkv * G
+    q = r.standard_normal((B, Hq, 1, D))
+    kc = r.standard_normal((B, Hkv, T, D))
+    vc = r.standard_normal((B, Hkv, T, D))
+    lens = r.integers(1, T + 1, B)
+    scale = 0.7
+    O, L = oracle.decode(q, kc, vc, lens, scale)
+    bO, bL = brute.decode(q[:, :, 0].tolist(), kc.tolist(), vc.tolist(), lens.tolist(), scale)
+    for b in range(B):
+        for h in range(Hq):
+            assert abs(L[b, h] - bL[b][h]) <= 1e-12
+            assert np.max(np.abs(O[b, h, 0] - np.array(bO[b][h]))) <= 1e-12
+
+
+def test_decode_heads_subset():
+    w = workloads.make_decode(3, 8, 2, 16, 3, 12, torch.float32, seed=2)
+    O, L = oracle.decode(w.q, w.k_cache, w.v_cache, w.lens, w.scale)
+    heads = [(0, 7), (2, 0), (1, 3)]
+    Os, Ls = oracle.decode(w.q, w.k_cache, w.v_cache, w.lens, w.scale, heads=heads)
+    for i, (b, h) in enumerate(heads):
+        assert np.array_equal(Os[i], O[b, h, 0]) and Ls[i] == L[b, h]
+
+
+# ---- closed forms -------------------------------------------------------------------
+
+def test_zero_query_gives_uniform_weights():
+    r = _rng(1)
+    B, H, Tq, Tk, D = 2, 2, 3, 8, 5
+    q = np.zeros((B, H, Tq, D))
+    k = r.standard_normal((B, H, Tk, D))
+    v = r.standard_normal((B, H, Tk, D))
+    mask = np.zeros((B, Tk), np.uint8)
+    mask[0, 5:] = 1
+    mask[1, [0, 2, 3]] = 1
+    O, L = oracle.attention(q, k, v, mask, 0.9)
+    for b in range(B):
+        valid = mask[b] == 0
+        n = int(valid.sum())
+        for h in range(H):
+            expect = v[b, h, valid].mean(axis=0)
+            assert np.allclose(O[b, h], expect[None, :], atol=1e-14, rtol=0)
+            assert np.allclose(L[b, h], math.log(n), atol=1e-14, rtol=0)
+
+
+def test_zero_keys_give_uniform_weights():
+    r = _rng(2)
+    q = r.standard_normal((1, 1, 4, 6))
+    k = np.zeros((1, 1, 7, 6))
+    v = r.standard_normal((1, 1, 7, 6))
+    O, L = oracle.attention(q, k, v, None, 0.3)
+    assert np.allclose(O[0, 0], v[0, 0].mean(axis=0)[None], atol=1e-14, rtol=0)
+    assert np.allclose(L, math.log(7), atol=1e-14, rtol=0)
+
+
+def test_single_valid_key():
+    r = _rng(3)
+    q = r.standard_normal((1, 2, 3, 4))
+    k = r.standard_normal((1, 2, 6, 4))
+    v = r.standard_normal((1, 2, 6, 4))
+    mask = np.ones((1, 6), np.uint8)
+    mask[0, 4] = 0
+    s = 0.6
+    O, L = oracle.attention(q, k, v, mask, s)
+    for h in range(2):
+        for i in range(3):
+            assert np.array_equal(O[0, h, i], v[0, h, 4])
+            assert abs(L[0, h, i] - s * float(q[0, h, i] @ k[0, h, 4])) <= 1e-14
+
+
+def test_constant_values_pass_through():
+    r = _rng(4)
+    q = r.standard_normal((1, 1, 5, 3))
+    k = r.standard_normal((1, 1, 9, 3))
+    c = np.array([0.25, -1.5, 3.0])
+    v = np.broadcast_to(c, (1, 1, 9, 3)).copy()
+    O, _ = oracle.attention(q, k, v, (r.random((1, 9)) < 0.3).astype(np.uint8), 1.0)
+    assert np.allclose(O[0, 0], c[None], atol=1e-14, rtol=0)
+
+
+def test_single_key():
+    r = _rng(5)
+    q = r.standard_normal((1, 1, 4, 3))
+    k = r.standard_normal((1, 1, 1, 3))
+    v = r.standard_normal((1, 1, 1, 3))
+    O, L = oracle.attention(q, k, v, None, 0.5)
+    assert np.array_equal(O[0, 0], np.repeat(v[0, 0], 4, axis=0))
+    assert np.allclose(L[0, 0], 0.5 * (q[0, 0] @ k[0, 0, 0]), atol=1e-15, rtol=0)
+
+
+def test_two_keys_logistic():
+    # Two keys with score gap d: the weight of key 0 is the logistic function of d.
+    q = np.array([[[[1.0, 0.0]]]])
+    k = np.array([[[[2.0, 0.0], [0.5, 0.0]]]])
+    v = np.array([[[[1.0, 0.0], [0.0, 1.0]]]])
+    s = 0.8
+    O, L = oracle.attention(q, k, v, None, s)
+    d = s * (2.0 - 0.5)
+    w0 = 1.0 / (1.0 + math.exp(-d))
+    assert abs(O[0, 0, 0, 0] - w0) < 1e-15 and abs(O[0, 0, 0, 1] - (1 - w0)) < 1e-15
+    assert abs(L[0, 0, 0] - math.log(math.exp(s * 2.0) + math.exp(s * 0.5))) < 1e-14
+
+
+def test_fully_padded_sequence():
+    r = _rng(6)
+    q, k, v = (r.standard_normal((2, 1, 3, 4)) for _ in range(3))
+    mask = np.zeros((2, 3), np.uint8)
+    mask[1] = 1
+    O, L = oracle.attention(q, k, v, mask, 1.0)
+    assert np.all(O[1] == 0) and np.all(L[1] == -np.inf)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L[0]))
+
+
+# ---- invariants ----------------------------------------------------------------------
+
+def test_softmax_rows_sum_to_one_and_padded_weight_zero():
+    r = _rng(7)
+    S = r.standard_normal((6, 11)) * 4
+    padded = r.random(11) < 0.4
+    padded[0] = False
+    W, m, l = oracle.masked_softmax(S, padded)
+    assert np.all(W[:, padded] == 0.0)
+    assert np.max(np.abs(W.sum(axis=1) - 1.0)) <= 1e-12
+    assert np.all(W >= 0)
+    assert np.array_equal(m, np.where(padded[None], -np.inf, S).max(axis=1))
+
+
+def test_garbage_in_padded_keys_is_ignored():
+    w = workloads.make_prefill(2, 3, 7, 10, 8, torch.float32, valid=[6, 10], seed=8)
+    O, L = oracle.attention(w.q, w.k, w.v, w.mask, w.scale)
+    k = w.k.clone()
+    v = w.v.clone()
+    k[0, :, 6:] = 1e4
+    v[0, :, 6:] = -7e3
+    O2, L2 = oracle.attention(w.q, k, v, w.mask, w.scale)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2)
+
+
+def test_masked_equals_truncated():
+    w = workloads.make_prefill(1, 2, 9, 12, 6, torch.float32, valid=[8], seed=9)
+    O, L = oracle.attention(w.q, w.k, w.v, w.mask, w.scale)
+    Ot, Lt = oracle.attention(w.q, w.k[:, :, :8], w.v[:, :, :8], None, w.scale)
+    assert np.max(np.abs(O - Ot)) <= 1e-14 and np.max(np.abs(L - Lt)) <= 1e-14
+
+
+def test_key_permutation_invariance():
+    r = _rng(10)
+    w = workloads.make_prefill(1, 2, 5, 9, 4, torch.float32,
+                               mask=torch.tensor([[0, 1, 0, 0, 1, 0, 0, 0, 1]]), seed=10)
+    perm = r.permutation(9)
+    O, L = oracle.attention(w.q, w.k, w.v, w.mask, w.scale)
+    Op, Lp = oracle.attention(w.q, w.k[:, :, perm], w.v[:, :, perm], w.mask[:, perm], w.scale)
+    assert np.max(np.abs(O - Op)) <= 1e-13 and np.max(np.abs(L - Lp)) <= 1e-13
+
+
+def test_mask_polarity_matters():
+    w = workloads.make_prefill(1, 2, 16, 16, 8, torch.float32, valid=[10], seed=11)
+    O, _ = oracle.attention(w.q, w.k, w.v, w.mask, w.scale)
+    Oinv, _ = oracle.attention(w.q, w.k, w.v, 1 - w.mask, w.scale)
+    assert np.max(np.abs(O - Oinv)) > 0.1
+
+
+@pytest.mark.parametrize("splits", [[13], [5, 8], [1, 6, 6], [3, 3, 3, 4]])
+def test_chunked_merge_equals_single_pass(splits):
+    w = workloads.make_chunked(2, 2, 7, splits, 8, torch.float32, seed=12)
+    parts = [oracle.attention(w.q, kc, vc, None, w.scale) for kc, vc in zip(w.k_chunks, w.v_chunks)]
+    O, L = oracle.merge_lse([p[0] for p in parts], [p[1] for p in parts])
+    k = torch.cat(w.k_chunks, dim=2)
+    v = torch.cat(w.v_chunks, dim=2)
+    Of, Lf = oracle.attention(w.q, k, v, None, w.scale)
+    assert np.max(np.abs(O - Of)) <= 1e-13 and np.max(np.abs(L - Lf)) <= 1e-13
+
+
+def test_merge_single_chunk_is_identity():
+    r = _rng(13)
+    o, l = r.standard_normal((4, 3, 5)), r.standard_normal((4, 3))
+    O, L = oracle.merge_lse([o], [l])
+    assert np.max(np.abs(O - o)) <= 1e-15 and np.max(np.abs(L - l)) <= 1e-15
+
+
+def test_append_touches_only_slot_len():
+    w = workloads.make_decode(3, 4, 2, 8, 2, 10, torch.float32, T_max=16, seed=14)
+    kc, vc, lens = oracle.kv_append(w.k_cache.numpy(), w.v_cache.numpy(), w.lens.numpy(),
+                                    w.k_new.numpy(), w.v_new.numpy())
+    for b in range(3):
+        t = int(w.lens[b])
+        assert lens[b] == t + 1
+        assert np.array_equal(kc[b, :, t], w.k_new[b, :, 0].numpy())
+        assert np.array_equal(vc[b, :, t], w.v_new[b, :, 0].numpy())
+        keep = [i for i in range(16) if i != t]
+        assert np.array_equal(kc[b][:, keep], w.k_cache.numpy()[b][:, keep])
+        assert np.array_equal(vc[b][:, keep], w.v_cache.numpy()[b][:, keep])
+
+
+def test_decode_equals_full_attention_over_cache_prefix():
+    w = workloads.make_decode(3, 6, 2, 8, 4, 20, torch.float32, seed=15)
+    kc, vc, lens = oracle.kv_append(w.k_cache.numpy(), w.v_cache.numpy(), w.lens.numpy(),
+                                    w.k_new.numpy(), w.v_new.numpy())
+    O, L = oracle.decode(w.q, kc, vc, lens, w.scale)
+    G = 3
+    for b in range(3):
+        n = int(lens[b])
+        k = np.repeat(kc[b:b + 1, :, :n], G, axis=1)      # expand KV heads to query heads
+        v = np.repeat(vc[b:b + 1, :, :n], G, axis=1)
+        Of, Lf = oracle.attention(w.q[b:b + 1].numpy(), k, v, None, w.scale)
+        assert np.max(np.abs(O[b] - Of[0])) <= 1e-14 and np.max(np.abs(L[b] - Lf[0, :, 0])) <= 1e-14
+
+
+# ---- library cross-check ---------------------------------------------------------------
+
+def test_oracle_matches_torch_sdpa_on_cfg1():
+    """The pages compare the materialising MHA path against SDPA on the CPU and see
+    them agree to ~5e-8 in fp32; the oracle must agree with SDPA (additive -inf
+    mask) the same way.  Passing the key-padding mask as SDPA's boolean mask
+    unconverted must give a large error."""
+    w = workloads.cfg1_fp32_masked()
+    O, L = oracle.attention(w.q, w.k, w.v, w.mask, w.scale)
+    add = torch.zeros(1, 1, 1, 512)
+    add[..., w.mask[0].bool()] = float("-inf")
+    ref = torch.nn.functional.scaled_dot_product_attention(w.q, w.k, w.v, attn_mask=add, scale=w.scale)
+    assert np.max(np.abs(O - ref.double().numpy())) < 2e-6
+    wrong = torch.nn.functional.scaled_dot_product_attention(
+        w.q, w.k, w.v, attn_mask=w.mask.bool()[:, None, None, :], scale=w.scale)
+    assert np.max(np.abs(O - wrong.double().numpy())) > 0.5
+    # LSE against torch's logsumexp over the masked scores
+    s = (w.q.double() @ w.k.double().transpose(-1, -2)) * w.scale + add.double()
+    assert np.max(np.abs(L - torch.logsumexp(s, dim=-1).numpy())) < 1e-12
+
+
+# ---- page-printed figures ---------------------------------------------------------------
+
+def _golden():
+    with open(os.path.join(GOLDEN, "page_numbers.json")) as f:
+        return json.load(f)
+
+
+def test_score_matrix_bytes_page_figures():
+    g = _golden()
+    e = g["score_matrix_3mp_bf16"]
+    nbytes = oracle.score_matrix_bytes(e["heads"], e["P"], e["elem_bytes"])
+    assert nbytes == 4_317_806_592
+    assert round(nbytes / 1e9, 2) == e["approx_GB"]
+    assert 4 * nbytes / 1e9 == pytest.approx(18.02, rel=0.05)   # "about four of them"
+    e = g["score_matrix_8mp_bf16"]
+    # 30.75 GiB for one matrix pins P to about 32.1 thousand, consistent with "about 32k"
+    P = math.sqrt(e["GiB"] * 2**30 / (e["heads"] * e["elem_bytes"]))
+    assert abs(P - e["P_approx"]) / e["P_approx"] < 0.01
+    e = g["cpu_theory_p1024_fp32"]
+    assert oracle.score_matrix_bytes(e["heads"], e["P"], e["elem_bytes"]) == e["MiB"] * 2**20
+
+
+def test_kv_bytes_page_figures():
+    g = _golden()
+    e = g["gqa_kv_bytes_per_token"]
+    bpt = oracle.kv_bytes_per_token(e["layers"], e["H_kv"], e["D"], e["elem_bytes"])
+    assert bpt == e["bytes"]
+    assert bpt * g["gqa_kv_8k_sequence"]["tokens"] == g["gqa_kv_8k_sequence"]["GiB"] * 2**30
+    e32 = g["gqa_kv_32x8k"]
+    assert bpt * e32["tokens"] * e32["sequences"] == e32["GiB"] * 2**30
+    assert oracle.kv_bytes_per_token(32, g["mha_vs_gqa_factor"]["H_kv_mha"], 128, 2) == \
+        g["mha_vs_gqa_factor"]["bytes_per_token"]
+    assert oracle.kv_bytes_per_token(32, g["mqa_factor"]["H_kv_mqa"], 128, 2) == g["mqa_factor"]["bytes_per_token"]
+    # one layer of the same shape reads 4 KiB per cached token
+    assert oracle.decode_kv_bytes([1, 2, 3], 8, 128, 2) == 6 * 4096
+
+
+def test_attention_flops_count():
+    # 4·D·H·Tq·n_valid: at the 3 MP workload (16 heads, P 11,616, 16 padded keys)
+    assert oracle.attention_flops(16, 64, 11616, [11600]) == 4 * 64 * 16 * 11616 * 11600
+    # brute count of multiply-adds in Q·Kᵀ and P·V on a tiny case
+    H, D, Tq, n = 2, 3, 4, [5, 2]
+    macs = sum(H * Tq * nv * D * 2 for nv in n)
+    assert oracle.attention_flops(H, D, Tq, n) == 2 * macs

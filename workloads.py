@@ -1,0 +1,191 @@
+"""Seeded synthetic inputs for the attention library and its CPU oracle.
+
+This module holds no attention arithmetic: it draws random tensors, casts
+them to the storage dtype, and builds key-padding masks and cache lengths.
+Both the GPU path (tests, bench) and the oracle receive exactly the tensors
+made here, so the oracle sees the same bits the kernels see (the bf16 cast
+happens once, here).
+
+Recipe (shared by every workload):
+  * CPU ``torch.Generator().manual_seed(seed)``, seed 0 unless stated; the
+    mask-polarity demonstration on the MultiheadAttention fast-path page
+    (molayo1419.me, section "출력은 달라졌는가") seeds its RNG with 0 too.
+  * ``torch.randn`` in the order Q, K, V (decode: lengths, K cache, V cache,
+    k_new, v_new, Q), multiplied by ``amp`` (a power of two, so exact), then
+    ``.to(dtype)`` (round-to-nearest-even for bf16).
+  * Key-padding masks are uint8 ``[B, Tk]``, nonzero = padded = ignored (the
+    nn.MultiheadAttention ``key_padding_mask`` polarity the same page warns
+    about), built from per-sequence valid lengths or an explicit pattern.
+
+The named workloads mirror the shapes the pages measure: 16-head patch
+self-attention at P = 1,944 and 11,616 patches (0.5 MP and ~3 MP images cut
+into 16x16-pixel patches; MultiheadAttention fast-path page, section
+"무엇이 일어나고 있었는가"), a 512-token 16-head fp32 case matching the CPU
+profiler run on that page ("프로파일러로 검증하기"), a two-chunk KV split as
+one ring-attention hop sees it (sglang PR 49078 analysis, section "1. aiter.py"),
+and GQA decode with 32 query / 8 KV heads at head_dim 128 (LLM inference
+memory accounting 2/10, section "11. 계산 예시: GQA Decoder").
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = [
+    "Prefill", "Chunked", "Decode",
+    "make_prefill", "make_chunked", "make_decode",
+    "mask_from_valid_lengths", "round_up",
+    "cfg1_fp32_masked", "cfg2_patch_0p5mp", "cfg3_patch_3mp",
+    "cfg4_chunked", "cfg5_decode",
+]
+
+
+def round_up(x: int, m: int) -> int:
+    return (x + m - 1) // m * m
+
+
+@dataclass
+class Prefill:
+    q: torch.Tensor            # [B, H, Tq, D]
+    k: torch.Tensor            # [B, H, Tk, D]
+    v: torch.Tensor            # [B, H, Tk, D]
+    mask: Optional[torch.Tensor]  # uint8 [B, Tk], nonzero = padded; None = no padding
+    scale: float
+    name: str = ""
+
+    @property
+    def shape(self):
+        B, H, Tq, D = self.q.shape
+        return B, H, Tq, self.k.shape[2], D
+
+
+@dataclass
+class Chunked:
+    q: torch.Tensor                    # [B, H, Tq, D]
+    k_chunks: list                     # each [B, H, Tk_i, D]
+    v_chunks: list
+    scale: float
+    name: str = ""
+
+
+@dataclass
+class Decode:
+    q: torch.Tensor        # [B, H_q, 1, D]
+    k_cache: torch.Tensor  # [B, H_kv, T_max, D]
+    v_cache: torch.Tensor
+    k_new: torch.Tensor    # [B, H_kv, 1, D]
+    v_new: torch.Tensor
+    lens: torch.Tensor     # int32 [B], cached length BEFORE the append
+    scale: float
+    name: str = ""
+
+
+def _gen(seed: int) -> torch.Generator:
+    g = torch.Generator()
+    g.manual_seed(seed)
+    return g
+
+
+def _randn(g, shape, amp, dtype):
+    x = torch.randn(*shape, generator=g, dtype=torch.float32)
+    if amp != 1.0:
+        x.mul_(amp)
+    return x.to(dtype).contiguous()
+
+
+def mask_from_valid_lengths(valid: Sequence[int], Tk: int) -> torch.Tensor:
+    """uint8 [B, Tk]; keys at index >= valid[b] are marked padded (1)."""
+    idx = torch.arange(Tk)
+    return torch.stack([(idx >= int(n)).to(torch.uint8) for n in valid]).contiguous()
+
+
+def make_prefill(B, H, Tq, Tk, D, dtype=torch.bfloat16, *, valid=None, mask=None,
+                 amp=1.0, seed=0, scale=None, name="") -> Prefill:
+    g = _gen(seed)
+    q = _randn(g, (B, H, Tq, D), amp, dtype)
+    k = _randn(g, (B, H, Tk, D), amp, dtype)
+    v = _randn(g, (B, H, Tk, D), amp, dtype)
+    if mask is None and valid is not None:
+        mask = mask_from_valid_lengths(valid, Tk)
+    if mask is not None:
+        mask = mask.to(torch.uint8).contiguous()
+        assert mask.shape == (B, Tk)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return Prefill(q, k, v, mask, float(scale), name)
+
+
+def make_chunked(B, H, Tq, chunk_lens, D, dtype=torch.bfloat16, *, amp=1.0, seed=0,
+                 scale=None, name="") -> Chunked:
+    """Q plus K/V drawn as one [B, H, sum(chunk_lens), D] tensor, then split."""
+    g = _gen(seed)
+    Tk = int(sum(chunk_lens))
+    q = _randn(g, (B, H, Tq, D), amp, dtype)
+    k = _randn(g, (B, H, Tk, D), amp, dtype)
+    v = _randn(g, (B, H, Tk, D), amp, dtype)
+    ks, vs, s = [], [], 0
+    for n in chunk_lens:
+        ks.append(k[:, :, s:s + n].contiguous())
+        vs.append(v[:, :, s:s + n].contiguous())
+        s += n
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return Chunked(q, ks, vs, float(scale), name)
+
+
+def make_decode(B, H_q, H_kv, D, len_lo, len_hi, dtype=torch.bfloat16, *, T_max=None,
+                amp=1.0, seed=0, scale=None, lens=None, name="") -> Decode:
+    """Cached lengths uniform in [len_lo, len_hi] (inclusive) unless given.
+
+    T_max defaults to the smallest multiple of 64 that holds the longest
+    sequence after one appended token.
+    """
+    g = _gen(seed)
+    if lens is None:
+        lens = torch.randint(len_lo, len_hi + 1, (B,), generator=g, dtype=torch.int64)
+    lens = torch.as_tensor(lens, dtype=torch.int64)
+    if T_max is None:
+        T_max = round_up(len_hi + 1, 64)
+    kc = _randn(g, (B, H_kv, T_max, D), amp, dtype)
+    vc = _randn(g, (B, H_kv, T_max, D), amp, dtype)
+    kn = _randn(g, (B, H_kv, 1, D), amp, dtype)
+    vn = _randn(g, (B, H_kv, 1, D), amp, dtype)
+    q = _randn(g, (B, H_q, 1, D), amp, dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return Decode(q, kc, vc, kn, vn, lens.to(torch.int32), float(scale), name)
+
+
+# ---- the five named workloads -------------------------------------------------
+
+def cfg1_fp32_masked(seed=0) -> Prefill:
+    """fp32, B1 H16 T512 D64, last 48 keys padded, scale 1/sqrt(64)."""
+    return make_prefill(1, 16, 512, 512, 64, torch.float32, valid=[512 - 48], seed=seed,
+                        name="fp32 masked self-attention B1 H16 T512 D64, 48 padded keys")
+
+
+def cfg2_patch_0p5mp(seed=0) -> Prefill:
+    """bf16, B2 H16 P1944 D64, valid lengths 1,944 and 1,700."""
+    return make_prefill(2, 16, 1944, 1944, 64, torch.bfloat16, valid=[1944, 1700], seed=seed,
+                        name="bf16 patch self-attention B2 H16 P1944 D64, valid 1944/1700")
+
+
+def cfg3_patch_3mp(seed=0) -> Prefill:
+    """bf16, B1 H16 P11616 D64, last 16 keys padded, inputs N(0,1)*0.5."""
+    return make_prefill(1, 16, 11616, 11616, 64, torch.bfloat16, valid=[11616 - 16], amp=0.5,
+                        seed=seed, name="bf16 patch self-attention B1 H16 P11616 D64, 16 padded keys")
+
+
+def cfg4_chunked(seed=0) -> Chunked:
+    """bf16, Q T8192 H24 D128 against 2 KV chunks of 8,192 keys, no mask."""
+    return make_chunked(1, 24, 8192, [8192, 8192], 128, torch.bfloat16, seed=seed,
+                        name="bf16 chunked KV B1 H24 Tq8192 D128, 2x8192 keys + LSE merge")
+
+
+def cfg5_decode(seed=0) -> Decode:
+    """bf16 GQA decode: B32, H_q 32 / H_kv 8, D128, cached len ~ U{512..8192}."""
+    return make_decode(32, 32, 8, 128, 512, 8192, torch.bfloat16, seed=seed,
+                       name="bf16 GQA decode B32 Hq32 Hkv8 D128, len U[512,8192] + 1 appended")
