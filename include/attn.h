@@ -1,0 +1,167 @@
+/*
+ * attn.h — C ABI of the MI355X (gfx950) masked / LSE / decode attention library.
+ *
+ * Exact scaled-dot-product attention that never materialises the
+ * heads x Tq x Tk score matrix.  Every call only enqueues HIP kernels on the
+ * caller's stream and returns; there is no host synchronisation, no device
+ * allocation and no pointer retained after return.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller, dense and
+ *     row-major in the layouts stated below, 16-byte aligned.
+ *   - `dtype` is ATTN_F32 (float) or ATTN_BF16 (bfloat16); all tensor
+ *     operands of one call share it, except LSE arrays, which are always
+ *     float32, the mask (uint8) and cache lengths (int32).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   - Head dimension D must be 64 or 128.
+ *   - Outputs must not alias inputs.
+ *   - Return value: an attn_status.  Argument checks happen on the host
+ *     before anything is enqueued; a failed check enqueues nothing.  A
+ *     launch failure reported by hipGetLastError maps to ATTN_ERR_LAUNCH.
+ *   - Arithmetic: bf16 inputs feed bf16 matrix-core products with float32
+ *     accumulation; the softmax statistics, normalisation and LSE are float32;
+ *     bf16 outputs are rounded to nearest even.  float32 inputs are computed
+ *     in float32 throughout.
+ */
+#ifndef MASKED_ATTN_ATTN_H
+#define MASKED_ATTN_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_F32 = 0,
+    ATTN_BF16 = 1
+} attn_dtype;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,         /* a required pointer is NULL */
+    ATTN_ERR_SHAPE = 2,        /* a size is out of range or inconsistent */
+    ATTN_ERR_UNSUPPORTED = 3,  /* D not in {64,128}, unknown dtype, too many chunks */
+    ATTN_ERR_WORKSPACE = 4,    /* decode workspace missing or too small */
+    ATTN_ERR_LAUNCH = 5,       /* hipGetLastError reported a failure after enqueueing */
+    ATTN_ERR_VALUE = 6,        /* scale is not a finite positive number */
+    ATTN_ERR_ALIGN = 7,        /* a tensor pointer is not 16-byte aligned */
+    ATTN_ERR_ALIAS = 8         /* an output pointer equals an input pointer */
+} attn_status;
+
+/*
+ * attn_fwd_masked — non-causal masked attention, O = softmax(scale·Q·Kᵀ + pad)·V.
+ *
+ * Defines the operation the MultiheadAttention inference fast path computes
+ * with a key-padding mask (molayo1419.me, "MultiheadAttention의 고속 경로가
+ * VRAM을 18GB나 소모했던 이야기", section "소스의 현실": scores [B, heads,
+ * T, T], masked softmax, product with V), computed here tile by tile so
+ * that only O(Tq + Tk) extra memory exists; padding acts as an additive -inf
+ * on the scores of padded keys (same page, "CPU에서 양을 측정하기").
+ *
+ *   q    [B, H, Tq, D]   queries
+ *   k, v [B, H, Tk, D]   keys and values
+ *   key_padding_mask  [B, Tk] uint8; NONZERO = padded = ignored (the
+ *        key_padding_mask polarity, the opposite of a boolean SDPA mask; same
+ *        page, "출력은 달라졌는가").  NULL = no padding.  Values stored at
+ *        padded keys are ignored but V there must be finite.
+ *   o    [B, H, Tq, D]   output, same dtype as q
+ *   scale  multiplier of Q·Kᵀ, finite and > 0 (usually 1/sqrt(D))
+ * Sizes: B, H, Tq, Tk >= 1.  A query whose keys are all padded gets O = 0.
+ * Queries are never masked: every query row is computed.
+ */
+int attn_fwd_masked(const void* q, const void* k, const void* v,
+                    const uint8_t* key_padding_mask, void* o,
+                    int B, int H, int Tq, int Tk, int D,
+                    float scale, int dtype, void* stream);
+
+/*
+ * attn_fwd_lse — attn_fwd_masked that also writes the per-row log-sum-exp.
+ *
+ * The LSE is what an online-softmax merge of results over separate KV
+ * chunks needs (blog.secrett2633.cloud, sglang PR 49078 analysis, section
+ * "1. aiter.py — LSE 반환과 ring 지원 선언").
+ *   lse [B, H, Tq] float32: natural-log log-sum-exp over unpadded keys of the
+ *       scaled scores, lse = log sum_j exp(scale·q·k_j); -inf for a row with
+ *       no unpadded key.
+ * All other arguments as attn_fwd_masked.
+ */
+int attn_fwd_lse(const void* q, const void* k, const void* v,
+                 const uint8_t* key_padding_mask, void* o, float* lse,
+                 int B, int H, int Tq, int Tk, int D,
+                 float scale, int dtype, void* stream);
+
+/*
+ * attn_merge_lse — combine n partial results over disjoint KV chunks.
+ *
+ * out = sum_i exp(lse_i - lse)·out_i with lse = log sum_i exp(lse_i), the
+ * merge ring attention applies per hop (sglang PR 49078 analysis, section
+ * "1. aiter.py"); rows with every lse_i = -inf give out = 0, lse = -inf.
+ *   n_chunks  1..32
+ *   outs  HOST array of n_chunks device pointers, each [B, H, T, D] (dtype)
+ *   lses  HOST array of n_chunks device pointers, each [B, H, T] float32
+ *   out   [B, H, T, D] (dtype); must not be any outs[i] (nor lse_out any lses[i])
+ *   lse_out  [B, H, T] float32, or NULL to skip
+ */
+int attn_merge_lse(int n_chunks, const void* const* outs, const float* const* lses,
+                   void* out, float* lse_out,
+                   int B, int H, int T, int D, int dtype, void* stream);
+
+/*
+ * kv_append — append one token per sequence to preallocated K/V caches.
+ *
+ * After the prompt is cached, each decode step computes K and V only for
+ * the newest token and adds them to the cache (agentlenshq.com, "nanoVLM에서
+ * KV 캐시 구현", sections "KV 캐싱이 추론을 최적화하는 방법" and
+ * "1. 어텐션 블록 업데이트"; cache tensors are (batch, heads, seq_len_cached,
+ * head_dim)).  Here the cache has fixed capacity T_max and appending writes
+ * slot cache_seqlens[b] and then increments it.
+ *   k_cache, v_cache  [B, H_kv, T_max, D] (dtype), modified in place
+ *   cache_seqlens     [B] int32 device array, read then incremented in place
+ *   k_new, v_new      [B, H_kv, 1, D] (dtype)
+ * A sequence whose length is < 0 or >= T_max is left untouched (no write,
+ * no increment); keeping len < T_max is the caller's responsibility.
+ */
+int kv_append(void* k_cache, void* v_cache, int32_t* cache_seqlens,
+              const void* k_new, const void* v_new,
+              int B, int H_kv, int T_max, int D, int dtype, void* stream);
+
+/*
+ * attn_decode — one query token per sequence against the KV cache (GQA).
+ *
+ * The current token's query attends over every cached position (nanoVLM
+ * KV-cache page, "KV 캐싱이 추론을 최적화하는 방법"); the bytes that must be
+ * read are 2·H_kv·D·elem_bytes per cached token (blog.ruahverce.com, LLM
+ * inference memory accounting 2/10, sections "10. KV Cache Byte 공식" and
+ * "13. KV는 Token마다 자란다"), and query heads that share a KV head share
+ * its reads (same page, "11. 계산 예시: GQA Decoder").
+ *   q   [B, H_q, 1, D]; query head h uses KV head h / (H_q / H_kv)
+ *   k_cache, v_cache  [B, H_kv, T_max, D]
+ *   cache_seqlens [B] int32 device: positions 0..len-1 are attended
+ *       (len = 0 gives O = 0, LSE = -inf; a length outside [0, T_max] is
+ *       clamped to that range)
+ *   o   [B, H_q, 1, D] (dtype);  lse [B, H_q] float32 or NULL
+ *   workspace  device scratch of at least attn_decode_workspace_bytes(...)
+ *       bytes, owned by the caller, 16-byte aligned; contents on entry are
+ *       ignored and are garbage on return.  Calls that share a workspace
+ *       must be ordered on one stream.
+ * H_q must be a multiple of H_kv.
+ */
+int attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* cache_seqlens, void* o, float* lse,
+                int B, int H_q, int H_kv, int T_max, int D,
+                float scale, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace attn_decode needs for these sizes (0 on invalid sizes). */
+size_t attn_decode_workspace_bytes(int B, int H_q, int H_kv, int T_max, int D);
+
+/* Static, human-readable name of a status code. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MASKED_ATTN_ATTN_H */

@@ -1,0 +1,10 @@
+"""MI355X (gfx950) masked / LSE / decode attention.
+
+Python names mirror the C ABI in include/attn.h; all compute runs in the
+HIP kernels of libmasked_attn.so.
+"""
+from ._lib import (  # noqa: F401
+    ATTN_BF16, ATTN_F32, AttnError, EXPORTS, LIB_PATH, STATUS,
+    attn_decode, attn_decode_workspace_bytes, attn_fwd_lse, attn_fwd_masked,
+    attn_merge_lse, kv_append, load,
+)

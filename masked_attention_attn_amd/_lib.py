@@ -1,0 +1,235 @@
+"""ctypes binding of libmasked_attn.so, with the C ABI's names.
+
+Argument marshalling only: each function checks that tensors are CUDA
+(HIP) tensors of the right dtype, shape and contiguity, allocates missing
+outputs with torch, and passes raw device pointers plus the current torch
+stream to the C entry point.  Every step of the computation runs in the HIP
+kernels; there is no fallback.  If the shared library has not been built, the
+first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmasked_attn.so")
+
+ATTN_F32 = 0
+ATTN_BF16 = 1
+
+STATUS = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
+    4: "ATTN_ERR_WORKSPACE", 5: "ATTN_ERR_LAUNCH", 6: "ATTN_ERR_VALUE", 7: "ATTN_ERR_ALIGN",
+    8: "ATTN_ERR_ALIAS",
+}
+
+EXPORTS = ("attn_fwd_masked", "attn_fwd_lse", "attn_merge_lse", "kv_append", "attn_decode",
+           "attn_decode_workspace_bytes", "attn_status_string")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the shared library (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library {path} is not built; run __graft_entry__.build() "
+                           "(or python -m masked_attention_attn_amd.build)")
+    lib = ctypes.CDLL(path)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_fwd_masked.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P]
+    lib.attn_fwd_lse.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, P]
+    lib.attn_merge_lse.argtypes = [I, ctypes.POINTER(P), ctypes.POINTER(P), P, P, I, I, I, I, I, P]
+    lib.kv_append.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
+    lib.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, P, S, P]
+    lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.attn_decode_workspace_bytes.restype = S
+    lib.attn_status_string.argtypes = [I]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    for name in ("attn_fwd_masked", "attn_fwd_lse", "attn_merge_lse", "kv_append", "attn_decode"):
+        getattr(lib, name).restype = I
+    _lib = lib
+    return lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise AttnError(fn, status, load().attn_status_string(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (cuda/HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _fwd(fn, q, k, v, key_padding_mask, scale, out, lse):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, T, D]")
+    B, H, Tq, D = q.shape
+    Tk = k.shape[2]
+    if k.shape != (B, H, Tk, D) or v.shape != (B, H, Tk, D):
+        raise ValueError(f"k/v shapes {tuple(k.shape)}/{tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    code = _dtype_code(q)
+    if key_padding_mask is not None:
+        _dev(key_padding_mask, "key_padding_mask")
+        if key_padding_mask.shape != (B, Tk):
+            raise ValueError(f"key_padding_mask must be [B, Tk] = {(B, Tk)}")
+        if key_padding_mask.dtype == torch.bool:
+            key_padding_mask = key_padding_mask.view(torch.uint8)
+        if key_padding_mask.dtype != torch.uint8:
+            raise TypeError("key_padding_mask must be uint8 or bool (nonzero/True = padded)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out")
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    lib = load()
+    st = _stream(q.device)
+    if fn == "attn_fwd_masked":
+        _check(fn, lib.attn_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(key_padding_mask), _ptr(out),
+                                       B, H, Tq, Tk, D, float(scale), code, st))
+        return out
+    if lse is None:
+        lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
+    else:
+        _dev(lse, "lse")
+        if lse.shape != (B, H, Tq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [B, H, Tq]")
+    _check(fn, lib.attn_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(key_padding_mask), _ptr(out), _ptr(lse),
+                                B, H, Tq, Tk, D, float(scale), code, st))
+    return out, lse
+
+
+def attn_fwd_masked(q, k, v, key_padding_mask=None, scale=None, out=None):
+    """O = softmax(scale·Q·Kᵀ with padded keys at -inf)·V; q/k/v [B, H, T, D]."""
+    return _fwd("attn_fwd_masked", q, k, v, key_padding_mask, scale, out, None)
+
+
+def attn_fwd_lse(q, k, v, key_padding_mask=None, scale=None, out=None, lse=None):
+    """As attn_fwd_masked, also returning the float32 natural-log LSE [B, H, Tq]."""
+    return _fwd("attn_fwd_lse", q, k, v, key_padding_mask, scale, out, lse)
+
+
+def attn_merge_lse(outs: Sequence[torch.Tensor], lses: Sequence[torch.Tensor], out=None,
+                   lse_out=None, want_lse: bool = True):
+    """Merge per-chunk (O_i [B,H,T,D], LSE_i [B,H,T]) into (O, LSE)."""
+    n = len(outs)
+    if n == 0 or len(lses) != n:
+        raise ValueError("need matching, non-empty lists of outputs and LSEs")
+    o0 = outs[0]
+    for i in range(n):
+        _dev(outs[i], f"outs[{i}]")
+        _dev(lses[i], f"lses[{i}]")
+        if outs[i].shape != o0.shape or outs[i].dtype != o0.dtype:
+            raise ValueError("all outs must share shape and dtype")
+        if lses[i].shape != o0.shape[:3] or lses[i].dtype != torch.float32:
+            raise ValueError("each lse must be float32 [B, H, T]")
+    B, H, T, D = o0.shape
+    code = _dtype_code(o0)
+    if out is None:
+        out = torch.empty_like(o0)
+    if want_lse and lse_out is None:
+        lse_out = torch.empty((B, H, T), dtype=torch.float32, device=o0.device)
+    P = ctypes.c_void_p
+    optrs = (P * n)(*[t.data_ptr() for t in outs])
+    lptrs = (P * n)(*[t.data_ptr() for t in lses])
+    lib = load()
+    _check("attn_merge_lse", lib.attn_merge_lse(n, optrs, lptrs, _ptr(out), _ptr(lse_out if want_lse else None),
+                                                B, H, T, D, code, _stream(o0.device)))
+    return (out, lse_out) if want_lse else out
+
+
+def kv_append(k_cache, v_cache, cache_seqlens, k_new, v_new):
+    """Write k_new/v_new [B, H_kv, 1, D] at slot cache_seqlens[b], then increment it (in place)."""
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (cache_seqlens, "cache_seqlens"),
+                 (k_new, "k_new"), (v_new, "v_new")):
+        _dev(t, n)
+    B, Hkv, Tmax, D = k_cache.shape
+    if v_cache.shape != k_cache.shape or k_new.shape != (B, Hkv, 1, D) or v_new.shape != (B, Hkv, 1, D):
+        raise ValueError("cache / new-token shapes are inconsistent")
+    if cache_seqlens.shape != (B,) or cache_seqlens.dtype != torch.int32:
+        raise ValueError("cache_seqlens must be int32 [B]")
+    code = _dtype_code(k_cache)
+    for t in (v_cache, k_new, v_new):
+        if t.dtype != k_cache.dtype:
+            raise TypeError("caches and new tokens must share a dtype")
+    _check("kv_append", load().kv_append(_ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens), _ptr(k_new),
+                                         _ptr(v_new), B, Hkv, Tmax, D, code, _stream(k_cache.device)))
+
+
+def attn_decode_workspace_bytes(B, H_q, H_kv, T_max, D) -> int:
+    return int(load().attn_decode_workspace_bytes(B, H_q, H_kv, T_max, D))
+
+
+def attn_decode(q, k_cache, v_cache, cache_seqlens, scale=None, out=None, lse=None, workspace=None,
+                want_lse: bool = False):
+    """One query token per sequence (q [B, H_q, 1, D]) against the first
+    cache_seqlens[b] positions of k_cache/v_cache [B, H_kv, T_max, D]."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (cache_seqlens, "cache_seqlens")):
+        _dev(t, n)
+    B, Hq, one, D = q.shape
+    if one != 1:
+        raise ValueError("q must be [B, H_q, 1, D]")
+    _, Hkv, Tmax, Dk = k_cache.shape
+    if k_cache.shape[0] != B or Dk != D or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shapes do not match q")
+    if cache_seqlens.shape != (B,) or cache_seqlens.dtype != torch.int32:
+        raise ValueError("cache_seqlens must be int32 [B]")
+    code = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and caches must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, Tmax, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("attn_decode", load().attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
+                                             _ptr(out), _ptr(lse if want_lse else None), B, Hq, Hkv, Tmax, D,
+                                             float(scale), code, _ptr(workspace), nbytes, _stream(q.device)))
+    return (out, lse) if want_lse else out

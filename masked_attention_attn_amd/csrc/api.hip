@@ -1,0 +1,146 @@
+// C ABI entry points: host-side argument checks, dtype / head-dim dispatch,
+// launch on the caller's stream.  Nothing here allocates, synchronises or
+// keeps a pointer; every check runs before the first HIP call, so a rejected
+// call enqueues nothing.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/attn.h"
+#include "launch.h"
+
+using namespace mattn;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool head_dim_ok(int D) { return D == 64 || D == 128; }
+bool dtype_ok(int dtype) { return dtype == ATTN_F32 || dtype == ATTN_BF16; }
+int elem_bytes(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+
+// Work counts are kept in int on the device side; refuse sizes whose element
+// counts would not fit comfortably in 63 bits or whose grids overflow.
+bool fits(long long a, long long b, long long c, long long d) {
+    const long long lim = 1ll << 46;
+    if (a <= 0 || b <= 0 || c <= 0 || d <= 0) return false;
+    long long x = a;
+    if ((x *= b) > lim || (x *= c) > lim || (x *= d) > lim) return false;
+    return true;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
+
+int fwd_common(const void* q, const void* k, const void* v, const uint8_t* mask, void* o,
+               float* lse, bool need_lse, int B, int H, int Tq, int Tk, int D, float scale,
+               int dtype, void* stream) {
+    if (!q || !k || !v || !o || (need_lse && !lse)) return ATTN_ERR_NULL;
+    if (!dtype_ok(dtype) || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+    if (!fits(B, H, Tq, D) || !fits(B, H, Tk, D) || (long long)B * H > (1ll << 24) ||
+        (long long)B * H * ((Tq + 127) / 128) > (1ll << 31) - 64)
+        return ATTN_ERR_SHAPE;
+    if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
+    if (o == k || o == v || (lse && ((void*)lse == q || (void*)lse == k || (void*)lse == v || (void*)lse == o)))
+        return ATTN_ERR_ALIAS;
+    FwdArgs a{q, k, v, mask, o, lse, B, H, Tq, Tk, D, scale, stream};
+    return finish(dtype == ATTN_BF16 ? launch_fwd_bf16(a) : launch_fwd_f32(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_masked(const void* q, const void* k, const void* v, const uint8_t* key_padding_mask,
+                    void* o, int B, int H, int Tq, int Tk, int D, float scale, int dtype,
+                    void* stream) {
+    return fwd_common(q, k, v, key_padding_mask, o, nullptr, false, B, H, Tq, Tk, D, scale, dtype,
+                      stream);
+}
+
+int attn_fwd_lse(const void* q, const void* k, const void* v, const uint8_t* key_padding_mask,
+                 void* o, float* lse, int B, int H, int Tq, int Tk, int D, float scale, int dtype,
+                 void* stream) {
+    return fwd_common(q, k, v, key_padding_mask, o, lse, true, B, H, Tq, Tk, D, scale, dtype,
+                      stream);
+}
+
+int attn_merge_lse(int n_chunks, const void* const* outs, const float* const* lses, void* out,
+                   float* lse_out, int B, int H, int T, int D, int dtype, void* stream) {
+    if (!outs || !lses || !out) return ATTN_ERR_NULL;
+    if (!dtype_ok(dtype) || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+    if (n_chunks < 1) return ATTN_ERR_SHAPE;
+    if (n_chunks > kMaxMergeChunks) return ATTN_ERR_UNSUPPORTED;
+    if (!fits(B, H, T, D) || (long long)B * H * T > (1ll << 31) - 1) return ATTN_ERR_SHAPE;
+    if (!aligned16(out)) return ATTN_ERR_ALIGN;
+    MergeArgs a{};
+    a.n = n_chunks;
+    for (int i = 0; i < n_chunks; ++i) {
+        if (!outs[i] || !lses[i]) return ATTN_ERR_NULL;
+        if (!aligned16(outs[i])) return ATTN_ERR_ALIGN;
+        if (outs[i] == out || (lse_out && lses[i] == lse_out)) return ATTN_ERR_ALIAS;
+        a.outs[i] = outs[i];
+        a.lses[i] = lses[i];
+    }
+    a.out = out;
+    a.lse_out = lse_out;
+    a.rows = B * H * T;
+    a.D = D;
+    a.stream = stream;
+    return finish(dtype == ATTN_BF16 ? launch_merge_bf16(a) : launch_merge_f32(a));
+}
+
+int kv_append(void* k_cache, void* v_cache, int32_t* cache_seqlens, const void* k_new,
+              const void* v_new, int B, int H_kv, int T_max, int D, int dtype, void* stream) {
+    if (!k_cache || !v_cache || !cache_seqlens || !k_new || !v_new) return ATTN_ERR_NULL;
+    if (!dtype_ok(dtype) || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+    if (!fits(B, H_kv, T_max, D) || B > (1 << 30)) return ATTN_ERR_SHAPE;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+        return ATTN_ERR_ALIGN;
+    if (k_cache == v_cache || k_new == k_cache || v_new == v_cache) return ATTN_ERR_ALIAS;
+    AppendArgs a{k_cache, v_cache, cache_seqlens, k_new, v_new, B, H_kv, T_max, D,
+                 elem_bytes(dtype), stream};
+    return finish(launch_kv_append(a));
+}
+
+size_t attn_decode_workspace_bytes(int B, int H_q, int H_kv, int T_max, int D) {
+    if (B <= 0 || H_q <= 0 || H_kv <= 0 || T_max <= 0 || !head_dim_ok(D) || H_q % H_kv != 0)
+        return 0;
+    return decode_workspace_bytes(B, H_q, T_max, D);
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* cache_seqlens, void* o, float* lse, int B, int H_q, int H_kv,
+                int T_max, int D, float scale, int dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !cache_seqlens || !o) return ATTN_ERR_NULL;
+    if (!dtype_ok(dtype) || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+    if (H_kv <= 0 || H_q <= 0 || H_q % H_kv != 0) return ATTN_ERR_SHAPE;
+    if (!fits(B, H_kv, T_max, D) || !fits(B, H_q, 1, D) || (long long)B * H_q > (1 << 30))
+        return ATTN_ERR_SHAPE;
+    if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
+    if (!workspace || workspace_bytes < decode_workspace_bytes(B, H_q, T_max, D))
+        return ATTN_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+        !aligned16(workspace))
+        return ATTN_ERR_ALIGN;
+    if (o == q || o == k_cache || o == v_cache) return ATTN_ERR_ALIAS;
+    DecodeArgs a{q, k_cache, v_cache, cache_seqlens, o, lse, B, H_q, H_kv, T_max, D, scale,
+                 workspace, stream};
+    return finish(dtype == ATTN_BF16 ? launch_decode_bf16(a) : launch_decode_f32(a));
+}
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL: return "a required pointer is NULL";
+        case ATTN_ERR_SHAPE: return "a size is out of range or inconsistent";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension, dtype or chunk count";
+        case ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+        case ATTN_ERR_LAUNCH: return "kernel launch failed";
+        case ATTN_ERR_VALUE: return "scale must be finite and > 0";
+        case ATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case ATTN_ERR_ALIAS: return "an output aliases an input";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

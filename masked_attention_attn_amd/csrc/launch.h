@@ -1,0 +1,66 @@
+// Internal launchers behind the C ABI.  Arguments are already validated by
+// the API layer; each launcher enqueues its kernels on `stream` and returns
+// hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mattn {
+
+struct FwdArgs {
+    const void* q; const void* k; const void* v;
+    const uint8_t* mask;
+    void* o; float* lse;          // lse may be null
+    int B, H, Tq, Tk, D;
+    float scale;
+    void* stream;
+};
+
+constexpr int kMaxMergeChunks = 32;
+
+struct MergeArgs {
+    int n;
+    const void* outs[kMaxMergeChunks];
+    const float* lses[kMaxMergeChunks];
+    void* out; float* lse_out;    // lse_out may be null
+    int rows, D;                  // rows = B*H*T
+    void* stream;
+};
+
+struct AppendArgs {
+    void* k_cache; void* v_cache; int32_t* lens;
+    const void* k_new; const void* v_new;
+    int B, H_kv, T_max, D, elem_bytes;
+    void* stream;
+};
+
+struct DecodeArgs {
+    const void* q; const void* k_cache; const void* v_cache;
+    const int32_t* lens;
+    void* o; float* lse;          // lse may be null
+    int B, H_q, H_kv, T_max, D;
+    float scale;
+    void* workspace;
+    void* stream;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_f32(const FwdArgs& a);
+hipError_t launch_merge_bf16(const MergeArgs& a);
+hipError_t launch_merge_f32(const MergeArgs& a);
+hipError_t launch_kv_append(const AppendArgs& a);
+hipError_t launch_decode_bf16(const DecodeArgs& a);
+hipError_t launch_decode_f32(const DecodeArgs& a);
+
+// Split-K geometry of the decode path (shared by the workspace-size query
+// and the launcher).
+constexpr int kDecodeSplit = 512;     // cached tokens per split workgroup
+inline int decode_nsplit(int T_max) { return (T_max + kDecodeSplit - 1) / kDecodeSplit; }
+inline size_t decode_workspace_bytes(int B, int H_q, int T_max, int D) {
+    const size_t parts = (size_t)B * H_q * decode_nsplit(T_max);
+    return parts * (size_t)D * sizeof(float) + parts * 2 * sizeof(float);
+}
+
+}  // namespace mattn

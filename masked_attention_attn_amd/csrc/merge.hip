@@ -1,0 +1,106 @@
+// LSE merge of attention results computed over disjoint KV chunks.
+//
+// For every row: lse = M + log sum_i exp(lse_i - M) with M = max_i lse_i,
+// out = sum_i exp(lse_i - lse)·out_i — the online-softmax merge that ring
+// attention applies to per-hop partial outputs (blog.secrett2633.cloud,
+// sglang PR 49078 analysis, section "1. aiter.py — LSE 반환과 ring 지원
+// 선언").  Rows where every chunk is empty (all lse_i = -inf) give out = 0
+// and lse = -inf.
+//
+// Memory-bound: each thread owns 8 consecutive elements of one row, reads
+// them once from every chunk with 16- or 32-byte vector loads and writes the
+// merged 8 once; the per-row LSEs are tiny and cached.
+#include "common.cuh"
+#include "launch.h"
+
+namespace mattn {
+namespace {
+
+constexpr int NT = 256;
+
+struct ChunkPtrs {
+    const void* outs[kMaxMergeChunks];
+    const float* lses[kMaxMergeChunks];
+};
+
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> {
+    static __device__ __forceinline__ void load(const void* p, float* x) {
+        const u32x4 w = ldg128(p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { x[2 * j] = bf16_lo(w[j]); x[2 * j + 1] = bf16_hi(w[j]); }
+    }
+    static __device__ __forceinline__ void store(void* p, const float* x) {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+        stg128(p, w);
+    }
+};
+template <> struct Vec8<float> {
+    static __device__ __forceinline__ void load(const void* p, float* x) {
+        const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
+        const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { x[j] = a[j]; x[4 + j] = b[j]; }
+    }
+    static __device__ __forceinline__ void store(void* p, const float* x) {
+        f32x4 a = {x[0], x[1], x[2], x[3]}, b = {x[4], x[5], x[6], x[7]};
+        reinterpret_cast<f32x4*>(p)[0] = a;
+        reinterpret_cast<f32x4*>(p)[1] = b;
+    }
+};
+
+template <typename T>
+__global__ __launch_bounds__(NT)
+void merge_kernel(ChunkPtrs ptrs, int n, T* __restrict__ out, float* __restrict__ lse_out,
+                  int rows, int D) {
+    const int per_row = D / 8;
+    const long idx = (long)blockIdx.x * NT + threadIdx.x;
+    const long row = idx / per_row;
+    const int ch = (int)(idx - row * per_row);
+    if (row >= rows) return;
+
+    float M = kNegInf;
+    for (int i = 0; i < n; ++i) M = fmaxf(M, ptrs.lses[i][row]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const size_t off = (size_t)row * D + (size_t)ch * 8;
+    if (M == kNegInf) {
+        Vec8<T>::store(out + off, acc);
+        if (lse_out && ch == 0) lse_out[row] = kNegInf;
+        return;
+    }
+    float tot = 0.f;
+    for (int i = 0; i < n; ++i) tot += __expf(ptrs.lses[i][row] - M);
+    const float lse = M + __logf(tot);
+    for (int i = 0; i < n; ++i) {
+        const float w = __expf(ptrs.lses[i][row] - lse);   // empty chunk: exp(-inf) = 0
+        float x[8];
+        Vec8<T>::load(static_cast<const T*>(ptrs.outs[i]) + off, x);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = __builtin_fmaf(w, x[j], acc[j]);
+    }
+    Vec8<T>::store(out + off, acc);
+    if (lse_out && ch == 0) lse_out[row] = lse;
+}
+
+template <typename T>
+hipError_t launch(const MergeArgs& a) {
+    ChunkPtrs p;
+    for (int i = 0; i < kMaxMergeChunks; ++i) {
+        p.outs[i] = i < a.n ? a.outs[i] : nullptr;
+        p.lses[i] = i < a.n ? a.lses[i] : nullptr;
+    }
+    const long threads = (long)a.rows * (a.D / 8);
+    const long grid = (threads + NT - 1) / NT;
+    hipLaunchKernelGGL(merge_kernel<T>, dim3((unsigned)grid), dim3(NT), 0, (hipStream_t)a.stream,
+                       p, a.n, (T*)a.out, a.lse_out, a.rows, a.D);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_merge_bf16(const MergeArgs& a) { return launch<bf16>(a); }
+hipError_t launch_merge_f32(const MergeArgs& a) { return launch<float>(a); }
+
+}  // namespace mattn

@@ -1,0 +1,135 @@
+"""The C ABI library loads, exports every symbol include/attn.h declares, and
+rejects bad arguments on the host (before any HIP call, so these run without
+a GPU: the pointers passed are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import masked_attention_attn_amd as ma
+    if not os.path.exists(ma.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return ma.load()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_five_calls():
+    names = _declared()
+    for n in ("attn_fwd_masked", "attn_fwd_lse", "attn_merge_lse", "kv_append", "attn_decode"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    import masked_attention_attn_amd as ma
+    names = _declared()
+    assert set(names) == set(ma.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        s = lib.attn_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.attn_status_string(99).decode() == "unknown status"
+
+
+A = 0x10000      # fake, 16-byte aligned device addresses (never dereferenced)
+B_ = 0x20000
+C = 0x30000
+O = 0x40000
+L = 0x50000
+
+
+def fwd(lib, q=A, k=B_, v=C, m=0, o=O, B=1, H=2, Tq=8, Tk=8, D=64, scale=0.125, dtype=1):
+    return lib.attn_fwd_masked(q, k, v, m, o, B, H, Tq, Tk, D, scale, dtype, None)
+
+
+def test_fwd_validation(lib):
+    assert fwd(lib, q=0) == 1
+    assert fwd(lib, o=0) == 1
+    assert fwd(lib, D=96) == 3
+    assert fwd(lib, D=32) == 3
+    assert fwd(lib, dtype=7) == 3
+    assert fwd(lib, B=0) == 2
+    assert fwd(lib, Tq=0) == 2
+    assert fwd(lib, Tk=-1) == 2
+    assert fwd(lib, scale=0.0) == 6
+    assert fwd(lib, scale=-1.0) == 6
+    assert fwd(lib, scale=float("nan")) == 6
+    assert fwd(lib, scale=float("inf")) == 6
+    assert fwd(lib, q=A + 2) == 7
+    assert fwd(lib, o=O + 8) == 7
+    assert fwd(lib, o=B_) == 8
+    assert fwd(lib, o=C) == 8
+    # LSE variant: missing lse pointer, lse aliasing an input
+    assert lib.attn_fwd_lse(A, B_, C, 0, O, 0, 1, 2, 8, 8, 64, 0.125, 1, None) == 1
+    assert lib.attn_fwd_lse(A, B_, C, 0, O, A, 1, 2, 8, 8, 64, 0.125, 1, None) == 8
+
+
+def test_merge_validation(lib):
+    P = ctypes.c_void_p
+    outs = (P * 2)(A, B_)
+    lses = (P * 2)(C, L)
+    assert lib.attn_merge_lse(0, outs, lses, O, 0, 1, 2, 8, 64, 1, None) == 2
+    assert lib.attn_merge_lse(33, outs, lses, O, 0, 1, 2, 8, 64, 1, None) == 3
+    assert lib.attn_merge_lse(2, None, lses, O, 0, 1, 2, 8, 64, 1, None) == 1
+    bad = (P * 2)(A, 0)
+    assert lib.attn_merge_lse(2, bad, lses, O, 0, 1, 2, 8, 64, 1, None) == 1
+    assert lib.attn_merge_lse(2, outs, lses, A, 0, 1, 2, 8, 64, 1, None) == 8
+    assert lib.attn_merge_lse(2, outs, lses, O, L, 1, 2, 8, 64, 1, None) == 8
+    assert lib.attn_merge_lse(2, outs, lses, O, 0, 1, 2, 8, 100, 1, None) == 3
+    assert lib.attn_merge_lse(2, outs, lses, O + 4, 0, 1, 2, 8, 64, 1, None) == 7
+    assert lib.attn_merge_lse(2, outs, lses, O, 0, 1, 0, 8, 64, 1, None) == 2
+
+
+def test_append_validation(lib):
+    assert lib.kv_append(A, B_, 0, C, L, 2, 2, 16, 64, 1, None) == 1
+    assert lib.kv_append(A, B_, O, C, L, 2, 2, 16, 80, 1, None) == 3
+    assert lib.kv_append(A, B_, O, C, L, 2, 2, 0, 64, 1, None) == 2
+    assert lib.kv_append(A, A, O, C, L, 2, 2, 16, 64, 1, None) == 8
+    assert lib.kv_append(A + 2, B_, O, C, L, 2, 2, 16, 64, 1, None) == 7
+
+
+def test_decode_validation(lib):
+    ws = lib.attn_decode_workspace_bytes(4, 8, 2, 1000, 128)
+    assert ws > 0
+    W = 0x60000
+
+    def dec(**kw):
+        a = dict(q=A, k=B_, v=C, lens=L, o=O, lse=0, B=4, Hq=8, Hkv=2, Tmax=1000, D=128,
+                 scale=0.088, dtype=1, ws=W, wsb=ws)
+        a.update(kw)
+        return lib.attn_decode(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["B"], a["Hq"],
+                               a["Hkv"], a["Tmax"], a["D"], a["scale"], a["dtype"], a["ws"], a["wsb"], None)
+    assert dec(lens=0) == 1
+    assert dec(Hq=6, Hkv=4) == 2
+    assert dec(Hkv=0) == 2
+    assert dec(D=256) == 3
+    assert dec(scale=0.0) == 6
+    assert dec(ws=0) == 4
+    assert dec(wsb=ws - 1) == 4
+    assert dec(o=A) == 8
+    assert dec(q=A + 1) == 7
+    assert lib.attn_decode_workspace_bytes(4, 6, 4, 1000, 128) == 0
+    assert lib.attn_decode_workspace_bytes(0, 8, 2, 1000, 128) == 0
+
+
+def test_workspace_grows_linearly_with_cache_capacity(lib):
+    # O(T_max) scratch, never O(T_max^2): doubling capacity at most doubles it (+ one split)
+    a = lib.attn_decode_workspace_bytes(32, 32, 8, 8256, 128)
+    b = lib.attn_decode_workspace_bytes(32, 32, 8, 16512, 128)
+    assert a > 0 and b <= 2 * a + 32 * 32 * (128 + 2) * 4

@@ -1,0 +1,264 @@
+"""GPU parity: every entry point through the C ABI against the CPU oracle.
+
+Tolerances (max-abs over every element, fp64 comparison, NaN fails):
+  fp32 inputs: O and LSE <= 1e-4
+  bf16 inputs (fp32 accumulation): O <= 2e-2, LSE <= 1e-3
+An oracle -inf LSE must be exactly -inf on the GPU with an O row of exactly 0.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: (1e-4, 1e-4), torch.bfloat16: (2e-2, 1e-3)}
+DEV = "cuda"
+
+
+def _np(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def check_attn(O, L, Oref, Lref, dtype, what=""):
+    to, tl = TOL[dtype]
+    O = _np(O)
+    assert not np.isnan(O).any(), f"{what}: NaN in O"
+    dead = np.isneginf(Lref)
+    if L is not None:
+        L = L.detach().cpu().double().numpy()
+        assert not np.isnan(L).any(), f"{what}: NaN in LSE"
+        assert np.array_equal(np.isneginf(L), dead), f"{what}: -inf LSE pattern differs"
+        if (~dead).any():
+            el = np.max(np.abs(L[~dead] - Lref[~dead]))
+            assert el <= tl, f"{what}: max|dLSE| = {el:.3e} > {tl}"
+    if dead.any():
+        assert np.all(O[dead] == 0.0), f"{what}: rows with no unpadded key must be exactly 0"
+    eo = np.max(np.abs(O - Oref)) if O.size else 0.0
+    assert eo <= to, f"{what}: max|dO| = {eo:.3e} > {to}"
+    return eo
+
+
+def run_fwd(ma, w, lse=True):
+    q, k, v = (t.to(DEV) for t in (w.q, w.k, w.v))
+    m = w.mask.to(DEV) if w.mask is not None else None
+    if lse:
+        o, l = ma.attn_fwd_lse(q, k, v, m, w.scale)
+    else:
+        o, l = ma.attn_fwd_masked(q, k, v, m, w.scale), None
+    torch.cuda.synchronize()
+    return o, l
+
+
+# ---- prefill, element by element ------------------------------------------------------
+
+SHAPES = [
+    # B, H, Tq, Tk, D, mask kind
+    (1, 1, 1, 1, 64, None),
+    (1, 2, 17, 5, 64, "suffix"),
+    (2, 2, 64, 64, 64, "random"),
+    (1, 3, 255, 257, 64, "suffix"),
+    (2, 2, 256, 300, 64, "random"),
+    (1, 2, 513, 129, 64, "none"),
+    (2, 1, 300, 1000, 64, "holes"),
+    (1, 2, 100, 77, 128, "suffix"),
+    (2, 2, 130, 300, 128, "random"),
+    (1, 1, 257, 33, 128, "none"),
+]
+
+
+def _mask(kind, B, Tk, seed):
+    g = torch.Generator().manual_seed(seed)
+    if kind in (None, "none"):
+        return None
+    if kind == "suffix":
+        valid = torch.randint(1, Tk + 1, (B,), generator=g)
+        return W.mask_from_valid_lengths(valid.tolist(), Tk)
+    if kind == "random":
+        m = (torch.rand(B, Tk, generator=g) < 0.3).to(torch.uint8)
+        m[:, 0] = 0
+        return m
+    if kind == "holes":   # whole 64-key tiles padded in the middle plus a ragged tail
+        m = torch.zeros(B, Tk, dtype=torch.uint8)
+        m[:, 64:192] = 1
+        m[:, 500:533] = 1
+        m[-1, Tk - 7:] = 1
+        return m
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_fwd_shapes(ma, shape, dtype):
+    B, H, Tq, Tk, D, kind = shape
+    w = W.make_prefill(B, H, Tq, Tk, D, dtype, mask=_mask(kind, B, Tk, Tq + Tk), seed=Tq * 7 + Tk)
+    o, l = run_fwd(ma, w)
+    Or, Lr = oracle.attention(w.q, w.k, w.v, w.mask, w.scale)
+    check_attn(o, l, Or, Lr, dtype, f"{shape} {dtype}")
+    o2, _ = run_fwd(ma, w, lse=False)
+    assert torch.equal(o, o2), "attn_fwd_masked must equal attn_fwd_lse's O"
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_fwd_fully_padded_sequence(ma, dtype):
+    m = torch.zeros(3, 200, dtype=torch.uint8)
+    m[1] = 1
+    m[2, 5:] = 1
+    w = W.make_prefill(3, 2, 70, 200, 64, dtype, mask=m, seed=3)
+    o, l = run_fwd(ma, w)
+    Or, Lr = oracle.attention(w.q, w.k, w.v, w.mask, w.scale)
+    check_attn(o, l, Or, Lr, dtype, "fully padded sequence")
+    assert torch.all(o[1] == 0) and torch.all(torch.isneginf(l[1]))
+
+
+@pytest.mark.parametrize("amp", [4.0, 8.0])
+def test_fwd_peaky_scores(ma, amp):
+    """Large scores: exercises the lazy-rescale path (max grows by more than the threshold)."""
+    w = W.make_prefill(1, 2, 300, 700, 64, torch.bfloat16, valid=[650], amp=amp, seed=int(amp))
+    o, l = run_fwd(ma, w)
+    Or, Lr = oracle.attention(w.q, w.k, w.v, w.mask, w.scale)
+    # O tolerance scales with |V| = amp
+    to, tl = 2e-2 * amp, 1e-3 * amp * amp
+    assert np.max(np.abs(_np(o) - Or)) <= to
+    assert np.max(np.abs(l.cpu().double().numpy() - Lr)) <= tl
+
+
+def test_cfg1_fp32(ma):
+    w = W.cfg1_fp32_masked()
+    o, l = run_fwd(ma, w)
+    Or, Lr = oracle.attention(w.q, w.k, w.v, w.mask, w.scale)
+    check_attn(o, l, Or, Lr, torch.float32, "cfg1 fp32")
+
+
+def test_cfg2_patch_0p5mp(ma):
+    w = W.cfg2_patch_0p5mp()
+    o, l = run_fwd(ma, w)
+    Or, Lr = oracle.attention(w.q, w.k, w.v, w.mask, w.scale)
+    check_attn(o, l, Or, Lr, torch.bfloat16, "cfg2 bf16 P1944")
+
+
+def test_cfg3_patch_3mp_sampled_rows(ma):
+    """P = 11,616 at full size: sampled query rows of every head against the oracle."""
+    w = W.cfg3_patch_3mp()
+    o, l = run_fwd(ma, w)
+    assert not torch.isnan(o).any() and torch.isfinite(l).all()
+    g = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([g.choice(11616, 40, replace=False), [0, 255, 256, 11615, 11614]]))
+    Or, Lr = oracle.attention(w.q, w.k, w.v, w.mask, w.scale, rows=rows)
+    check_attn(o[:, :, rows], l[:, :, rows], Or, Lr, torch.bfloat16, "cfg3 sampled rows")
+
+
+# ---- merge ---------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("n", [1, 2, 3, 5])
+def test_merge_random_partials(ma, n, dtype):
+    g = torch.Generator().manual_seed(n)
+    B, H, T, D = 2, 3, 37, 128 if n % 2 else 64
+    outs = [torch.randn(B, H, T, D, generator=g).to(dtype) for _ in range(n)]
+    lses = [torch.randn(B, H, T, generator=g) * 3 for _ in range(n)]
+    lses[0][0, 0, 3] = -math.inf
+    for i in range(n):
+        lses[i][1, 2, 5] = -math.inf     # a row empty in every chunk
+    o, l = ma.attn_merge_lse([t.to(DEV) for t in outs], [t.to(DEV) for t in lses])
+    torch.cuda.synchronize()
+    Or, Lr = oracle.merge_lse(outs, lses)
+    check_attn(o, l, Or, Lr, dtype, f"merge n={n}")
+
+
+def test_cfg4_chunked_merge_equals_single_pass(ma):
+    """Two 8,192-key chunks via attn_fwd_lse + attn_merge_lse equal one call over 16,384 keys."""
+    w = W.cfg4_chunked()
+    q = w.q.to(DEV)
+    parts = [ma.attn_fwd_lse(q, kc.to(DEV), vc.to(DEV), None, w.scale) for kc, vc in zip(w.k_chunks, w.v_chunks)]
+    om, lm = ma.attn_merge_lse([p[0] for p in parts], [p[1] for p in parts])
+    k = torch.cat(w.k_chunks, dim=2).to(DEV)
+    v = torch.cat(w.v_chunks, dim=2).to(DEV)
+    of, lf = ma.attn_fwd_lse(q, k, v, None, w.scale)
+    torch.cuda.synchronize()
+    # merged vs single pass on the GPU (both bf16 outputs: two roundings apart)
+    assert (om.float() - of.float()).abs().max().item() <= 2e-2
+    assert (lm - lf).abs().max().item() <= 1e-3
+    # both vs the oracle on sampled rows
+    rows = np.array([0, 1, 4095, 4096, 8191, 1234, 7777])
+    Or, Lr = oracle.attention(w.q, torch.cat(w.k_chunks, 2), torch.cat(w.v_chunks, 2), None, w.scale, rows=rows)
+    check_attn(om[:, :, rows], lm[:, :, rows], Or, Lr, torch.bfloat16, "cfg4 merged")
+    check_attn(of[:, :, rows], lf[:, :, rows], Or, Lr, torch.bfloat16, "cfg4 single pass")
+
+
+# ---- append + decode -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_kv_append_bit_exact(ma, dtype):
+    w = W.make_decode(5, 4, 2, 64, 0, 30, dtype, T_max=32, seed=9,
+                      lens=[0, 7, 31, 32, 40])          # 32 and 40: full / over capacity
+    kc, vc = w.k_cache.to(DEV), w.v_cache.to(DEV)
+    lens = w.lens.to(DEV)
+    ma.kv_append(kc, vc, lens, w.k_new.to(DEV), w.v_new.to(DEV))
+    torch.cuda.synchronize()
+    ok = [0, 1, 2]
+    ek, ev, el = oracle.kv_append(w.k_cache[ok].float().numpy(), w.v_cache[ok].float().numpy(),
+                                  w.lens[ok].numpy(), w.k_new[ok].float().numpy(), w.v_new[ok].float().numpy())
+    assert torch.equal(kc[ok].cpu(), torch.from_numpy(ek).to(dtype))
+    assert torch.equal(vc[ok].cpu(), torch.from_numpy(ev).to(dtype))
+    assert lens.cpu().tolist() == el.tolist() + [32, 40]
+    # sequences at or past capacity are untouched
+    assert torch.equal(kc[3:].cpu(), w.k_cache[3:]) and torch.equal(vc[3:].cpu(), w.v_cache[3:])
+
+
+DEC_SHAPES = [
+    # B, Hq, Hkv, D, len_lo, len_hi, T_max
+    (3, 4, 4, 64, 1, 40, 64),
+    (4, 8, 2, 128, 1, 1500, 1536),
+    (2, 32, 8, 128, 500, 1100, 1152),
+    (3, 6, 2, 64, 0, 600, 640),
+    (2, 16, 2, 128, 1, 700, 768),
+    (2, 3, 1, 128, 510, 514, 576),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shape", DEC_SHAPES)
+def test_append_then_decode(ma, shape, dtype):
+    B, Hq, Hkv, D, lo, hi, Tm = shape
+    w = W.make_decode(B, Hq, Hkv, D, lo, hi, dtype, T_max=Tm, seed=B * 100 + Hq)
+    kc, vc, lens = w.k_cache.to(DEV), w.v_cache.to(DEV), w.lens.to(DEV)
+    ma.kv_append(kc, vc, lens, w.k_new.to(DEV), w.v_new.to(DEV))
+    o, l = ma.attn_decode(w.q.to(DEV), kc, vc, lens, w.scale, want_lse=True)
+    torch.cuda.synchronize()
+    ek, ev, el = oracle.kv_append(w.k_cache.float().numpy(), w.v_cache.float().numpy(), w.lens.numpy(),
+                                  w.k_new.float().numpy(), w.v_new.float().numpy())
+    Or, Lr = oracle.decode(w.q, ek, ev, el, w.scale)
+    check_attn(o, l, Or, Lr, dtype, f"decode {shape}")
+
+
+def test_decode_zero_length(ma):
+    w = W.make_decode(2, 4, 2, 128, 0, 10, torch.bfloat16, T_max=64, lens=[0, 9], seed=1)
+    o, l = ma.attn_decode(w.q.to(DEV), w.k_cache.to(DEV), w.v_cache.to(DEV), w.lens.to(DEV), w.scale,
+                          want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(l[0]))
+    Or, Lr = oracle.decode(w.q[1:], w.k_cache[1:], w.v_cache[1:], w.lens[1:], w.scale)
+    check_attn(o[1:], l[1:], Or, Lr, torch.bfloat16, "decode len 0 / 9")
+
+
+def test_cfg5_decode_sampled_heads(ma):
+    """Full decode workload (B32, 32/8 heads, len U[512, 8192] + 1) on sampled (b, h)."""
+    w = W.cfg5_decode()
+    kc, vc, lens = w.k_cache.to(DEV), w.v_cache.to(DEV), w.lens.to(DEV)
+    ma.kv_append(kc, vc, lens, w.k_new.to(DEV), w.v_new.to(DEV))
+    o, l = ma.attn_decode(w.q.to(DEV), kc, vc, lens, w.scale, want_lse=True)
+    torch.cuda.synchronize()
+    assert lens.cpu().tolist() == (w.lens + 1).tolist()
+    g = np.random.default_rng(5)
+    heads = [(int(b), int(h)) for b, h in zip(g.integers(0, 32, 24), g.integers(0, 32, 24))]
+    heads += [(int(np.argmax(w.lens)), 0), (int(np.argmin(w.lens)), 31)]
+    kc_h, vc_h = kc.cpu(), vc.cpu()
+    Or, Lr = oracle.decode(w.q, kc_h, vc_h, lens.cpu().numpy(), w.scale, heads=heads)
+    got_o = torch.stack([o[b, h, 0] for b, h in heads])
+    got_l = torch.stack([l[b, h] for b, h in heads])
+    check_attn(got_o, got_l, Or, Lr, torch.bfloat16, "cfg5 sampled heads")
