@@ -1,0 +1,270 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step runs every stage of the path once on seeded synthetic inputs that
+are already resident in device memory:
+  1. masked prefill with LSE, bf16, B1 H16 P11,616 D64, last 16 keys padded
+     (attn_fwd_lse; the ~3 MP patch self-attention case),
+  2. chunked-KV attention: Q 8,192 x H24 x D128 against two 8,192-key
+     chunks (2 x attn_fwd_lse) and their LSE merge (attn_merge_lse),
+  3. one decode step: kv_append + attn_decode, bf16 GQA B32, 32 query / 8 KV
+     heads, D128, cached lengths U[512, 8192] (then +1 appended).
+The cache lengths are restored before every step so each step is the same
+workload.
+
+The headline value is the prefill's algorithmic throughput (4·D·H·Tq·n_valid
+FLOP over the prefill call's duration, from HIP events on the launch stream
+over the timed steps); the decode's algorithmic HBM rate (K and V bytes of
+every cached token, plus q and o, over the attn_decode duration) and the
+merge's rate are reported beside it.  `cpu_baseline` times the float64 CPU
+oracle on a bounded sample of the prefill workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E (published)
+PREFILL_SRCS = [os.path.join(ROOT, "masked_attention_attn_amd", "csrc", f)
+                for f in ("fwd_bf16.cuh", "fwd_bf16_d64.hip")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_p11616_traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="approximate CPU time budget of the oracle baseline")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run 3 plain device-to-device copies of MIB MiB (reference kernel "
+                        "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    return p.parse_args()
+
+
+def calibrate_copy(mib):
+    import torch
+    n = mib * 2**20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": n, "copies": 3}))
+
+
+def src_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the prefill kernel from the committed rocprofv3 PMC
+    summary, or None if it is missing or was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != src_hash(PREFILL_SRCS):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s):
+    """Time the float64 oracle on whole heads of the prefill workload until the
+    time budget is used (at least one head)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else os.cpu_count()
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    B, H, Tq, D = w.q.shape
+    n_valid = int((w.mask[0] == 0).sum())
+    heads, t0 = 0, time.perf_counter()
+    while heads < H:
+        oracle.attention(w.q[:, heads:heads + 1], w.k[:, heads:heads + 1], w.v[:, heads:heads + 1],
+                         w.mask, w.scale)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = oracle.attention_flops(heads, D, Tq, [n_valid])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} of {H} heads of the P=11,616 prefill (all {Tq} query rows each), "
+                      f"float64 NumPy with the full masked softmax per head; {dt:.1f} s",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import masked_attention_attn_amd as ma
+    import workloads as W
+
+    if not os.path.exists(ma.LIB_PATH):
+        raise SystemExit(f"{ma.LIB_PATH} is not built: run python __graft_entry__.py first")
+    ma.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs (host generation, then resident on the device)
+    pf = W.patch_p11616()
+    ch = W.chunked_kv_2x8192()
+    dc = W.gqa_decode_b32()
+    q3, k3, v3, m3 = (t.to(dev) for t in (pf.q, pf.k, pf.v, pf.mask))
+    o3 = torch.empty_like(q3)
+    l3 = torch.empty(q3.shape[:3], dtype=torch.float32, device=dev)
+    q4 = ch.q.to(dev)
+    k4 = [t.to(dev) for t in ch.k_chunks]
+    v4 = [t.to(dev) for t in ch.v_chunks]
+    o4 = [torch.empty_like(q4) for _ in range(2)]
+    l4 = [torch.empty(q4.shape[:3], dtype=torch.float32, device=dev) for _ in range(2)]
+    om4 = torch.empty_like(q4)
+    lm4 = torch.empty(q4.shape[:3], dtype=torch.float32, device=dev)
+    kc, vc = dc.k_cache.to(dev), dc.v_cache.to(dev)
+    kn, vn, q5 = dc.k_new.to(dev), dc.v_new.to(dev), dc.q.to(dev)
+    lens0 = dc.lens.to(dev)
+    lens = lens0.clone()
+    o5 = torch.empty_like(q5)
+    l5 = torch.empty(q5.shape[:2], dtype=torch.float32, device=dev)
+    B5, Hq5, _, D5 = q5.shape
+    Hkv5, Tmax5 = kc.shape[1], kc.shape[2]
+    ws = torch.empty(ma.attn_decode_workspace_bytes(B5, Hq5, Hkv5, Tmax5, D5), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    n_ev = 6
+
+    def step(ev=None):
+        lens.copy_(lens0)
+        if ev: ev[0].record(stream)
+        ma.attn_fwd_lse(q3, k3, v3, m3, pf.scale, out=o3, lse=l3)
+        if ev: ev[1].record(stream)
+        for i in range(2):
+            ma.attn_fwd_lse(q4, k4[i], v4[i], None, ch.scale, out=o4[i], lse=l4[i])
+        if ev: ev[2].record(stream)
+        ma.attn_merge_lse(o4, l4, out=om4, lse_out=lm4)
+        if ev: ev[3].record(stream)
+        ma.kv_append(kc, vc, lens, kn, vn)
+        if ev: ev[4].record(stream)
+        ma.attn_decode(q5, kc, vc, lens, dc.scale, out=o5, lse=l5, workspace=ws, want_lse=True)
+        if ev: ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()       # with W >= 1, code objects are loaded before free memory is read
+    free_before = torch.cuda.mem_get_info()[0]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    free_after = torch.cuda.mem_get_info()[0]
+
+    def span(a, b):
+        return sum(events[s][a].elapsed_time(events[s][b]) for s in range(args.steps)) / args.steps / 1e3
+
+    t_prefill, t_chunks, t_merge, t_append, t_decode = (span(0, 1), span(1, 2), span(2, 3), span(3, 4),
+                                                        span(4, 5))
+    # ---- algorithmic work
+    B, H, P, D = pf.q.shape
+    n_valid = int((pf.mask[0] == 0).sum())
+    flop_prefill = 4 * D * H * P * n_valid
+    tf_prefill = flop_prefill / t_prefill / 1e12
+    Hc, Tqc, Dc = ch.q.shape[1], ch.q.shape[2], ch.q.shape[3]
+    flop_chunks = 2 * 4 * Dc * Hc * Tqc * ch.k_chunks[0].shape[2]
+    merge_bytes = (2 * (om4.numel() * 2 + lm4.numel() * 4)) + om4.numel() * 2 + lm4.numel() * 4
+    lens_after = dc.lens.long() + 1
+    kv_bytes = int(lens_after.sum().item()) * 2 * Hkv5 * D5 * 2
+    decode_bytes = kv_bytes + q5.numel() * 2 + o5.numel() * 2
+    decode_gbps = decode_bytes / t_decode / 1e9
+    traffic = measured_traffic()
+
+    prefill_extra = o3.numel() * o3.element_size() + l3.numel() * 4
+    out = {
+        "metric": "masked attn prefill TFLOP/s @P=11,616 (frac MFMA peak); decode HBM GB/s",
+        "value": round(tf_prefill, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs in the shapes the pages measure)",
+        "config": {
+            "workload": "masked patch self-attention prefill with LSE, bf16, B1 H16 P11616 D64, "
+                        "last 16 keys padded, inputs N(0,1)*0.5",
+            "B": B, "H": H, "P": P, "D": D, "n_valid_keys": n_valid,
+            "also_in_step": ["chunked KV: Q 8192 x H24 x D128 vs 2 x 8192 keys + LSE merge",
+                             "decode: kv_append + attn_decode, B32 Hq32 Hkv8 D128, len U[512,8192]+1"],
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": "fwd_bf16_kernel<64, LSE>",
+            "achieved": round(tf_prefill, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf_prefill / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+            "algorithmic_flop_per_launch": flop_prefill, "avg_launch_us": round(t_prefill * 1e6, 2),
+        },
+        "decode": {
+            "metric": "decode HBM GB/s", "value": round(decode_gbps, 1), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(decode_gbps, 1), "peak": PEAK_HBM_GBPS,
+                         "unit": "GB/s", "frac": round(decode_gbps / PEAK_HBM_GBPS, 4),
+                         "algorithmic_bytes_per_launch": decode_bytes},
+            "attn_decode_us": round(t_decode * 1e6, 2), "kv_append_us": round(t_append * 1e6, 2),
+            "cached_tokens": int(lens_after.sum().item()),
+        },
+        "chunked": {
+            "fwd_lse_x2_us": round(t_chunks * 1e6, 2),
+            "tflops": round(flop_chunks / t_chunks / 1e12, 2),
+            "frac_mfma": round(flop_chunks / t_chunks / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "merge_us": round(t_merge * 1e6, 2),
+            "merge_gbps": round(merge_bytes / t_merge / 1e9, 1),
+        },
+        "memory": {
+            "library_device_allocations_bytes": int(free_before - free_after),
+            "prefill_call_extra_bytes": int(prefill_extra),
+            "prefill_call_extra_GB": round(prefill_extra / 1e9, 4),
+            "avoided_score_matrix_bytes": H * P * P * 2,
+            "decode_workspace_bytes": int(ws.numel()),
+        },
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(pf, args.cpu_seconds)
+        cb.pop("seconds", None)
+        out["cpu_baseline"] = cb
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -26,32 +26,45 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
+# Per-source extras for the bf16 prefill kernels:
+#  * -fno-honor-nans: the kernels produce no NaN (infinities are still honoured,
+#    -inf marks padded keys), which lets fmaxf lower to v_max3_f32 on raw MFMA
+#    results instead of canonicalise-then-max.
+#  * VGPR-form MFMAs at D = 64 keep the score blocks in VGPRs for the vector
+#    unit (no AGPR<->VGPR copies).
+EXTRA = {
+    "fwd_bf16_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fwd_bf16_d128.hip": ["-fno-honor-nans"],
+}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, include_first=None) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src).replace(".hip", ".o"))
+    inc = ["-I", include_first] if include_first else []
+    cmd = [HIPCC, *inc, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+def build(verbose: bool = True, out: str = LIB, build_dir: str = BUILD, csrc: str = CSRC) -> str:
+    """Compile csrc/*.hip into `out` (default: the in-tree library)."""
+    os.makedirs(build_dir, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(csrc, "*.hip")))
+
     workers = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda f: _compile(f, build_dir), srcs))
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
-    return LIB
+        print(f"built {out} from {len(srcs)} sources")
+    return out
 
 
 if __name__ == "__main__":

@@ -5,7 +5,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/attn.h"
+#include "attn.h"
 #include "launch.h"
 
 using namespace mattn;
@@ -41,8 +41,11 @@ int fwd_common(const void* q, const void* k, const void* v, const uint8_t* mask,
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
     if (o == k || o == v || (lse && ((void*)lse == q || (void*)lse == k || (void*)lse == v || (void*)lse == o)))
         return ATTN_ERR_ALIAS;
+    // the bf16 kernel addresses one head's K/V through a 32-bit buffer range
+    if (dtype == ATTN_BF16 && (long long)Tk * D * 2 > (1ll << 31) - 1) return ATTN_ERR_SHAPE;
     FwdArgs a{q, k, v, mask, o, lse, B, H, Tq, Tk, D, scale, stream};
-    return finish(dtype == ATTN_BF16 ? launch_fwd_bf16(a) : launch_fwd_f32(a));
+    if (dtype == ATTN_F32) return finish(launch_fwd_f32(a));
+    return finish(D == 64 ? launch_fwd_bf16_d64(a) : launch_fwd_bf16_d128(a));
 }
 
 }  // namespace

@@ -46,7 +46,8 @@ struct DecodeArgs {
     void* stream;
 };
 
-hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_bf16_d64(const FwdArgs& a);
+hipError_t launch_fwd_bf16_d128(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_merge_bf16(const MergeArgs& a);
 hipError_t launch_merge_f32(const MergeArgs& a);

@@ -291,12 +291,12 @@ def test_decode_equals_full_attention_over_cache_prefix():
 
 # ---- library cross-check ---------------------------------------------------------------
 
-def test_oracle_matches_torch_sdpa_on_cfg1():
+def test_oracle_matches_torch_sdpa_on_fp32_t512():
     """The pages compare the materialising MHA path against SDPA on the CPU and see
     them agree to ~5e-8 in fp32; the oracle must agree with SDPA (additive -inf
     mask) the same way.  Passing the key-padding mask as SDPA's boolean mask
     unconverted must give a large error."""
-    w = workloads.cfg1_fp32_masked()
+    w = workloads.fp32_masked_t512()
     O, L = oracle.attention(w.q, w.k, w.v, w.mask, w.scale)
     add = torch.zeros(1, 1, 1, 512)
     add[..., w.mask[0].bool()] = float("-inf")

@@ -127,29 +127,29 @@ def test_fwd_peaky_scores(ma, amp):
     assert np.max(np.abs(l.cpu().double().numpy() - Lr)) <= tl
 
 
-def test_cfg1_fp32(ma):
-    w = W.cfg1_fp32_masked()
+def test_fp32_masked_t512(ma):
+    w = W.fp32_masked_t512()
     o, l = run_fwd(ma, w)
     Or, Lr = oracle.attention(w.q, w.k, w.v, w.mask, w.scale)
-    check_attn(o, l, Or, Lr, torch.float32, "cfg1 fp32")
+    check_attn(o, l, Or, Lr, torch.float32, "fp32 T512")
 
 
-def test_cfg2_patch_0p5mp(ma):
-    w = W.cfg2_patch_0p5mp()
+def test_patch_p1944(ma):
+    w = W.patch_p1944()
     o, l = run_fwd(ma, w)
     Or, Lr = oracle.attention(w.q, w.k, w.v, w.mask, w.scale)
-    check_attn(o, l, Or, Lr, torch.bfloat16, "cfg2 bf16 P1944")
+    check_attn(o, l, Or, Lr, torch.bfloat16, "bf16 P1944")
 
 
-def test_cfg3_patch_3mp_sampled_rows(ma):
+def test_patch_p11616_sampled_rows(ma):
     """P = 11,616 at full size: sampled query rows of every head against the oracle."""
-    w = W.cfg3_patch_3mp()
+    w = W.patch_p11616()
     o, l = run_fwd(ma, w)
     assert not torch.isnan(o).any() and torch.isfinite(l).all()
     g = np.random.default_rng(0)
     rows = np.unique(np.concatenate([g.choice(11616, 40, replace=False), [0, 255, 256, 11615, 11614]]))
     Or, Lr = oracle.attention(w.q, w.k, w.v, w.mask, w.scale, rows=rows)
-    check_attn(o[:, :, rows], l[:, :, rows], Or, Lr, torch.bfloat16, "cfg3 sampled rows")
+    check_attn(o[:, :, rows], l[:, :, rows], Or, Lr, torch.bfloat16, "P11616 sampled rows")
 
 
 # ---- merge ---------------------------------------------------------------------------------
@@ -170,9 +170,9 @@ def test_merge_random_partials(ma, n, dtype):
     check_attn(o, l, Or, Lr, dtype, f"merge n={n}")
 
 
-def test_cfg4_chunked_merge_equals_single_pass(ma):
+def test_chunked_kv_2x8192_merge_equals_single_pass(ma):
     """Two 8,192-key chunks via attn_fwd_lse + attn_merge_lse equal one call over 16,384 keys."""
-    w = W.cfg4_chunked()
+    w = W.chunked_kv_2x8192()
     q = w.q.to(DEV)
     parts = [ma.attn_fwd_lse(q, kc.to(DEV), vc.to(DEV), None, w.scale) for kc, vc in zip(w.k_chunks, w.v_chunks)]
     om, lm = ma.attn_merge_lse([p[0] for p in parts], [p[1] for p in parts])
@@ -186,8 +186,8 @@ def test_cfg4_chunked_merge_equals_single_pass(ma):
     # both vs the oracle on sampled rows
     rows = np.array([0, 1, 4095, 4096, 8191, 1234, 7777])
     Or, Lr = oracle.attention(w.q, torch.cat(w.k_chunks, 2), torch.cat(w.v_chunks, 2), None, w.scale, rows=rows)
-    check_attn(om[:, :, rows], lm[:, :, rows], Or, Lr, torch.bfloat16, "cfg4 merged")
-    check_attn(of[:, :, rows], lf[:, :, rows], Or, Lr, torch.bfloat16, "cfg4 single pass")
+    check_attn(om[:, :, rows], lm[:, :, rows], Or, Lr, torch.bfloat16, "chunked merged")
+    check_attn(of[:, :, rows], lf[:, :, rows], Or, Lr, torch.bfloat16, "chunked single pass")
 
 
 # ---- append + decode -------------------------------------------------------------------------
@@ -246,9 +246,9 @@ def test_decode_zero_length(ma):
     check_attn(o[1:], l[1:], Or, Lr, torch.bfloat16, "decode len 0 / 9")
 
 
-def test_cfg5_decode_sampled_heads(ma):
+def test_gqa_decode_b32_sampled_heads(ma):
     """Full decode workload (B32, 32/8 heads, len U[512, 8192] + 1) on sampled (b, h)."""
-    w = W.cfg5_decode()
+    w = W.gqa_decode_b32()
     kc, vc, lens = w.k_cache.to(DEV), w.v_cache.to(DEV), w.lens.to(DEV)
     ma.kv_append(kc, vc, lens, w.k_new.to(DEV), w.v_new.to(DEV))
     o, l = ma.attn_decode(w.q.to(DEV), kc, vc, lens, w.scale, want_lse=True)
@@ -261,4 +261,4 @@ def test_cfg5_decode_sampled_heads(ma):
     Or, Lr = oracle.decode(w.q, kc_h, vc_h, lens.cpu().numpy(), w.scale, heads=heads)
     got_o = torch.stack([o[b, h, 0] for b, h in heads])
     got_l = torch.stack([l[b, h] for b, h in heads])
-    check_attn(got_o, got_l, Or, Lr, torch.bfloat16, "cfg5 sampled heads")
+    check_attn(got_o, got_l, Or, Lr, torch.bfloat16, "decode sampled heads")

@@ -38,8 +38,8 @@ __all__ = [
     "Prefill", "Chunked", "Decode",
     "make_prefill", "make_chunked", "make_decode",
     "mask_from_valid_lengths", "round_up",
-    "cfg1_fp32_masked", "cfg2_patch_0p5mp", "cfg3_patch_3mp",
-    "cfg4_chunked", "cfg5_decode",
+    "fp32_masked_t512", "patch_p1944", "patch_p11616",
+    "chunked_kv_2x8192", "gqa_decode_b32",
 ]
 
 
@@ -161,31 +161,31 @@ def make_decode(B, H_q, H_kv, D, len_lo, len_hi, dtype=torch.bfloat16, *, T_max=
 
 # ---- the five named workloads -------------------------------------------------
 
-def cfg1_fp32_masked(seed=0) -> Prefill:
+def fp32_masked_t512(seed=0) -> Prefill:
     """fp32, B1 H16 T512 D64, last 48 keys padded, scale 1/sqrt(64)."""
     return make_prefill(1, 16, 512, 512, 64, torch.float32, valid=[512 - 48], seed=seed,
                         name="fp32 masked self-attention B1 H16 T512 D64, 48 padded keys")
 
 
-def cfg2_patch_0p5mp(seed=0) -> Prefill:
+def patch_p1944(seed=0) -> Prefill:
     """bf16, B2 H16 P1944 D64, valid lengths 1,944 and 1,700."""
     return make_prefill(2, 16, 1944, 1944, 64, torch.bfloat16, valid=[1944, 1700], seed=seed,
                         name="bf16 patch self-attention B2 H16 P1944 D64, valid 1944/1700")
 
 
-def cfg3_patch_3mp(seed=0) -> Prefill:
+def patch_p11616(seed=0) -> Prefill:
     """bf16, B1 H16 P11616 D64, last 16 keys padded, inputs N(0,1)*0.5."""
     return make_prefill(1, 16, 11616, 11616, 64, torch.bfloat16, valid=[11616 - 16], amp=0.5,
                         seed=seed, name="bf16 patch self-attention B1 H16 P11616 D64, 16 padded keys")
 
 
-def cfg4_chunked(seed=0) -> Chunked:
+def chunked_kv_2x8192(seed=0) -> Chunked:
     """bf16, Q T8192 H24 D128 against 2 KV chunks of 8,192 keys, no mask."""
     return make_chunked(1, 24, 8192, [8192, 8192], 128, torch.bfloat16, seed=seed,
                         name="bf16 chunked KV B1 H24 Tq8192 D128, 2x8192 keys + LSE merge")
 
 
-def cfg5_decode(seed=0) -> Decode:
+def gqa_decode_b32(seed=0) -> Decode:
     """bf16 GQA decode: B32, H_q 32 / H_kv 8, D128, cached len ~ U{512..8192}."""
     return make_decode(32, 32, 8, 128, 512, 8192, torch.bfloat16, seed=seed,
                        name="bf16 GQA decode B32 Hq32 Hkv8 D128, len U[512,8192] + 1 appended")
