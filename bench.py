@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--settle", type=float, default=0.5,
+                   help="seconds of untimed steps before the warm-up (clock ramp)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline")
@@ -178,6 +180,16 @@ def main():
         ma.attn_decode(q5, kc, vc, lens, dc.scale, out=o5, lse=l5, workspace=ws, want_lse=True)
         if ev: ev[5].record(stream)
 
+    # The GPU clocks ramp up over the first ~30 ms of continuous work and drop
+    # again after idling; run untimed steps for --settle seconds first so the
+    # timed steps see the steady-state clock.
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t_settle < args.settle:
+        step()
+        n_settle += 1
+        if n_settle % 4 == 0:
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
@@ -217,6 +229,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": {"seconds": args.settle, "untimed_steps": n_settle},
         "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",

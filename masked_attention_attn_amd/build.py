@@ -33,7 +33,7 @@ FLAGS = [
 #  * VGPR-form MFMAs at D = 64 keep the score blocks in VGPRs for the vector
 #    unit (no AGPR<->VGPR copies).
 EXTRA = {
-    "fwd_bf16_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fwd_bf16_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
     "fwd_bf16_d128.hip": ["-fno-honor-nans"],
 }
 

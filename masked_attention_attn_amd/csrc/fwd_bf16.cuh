@@ -27,25 +27,41 @@
 //   the eight P values a lane needs as one B operand of the second product
 //   are eight consecutive accumulator elements of the first.
 //
+// LDS tiles are filled by direct global->LDS buffer loads (no staging
+// registers): lane i of a load writes bytes [16i, 16i+16) of a 1 KiB chunk,
+// so each lane picks the global 16 bytes that belong there.  Both tiles are
+// unpadded with an XOR swizzle of the 16-byte chunk index: K chunk c of row r
+// sits at c ^ (r & 7) (conflict-free 16-byte row reads); V keeps its natural
+// [key][d] layout with chunk c of row r at c ^ 2(r & 3), and the Vᵀ operand
+// is read with the gfx950 transposing LDS read (ds_read_b64_tr_b16: within
+// each 16-lane group, lane j receives element j%4 of the 8-byte rows
+// addressed by lanes j/4 + 4k), which the swizzle keeps conflict-free.
+//
 // Software pipeline.  Step u holds the raw scores S_u of key block u in
 // registers (computed by step u-1) and, in one straight block of code whose
 // issue order is fixed slot by slot, turns S_u into P_u while issuing the
 // matrix-core work S_{u+1} = K_{u+1}·Qᵀ and O += V_uᵀ·P_u: the exp / convert
-// / sum vector work of one block overlaps the MFMAs of two.  K tiles live in
-// a ring of three LDS buffers (the pipeline reads tile T+1 while tile T+2 is
-// being stored), V tiles in a ring of three (a deferred PV reads the previous
-// tile); global loads go through buffer
-// resources whose range check returns zeros past Tk, so no lane branches.
-// Padding (a rare, workgroup-uniform case) and the lazy rescale are handled
-// before the fixed block, so the common path has no per-element masking.
-// Leading and trailing fully padded key blocks are never visited: the
-// workgroup first finds its sequence's first and last unpadded keys.
+// / sum vector work of one block overlaps the MFMAs of two.  The K operands
+// of S_{u+1} are read from LDS during step u-1.  K tiles live in a ring of
+// three LDS buffers (tile T+1 is readable during tile T while tile T+2 is
+// being stored), V tiles in a ring of two; the buffer resources' range check
+// returns zeros past Tk, so no lane branches.
+// Padding (a rare, workgroup-uniform case) is applied before the fixed block,
+// so the common path has no per-element masking.  One pass over the mask
+// finds the sequence's first and last unpadded keys and whether any padded
+// key lies between them: leading and trailing fully padded key blocks are
+// never visited, and without interior holes the mask of every visited block
+// follows from the two indices, with no mask reads in the loop.
 //
-// Online softmax with lazy rescaling: the running max m of a row is only
-// moved (and O, l rescaled) when a block raises the max by more than TAU in
-// log2 units; otherwise the stale max is kept, which bounds every weight by
-// 2^TAU.  Final O = acc / l and LSE = (m·c + log2 l)·ln 2 are exact for any
-// reference max, so this changes rounding only.
+// Online softmax with a lazily raised reference: weights are 2^(S·c - mc)
+// with mc set once from the exact row max of the first block that holds an
+// unpadded key.  The common path computes no row max at all: after each
+// 16-key chunk is exponentiated, its per-lane weight sum is compared with
+// 2^TAU, and only if some lane exceeds it (the scores rose well above the
+// reference) is mc raised to the chunk's row max, O and l scaled by
+// 2^(old - new) and the chunk redone.  Every weight used is therefore at most
+// 2^TAU.  Final O = acc / l and LSE = (mc + log2 l)·ln 2 are exact for any
+// reference, so this changes rounding only.
 #pragma once
 
 #include "common.cuh"
@@ -56,12 +72,12 @@ namespace fwdk {
 
 constexpr int NWAVE = 4;
 constexpr int NT = 64 * NWAVE;  // threads per workgroup
-constexpr int PAD = 8;          // bf16 elements of row padding in LDS
 constexpr int CK = 32;          // keys per compute step
 constexpr int NB = 2;           // 32-query column blocks per wave
 constexpr int QW = NB * 32;     // queries per wave
 constexpr int BM = QW * NWAVE;  // queries per workgroup
 constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
+constexpr float kRescaleSum = 256.0f;   // 2^TAU: a lane's chunk sum above this forces a rescale
 
 template <int D> struct Tile;
 template <> struct Tile<64> { static constexpr int TK = 64; };
@@ -70,11 +86,10 @@ template <> struct Tile<128> { static constexpr int TK = 32; };
 template <int D>
 struct Lds {
     static constexpr int TK = Tile<D>::TK;
-    static constexpr int KS = D + PAD;    // K tile row stride (elements), [key][d]
-    static constexpr int VS = TK + PAD;   // Vᵀ tile row stride (elements), [d][key]
-    static constexpr int K_TILE = TK * KS;
-    static constexpr int V_TILE = D * VS;
-    static constexpr int K_RING = 3, V_RING = 3;
+    static constexpr int RB = D * 2;      // bytes per K or V row (unpadded, swizzled)
+    static constexpr int K_TILE = TK * D; // elements
+    static constexpr int V_TILE = TK * D;
+    static constexpr int K_RING = 3, V_RING = 2;
     static constexpr int ELEMS = K_RING * K_TILE + V_RING * V_TILE;
     static constexpr int BYTES = ELEMS * (int)sizeof(bf16);
 };
@@ -96,12 +111,44 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Raw buffer over `bytes` bytes at p: loads at offsets >= bytes return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+// Buffer descriptor over `bytes` bytes at p (gfx9 layout: base, stride 0,
+// num_records = bytes, raw dword format): loads at offsets >= bytes return zero.
+typedef int i32x4_sgpr __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_sgpr make_rsrc(const void* p, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    i32x4_sgpr r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
 }
-__device__ __forceinline__ u32x4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+// 16 bytes per lane from a buffer straight into LDS at lds_base + 16*lane.
+// Written as inline assembly on purpose: the compiler cannot tell these LDS
+// writes apart from the operand reads of other ring slots and would put a
+// wait for every outstanding global load in front of the next LDS read.  The
+// kernel orders them itself (wait_vmem + barrier at the end of each tile);
+// loads the compiler does not see only make its own vmcnt waits stricter.
+__device__ __forceinline__ void dma16(i32x4_sgpr r, unsigned char* lds_base, uint32_t voff, uint32_t soff) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)lds_base));
+    uint32_t saved;     // M0 is restored, so the compiler's view of it stays valid
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
+                 "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(m0), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
+                 : "memory");
+}
+// Wait for this wave's outstanding global loads (including LDS-direct ones).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+typedef __bf16 bf16x4_lds __attribute__((ext_vector_type(4)));
+// Transposing 8-byte LDS read (see the layout note above).
+__device__ __forceinline__ u32x2 ds_read_tr(const bf16* p) {
+    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf;
+    const v4bf r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) v4bf*)(const_cast<bf16*>(p)));
+    return __builtin_bit_cast(u32x2, r);
 }
 
 template <int D, bool WRITE_LSE>
@@ -120,7 +167,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     bf16* smem = reinterpret_cast<bf16*>(smem_raw);
-    __shared__ int red_s[NWAVE];
+    __shared__ int red_s[3 * NWAVE];
 
     const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
     if (logical >= total) return;
@@ -130,8 +177,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const bf16* qp = q + (size_t)bh * Tq * D;
     const uint8_t* mp = mask ? mask + (size_t)b * Tk : nullptr;
     const uint32_t kv_bytes = (uint32_t)Tk * D * (uint32_t)sizeof(bf16);
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + (size_t)bh * Tk * D, kv_bytes);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + (size_t)bh * Tk * D, kv_bytes);
+    const i32x4_sgpr krs = make_rsrc(k + (size_t)bh * Tk * D, kv_bytes);
+    const i32x4_sgpr vrs = make_rsrc(v + (size_t)bh * Tk * D, kv_bytes);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -140,29 +187,56 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int l32 = lane & 31;
     const int q0 = qt * BM + wave * QW;
 
-    // ---- first and last unpadded key of this sequence (workgroup-wide scans)
-    int first = 0, last = Tk - 1;
+    // ---- one pass over this sequence's mask: first and last unpadded key, and
+    // whether a padded key lies strictly between them (an interior hole).  Without
+    // holes the only padded keys a visited block can hold lie outside
+    // [first, last], so the per-block masks follow from the two indices alone.
+    int first = 0, last = Tk - 1, holes = 0;
     if (mp) {
-        last = -1;
-        for (int base = Tk - 1; base >= 0; base -= NT) {       // backwards, NT keys per round
-            const int key = base - tid;
-            const uint64_t bal = __ballot(key >= 0 && mp[key] == 0);
-            if (lane == 0) red_s[wave] = bal ? base - (wave * 64 + __builtin_ctzll(bal)) : -1;
-            __syncthreads();
-            last = max(max(red_s[0], red_s[1]), max(red_s[2], red_s[3]));
-            __syncthreads();
-            if (last >= 0) break;
+        int f = 0x7fffffff, l = -1, n = 0;
+        for (int base = tid * 16; base < Tk; base += NT * 16) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int key = base + j;
+                if (key < Tk && mp[key] == 0) {
+                    f = min(f, key);
+                    l = max(l, key);
+                    ++n;
+                }
+            }
         }
-        first = last + 1;
-        for (int base = 0; base <= last; base += NT) {           // forwards
-            const int key = base + tid;
-            const uint64_t bal = __ballot(key <= last && mp[key] == 0);
-            if (lane == 0) red_s[wave] = bal ? base + wave * 64 + __builtin_ctzll(bal) : 0x7fffffff;
-            __syncthreads();
-            first = min(min(red_s[0], red_s[1]), min(red_s[2], red_s[3]));
-            __syncthreads();
-            if (first <= last) break;
+#pragma unroll
+        for (int sh = 32; sh >= 1; sh >>= 1) {
+            f = min(f, __shfl_xor(f, sh));
+            l = max(l, __shfl_xor(l, sh));
+            n += __shfl_xor(n, sh);
         }
+        if (lane == 0) {
+            red_s[wave] = f;
+            red_s[NWAVE + wave] = l;
+            red_s[2 * NWAVE + wave] = n;
+        }
+        __syncthreads();
+        f = red_s[0];
+        l = red_s[NWAVE];
+        n = red_s[2 * NWAVE];
+#pragma unroll
+        for (int w = 1; w < NWAVE; ++w) {
+            f = min(f, red_s[w]);
+            l = max(l, red_s[NWAVE + w]);
+            n += red_s[2 * NWAVE + w];
+        }
+        if (n == 0) {
+            first = 0;
+            last = -1;
+        } else {
+            first = f;
+            last = l;
+            holes = n != l - f + 1;
+        }
+        first = __builtin_amdgcn_readfirstlane(first);
+        last = __builtin_amdgcn_readfirstlane(last);
+        holes = __builtin_amdgcn_readfirstlane(holes);
     }
     // Visited key blocks: [u_first, u_last] in units of CK keys; LDS tiles of TK keys.
     const int t_first = first / TK;
@@ -182,67 +256,52 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             qreg[nb][kk] = as_bf16x8(ldg128(qp + (size_t)row * D + kk * 16 + hl * 8));
     }
 
-    // ---- cooperative tile loads: K as 16-byte row chunks; V as key pairs so the
-    // transposed LDS tile is written one 32-bit (two-key) word at a time.  Keys
-    // past Tk read as zeros (buffer range check; they are masked).
-    constexpr int KCH = D / 8;
-    constexpr int K_LOADS = TK * KCH / NT;
-    constexpr int V_TASKS_ALL = (TK / 2) * KCH;
-    constexpr int V_TASKS = (V_TASKS_ALL + NT - 1) / NT;
-    static_assert(K_LOADS * NT == TK * KCH, "tile split");
-    u32x4 kr[K_LOADS];
-    u32x4 vr[V_TASKS][2];
-    uint32_t k_voff[K_LOADS], v_voff[V_TASKS];
+    // ---- tile loads straight into LDS: a tile is 8 KiB = 8 chunks of 1 KiB, wave w
+    // fills chunks 2w, 2w+1.  For LDS byte o of a tile (row r = o / RB, chunk
+    // position p), K takes key perm(r) (bits 2,3 swapped within 32-row blocks),
+    // chunk p ^ (r & 7); V takes key r, chunk p ^ 2(r & 3).  Keys past Tk read
+    // as zeros (buffer range check; they are masked).
+    static_assert(TK * D * 2 == 8192, "8 KiB tiles");
+    uint32_t k_voff[2], v_voff[2];
 #pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-        const int cidx = tid + i * NT;
-        k_voff[i] = (uint32_t)((cidx / KCH) * D + (cidx % KCH) * 8) * 2u;
+    for (int i = 0; i < 2; ++i) {
+        const int o = (2 * wave + i) * 1024 + lane * 16;
+        const int r = o / L::RB, pch = (o % L::RB) / 16;
+        const int kr = (r & ~31) | swap_bits23(r & 31);
+        k_voff[i] = (uint32_t)(kr * D + (pch ^ (r & 7)) * 8) * 2u;
+        v_voff[i] = (uint32_t)(r * D + (pch ^ (2 * (r & 3))) * 8) * 2u;
     }
+    // Ring slots are counted from the first visited tile: tile t sits in K slot
+    // (t - t_first) % K_RING and V slot (t - t_first) % V_RING; kcur / vcur
+    // track the slots of the current tile.
+    auto kslot_b = [&](int sl) -> unsigned char* { return smem_raw + sl * L::K_TILE * 2; };
+    auto vslot_b = [&](int sl) -> unsigned char* { return smem_raw + (L::K_RING * L::K_TILE + sl * L::V_TILE) * 2; };
+    auto kslot = [&](int sl) -> const bf16* { return reinterpret_cast<const bf16*>(kslot_b(sl)); };
+    auto vslot = [&](int sl) -> const bf16* { return reinterpret_cast<const bf16*>(vslot_b(sl)); };
+    auto dma_k = [&](int t, int sl) {
 #pragma unroll
-    for (int i = 0; i < V_TASKS; ++i) {
-        const int cidx = tid + i * NT;
-        v_voff[i] = (uint32_t)((2 * (cidx % (TK / 2))) * D + (cidx / (TK / 2)) * 8) * 2u;
-    }
-    auto gload = [&](int tk, int tv) {
-        const uint32_t ks_off = (uint32_t)tk * TK * D * 2u, vs_off = (uint32_t)tv * TK * D * 2u;
-#pragma unroll
-        for (int i = 0; i < K_LOADS; ++i) kr[i] = bload128(krs, k_voff[i], ks_off);
-#pragma unroll
-        for (int i = 0; i < V_TASKS; ++i) {
-            if (V_TASKS * NT == V_TASKS_ALL || tid + i * NT < V_TASKS_ALL) {
-                vr[i][0] = bload128(vrs, v_voff[i], vs_off);
-                vr[i][1] = bload128(vrs, v_voff[i] + D * 2u, vs_off);
-            }
-        }
+        for (int i = 0; i < 2; ++i)
+            dma16(krs, kslot_b(sl) + (2 * wave + i) * 1024, k_voff[i], (uint32_t)t * TK * D * 2u);
     };
-    auto kslot = [&](int t) -> bf16* { return smem + (t % L::K_RING) * L::K_TILE; };
-    auto vslot = [&](int t) -> bf16* { return smem + L::K_RING * L::K_TILE + (t % L::V_RING) * L::V_TILE; };
-    // K row r of a 32-row block goes to LDS row swap23(r) (an involution), so
-    // lane l reading LDS row l%32 receives key swap23(l%32) on conflict-free rows.
-    auto sstore = [&](bf16* ks, bf16* vs) {
+    auto dma_v = [&](int t, int sl) {
 #pragma unroll
-        for (int i = 0; i < K_LOADS; ++i) {
-            const int cidx = tid + i * NT;
-            const int row = cidx / KCH;
-            const int lrow = (row & ~31) | swap_bits23(row & 31);
-            *reinterpret_cast<u32x4*>(ks + lrow * L::KS + (cidx % KCH) * 8) = kr[i];
-        }
-#pragma unroll
-        for (int i = 0; i < V_TASKS; ++i) {
-            const int cidx = tid + i * NT;
-            if (V_TASKS * NT == V_TASKS_ALL || cidx < V_TASKS_ALL) {
-                const int kpair = cidx % (TK / 2), col = cidx / (TK / 2);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t a = vr[i][0][j], bb = vr[i][1][j];
-                    *reinterpret_cast<uint32_t*>(vs + (col * 8 + 2 * j) * L::VS + 2 * kpair) =
-                        __builtin_amdgcn_perm(bb, a, 0x05040100u);            // d = col*8+2j
-                    *reinterpret_cast<uint32_t*>(vs + (col * 8 + 2 * j + 1) * L::VS + 2 * kpair) =
-                        __builtin_amdgcn_perm(bb, a, 0x07060302u);            // d = col*8+2j+1
-                }
-            }
-        }
+        for (int i = 0; i < 2; ++i)
+            dma16(vrs, vslot_b(sl) + (2 * wave + i) * 1024, v_voff[i], (uint32_t)t * TK * D * 2u);
     };
+    int kcur = 0, vcur = 0;
+    static_assert(L::K_RING == 3 && L::V_RING == 2, "slot arithmetic below");
+    // Per-lane LDS offsets of the operand reads.
+    //  K (A of K·Qᵀ): row hf*32 + l%32, chunk (kk*2 + hl) ^ (l & 7).
+    const int kx = hl ^ (l32 & 7);
+    //  Vᵀ (A of Vᵀ·Pᵀ, transposed read): lane 16g+m addresses key row
+    //  (g/2)*8 + m/4 (+4 for the second half) and d = db*32 + 16(g%2) + 4(m%4).
+    const int vg = lane >> 4, vm = lane & 15;
+    const int vrow = (vg >> 1) * 8 + (vm >> 2);
+    const int vfv = 2 * (vrow & 3);
+    const int vc0 = 2 * (vg & 1) + ((vm & 3) >> 1);
+    const int vin = (vm & 1) * 4;                    // element offset inside the 16-byte chunk
+    auto v_off = [&](int db) { return vrow * D + (((db * 4 + vc0) ^ vfv) * 8) + vin; };
+
     // Lane j reports whether key t*TK + j is padded or past Tk (lanes >= TK report 1).
     auto pad_flag = [&](int t) -> int {
         const int key = t * TK + lane;
@@ -257,20 +316,24 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[db][nb][i] = 0.f;
-    float mrun[NB], mc[NB], lsum[NB];
+    // mc: the reference the weights are taken against, 2^(S·c - mc), in log2
+    // units; always finite.  lsum: running sum of the weights.
+    float mc[NB], lsum[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) { mrun[nb] = kNegInf; mc[nb] = 0.f; lsum[nb] = 0.f; }
+    for (int nb = 0; nb < NB; ++nb) { mc[nb] = 0.f; lsum[nb] = 0.f; }
 
     // Sᵀ = K·Qᵀ for one key block (u) from a tile in LDS: element i of lane l
     // holds key (i/8)*16 + (l/32)*8 + i%8 of the block.
-    auto kblock = [&](int u) -> const bf16* {
-        return kslot(u / HALVES) + ((u % HALVES) * 32 + l32) * L::KS + hl * 8;
+    // K rows of key block h (0 .. HALVES-1) of the tile in slot sl
+    auto kblock = [&](int sl, int h) -> const bf16* { return kslot(sl) + (h * 32 + l32) * D; };
+    auto k_opnd = [&](const bf16* krow, int kk) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8*>(krow + ((kk * 2) ^ kx) * 8);
     };
-    auto qk_full = [&](int u, f32x16 (&S)[NB], float (&mx)[NB]) {
-        const bf16* kp_ = kblock(u);
+    auto qk_full = [&](f32x16 (&S)[NB]) {     // first block of slot 0
+        const bf16* kp_ = kblock(0, 0);
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp_ + kk * 16);
+            const bf16x8 a = k_opnd(kp_, kk);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 if (kk == 0) {
@@ -281,98 +344,89 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 }
             }
         }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            float m = S[nb][0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) m = fmaxf(m, S[nb][i]);
-            mx[nb] = m;
-        }
     };
 
+    // bit i set: key u*CK + i of block u lies outside [first, last]
+    auto edge_bits = [&](int u) -> uint32_t {
+        const int lo = first - u * CK, hi = last - u * CK;
+        uint32_t m = 0u;
+        if (lo > 0) m |= lo >= 32 ? ~0u : (1u << lo) - 1u;
+        if (hi < 31) m |= hi < 0 ? ~0u : ~((2u << hi) - 1u);
+        return m;
+    };
+    // With interior holes, lane j of padf / padf_nxt flags key j of the current /
+    // next LDS tile; the next tile's flags are loaded a tile ahead, so reading
+    // them never waits on the tile loads issued at the same time.
     uint64_t pm_tile = 0;
-    int padf = 0;
-    // Running-max threshold per query block: a block whose scores stay at or
-    // below mthr needs no rescale (every weight stays <= 2^TAU).
-    float mthr[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) mthr[nb] = kNegInf;
-
-    // The second PV k-step of block u is issued at the start of step u+1 (so
-    // the MFMA stream never idles); pw_pend / va_pend carry its operands.
-    u32x4 pw_pend[NB];
-    const bf16* vp_pend = vslot(t_first) + l32 * L::VS + hl * 8;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) pw_pend[nb] = u32x4{0u, 0u, 0u, 0u};
-    auto pv_pend = [&](int db, int nb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vp_pend + db * 32 * L::VS + 16);
-        oacc[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pw_pend[nb]), oacc[db][nb], 0, 0, 0);
+    int padf = 0, padf_nxt = 0;
+    // Vᵀ operand (8 keys x one d per lane) of k-step k2 of half hf of the current V tile
+    auto v_opnd = [&](int hf, int k2, int db) -> u32x4 {
+        const bf16* base = vslot(vcur) + (hf * 32 + k2 * 16) * D + v_off(db);
+        const u32x2 lo = ds_read_tr(base);
+        const u32x2 hi = ds_read_tr(base + 4 * D);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
     };
 
-    // One pipeline step for key block u = u_first + j: S holds its raw scores and
-    // mx their in-lane row max; Sn / mxn receive block u+1's.  hf (the step's
-    // half within its LDS tile) is a constant at each call site.
-    auto step = [&](int j, const int hf, f32x16 (&S)[NB], float (&mx)[NB], f32x16 (&Sn)[NB],
-                    float (&mxn)[NB]) {
+    // The reference mc is set from the exact row max of the first visited block
+    // that holds an unpadded key (then every weight of that block is <= 1) and
+    // raised only when a 16-key chunk's weights sum past 2^TAU in some lane.
+    bool mc_set = false;
+
+    // One pipeline step for key block u = u_first + j: S holds its raw scores;
+    // Sn receives block u+1's.  hf (the step's half within its LDS tile) is a
+    // constant at each call site.
+    // ka holds the K operands of the next QK product (block u+1 at step u):
+    // they are read from LDS during the step before, so no step starts by
+    // waiting on LDS.
+    bf16x8 ka[KSTEPS];
+    auto step = [&](int j, const int hf, f32x16 (&S)[NB], f32x16 (&Sn)[NB]) {
         const int u = u_first + j;
         const int T = u / HALVES;
-        if (hf == 0) pm_tile = __ballot(padf) & TILE_BITS;
-        const uint32_t pm = (uint32_t)(pm_tile >> (hf * 32));   // bit i: key u*32+i padded
-        if (pm != 0u) {             // workgroup-uniform, rare: mask and redo the row max
+        uint32_t pm = edge_bits(u);                 // bit i: key u*32+i padded
+        if (holes) {
+            if (hf == 0) pm_tile = __ballot(padf) & TILE_BITS;
+            pm |= (uint32_t)(pm_tile >> (hf * 32));
+        }
+        if (pm != 0u) {             // workgroup-uniform, rare: padded keys get -inf
+            // element i of this lane is key (i/8)*16 + hl*8 + i%8 of the block
+            const uint32_t pl = ((pm >> (hl * 8)) & 0xFFu) | (((pm >> (16 + hl * 8)) & 0xFFu) << 8);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int kl = (i >> 3) * 16 + hl * 8 + (i & 7);
-                if ((pm >> kl) & 1u) {
+                if ((pl >> i) & 1u) {
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) S[nb][i] = kNegInf;
                 }
             }
+        }
+        if (!mc_set && pm != ~0u) {   // once: first block with an unpadded key
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 float m = S[nb][0];
 #pragma unroll
                 for (int i = 1; i < 16; ++i) m = fmaxf(m, S[nb][i]);
-                mx[nb] = m;
+                mc[nb] = pair_max(m) * c;
             }
-        }
-        bool need = false;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) need |= mx[nb] > mthr[nb];
-        if (__ballot(need)) {       // lazy rescale: rare once the running max settles
-            // finish block u-1 under the old scale, then rescale O and l
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) pv_pend(db, nb);
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                pw_pend[nb] = u32x4{0u, 0u, 0u, 0u};
-                const float mnew = fmaxf(mrun[nb], pair_max(mx[nb]));
-                const float alpha = __builtin_amdgcn_exp2f((mrun[nb] - mnew) * c);
-                mrun[nb] = mnew;
-                mc[nb] = mnew * c;
-                mthr[nb] = mnew + TAU / c;
-                lsum[nb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[db][nb][i] *= alpha;
-            }
+            mc_set = true;
         }
 
         // ---- fixed block, issued slot by slot: the MFMA stream is
-        //   PV(u-1, k-step 1) | QK(u+1) | PV(u, k-step 0)
+        //   QK(u+1) | PV(u, k-step 0) | PV(u, k-step 1)
         // and each slot also carries one stage of a three-stage softmax pipeline
-        // (A: x = S·c - m·c, B: p = 2^x, C: l += p, pack to bf16), so every slot
-        // has independent vector work; LDS operands are read a few slots ahead.
-        const bf16* kp_ = kblock(u + 1);
-        const bf16* vp_ = vslot(T) + l32 * L::VS + hf * 32 + hl * 8;
-        bf16x8 ka[KSTEPS];
-        bf16x8 va[DB];
+        // (A: x = S·c - mc, B: p = 2^x, C: chunk sum += p, pack to bf16), so every
+        // slot has independent vector work; LDS operands are read a few slots
+        // ahead.  After each 16-key chunk is packed and before its PV MFMAs, its
+        // per-lane sums are checked against 2^TAU (see rescale below).
+        // K rows of block u+2, read here for the next step: at D = 64 (two blocks
+        // per tile) that block is in tile T+1, published since the end of tile
+        // T-1; at D = 128 it is tile T+2, read after this step's tile-end barrier.
+        const int knext = kcur == 2 ? 0 : kcur + 1;
+        u32x4 va[DB], va1[DB];
         u32x4 pw[NB][PSTEPS];
+        float cs[NB][PSTEPS];
         float xs[16][2], ps[16][2];
-        auto rd_k = [&](int kk) { ka[kk] = *reinterpret_cast<const bf16x8*>(kp_ + kk * 16); };
-        auto rd_v = [&](int db) { va[db] = *reinterpret_cast<const bf16x8*>(vp_ + db * 32 * L::VS); };
+        auto rd_k = [&](int kk) { ka[kk] = k_opnd(kblock(knext, hf), kk); };
+        auto rd_v = [&](int db) { va[db] = v_opnd(hf, 0, db); };
+        auto rd_v1 = [&](int db) { va1[db] = v_opnd(hf, 1, db); };
         // pair pp: chunk k2 = pp / (4*NB), query block nb, elements i, i+1
         auto pair_nb = [&](int pp) { return (pp / 4) % NB; };
         auto pair_i = [&](int pp) { return (pp / (4 * NB)) * 8 + (pp % 4) * 2; };
@@ -386,15 +440,58 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             ps[pp][1] = __builtin_amdgcn_exp2f(xs[pp][1]);
         };
         auto stC = [&](int pp) {
-            const int nb = pair_nb(pp);
-            lsum[nb] += ps[pp][0];
-            lsum[nb] += ps[pp][1];
-            pw[nb][pp / (4 * NB)][pp % 4] = pack_bf16x2(ps[pp][0], ps[pp][1]);
+            const int nb = pair_nb(pp), k2 = pp / (4 * NB);
+            if (pp % 4 == 0) cs[nb][k2] = ps[pp][0] + ps[pp][1];
+            else cs[nb][k2] += ps[pp][0] + ps[pp][1];
+            pw[nb][k2][pp % 4] = pack_bf16x2(ps[pp][0], ps[pp][1]);
         };
         auto softmax_slot = [&](int sl) {     // stages for slot sl of 18
             if (sl >= 1 && sl <= 16) stB(sl - 1);
             if (sl < 16) stA(sl);
             if (sl >= 2 && sl <= 17) stC(sl - 2);
+        };
+        // Lazy rescale of chunk k2 (rare; the common path never computes a row
+        // max): if some lane's weights of the chunk sum past 2^TAU, raise mc to
+        // the chunk's exact row max where that is higher, scale l and O by
+        // 2^(old - new), and redo the chunk's weights, plus the stages of the
+        // next chunk already in flight (at the check after slot 9, chunk 1's
+        // stage A of pairs 8, 9 and stage B of pair 8).  Final O = acc / l and
+        // LSE = (mc + log2 l)·ln 2 hold for any reference, so only rounding
+        // changes.
+        auto check = [&](int k2) {
+            bool over = false;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) over |= cs[nb][k2] > kRescaleSum;
+            if (__ballot(over)) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    float m = S[nb][k2 * 8];
+#pragma unroll
+                    for (int i = 1; i < 8; ++i) m = fmaxf(m, S[nb][k2 * 8 + i]);
+                    const float mn = fmaxf(mc[nb], pair_max(m) * c);
+                    const float alpha = __builtin_amdgcn_exp2f(mc[nb] - mn);
+                    mc[nb] = mn;
+                    lsum[nb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) oacc[db][nb][i] *= alpha;
+                }
+#pragma unroll
+                for (int q = 0; q < 4 * NB; ++q) {
+                    const int pp = k2 * 4 * NB + q;
+                    stA(pp);
+                    stB(pp);
+                    stC(pp);
+                }
+                if (k2 == 0) {
+                    stA(8);
+                    stA(9);
+                    stB(8);
+                }
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) lsum[nb] += cs[nb][k2];
         };
         auto qk_one = [&](int qi) {     // qi = kk*NB + nb
             const int nb = qi % NB, kk = qi / NB;
@@ -405,94 +502,95 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 Sn[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qreg[nb][kk], Sn[nb], 0, 0, 0);
             }
         };
-        auto pv0_one = [&](int pi) {    // PV(u, k-step 0): pi = db*NB + nb
+        auto pv_one = [&](int k2, int pi) {    // PV(u, k-step k2): pi = db*NB + nb
             const int nb = pi % NB, db = pi / NB;
-            oacc[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], as_bf16x8(pw[nb][0]), oacc[db][nb], 0, 0, 0);
-        };
-        auto max_part = [&](int nb, int i0, int n) {   // running in-lane max of Sn[nb][i0 .. i0+n)
-            float m = Sn[nb][i0];
-#pragma unroll
-            for (int i = i0 + 1; i < i0 + n; ++i) m = fmaxf(m, Sn[nb][i]);
-            mxn[nb] = i0 == 0 ? m : fmaxf(mxn[nb], m);
+            const u32x4 a = k2 == 0 ? va[db] : va1[db];
+            oacc[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pw[nb][k2]),
+                                                                    oacc[db][nb], 0, 0, 0);
         };
         auto fence = [&]() { __builtin_amdgcn_sched_barrier(0); };
 
         if constexpr (D == 64) {
-            // 16 MFMA slots + 2 drain slots:
-            //   0-3 PV(u-1,1)   4-11 QK(u+1)   12-15 PV(u,0)   16-17 softmax drain
-            // row max of S_{u+1}: 4 max3 per slot in 14-17 (QK done by slot 11).
-            rd_k(0); rd_k(1);
-            fence();
+            // 22 slots: 0-7 QK(u+1), 10-13 PV(u,0) (chunk 0 packed by slot 9),
+            // 18-21 PV(u,1) (chunk 1 packed by slot 17); softmax in 0-17.
 #pragma unroll
-            for (int sl = 0; sl < 18; ++sl) {
-                if (sl == 0) { rd_k(2); rd_k(3); }
-                if (sl == 6) { rd_v(0); rd_v(1); }
-                if (sl < 4) pv_pend(sl / NB, sl % NB);
-                else if (sl < 12) qk_one(sl - 4);
-                else if (sl < 16) pv0_one(sl - 12);
-                softmax_slot(sl);
-                if (sl >= 14) max_part((sl - 14) >> 1, ((sl - 14) & 1) * 8, 8);
+            for (int sl = 0; sl < 22; ++sl) {
+                if (sl == 4) { rd_v(0); rd_v(1); }
+                if (sl == 12) { rd_v1(0); rd_v1(1); }
+                if (sl == 14) { rd_k(0); rd_k(1); }      // QK(u+2) operands: after QK(u+1) issued
+                if (sl == 15) { rd_k(2); rd_k(3); }
+                if (sl < 8) qk_one(sl);
+                else if (sl >= 10 && sl < 14) pv_one(0, sl - 10);
+                else if (sl >= 18) pv_one(1, sl - 18);
+                if (sl < 18) softmax_slot(sl);
                 fence();
+                if (sl == 9) check(0);
+                if (sl == 17) check(1);
             }
         } else {
-            // D=128: 32 MFMA slots:
-            //   0-7 PV(u-1,1)   8-23 QK(u+1)   24-31 PV(u,0)
-            // softmax pipeline in slots 0-17 (chunk 0 packed by slot 9), row max in 26-31.
-            rd_k(0); rd_k(1);
-            fence();
+            // D=128: 0-15 QK(u+1), 16-23 PV(u,0), 24-31 PV(u,1); softmax in 0-17
+            // (chunk 0 packed by slot 9, chunk 1 by slot 17).
 #pragma unroll
             for (int sl = 0; sl < 32; ++sl) {
-                if (sl == 0) { rd_k(2); rd_k(3); }
-                if (sl == 8) { rd_k(4); rd_k(5); }
-                if (sl == 12) { rd_k(6); rd_k(7); }
-                if (sl == 18) { rd_v(0); rd_v(1); }
-                if (sl == 20) { rd_v(2); rd_v(3); }
-                if (sl < 8) pv_pend(sl / NB, sl % NB);
-                else if (sl < 24) qk_one(sl - 8);
-                else pv0_one(sl - 24);
+                if (sl == 10) { rd_v(0); rd_v(1); }
+                if (sl == 12) { rd_v(2); rd_v(3); }
+                if (sl == 18) { rd_v1(0); rd_v1(1); }
+                if (sl == 20) { rd_v1(2); rd_v1(3); }
+                if (sl < 16) qk_one(sl);
+                else if (sl < 24) pv_one(0, sl - 16);
+                else pv_one(1, sl - 24);
                 if (sl < 18) softmax_slot(sl);
-                if (sl >= 26 && sl < 30) max_part((sl - 26) >> 1, ((sl - 26) & 1) * 8, 8);
                 fence();
+                if (sl == 9) check(0);
+                if (sl == 17) check(1);
             }
         }
-        // hand block u's second k-step to step u+1
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) pw_pend[nb] = pw[nb][1];
-        vp_pend = vp_;
 
-        // ---- end of an LDS tile: store the tile loaded during this one, then
+        // ---- end of an LDS tile: publish the tiles loaded during this one, then
         // start loading the next (K tile T+3 and V tile T+2 land by T+1's end).
-        // V tile T is still read by the pending PV of the next step, and tile
-        // T-1 by this tile's first step: a ring of three V slots keeps both
-        // while slot T+1 is written here.
         if (hf == HALVES - 1) {
-            sstore(kslot(T + 2), vslot(T + 1));
+            wait_vmem();            // this wave's part of K_{T+2} and V_{T+1} has landed
             __syncthreads();
-            gload(min(T + 3, t_last), min(T + 2, t_last));
-            padf = pad_flag(min(T + 1, t_last));
+            if (T + 3 <= t_last) dma_k(T + 3, kcur);     // into the slot tile T leaves
+            if (T + 2 <= t_last) dma_v(T + 2, vcur);
+            kcur = knext;
+            vcur ^= 1;
+            if constexpr (HALVES == 1) {    // D = 128: K of block u+2 = tile T+2, just published
+#pragma unroll
+                for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = k_opnd(kblock(kcur == 2 ? 0 : kcur + 1, 0), kk);
+            }
+            if (holes) {
+                padf = padf_nxt;
+                padf_nxt = pad_flag(min(T + 2, t_last));
+            }
         }
     };
 
     if (nsteps > 0) {
         f32x16 sA[NB], sB[NB];
-        float mxA[NB], mxB[NB];
-        padf = pad_flag(t_first);
-        gload(t_first, t_first);
-        sstore(kslot(t_first), vslot(t_first));
-        gload(min(t_first + 1, t_last), t_first);
-        sstore(kslot(t_first + 1), vslot(t_first + 1));
-        __syncthreads();
-        gload(min(t_first + 2, t_last), min(t_first + 1, t_last));   // stored by tile t_first's end
-        qk_full(u_first, sA, mxA);
-        for (int j = 0; j < nsteps; j += 2) {
-            step(j, 0, sA, mxA, sB, mxB);
-            if (j + 1 < nsteps) step(j + 1, HALVES - 1, sB, mxB, sA, mxA);
+        dma_k(t_first, 0);
+        dma_v(t_first, 0);
+        if (t_first + 1 <= t_last) {
+            dma_k(t_first + 1, 1);
+            dma_v(t_first + 1, 1);
         }
-        // flush the pending second k-step of the last block
+        if (holes) {
+            padf = pad_flag(t_first);
+            padf_nxt = pad_flag(min(t_first + 1, t_last));
+        }
+        wait_vmem();
+        __syncthreads();
+        if (t_first + 2 <= t_last) dma_k(t_first + 2, 2);   // waited for at the end of tile t_first
+        qk_full(sA);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) pv_pend(db, nb);
+        for (int kk = 0; kk < KSTEPS; ++kk)     // K of block u_first + 1
+            ka[kk] = HALVES == 1 ? k_opnd(kblock(1, 0), kk) : k_opnd(kblock(0, 1), kk);
+        int j = 0;
+        for (; j + 1 < nsteps; j += 2) {
+            step(j, 0, sA, sB);
+            step(j + 1, HALVES - 1, sB, sA);
+        }
+        if (j < nsteps) step(j, 0, sA, sB);
     }
 
     // ---- epilogue: O = acc / l, LSE = (m·c + log2 l)·ln 2

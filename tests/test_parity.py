@@ -65,6 +65,10 @@ SHAPES = [
     (2, 2, 256, 300, 64, "random"),
     (1, 2, 513, 129, 64, "none"),
     (2, 1, 300, 1000, 64, "holes"),
+    (2, 2, 200, 700, 64, "prefix"),
+    (2, 1, 150, 500, 64, "window"),
+    (3, 1, 64, 300, 64, "single"),
+    (1, 2, 90, 333, 128, "window"),
     (1, 2, 100, 77, 128, "suffix"),
     (2, 2, 130, 300, 128, "random"),
     (1, 1, 257, 33, 128, "none"),
@@ -81,6 +85,19 @@ def _mask(kind, B, Tk, seed):
     if kind == "random":
         m = (torch.rand(B, Tk, generator=g) < 0.3).to(torch.uint8)
         m[:, 0] = 0
+        return m
+    if kind in ("prefix", "window", "single"):
+        # one contiguous run of valid keys [a, b]: leading (and trailing) padding only
+        m = torch.ones(B, Tk, dtype=torch.uint8)
+        for bi in range(B):
+            a = int(torch.randint(1, Tk // 2, (1,), generator=g))
+            if kind == "prefix":
+                b = Tk - 1
+            elif kind == "single":
+                b = a
+            else:
+                b = int(torch.randint(a, Tk, (1,), generator=g))
+            m[bi, a:b + 1] = 0
         return m
     if kind == "holes":   # whole 64-key tiles padded in the middle plus a ragged tail
         m = torch.zeros(B, Tk, dtype=torch.uint8)
