@@ -68,8 +68,10 @@ typedef enum {
  *        padded keys are ignored but V there must be finite.
  *   o    [B, H, Tq, D]   output, same dtype as q
  *   scale  multiplier of Q·Kᵀ, finite and > 0 (usually 1/sqrt(D))
- * Sizes: B, H, Tq, Tk >= 1.  A query whose keys are all padded gets O = 0.
- * Queries are never masked: every query row is computed.
+ * Sizes: B, H, Tq, Tk >= 1; bf16: Tk·D·2 below 2^31 (one head's K or V is
+ * addressed through a 32-bit range), else ATTN_ERR_SHAPE.  A query whose keys
+ * are all padded gets O = 0.  Queries are never masked: every query row is
+ * computed.
  */
 int attn_fwd_masked(const void* q, const void* k, const void* v,
                     const uint8_t* key_padding_mask, void* o,
@@ -146,7 +148,9 @@ int kv_append(void* k_cache, void* v_cache, int32_t* cache_seqlens,
  *       bytes, owned by the caller, 16-byte aligned; contents on entry are
  *       ignored and are garbage on return.  Calls that share a workspace
  *       must be ordered on one stream.
- * H_q must be a multiple of H_kv.
+ * H_q must be a multiple of H_kv.  bf16: T_max·D·2 must stay below 2^31 (one
+ * (sequence, KV head) is addressed through a 32-bit range), else
+ * ATTN_ERR_SHAPE.
  */
 int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* cache_seqlens, void* o, float* lse,

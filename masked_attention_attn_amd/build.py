@@ -35,6 +35,7 @@ FLAGS = [
 EXTRA = {
     "fwd_bf16_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
     "fwd_bf16_d128.hip": ["-fno-honor-nans"],
+    "decode_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
 }
 
 

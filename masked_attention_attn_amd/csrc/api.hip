@@ -126,6 +126,8 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
         !aligned16(workspace))
         return ATTN_ERR_ALIGN;
     if (o == q || o == k_cache || o == v_cache) return ATTN_ERR_ALIAS;
+    // the bf16 kernel addresses one (sequence, KV head) through a 32-bit buffer range
+    if (dtype == ATTN_BF16 && (long long)T_max * D * 2 > (1ll << 31) - 1) return ATTN_ERR_SHAPE;
     DecodeArgs a{q, k_cache, v_cache, cache_seqlens, o, lse, B, H_q, H_kv, T_max, D, scale,
                  workspace, stream};
     return finish(dtype == ATTN_BF16 ? launch_decode_bf16(a) : launch_decode_f32(a));

@@ -232,9 +232,6 @@ hipError_t launch(const DecodeArgs& a) {
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeArgs& a) {
-    return a.D == 64 ? launch<bf16, 64>(a) : launch<bf16, 128>(a);
-}
 hipError_t launch_decode_f32(const DecodeArgs& a) {
     return a.D == 64 ? launch<float, 64>(a) : launch<float, 128>(a);
 }

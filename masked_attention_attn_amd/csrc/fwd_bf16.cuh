@@ -66,9 +66,11 @@
 
 #include "common.cuh"
 #include "launch.h"
+#include "mfma_lds.cuh"
 
 namespace mattn {
 namespace fwdk {
+using namespace mattn::mfma;
 
 constexpr int NWAVE = 4;
 constexpr int NT = 64 * NWAVE;  // threads per workgroup
@@ -93,63 +95,6 @@ struct Lds {
     static constexpr int ELEMS = K_RING * K_TILE + V_RING * V_TILE;
     static constexpr int BYTES = ELEMS * (int)sizeof(bf16);
 };
-
-__device__ __forceinline__ int swap_bits23(int r) {
-    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// max / sum of x over lanes l and l^32 (v_permlane32_swap exchanges the two
-// wave halves; the pair of results holds both halves' values in every lane).
-__device__ __forceinline__ float pair_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Buffer descriptor over `bytes` bytes at p (gfx9 layout: base, stride 0,
-// num_records = bytes, raw dword format): loads at offsets >= bytes return zero.
-typedef int i32x4_sgpr __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4_sgpr make_rsrc(const void* p, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(p);
-    i32x4_sgpr r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
-    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-    r[3] = 0x00020000;
-    return r;
-}
-// 16 bytes per lane from a buffer straight into LDS at lds_base + 16*lane.
-// Written as inline assembly on purpose: the compiler cannot tell these LDS
-// writes apart from the operand reads of other ring slots and would put a
-// wait for every outstanding global load in front of the next LDS read.  The
-// kernel orders them itself (wait_vmem + barrier at the end of each tile);
-// loads the compiler does not see only make its own vmcnt waits stricter.
-__device__ __forceinline__ void dma16(i32x4_sgpr r, unsigned char* lds_base, uint32_t voff, uint32_t soff) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)lds_base));
-    uint32_t saved;     // M0 is restored, so the compiler's view of it stays valid
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
-                 "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved)
-                 : "s"(m0), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
-                 : "memory");
-}
-// Wait for this wave's outstanding global loads (including LDS-direct ones).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-typedef __bf16 bf16x4_lds __attribute__((ext_vector_type(4)));
-// Transposing 8-byte LDS read (see the layout note above).
-__device__ __forceinline__ u32x2 ds_read_tr(const bf16* p) {
-    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf;
-    const v4bf r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (__attribute__((address_space(3))) v4bf*)(const_cast<bf16*>(p)));
-    return __builtin_bit_cast(u32x2, r);
-}
 
 template <int D, bool WRITE_LSE>
 __global__ __launch_bounds__(NT, 1)
@@ -260,7 +205,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // fills chunks 2w, 2w+1.  For LDS byte o of a tile (row r = o / RB, chunk
     // position p), K takes key perm(r) (bits 2,3 swapped within 32-row blocks),
     // chunk p ^ (r & 7); V takes key r, chunk p ^ 2(r & 3).  Keys past Tk read
-    // as zeros (buffer range check; they are masked).
+    // as zeros (the buffer range check covers the per-lane offset, which is why the
+    // tile offset is added there and not to the scalar offset; they are masked).
     static_assert(TK * D * 2 == 8192, "8 KiB tiles");
     uint32_t k_voff[2], v_voff[2];
 #pragma unroll
@@ -281,12 +227,12 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     auto dma_k = [&](int t, int sl) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-            dma16(krs, kslot_b(sl) + (2 * wave + i) * 1024, k_voff[i], (uint32_t)t * TK * D * 2u);
+            dma16(krs, kslot_b(sl) + (2 * wave + i) * 1024, k_voff[i] + (uint32_t)t * TK * D * 2u, 0u);
     };
     auto dma_v = [&](int t, int sl) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-            dma16(vrs, vslot_b(sl) + (2 * wave + i) * 1024, v_voff[i], (uint32_t)t * TK * D * 2u);
+            dma16(vrs, vslot_b(sl) + (2 * wave + i) * 1024, v_voff[i] + (uint32_t)t * TK * D * 2u, 0u);
     };
     int kcur = 0, vcur = 0;
     static_assert(L::K_RING == 3 && L::V_RING == 2, "slot arithmetic below");

@@ -57,10 +57,12 @@ hipError_t launch_decode_f32(const DecodeArgs& a);
 
 // Split-K geometry of the decode path (shared by the workspace-size query
 // and the launcher).
-constexpr int kDecodeSplit = 512;     // cached tokens per split workgroup
+constexpr int kDecodeSplit = 1024;    // cached tokens per split
 inline int decode_nsplit(int T_max) { return (T_max + kDecodeSplit - 1) / kDecodeSplit; }
+// Two partial results per (sequence, query head, split): a split is shared by
+// at most two wavefronts of the bf16 stream kernel.
 inline size_t decode_workspace_bytes(int B, int H_q, int T_max, int D) {
-    const size_t parts = (size_t)B * H_q * decode_nsplit(T_max);
+    const size_t parts = (size_t)B * H_q * decode_nsplit(T_max) * 2;
     return parts * (size_t)D * sizeof(float) + parts * 2 * sizeof(float);
 }
 

@@ -1,0 +1,80 @@
+// Device helpers shared by the matrix-core attention kernels (prefill and
+// decode): buffer descriptors, direct global->LDS tile loads, the gfx950
+// transposing LDS read and lane-pair reductions of the 32x32 MFMA layout.
+#pragma once
+
+#include "common.cuh"
+
+namespace mattn {
+namespace mfma {
+
+__device__ __forceinline__ int swap_bits23(int r) {
+    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// max / sum of x over lanes l and l^32 (v_permlane32_swap exchanges the two
+// wave halves; the pair of results holds both halves' values in every lane).
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Buffer descriptor over `bytes` bytes at p (gfx9 layout: base, stride 0,
+// num_records = bytes, raw dword format): loads at offsets >= bytes return zero.
+typedef int i32x4_sgpr __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_sgpr make_rsrc(const void* p, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    i32x4_sgpr r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+// 16 bytes per lane from a buffer straight into LDS at lds_base + 16*lane.
+// Written as inline assembly on purpose: the compiler cannot tell these LDS
+// writes apart from the operand reads of other ring slots and would put a
+// wait for every outstanding global load in front of the next LDS read.  The
+// calling kernel orders them itself (an explicit vmcnt wait, plus a barrier
+// where other waves read the data); loads the compiler does not see only make
+// its own vmcnt waits stricter, never too weak.
+__device__ __forceinline__ void dma16(i32x4_sgpr r, unsigned char* lds_base, uint32_t voff, uint32_t soff) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)lds_base));
+    uint32_t saved;     // M0 is restored, so the compiler's view of it stays valid
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
+                 "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(m0), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
+                 : "memory");
+}
+// Wait for this wave's outstanding global loads (including LDS-direct ones).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// gfx950 transposing 8-byte LDS read (ds_read_b64_tr_b16): within each
+// 16-lane group, lane j receives element j%4 of the 8-byte rows addressed by
+// lanes j/4 + 4k (k = 0..3), i.e. a 4x4 transpose of 16-bit elements.
+__device__ __forceinline__ u32x2 ds_read_tr(const bf16* p) {
+    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf;
+    const v4bf r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) v4bf*)(const_cast<bf16*>(p)));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+// Wait until at most N of this wave's global loads (including LDS-direct ones)
+// are outstanding; also a compiler barrier for memory operations, so no LDS
+// read of the landed data is moved above it.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+}  // namespace mfma
+}  // namespace mattn

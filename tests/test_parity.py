@@ -235,6 +235,11 @@ DEC_SHAPES = [
     (3, 6, 2, 64, 0, 600, 640),
     (2, 16, 2, 128, 1, 700, 768),
     (2, 3, 1, 128, 510, 514, 576),
+    (2, 40, 1, 64, 100, 900, 960),       # 40 query heads per KV head: two column groups
+    (70, 8, 4, 64, 1, 300, 320),         # more than 64 sequences; short items shared by two waves
+    (4, 8, 8, 128, 1023, 1023, 1024),    # lengths after the append are whole splits
+    (16, 64, 8, 128, 0, 3000, 3072),
+    (1, 1, 1, 128, 0, 0, 64),            # a single token
 ]
 
 
@@ -261,6 +266,19 @@ def test_decode_zero_length(ma):
     assert torch.all(o[0] == 0) and torch.all(torch.isneginf(l[0]))
     Or, Lr = oracle.decode(w.q[1:], w.k_cache[1:], w.v_cache[1:], w.lens[1:], w.scale)
     check_attn(o[1:], l[1:], Or, Lr, torch.bfloat16, "decode len 0 / 9")
+
+
+def test_decode_zero_lengths_mixed(ma):
+    """Empty sequences between non-empty ones (the work order skips them)."""
+    w = W.make_decode(6, 8, 2, 128, 0, 10, torch.bfloat16, T_max=768, lens=[0, 5, 0, 700, 0, 513], seed=2)
+    o, l = ma.attn_decode(w.q.to(DEV), w.k_cache.to(DEV), w.v_cache.to(DEV), w.lens.to(DEV), w.scale,
+                          want_lse=True)
+    torch.cuda.synchronize()
+    for b in (0, 2, 4):
+        assert torch.all(o[b] == 0) and torch.all(torch.isneginf(l[b]))
+    keep = [1, 3, 5]
+    Or, Lr = oracle.decode(w.q[keep], w.k_cache[keep], w.v_cache[keep], w.lens[keep], w.scale)
+    check_attn(o[keep], l[keep], Or, Lr, torch.bfloat16, "decode mixed zero lengths")
 
 
 def test_gqa_decode_b32_sampled_heads(ma):
