@@ -10,10 +10,11 @@
 // merge needs (sglang PR 49078 analysis, section "1. aiter.py").
 //
 // Work decomposition
-//   workgroup = 4 wavefronts (one per SIMD) of one (batch, head); each wave
-//   owns 64 queries (two 32-column blocks of the MFMA), so a workgroup covers
-//   256 queries.  K/V are staged in LDS in tiles of TK keys (64 at D = 64,
-//   32 at D = 128); the compute steps over blocks of 32 keys.
+//   workgroup = 256 queries of one (batch, head): at D = 64 four wavefronts of
+//   64 queries (two 32-column blocks of the MFMA), at D = 128 eight
+//   wavefronts of 32 queries.  K/V are staged in LDS in tiles of TK keys (64
+//   at D = 64, 32 at D = 128) shared by the workgroup; the compute steps over
+//   blocks of 32 keys.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, operands 8 bf16 per lane,
 // accumulator 16 fp32 per lane; lane l holds column l%32 of the result and
@@ -72,12 +73,16 @@ namespace mattn {
 namespace fwdk {
 using namespace mattn::mfma;
 
-constexpr int NWAVE = 4;
-constexpr int NT = 64 * NWAVE;  // threads per workgroup
 constexpr int CK = 32;          // keys per compute step
-constexpr int NB = 2;           // 32-query column blocks per wave
-constexpr int QW = NB * 32;     // queries per wave
-constexpr int BM = QW * NWAVE;  // queries per workgroup
+// Wavefronts per workgroup and 32-query column blocks per wavefront.  D = 64:
+// four waves of 64 queries (the K operand of a key block serves two query
+// blocks).  D = 128: eight waves of 32 queries, which keeps a wave's live
+// state (output 4x16, scores 2x16, Q 8x4, operands) within the 256 VGPRs of
+// two waves per SIMD; a workgroup covers 256 queries either way.
+template <int D> struct Cfg;
+template <> struct Cfg<64> { static constexpr int NWAVE = 4, NB = 2; };
+template <> struct Cfg<128> { static constexpr int NWAVE = 8, NB = 1; };
+template <int D> constexpr int kBM = Cfg<D>::NWAVE * Cfg<D>::NB * 32;   // queries per workgroup
 constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
 constexpr float kRescaleSum = 256.0f;   // 2^TAU: a lane's chunk sum above this forces a rescale
 
@@ -97,12 +102,19 @@ struct Lds {
 };
 
 template <int D, bool WRITE_LSE>
-__global__ __launch_bounds__(NT, 1)
+__global__ __launch_bounds__(64 * Cfg<D>::NWAVE, 1)
 void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                      const bf16* __restrict__ v, const uint8_t* __restrict__ mask,
                      bf16* __restrict__ o, float* __restrict__ lse,
                      int H, int Tq, int Tk, float c, int n_qt, int total) {
     using L = Lds<D>;
+    constexpr int NWAVE = Cfg<D>::NWAVE;
+    constexpr int NT = 64 * NWAVE;        // threads per workgroup
+    constexpr int NB = Cfg<D>::NB;        // 32-query column blocks per wave
+    constexpr int QW = NB * 32;           // queries per wave
+    constexpr int BM = QW * NWAVE;        // queries per workgroup
+    constexpr int NPP = 8 * NB;           // score pairs per lane and step
+    constexpr int CP = 4 * NB;            // pairs per 16-key chunk
     constexpr int TK = L::TK;             // keys per LDS tile
     constexpr int HALVES = TK / CK;       // compute steps per tile
     constexpr int KSTEPS = D / 16;        // MFMA k-steps of K·Qᵀ
@@ -202,16 +214,17 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
 
     // ---- tile loads straight into LDS: a tile is 8 KiB = 8 chunks of 1 KiB, wave w
-    // fills chunks 2w, 2w+1.  For LDS byte o of a tile (row r = o / RB, chunk
+    // fills chunks CPW*w .. CPW*w + CPW-1.  For LDS byte o of a tile (row r = o / RB, chunk
     // position p), K takes key perm(r) (bits 2,3 swapped within 32-row blocks),
     // chunk p ^ (r & 7); V takes key r, chunk p ^ 2(r & 3).  Keys past Tk read
     // as zeros (the buffer range check covers the per-lane offset, which is why the
     // tile offset is added there and not to the scalar offset; they are masked).
     static_assert(TK * D * 2 == 8192, "8 KiB tiles");
-    uint32_t k_voff[2], v_voff[2];
+    constexpr int CPW = 8 / NWAVE;        // 1 KiB chunks per wave and tile
+    uint32_t k_voff[CPW], v_voff[CPW];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int o = (2 * wave + i) * 1024 + lane * 16;
+    for (int i = 0; i < CPW; ++i) {
+        const int o = (CPW * wave + i) * 1024 + lane * 16;
         const int r = o / L::RB, pch = (o % L::RB) / 16;
         const int kr = (r & ~31) | swap_bits23(r & 31);
         k_voff[i] = (uint32_t)(kr * D + (pch ^ (r & 7)) * 8) * 2u;
@@ -226,13 +239,13 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     auto vslot = [&](int sl) -> const bf16* { return reinterpret_cast<const bf16*>(vslot_b(sl)); };
     auto dma_k = [&](int t, int sl) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            dma16(krs, kslot_b(sl) + (2 * wave + i) * 1024, k_voff[i] + (uint32_t)t * TK * D * 2u, 0u);
+        for (int i = 0; i < CPW; ++i)
+            dma16(krs, kslot_b(sl) + (CPW * wave + i) * 1024, k_voff[i] + (uint32_t)t * TK * D * 2u, 0u);
     };
     auto dma_v = [&](int t, int sl) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            dma16(vrs, vslot_b(sl) + (2 * wave + i) * 1024, v_voff[i] + (uint32_t)t * TK * D * 2u, 0u);
+        for (int i = 0; i < CPW; ++i)
+            dma16(vrs, vslot_b(sl) + (CPW * wave + i) * 1024, v_voff[i] + (uint32_t)t * TK * D * 2u, 0u);
     };
     int kcur = 0, vcur = 0;
     static_assert(L::K_RING == 3 && L::V_RING == 2, "slot arithmetic below");
@@ -391,17 +404,17 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             else cs[nb][k2] += ps[pp][0] + ps[pp][1];
             pw[nb][k2][pp % 4] = pack_bf16x2(ps[pp][0], ps[pp][1]);
         };
-        auto softmax_slot = [&](int sl) {     // stages for slot sl of 18
-            if (sl >= 1 && sl <= 16) stB(sl - 1);
-            if (sl < 16) stA(sl);
-            if (sl >= 2 && sl <= 17) stC(sl - 2);
+        auto softmax_slot = [&](int sl) {     // stages for slot sl of NPP + 2
+            if (sl >= 1 && sl <= NPP) stB(sl - 1);
+            if (sl < NPP) stA(sl);
+            if (sl >= 2 && sl <= NPP + 1) stC(sl - 2);
         };
         // Lazy rescale of chunk k2 (rare; the common path never computes a row
         // max): if some lane's weights of the chunk sum past 2^TAU, raise mc to
         // the chunk's exact row max where that is higher, scale l and O by
         // 2^(old - new), and redo the chunk's weights, plus the stages of the
-        // next chunk already in flight (at the check after slot 9, chunk 1's
-        // stage A of pairs 8, 9 and stage B of pair 8).  Final O = acc / l and
+        // next chunk already in flight (at the check after slot CP+1, chunk 1's
+        // stage A of pairs CP, CP+1 and stage B of pair CP).  Final O = acc / l and
         // LSE = (mc + log2 l)·ln 2 hold for any reference, so only rounding
         // changes.
         auto check = [&](int k2) {
@@ -431,9 +444,9 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     stC(pp);
                 }
                 if (k2 == 0) {
-                    stA(8);
-                    stA(9);
-                    stB(8);
+                    stA(CP);
+                    stA(CP + 1);
+                    stB(CP);
                 }
             }
 #pragma unroll
@@ -468,27 +481,34 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 if (sl < 8) qk_one(sl);
                 else if (sl >= 10 && sl < 14) pv_one(0, sl - 10);
                 else if (sl >= 18) pv_one(1, sl - 18);
-                if (sl < 18) softmax_slot(sl);
+                if (sl < NPP + 2) softmax_slot(sl);
                 fence();
-                if (sl == 9) check(0);
-                if (sl == 17) check(1);
+                if (sl == CP + 1) check(0);
+                if (sl == NPP + 1) check(1);
             }
         } else {
-            // D=128: 0-15 QK(u+1), 16-23 PV(u,0), 24-31 PV(u,1); softmax in 0-17
-            // (chunk 0 packed by slot 9, chunk 1 by slot 17).
+            // D=128, one query block: 16 slots.  QK(u+1) is one chain of 8 MFMAs
+            // (slots 0-5, 7, 9); PV(u,0) in 6, 8, 10, 11 once chunk 0 is packed
+            // (slot 5); PV(u,1) in 12-15 once chunk 1 is packed (slot 9);
+            // softmax in 0-9.
 #pragma unroll
-            for (int sl = 0; sl < 32; ++sl) {
-                if (sl == 10) { rd_v(0); rd_v(1); }
-                if (sl == 12) { rd_v(2); rd_v(3); }
-                if (sl == 18) { rd_v1(0); rd_v1(1); }
-                if (sl == 20) { rd_v1(2); rd_v1(3); }
-                if (sl < 16) qk_one(sl);
-                else if (sl < 24) pv_one(0, sl - 16);
-                else pv_one(1, sl - 24);
-                if (sl < 18) softmax_slot(sl);
+            for (int sl = 0; sl < 16; ++sl) {
+                if (sl == 1) { rd_v(0); rd_v(1); }
+                if (sl == 2) { rd_v(2); rd_v(3); }
+                if (sl == 7) { rd_v1(0); rd_v1(1); }
+                if (sl == 8) { rd_v1(2); rd_v1(3); }
+                if (sl < 6) qk_one(sl);
+                else if (sl == 7) qk_one(6);
+                else if (sl == 9) qk_one(7);
+                if (sl == 6) pv_one(0, 0);
+                else if (sl == 8) pv_one(0, 1);
+                else if (sl == 10) pv_one(0, 2);
+                else if (sl == 11) pv_one(0, 3);
+                else if (sl >= 12) pv_one(1, sl - 12);
+                if (sl < NPP + 2) softmax_slot(sl);
                 fence();
-                if (sl == 9) check(0);
-                if (sl == 17) check(1);
+                if (sl == CP + 1) check(0);
+                if (sl == NPP + 1) check(1);
             }
         }
 
@@ -570,11 +590,12 @@ hipError_t launch_one(const FwdArgs& a) {
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
     if (attr != hipSuccess) return attr;
+    constexpr int BM = kBM<D>;
     const int n_qt = (a.Tq + BM - 1) / BM;
     const int total = a.B * a.H * n_qt;
     const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
     const float c = a.scale * kLog2e;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), L::BYTES, (hipStream_t)a.stream,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * Cfg<D>::NWAVE), L::BYTES, (hipStream_t)a.stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.mask,
                        (bf16*)a.o, a.lse, a.H, a.Tq, a.Tk, c, n_qt, total);
     return hipGetLastError();
