@@ -88,7 +88,7 @@ constexpr float kRescaleSum = 256.0f;   // 2^TAU: a lane's chunk sum above this 
 
 template <int D> struct Tile;
 template <> struct Tile<64> { static constexpr int TK = 64; };
-template <> struct Tile<128> { static constexpr int TK = 32; };
+template <> struct Tile<128> { static constexpr int TK = 64; };
 
 template <int D>
 struct Lds {
@@ -219,8 +219,9 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // chunk p ^ (r & 7); V takes key r, chunk p ^ 2(r & 3).  Keys past Tk read
     // as zeros (the buffer range check covers the per-lane offset, which is why the
     // tile offset is added there and not to the scalar offset; they are masked).
-    static_assert(TK * D * 2 == 8192, "8 KiB tiles");
-    constexpr int CPW = 8 / NWAVE;        // 1 KiB chunks per wave and tile
+    constexpr int NCHUNK = TK * D * 2 / 1024;   // 1 KiB chunks per tile
+    constexpr int CPW = NCHUNK / NWAVE;         // chunks per wave and tile
+    static_assert(CPW * NWAVE == NCHUNK, "whole chunks per wave");
     uint32_t k_voff[CPW], v_voff[CPW];
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
@@ -497,6 +498,12 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 if (sl == 2) { rd_v(2); rd_v(3); }
                 if (sl == 7) { rd_v1(0); rd_v1(1); }
                 if (sl == 8) { rd_v1(2); rd_v1(3); }
+                if constexpr (HALVES == 2) {          // QK(u+2) operands, after QK(u+1) issued
+                    if (sl == 10) { rd_k(0); rd_k(1); }
+                    if (sl == 11) { rd_k(2); rd_k(3); }
+                    if (sl == 12) { rd_k(4); rd_k(5); }
+                    if (sl == 13) { rd_k(6); rd_k(7); }
+                }
                 if (sl < 6) qk_one(sl);
                 else if (sl == 7) qk_one(6);
                 else if (sl == 9) qk_one(7);
