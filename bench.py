@@ -38,7 +38,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E (published)
 PREFILL_SRCS = [os.path.join(ROOT, "masked_attention_attn_amd", "csrc", f)
-                for f in ("fwd_bf16.cuh", "fwd_bf16_d64.hip")]
+                for f in ("fwd_bf16.cuh", "fwd_bf16_d64.hip", "mfma_lds.cuh")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_p11616_traffic.json")
 
 
