@@ -289,16 +289,16 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
     const int hl = lane >> 5, l32 = lane & 31;
 
     // LDS byte o of a block: row r = o / RB, chunk position p.  K row r holds
-    // key swap_bits23(r), chunk p = global chunk p ^ (r & 7); V row r holds key r,
-    // chunk p = global chunk p ^ 2(r & 3).  A Q slot holds the group's heads as
+    // key swap_bits23(r), chunk p = global chunk p ^ k_swz(r); V row r holds key r,
+    // chunk p = global chunk p ^ v_swz(r).  A Q slot holds the group's heads as
     // rows in order.
     uint32_t k_voff[NCH], v_voff[NCH];
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
         const int o = ch * 1024 + lane * 16;
         const int r = o / RB, p = (o % RB) / 16;
-        k_voff[ch] = (uint32_t)(swap_bits23(r) * RB + (p ^ (r & 7)) * 16);
-        v_voff[ch] = (uint32_t)(r * RB + (p ^ (2 * (r & 3))) * 16);
+        k_voff[ch] = (uint32_t)(swap_bits23(r) * RB + (p ^ k_swz<D>(r)) * 16);
+        v_voff[ch] = (uint32_t)(r * RB + (p ^ v_swz<D>(r)) * 16);
     }
     auto kblk = [&](int sl) { return lds + sl * 2 * BLK; };
     auto vblk = [&](int sl) { return lds + sl * 2 * BLK + BLK; };
@@ -378,7 +378,7 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
     // Vᵀ operand reads (as in the prefill kernel)
     const int vg = lane >> 4, vm = lane & 15;
     const int vrow = (vg >> 1) * 8 + (vm >> 2);
-    const int vfv = 2 * (vrow & 3);
+    const int vfv = v_swz<D>(vrow);
     const int vc0 = 2 * (vg & 1) + ((vm & 3) >> 1);
     const int vin = (vm & 1) * 4;
     auto v_opnd = [&](int sl, int k2, int db) -> u32x4 {
@@ -426,7 +426,7 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
         f32x16 S = {};
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (((2 * kk + hl) ^ (l32 & 7)) * 8));
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (((2 * kk + hl) ^ k_swz<D>(l32)) * 8));
             S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], S, 0, 0, 0);
         }
         const int nvalid = cc.t_end - (cc.s * kDecodeSplit + cc.i * CK);   // keys before the item's end

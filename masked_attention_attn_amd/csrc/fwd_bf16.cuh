@@ -31,12 +31,11 @@
 // LDS tiles are filled by direct global->LDS buffer loads (no staging
 // registers): lane i of a load writes bytes [16i, 16i+16) of a 1 KiB chunk,
 // so each lane picks the global 16 bytes that belong there.  Both tiles are
-// unpadded with an XOR swizzle of the 16-byte chunk index: K chunk c of row r
-// sits at c ^ (r & 7) (conflict-free 16-byte row reads); V keeps its natural
-// [key][d] layout with chunk c of row r at c ^ 2(r & 3), and the Vᵀ operand
-// is read with the gfx950 transposing LDS read (ds_read_b64_tr_b16: within
-// each 16-lane group, lane j receives element j%4 of the 8-byte rows
-// addressed by lanes j/4 + 4k), which the swizzle keeps conflict-free.
+// unpadded with an XOR swizzle of the 16-byte chunk index (k_swz / v_swz,
+// chosen so that no read has bank conflicts); V keeps its natural [key][d]
+// layout and the Vᵀ operand is read with the gfx950 transposing LDS read
+// (ds_read_b64_tr_b16: within each 16-lane group, lane j receives element j%4
+// of the 8-byte rows addressed by lanes j/4 + 4k).
 //
 // Software pipeline.  Step u holds the raw scores S_u of key block u in
 // registers (computed by step u-1) and, in one straight block of code whose
@@ -216,7 +215,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // ---- tile loads straight into LDS: a tile is 8 KiB = 8 chunks of 1 KiB, wave w
     // fills chunks CPW*w .. CPW*w + CPW-1.  For LDS byte o of a tile (row r = o / RB, chunk
     // position p), K takes key perm(r) (bits 2,3 swapped within 32-row blocks),
-    // chunk p ^ (r & 7); V takes key r, chunk p ^ 2(r & 3).  Keys past Tk read
+    // chunk p ^ k_swz(r); V takes key r, chunk p ^ v_swz(r).  Keys past Tk read
     // as zeros (the buffer range check covers the per-lane offset, which is why the
     // tile offset is added there and not to the scalar offset; they are masked).
     constexpr int NCHUNK = TK * D * 2 / 1024;   // 1 KiB chunks per tile
@@ -228,8 +227,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const int o = (CPW * wave + i) * 1024 + lane * 16;
         const int r = o / L::RB, pch = (o % L::RB) / 16;
         const int kr = (r & ~31) | swap_bits23(r & 31);
-        k_voff[i] = (uint32_t)(kr * D + (pch ^ (r & 7)) * 8) * 2u;
-        v_voff[i] = (uint32_t)(r * D + (pch ^ (2 * (r & 3))) * 8) * 2u;
+        k_voff[i] = (uint32_t)(kr * D + (pch ^ k_swz<D>(r)) * 8) * 2u;
+        v_voff[i] = (uint32_t)(r * D + (pch ^ v_swz<D>(r)) * 8) * 2u;
     }
     // Ring slots are counted from the first visited tile: tile t sits in K slot
     // (t - t_first) % K_RING and V slot (t - t_first) % V_RING; kcur / vcur
@@ -251,13 +250,13 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     int kcur = 0, vcur = 0;
     static_assert(L::K_RING == 3 && L::V_RING == 2, "slot arithmetic below");
     // Per-lane LDS offsets of the operand reads.
-    //  K (A of K·Qᵀ): row hf*32 + l%32, chunk (kk*2 + hl) ^ (l & 7).
-    const int kx = hl ^ (l32 & 7);
+    //  K (A of K·Qᵀ): row hf*32 + l%32, chunk (kk*2 + hl) ^ k_swz(l % 32).
+    const int kx = hl ^ k_swz<D>(l32);
     //  Vᵀ (A of Vᵀ·Pᵀ, transposed read): lane 16g+m addresses key row
     //  (g/2)*8 + m/4 (+4 for the second half) and d = db*32 + 16(g%2) + 4(m%4).
     const int vg = lane >> 4, vm = lane & 15;
     const int vrow = (vg >> 1) * 8 + (vm >> 2);
-    const int vfv = 2 * (vrow & 3);
+    const int vfv = v_swz<D>(vrow);
     const int vc0 = 2 * (vg & 1) + ((vm & 3) >> 1);
     const int vin = (vm & 1) * 4;                    // element offset inside the 16-byte chunk
     auto v_off = [&](int db) { return vrow * D + (((db * 4 + vc0) ^ vfv) * 8) + vin; };

@@ -12,6 +12,16 @@ __device__ __forceinline__ int swap_bits23(int r) {
     return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// XOR swizzles of the 16-byte chunk index in LDS rows of D bf16 (2D bytes; the
+// LDS serves 64 banks of 4 bytes per pass).  Chunk c of row r sits at
+// c ^ k_swz(r) in a K tile and at c ^ v_swz(r) in a V tile, which makes the
+// K operand reads and the transposing Vᵀ reads (4 rows x 4 chunks per pass)
+// free of bank conflicts at D = 128, where a row fills a 256-byte bank cycle;
+// at D = 64 the K swizzle r & 7 measured faster than the shifted form a
+// 64-bank model prefers.
+template <int D> __device__ __forceinline__ int k_swz(int r) { return D == 64 ? (r & 7) : (r & 15); }
+template <int D> __device__ __forceinline__ int v_swz(int r) { return D == 64 ? 2 * (r & 3) : 4 * (r & 3); }
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // max / sum of x over lanes l and l^32 (v_permlane32_swap exchanges the two
