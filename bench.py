@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--settle", type=float, default=0.5,
                    help="seconds of untimed steps before the warm-up (clock ramp)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the sections measured outside the step: the P-sweep of the prefill "
+                        "(memory and TFLOP/s at P = 1,944 .. 32,122) and the packed varlen calls")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -115,6 +118,110 @@ def cpu_baseline(w, budget_s):
             "sample": f"{heads} of {H} heads of the P=11,616 prefill (all {Tq} query rows each), "
                       f"float64 NumPy with the full masked softmax per head; {dt:.1f} s",
             "seconds": dt}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+SWEEP_P = (1944, 3952, 7776, 11616, 32122)   # the pages' patch counts, up to their OOM point
+
+
+def p_sweep(torch, ma, dev):
+    """Masked prefill with LSE, bf16, B1 H16 D64, last 16 keys padded, at each P:
+    the call-level extra device bytes (the O and LSE the caller provides; the library
+    allocates nothing, which the free-memory reading around the call confirms) next to the
+    score matrix a materialising path would hold, and the TFLOP/s."""
+    rows = []
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    H, D = 16, 64
+    for P in SWEEP_P:
+        q, k, v = (torch.randn(1, H, P, D, device=dev, generator=g).mul_(0.5).to(torch.bfloat16)
+                   for _ in range(3))
+        mask = torch.zeros(1, P, dtype=torch.uint8, device=dev)
+        mask[0, P - 16:] = 1
+        before_out = torch.cuda.mem_get_info()[0]
+        o = torch.empty_like(q)
+        lse = torch.empty(1, H, P, dtype=torch.float32, device=dev)
+        extra = torch.cuda.mem_get_info()[0]
+        call = lambda: ma.attn_fwd_lse(q, k, v, mask, D ** -0.5, out=o, lse=lse)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        free0 = torch.cuda.mem_get_info()[0]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 5
+        e0.record()
+        for _ in range(n):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        free1 = torch.cuda.mem_get_info()[0]
+        t = e0.elapsed_time(e1) / n / 1e3
+        flop = 4 * D * H * P * (P - 16)
+        rows.append({"P": P, "us": round(t * 1e6, 1), "tflops": round(flop / t / 1e12, 1),
+                     "call_extra_bytes": o.numel() * 2 + lse.numel() * 4,
+                     "allocator_view_extra_bytes": int(before_out - extra),
+                     "library_alloc_bytes_during_calls": int(free0 - free1),
+                     "score_matrix_bytes_avoided": H * P * P * 2})
+        del q, k, v, mask, o, lse
+    # call-level bytes are linear in P: fit bytes = a*P + c
+    xs = [r["P"] for r in rows]
+    ys = [r["call_extra_bytes"] for r in rows]
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    a = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sum((x - mx) ** 2 for x in xs)
+    c = my - a * mx
+    return {"workload": "masked prefill with LSE, bf16, B1 H16 D64, last 16 keys padded, N(0,1)*0.5",
+            "rows": rows, "linear_fit_bytes_per_P": round(a, 3), "linear_fit_intercept_bytes": round(c, 1)}
+
+
+def _time_call(torch, call, n=5, warm=3):
+    for _ in range(warm):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n / 1e3
+
+
+def varlen_section(torch, ma, W, dev):
+    """Packed variable-length calls (attn_fwd_varlen), each timed on its own:
+      * the P = 1,944 pair (1,944 and 1,700 patches, H16 D64) packed, beside the same pair
+        through the masked [B, H, T, D] path, where the 244 padded query rows and the padded
+        keys of the second sequence are computed or skipped per block;
+      * one ring hop: 8,192 packed queries against an 8,192-key chunk, H24 D128, with LSE.
+    FLOP are algorithmic: 4·D·H·sum_b len_q,b·len_k,b."""
+    res = {}
+    for name, w in (("p1944_packed", W.varlen_p1944_packed()), ("ring_hop_8192", W.varlen_ring_hop_8192())):
+        q, k, v, cq, ck = (t.to(dev) for t in (w.q, w.k, w.v, w.cu_q, w.cu_k))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=dev)
+        t = _time_call(torch, lambda: ma.attn_fwd_varlen(q, k, v, cq, ck, w.max_q, w.scale, out=o, lse=lse))
+        H, D = q.shape[1], q.shape[2]
+        flop = 4 * D * H * sum(a * b for a, b in zip(w.lens_q, w.lens_k))
+        res[name] = {"workload": w.name, "us": round(t * 1e6, 1), "tflops": round(flop / t / 1e12, 1),
+                     "frac_mfma": round(flop / t / 1e12 / PEAK_BF16_TFLOPS, 4), "algorithmic_flop": flop}
+        del q, k, v, cq, ck, o, lse
+    pd = W.patch_p1944()
+    q, k, v, m = (t.to(dev) for t in (pd.q, pd.k, pd.v, pd.mask))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    t = _time_call(torch, lambda: ma.attn_fwd_lse(q, k, v, m, pd.scale, out=o, lse=lse))
+    res["p1944_padded_masked_us"] = round(t * 1e6, 1)
+    return res
 
 
 def main():
@@ -207,6 +314,8 @@ def main():
 
     t_prefill, t_chunks, t_merge, t_append, t_decode = (span(0, 1), span(1, 2), span(2, 3), span(3, 4),
                                                         span(4, 5))
+    per_step = sorted(events[s][0].elapsed_time(events[s][1]) * 1e3 for s in range(args.steps))
+    pct = lambda f: round(per_step[min(len(per_step) - 1, int(f * (len(per_step) - 1) + 0.5))], 2)
     # ---- algorithmic work
     B, H, P, D = pf.q.shape
     n_valid = int((pf.mask[0] == 0).sum())
@@ -248,6 +357,9 @@ def main():
             "achieved": round(tf_prefill, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf_prefill / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
             "algorithmic_flop_per_launch": flop_prefill, "avg_launch_us": round(t_prefill * 1e6, 2),
+            "launch_us_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+            "exps_per_launch": H * P * n_valid,
+            "exp_rate_Gexp_per_s": round(H * P * n_valid / t_prefill / 1e9, 1),
         },
         "decode": {
             "metric": "decode HBM GB/s", "value": round(decode_gbps, 1), "unit": "GB/s",
@@ -272,9 +384,13 @@ def main():
             "decode_workspace_bytes": int(ws.numel()),
         },
     }
+    if not args.no_sweep:
+        out["p_sweep"] = p_sweep(torch, ma, dev)
+        out["varlen"] = varlen_section(torch, ma, W, dev)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(pf, args.cpu_seconds)
         cb.pop("seconds", None)
+        cb["cpu_model"] = cpu_model()
         out["cpu_baseline"] = cb
     print(json.dumps(out))
 

@@ -95,6 +95,36 @@ int attn_fwd_lse(const void* q, const void* k, const void* v,
                  float scale, int dtype, void* stream);
 
 /*
+ * attn_fwd_varlen — attention of packed variable-length sequences, with LSE.
+ *
+ * The packed call a ring-attention hop makes (sglang PR 49078 analysis,
+ * section "1. aiter.py", forward_ring_kv_chunk): a [T, H, D] query attends
+ * a KV chunk, sequences delimited by cumulative-length arrays, non-causal,
+ * returning the LSE as [H, Tq].  Sequence b owns query rows
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key rows [cu_seqlens_k[b],
+ * cu_seqlens_k[b+1]); its queries attend exactly its keys (no mask: the
+ * packing replaces padding).
+ *   q, o  [total_q, H, D] bf16      k, v  [total_k, H, D] bf16
+ *   cu_seqlens_q, cu_seqlens_k  [B+1] int32 device arrays, non-decreasing from
+ *       0 to total; owned by the caller and only read (same page: the cached
+ *       cu_seqlens tensors must not be mutated).  Entries are clamped to
+ *       [0, total], so a malformed array gives wrong rows but no access out
+ *       of range.
+ *   lse   [H, total_q] float32 (natural log) or NULL; -inf for a query whose
+ *       sequence has no keys (its O row is 0)
+ *   max_seqlen_q  at least the longest query sequence (it sizes the grid;
+ *       rows past it are not written); 0 <= max_seqlen_q <= total_q
+ * bf16 only (ATTN_ERR_UNSUPPORTED otherwise); H·D <= 2^22, total_k·H·D < 2^30
+ * and total_q·H·D < 2^31 (else ATTN_ERR_SHAPE); the other rules as
+ * attn_fwd_masked.  total_q = 0 or max_seqlen_q = 0 is a no-op.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                    void* o, float* lse,
+                    int B, int H, int total_q, int total_k, int max_seqlen_q, int D,
+                    float scale, int dtype, void* stream);
+
+/*
  * attn_merge_lse — combine n partial results over disjoint KV chunks.
  *
  * out = sum_i exp(lse_i - lse)·out_i with lse = log sum_i exp(lse_i), the

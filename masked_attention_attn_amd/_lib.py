@@ -29,8 +29,8 @@ STATUS = {
     8: "ATTN_ERR_ALIAS",
 }
 
-EXPORTS = ("attn_fwd_masked", "attn_fwd_lse", "attn_merge_lse", "kv_append", "attn_decode",
-           "attn_decode_workspace_bytes", "attn_status_string")
+EXPORTS = ("attn_fwd_masked", "attn_fwd_lse", "attn_fwd_varlen", "attn_merge_lse", "kv_append",
+           "attn_decode", "attn_decode_workspace_bytes", "attn_status_string")
 
 _lib = None
 
@@ -53,6 +53,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_fwd_masked.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P]
     lib.attn_fwd_lse.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, P]
+    lib.attn_fwd_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P]
     lib.attn_merge_lse.argtypes = [I, ctypes.POINTER(P), ctypes.POINTER(P), P, P, I, I, I, I, I, P]
     lib.kv_append.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
     lib.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, P, S, P]
@@ -60,7 +61,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_decode_workspace_bytes.restype = S
     lib.attn_status_string.argtypes = [I]
     lib.attn_status_string.restype = ctypes.c_char_p
-    for name in ("attn_fwd_masked", "attn_fwd_lse", "attn_merge_lse", "kv_append", "attn_decode"):
+    for name in ("attn_fwd_masked", "attn_fwd_lse", "attn_fwd_varlen", "attn_merge_lse", "kv_append",
+                 "attn_decode"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -149,6 +151,45 @@ def attn_fwd_masked(q, k, v, key_padding_mask=None, scale=None, out=None):
 def attn_fwd_lse(q, k, v, key_padding_mask=None, scale=None, out=None, lse=None):
     """As attn_fwd_masked, also returning the float32 natural-log LSE [B, H, Tq]."""
     return _fwd("attn_fwd_lse", q, k, v, key_padding_mask, scale, out, lse)
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=None, out=None, lse=None,
+                    want_lse: bool = True):
+    """Packed variable-length attention: q/o [total_q, H, D], k/v [total_k, H, D] (bf16),
+    cu_seqlens_* int32 [B+1] on the device; returns O (and the LSE [H, total_q])."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
+        _dev(t, n)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [total, H, D]")
+    total_q, H, D = q.shape
+    total_k = k.shape[0]
+    if k.shape != (total_k, H, D) or v.shape != (total_k, H, D):
+        raise ValueError("k/v must be [total_k, H, D] with q's H and D")
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("attn_fwd_varlen takes bfloat16 q, k, v")
+    if (cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32 or cu_seqlens_q.dim() != 1
+            or cu_seqlens_q.shape != cu_seqlens_k.shape):
+        raise ValueError("cu_seqlens_q / cu_seqlens_k must be int32 [B+1] of equal length")
+    B = cu_seqlens_q.shape[0] - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out")
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    if want_lse and lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    if want_lse:
+        _dev(lse, "lse")
+        if lse.shape != (H, total_q) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [H, total_q]")
+    _check("attn_fwd_varlen", load().attn_fwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(out),
+        _ptr(lse if want_lse else None), B, H, total_q, total_k, int(max_seqlen_q), D, float(scale),
+        ATTN_BF16, _stream(q.device)))
+    return (out, lse) if want_lse else out
 
 
 def attn_merge_lse(outs: Sequence[torch.Tensor], lses: Sequence[torch.Tensor], out=None,

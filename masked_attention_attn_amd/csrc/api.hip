@@ -66,6 +66,34 @@ int attn_fwd_lse(const void* q, const void* k, const void* v, const uint8_t* key
                       stream);
 }
 
+int attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, void* o, float* lse, int B, int H, int total_q,
+                    int total_k, int max_seqlen_q, int D, float scale, int dtype, void* stream) {
+    if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL;
+    if (!dtype_ok(dtype) || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+    if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_q > total_q)
+        return ATTN_ERR_SHAPE;
+    // One packed row is H·D elements; tile offsets of 64 rows must fit the 32-bit buffer offset.
+    if ((long long)H * D > (1ll << 22) || (long long)total_q * H * D > (1ll << 31) - 1 ||
+        (long long)total_k * H * D > (1ll << 30) - 1 ||
+        (long long)B * H * ((max_seqlen_q + 127) / 128) > (1ll << 31) - 64)
+        return ATTN_ERR_SHAPE;
+    if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
+    if (o == q || o == k || o == v || (lse && ((void*)lse == q || (void*)lse == k || (void*)lse == v ||
+                                               (void*)lse == o)))
+        return ATTN_ERR_ALIAS;
+    if (total_q == 0 || max_seqlen_q == 0) return ATTN_OK;      // no query rows: nothing to write
+    FwdArgs a{q, k, v, nullptr, o, lse, B, H, max_seqlen_q, 0, D, scale, stream};
+    a.varlen = true;
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.total_q = total_q;
+    a.total_k = total_k;
+    return finish(D == 64 ? launch_fwd_bf16_d64(a) : launch_fwd_bf16_d128(a));
+}
+
 int attn_merge_lse(int n_chunks, const void* const* outs, const float* const* lses, void* out,
                    float* lse_out, int B, int H, int T, int D, int dtype, void* stream) {
     if (!outs || !lses || !out) return ATTN_ERR_NULL;

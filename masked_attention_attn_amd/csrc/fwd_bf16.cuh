@@ -100,12 +100,18 @@ struct Lds {
     static constexpr int BYTES = ELEMS * (int)sizeof(bf16);
 };
 
-template <int D, bool WRITE_LSE>
+// VARLEN = false: q/k/v/o [B, H, T, D], mask [B, Tk] (or none), lse [B, H, Tq].
+// VARLEN = true: packed q/o [total_q, H, D], k/v [total_k, H, D] holding the
+// sequences back to back at the offsets cu_q / cu_k (B+1 entries, clamped to
+// [0, total]); lse [H, total_q]; no mask; Tq = the longest sequence (grid).
+template <int D, bool WRITE_LSE, bool VARLEN>
 __global__ __launch_bounds__(64 * Cfg<D>::NWAVE, 1)
 void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                      const bf16* __restrict__ v, const uint8_t* __restrict__ mask,
                      bf16* __restrict__ o, float* __restrict__ lse,
-                     int H, int Tq, int Tk, float c, int n_qt, int total) {
+                     int H, int Tq, int Tk, float c, int n_qt, int total,
+                     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+                     int total_q, int total_k) {
     using L = Lds<D>;
     constexpr int NWAVE = Cfg<D>::NWAVE;
     constexpr int NT = 64 * NWAVE;        // threads per workgroup
@@ -130,11 +136,37 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int bh = logical / n_qt;
     const int qt = logical - bh * n_qt;
     const int b = bh / H;
-    const bf16* qp = q + (size_t)bh * Tq * D;
-    const uint8_t* mp = mask ? mask + (size_t)b * Tk : nullptr;
-    const uint32_t kv_bytes = (uint32_t)Tk * D * (uint32_t)sizeof(bf16);
-    const i32x4_sgpr krs = make_rsrc(k + (size_t)bh * Tk * D, kv_bytes);
-    const i32x4_sgpr vrs = make_rsrc(v + (size_t)bh * Tk * D, kv_bytes);
+    // This (b, h)'s rows: lengths, first rows and row strides (elements).
+    int Tq_, Tk_, rs;                     // rows of Q/O and K/V, row stride
+    size_t q_row0, k_row0, l_row0;        // element offset of row 0 (LSE: index of row 0)
+    size_t l_rs;                          // LSE stride between rows
+    if constexpr (VARLEN) {
+        const int h = bh - b * H;
+        const int sq = min(max(cu_q[b], 0), total_q), eq = min(max(cu_q[b + 1], sq), total_q);
+        const int sk = min(max(cu_k[b], 0), total_k), ek = min(max(cu_k[b + 1], sk), total_k);
+        Tq_ = __builtin_amdgcn_readfirstlane(eq - sq);
+        Tk_ = __builtin_amdgcn_readfirstlane(ek - sk);
+        rs = H * D;
+        q_row0 = ((size_t)sq * H + h) * D;
+        k_row0 = ((size_t)sk * H + h) * D;
+        l_row0 = (size_t)h * total_q + sq;
+        l_rs = 1;
+    } else {
+        Tq_ = Tq;
+        Tk_ = Tk;
+        rs = D;
+        q_row0 = (size_t)bh * Tq * D;
+        k_row0 = (size_t)bh * Tk * D;
+        l_row0 = (size_t)bh * Tq;
+        l_rs = 1;
+    }
+    if (qt * BM >= Tq_) return;           // whole workgroup: past this sequence's queries
+    const bf16* qp = q + q_row0;
+    const uint8_t* mp = VARLEN ? nullptr : mask ? mask + (size_t)b * Tk_ : nullptr;
+    // K/V buffer range ends after the last row, so rows >= Tk_ read as zero.
+    const uint32_t kv_bytes = Tk_ > 0 ? (uint32_t)((Tk_ - 1) * rs + D) * (uint32_t)sizeof(bf16) : 0u;
+    const i32x4_sgpr krs = make_rsrc(k + k_row0, kv_bytes);
+    const i32x4_sgpr vrs = make_rsrc(v + k_row0, kv_bytes);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -147,14 +179,14 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // whether a padded key lies strictly between them (an interior hole).  Without
     // holes the only padded keys a visited block can hold lie outside
     // [first, last], so the per-block masks follow from the two indices alone.
-    int first = 0, last = Tk - 1, holes = 0;
+    int first = 0, last = Tk_ - 1, holes = 0;
     if (mp) {
         int f = 0x7fffffff, l = -1, n = 0;
-        for (int base = tid * 16; base < Tk; base += NT * 16) {
+        for (int base = tid * 16; base < Tk_; base += NT * 16) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int key = base + j;
-                if (key < Tk && mp[key] == 0) {
+                if (key < Tk_ && mp[key] == 0) {
                     f = min(f, key);
                     l = max(l, key);
                     ++n;
@@ -206,10 +238,10 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     bf16x8 qreg[NB][KSTEPS];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        const int row = min(q0 + nb * 32 + l32, Tq - 1);
+        const int row = min(q0 + nb * 32 + l32, Tq_ - 1);
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk)
-            qreg[nb][kk] = as_bf16x8(ldg128(qp + (size_t)row * D + kk * 16 + hl * 8));
+            qreg[nb][kk] = as_bf16x8(ldg128(qp + (size_t)row * rs + kk * 16 + hl * 8));
     }
 
     // ---- tile loads straight into LDS: a tile is 8 KiB = 8 chunks of 1 KiB, wave w
@@ -227,8 +259,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const int o = (CPW * wave + i) * 1024 + lane * 16;
         const int r = o / L::RB, pch = (o % L::RB) / 16;
         const int kr = (r & ~31) | swap_bits23(r & 31);
-        k_voff[i] = (uint32_t)(kr * D + (pch ^ k_swz<D>(r)) * 8) * 2u;
-        v_voff[i] = (uint32_t)(r * D + (pch ^ v_swz<D>(r)) * 8) * 2u;
+        k_voff[i] = (uint32_t)(kr * rs + (pch ^ k_swz<D>(r)) * 8) * 2u;
+        v_voff[i] = (uint32_t)(r * rs + (pch ^ v_swz<D>(r)) * 8) * 2u;
     }
     // Ring slots are counted from the first visited tile: tile t sits in K slot
     // (t - t_first) % K_RING and V slot (t - t_first) % V_RING; kcur / vcur
@@ -240,12 +272,12 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     auto dma_k = [&](int t, int sl) {
 #pragma unroll
         for (int i = 0; i < CPW; ++i)
-            dma16(krs, kslot_b(sl) + (CPW * wave + i) * 1024, k_voff[i] + (uint32_t)t * TK * D * 2u, 0u);
+            dma16(krs, kslot_b(sl) + (CPW * wave + i) * 1024, k_voff[i] + (uint32_t)t * TK * rs * 2u, 0u);
     };
     auto dma_v = [&](int t, int sl) {
 #pragma unroll
         for (int i = 0; i < CPW; ++i)
-            dma16(vrs, vslot_b(sl) + (CPW * wave + i) * 1024, v_voff[i] + (uint32_t)t * TK * D * 2u, 0u);
+            dma16(vrs, vslot_b(sl) + (CPW * wave + i) * 1024, v_voff[i] + (uint32_t)t * TK * rs * 2u, 0u);
     };
     int kcur = 0, vcur = 0;
     static_assert(L::K_RING == 3 && L::V_RING == 2, "slot arithmetic below");
@@ -264,7 +296,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // Lane j reports whether key t*TK + j is padded or past Tk (lanes >= TK report 1).
     auto pad_flag = [&](int t) -> int {
         const int key = t * TK + lane;
-        if (lane >= TK || key >= Tk) return 1;
+        if (lane >= TK || key >= Tk_) return 1;
         return mp ? (int)(mp[key] != 0) : 0;
     };
 
@@ -571,8 +603,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const float lt = pair_sum(lsum[nb]);
         const float inv = lt > 0.f ? 1.0f / lt : 0.f;
         const int qi = q0 + nb * 32 + l32;
-        if (qi < Tq) {
-            bf16* orow = o + ((size_t)bh * Tq + qi) * D;
+        if (qi < Tq_) {
+            bf16* orow = o + q_row0 + (size_t)qi * rs;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -583,27 +615,28 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     *reinterpret_cast<u32x2*>(orow + db * 32 + g * 8 + hl * 4) = w;
                 }
             if (WRITE_LSE && hl == 0)
-                lse[(size_t)bh * Tq + qi] = lt > 0.f ? (mc[nb] + __log2f(lt)) * kLn2 : kNegInf;
+                lse[l_row0 + (size_t)qi * l_rs] = lt > 0.f ? (mc[nb] + __log2f(lt)) * kLn2 : kNegInf;
         }
     }
 }
 
-template <int D, bool WRITE_LSE>
+template <int D, bool WRITE_LSE, bool VARLEN>
 hipError_t launch_one(const FwdArgs& a) {
     using L = Lds<D>;
-    auto kern = fwd_bf16_kernel<D, WRITE_LSE>;
+    auto kern = fwd_bf16_kernel<D, WRITE_LSE, VARLEN>;
     // LDS above 64 KiB must be opted into once per kernel (thread-safe static init).
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
     if (attr != hipSuccess) return attr;
     constexpr int BM = kBM<D>;
-    const int n_qt = (a.Tq + BM - 1) / BM;
+    const int n_qt = (a.Tq + BM - 1) / BM;       // varlen: Tq = the longest sequence
     const int total = a.B * a.H * n_qt;
     const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
     const float c = a.scale * kLog2e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * Cfg<D>::NWAVE), L::BYTES, (hipStream_t)a.stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.mask,
-                       (bf16*)a.o, a.lse, a.H, a.Tq, a.Tk, c, n_qt, total);
+                       (bf16*)a.o, a.lse, a.H, a.Tq, a.Tk, c, n_qt, total,
+                       a.cu_q, a.cu_k, a.total_q, a.total_k);
     return hipGetLastError();
 }
 

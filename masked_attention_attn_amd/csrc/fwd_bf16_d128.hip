@@ -4,6 +4,8 @@
 
 namespace mattn {
 hipError_t launch_fwd_bf16_d128(const FwdArgs& a) {
-    return a.lse ? fwdk::launch_one<128, true>(a) : fwdk::launch_one<128, false>(a);
+    if (a.varlen)
+        return a.lse ? fwdk::launch_one<128, true, true>(a) : fwdk::launch_one<128, false, true>(a);
+    return a.lse ? fwdk::launch_one<128, true, false>(a) : fwdk::launch_one<128, false, false>(a);
 }
 }  // namespace mattn

@@ -5,6 +5,8 @@
 
 namespace mattn {
 hipError_t launch_fwd_bf16_d64(const FwdArgs& a) {
-    return a.lse ? fwdk::launch_one<64, true>(a) : fwdk::launch_one<64, false>(a);
+    if (a.varlen)
+        return a.lse ? fwdk::launch_one<64, true, true>(a) : fwdk::launch_one<64, false, true>(a);
+    return a.lse ? fwdk::launch_one<64, true, false>(a) : fwdk::launch_one<64, false, false>(a);
 }
 }  // namespace mattn

@@ -13,9 +13,14 @@ struct FwdArgs {
     const void* q; const void* k; const void* v;
     const uint8_t* mask;
     void* o; float* lse;          // lse may be null
-    int B, H, Tq, Tk, D;
+    int B, H, Tq, Tk, D;          // varlen: B sequences, Tq = the longest query sequence
     float scale;
     void* stream;
+    // packed variable-length layout ([total, H, D], offsets in cu_q / cu_k)
+    bool varlen = false;
+    const int32_t* cu_q = nullptr;
+    const int32_t* cu_k = nullptr;
+    int total_q = 0, total_k = 0;
 };
 
 constexpr int kMaxMergeChunks = 32;

@@ -5,6 +5,6 @@ benchmark's CPU-baseline leg, never by the library itself.  It shares no code
 with the HIP path.
 """
 from .attention import (  # noqa: F401
-    scores, masked_softmax, attention, merge_lse, kv_append, decode,
+    scores, masked_softmax, attention, attention_varlen, merge_lse, kv_append, decode,
     attention_flops, score_matrix_bytes, kv_bytes_per_token, decode_kv_bytes,
 )

@@ -37,7 +37,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "scores", "masked_softmax", "attention", "merge_lse", "kv_append", "decode",
+    "scores", "masked_softmax", "attention", "attention_varlen", "merge_lse", "kv_append", "decode",
     "attention_flops", "score_matrix_bytes", "kv_bytes_per_token", "decode_kv_bytes",
 ]
 
@@ -114,6 +114,48 @@ def attention(q, k, v, key_padding_mask=None, scale=None, rows=None):
             O[b, h] = W @ v[b, h]
             live = np.isfinite(m)
             LSE[b, h, live] = m[live] + np.log(l[live])
+    return O, LSE
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale=None):
+    """Attention of packed variable-length sequences (no mask, non-causal).
+
+    The packed layout a ring-attention hop passes to its varlen kernel
+    (sglang PR 49078 analysis, section "1. aiter.py", forward_ring_kv_chunk):
+    q [total_q, H, D], k and v [total_k, H, D], and cumulative lengths
+    cu_seqlens_q / cu_seqlens_k of B + 1 entries from 0 to the totals.
+    Sequence b is query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1 against
+    key rows cu_seqlens_k[b] .. cu_seqlens_k[b+1] - 1; nothing else is
+    attended, so each sequence is exactly ``attention`` on its own slice.
+
+    Returns O [total_q, H, D] and LSE [H, total_q] (the page's LSE layout) in
+    float64; a sequence with no keys has O = 0 and LSE = -inf.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cq = np.asarray(_f64(cu_seqlens_q), dtype=np.int64)
+    ck = np.asarray(_f64(cu_seqlens_k), dtype=np.int64)
+    total_q, H, D = q.shape
+    assert k.shape[1:] == (H, D) and v.shape == k.shape
+    assert cq.shape == ck.shape and cq.ndim == 1 and cq.size >= 1
+    assert cq[0] == 0 and ck[0] == 0 and cq[-1] == total_q and ck[-1] == k.shape[0]
+    assert np.all(np.diff(cq) >= 0) and np.all(np.diff(ck) >= 0)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    O = np.zeros((total_q, H, D))
+    LSE = np.full((H, total_q), NEG_INF)
+    for b in range(cq.size - 1):
+        q0, q1, k0, k1 = int(cq[b]), int(cq[b + 1]), int(ck[b]), int(ck[b + 1])
+        if q1 == q0:
+            continue
+        if k1 == k0:                    # no keys: the all-padded case
+            continue
+        # [T, H, D] -> [1, H, T, D]
+        qs = q[q0:q1].transpose(1, 0, 2)[None]
+        ks = k[k0:k1].transpose(1, 0, 2)[None]
+        vs = v[k0:k1].transpose(1, 0, 2)[None]
+        Ob, Lb = attention(qs, ks, vs, None, scale)
+        O[q0:q1] = Ob[0].transpose(1, 0, 2)
+        LSE[:, q0:q1] = Lb[0]
     return O, LSE
 
 

@@ -133,3 +133,30 @@ def test_workspace_grows_linearly_with_cache_capacity(lib):
     a = lib.attn_decode_workspace_bytes(32, 32, 8, 8256, 128)
     b = lib.attn_decode_workspace_bytes(32, 32, 8, 16512, 128)
     assert a > 0 and b <= 2 * a + 32 * 32 * (128 + 2) * 4
+
+
+def test_varlen_validation(lib):
+    CQ, CK = 0x70000, 0x80000
+
+    def vl(**kw):
+        a = dict(q=A, k=B_, v=C, cq=CQ, ck=CK, o=O, lse=L, B=2, H=4, tq=100, tk=90, mq=60, D=64,
+                 scale=0.125, dtype=1)
+        a.update(kw)
+        return lib.attn_fwd_varlen(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["o"], a["lse"], a["B"],
+                                   a["H"], a["tq"], a["tk"], a["mq"], a["D"], a["scale"], a["dtype"], None)
+    assert vl(cq=0) == 1
+    assert vl(ck=0) == 1
+    assert vl(o=0) == 1
+    assert vl(dtype=0) == 3             # bf16 only
+    assert vl(D=96) == 3
+    assert vl(B=0) == 2
+    assert vl(mq=101) == 2              # longer than the packed total
+    assert vl(tk=-1) == 2
+    assert vl(H=1 << 16, D=128) == 2    # one packed row too wide for the 32-bit tile offsets
+    assert vl(tk=(1 << 30) // 256) == 2
+    assert vl(scale=0.0) == 6
+    assert vl(k=B_ + 4) == 7
+    assert vl(o=A) == 8
+    assert vl(lse=C) == 8
+    assert vl(tq=0, mq=0) == 0          # nothing to do: no launch, no pointer touched
+    assert vl(mq=0) == 0

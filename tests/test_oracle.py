@@ -354,3 +354,82 @@ def test_attention_flops_count():
     H, D, Tq, n = 2, 3, 4, [5, 2]
     macs = sum(H * Tq * nv * D * 2 for nv in n)
     assert oracle.attention_flops(H, D, Tq, n) == 2 * macs
+
+
+# ---- packed variable-length sequences --------------------------------------------
+
+def _varlen_brute(q, k, v, cq, ck, scale):
+    """Row by row over the packed layout with the pure-Python attend_row."""
+    total_q, H, D = q.shape
+    O = np.zeros((total_q, H, D))
+    L = np.full((H, total_q), -np.inf)
+    for b in range(len(cq) - 1):
+        keys = range(ck[b], ck[b + 1])
+        for i in range(cq[b], cq[b + 1]):
+            for h in range(H):
+                kk = [k[j, h].tolist() for j in keys]
+                vv = [v[j, h].tolist() for j in keys]
+                o, l = brute.attend_row(q[i, h].tolist(), kk, vv, [False] * len(kk), scale)
+                if l != -math.inf:
+                    O[i, h] = o
+                L[h, i] = l
+    return O, L
+
+
+@pytest.mark.parametrize("lens", [([3], [4]), ([2, 0, 5], [3, 4, 0]), ([1, 4, 2, 3], [6, 1, 2, 5]),
+                                  ([0, 0], [2, 3])])
+def test_varlen_matches_brute_force(lens):
+    lq, lk = lens
+    r = _rng(sum(lq) * 7 + sum(lk))
+    H, D = 2, 5
+    cq, ck = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q = r.standard_normal((cq[-1], H, D)) * 1.3
+    k = r.standard_normal((ck[-1], H, D))
+    v = r.standard_normal((ck[-1], H, D))
+    scale = 0.7
+    O, L = oracle.attention_varlen(q, k, v, cq, ck, scale)
+    bO, bL = _varlen_brute(q, k, v, cq, ck, scale)
+    assert np.array_equal(np.isneginf(L), np.isneginf(bL))
+    live = ~np.isneginf(bL)
+    assert np.max(np.abs(L[live] - bL[live]), initial=0.0) <= 1e-12
+    assert np.max(np.abs(O - bO), initial=0.0) <= 1e-12
+
+
+def test_varlen_empty_key_sequence_gives_zero_and_neg_inf():
+    w = workloads.make_varlen([3, 2], [0, 4], 2, 8, torch.float32, seed=3)
+    O, L = oracle.attention_varlen(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale)
+    assert np.all(O[:3] == 0.0) and np.all(np.isneginf(L[:, :3]))
+    assert np.all(np.isfinite(L[:, 3:]))
+
+
+def test_varlen_sequences_do_not_see_each_other():
+    w = workloads.make_varlen([4, 5, 3], [6, 2, 7], 2, 8, torch.float32, seed=4)
+    O, L = oracle.attention_varlen(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale)
+    k2, v2 = w.k.clone(), w.v.clone()
+    k2[6:8] += 3.0                       # only sequence 1's keys and values change
+    v2[6:8] -= 2.0
+    O2, L2 = oracle.attention_varlen(w.q, k2, v2, w.cu_q, w.cu_k, w.scale)
+    for s, e in ((0, 4), (9, 12)):
+        assert np.array_equal(O[s:e], O2[s:e]) and np.array_equal(L[:, s:e], L2[:, s:e])
+    assert not np.allclose(O[4:9], O2[4:9])
+
+
+def test_varlen_equals_padded_masked_dense():
+    # Scattering the packed sequences into [B, H, T, D] with trailing key padding is the
+    # masked definition; the valid query rows must agree (padded queries are not packed).
+    lq, lk = [5, 1, 7], [3, 8, 6]
+    w = workloads.make_varlen(lq, lk, 3, 8, torch.float32, seed=5)
+    O, L = oracle.attention_varlen(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale)
+    B, H, D, Tq, Tk = 3, 3, 8, max(lq), max(lk)
+    qd = torch.zeros(B, H, Tq, D)
+    kd = torch.zeros(B, H, Tk, D)
+    vd = torch.zeros(B, H, Tk, D)
+    cq, ck = w.cu_q.tolist(), w.cu_k.tolist()
+    for b in range(B):
+        qd[b, :, :lq[b]] = w.q[cq[b]:cq[b + 1]].transpose(0, 1)
+        kd[b, :, :lk[b]] = w.k[ck[b]:ck[b + 1]].transpose(0, 1)
+        vd[b, :, :lk[b]] = w.v[ck[b]:ck[b + 1]].transpose(0, 1)
+    Od, Ld = oracle.attention(qd, kd, vd, workloads.mask_from_valid_lengths(lk, Tk), w.scale)
+    for b in range(B):
+        assert np.allclose(O[cq[b]:cq[b + 1]], Od[b, :, :lq[b]].transpose(1, 0, 2), atol=1e-13, rtol=0)
+        assert np.allclose(L[:, cq[b]:cq[b + 1]], Ld[b, :, :lq[b]], atol=1e-13, rtol=0)

@@ -297,3 +297,105 @@ def test_gqa_decode_b32_sampled_heads(ma):
     got_o = torch.stack([o[b, h, 0] for b, h in heads])
     got_l = torch.stack([l[b, h] for b, h in heads])
     check_attn(got_o, got_l, Or, Lr, torch.bfloat16, "decode sampled heads")
+
+
+# ---- packed variable-length sequences (cu_seqlens) -------------------------------------
+
+VARLEN = [
+    # lens_q, lens_k, H, D
+    ([1], [1], 1, 64),
+    ([300], [257], 2, 64),
+    ([5, 0, 300, 64], [70, 33, 0, 129], 2, 64),
+    ([256, 257, 1], [64, 65, 640], 3, 64),
+    ([700, 100, 256], [700, 100, 513], 2, 64),
+    ([77], [1000], 1, 128),
+    ([130, 0, 31, 257], [300, 5, 64, 0], 2, 128),
+    ([513, 200], [200, 513], 2, 128),
+]
+
+
+def run_varlen(ma, w, lse=True):
+    q, k, v, cq, ck = (t.to(DEV) for t in (w.q, w.k, w.v, w.cu_q, w.cu_k))
+    res = ma.attn_fwd_varlen(q, k, v, cq, ck, w.max_q, w.scale, want_lse=lse)
+    torch.cuda.synchronize()
+    return res if lse else (res, None)
+
+
+@pytest.mark.parametrize("case", VARLEN)
+def test_fwd_varlen(ma, case):
+    lq, lk, H, D = case
+    w = W.make_varlen(lq, lk, H, D, seed=len(lq) + H)
+    o, l = run_varlen(ma, w)
+    Oref, Lref = oracle.attention_varlen(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale)
+    check_attn(o, l.t(), Oref, Lref.T, torch.bfloat16, f"varlen {case}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_fwd_varlen_without_lse_matches_with(ma, D):
+    w = W.make_varlen([200, 3, 333], [90, 400, 0], 2, D, seed=D)
+    o1, _ = run_varlen(ma, w, lse=False)
+    o2, _ = run_varlen(ma, w, lse=True)
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_fwd_varlen_bitwise_equals_padded_masked(ma, D):
+    # The same sequences laid out [B, H, T, D] with trailing key padding go through the masked
+    # entry point; each valid query row must match the packed result bit for bit.
+    lq, lk = [300, 45, 129], [257, 511, 64]
+    w = W.make_varlen(lq, lk, 2, D, seed=11)
+    o, l = run_varlen(ma, w)
+    B, H, Tq, Tk = 3, 2, max(lq), max(lk)
+    cq, ck = w.cu_q.tolist(), w.cu_k.tolist()
+    qd = torch.zeros(B, H, Tq, D, dtype=torch.bfloat16)
+    kd = torch.zeros(B, H, Tk, D, dtype=torch.bfloat16)
+    vd = torch.zeros(B, H, Tk, D, dtype=torch.bfloat16)
+    for b in range(B):
+        qd[b, :, :lq[b]] = w.q[cq[b]:cq[b + 1]].transpose(0, 1)
+        kd[b, :, :lk[b]] = w.k[ck[b]:ck[b + 1]].transpose(0, 1)
+        vd[b, :, :lk[b]] = w.v[ck[b]:ck[b + 1]].transpose(0, 1)
+    m = W.mask_from_valid_lengths(lk, Tk)
+    od, ld = ma.attn_fwd_lse(qd.to(DEV), kd.to(DEV), vd.to(DEV), m.to(DEV), w.scale)
+    torch.cuda.synchronize()
+    o, l, od, ld = o.cpu(), l.cpu(), od.cpu(), ld.cpu()
+    for b in range(B):
+        assert torch.equal(o[cq[b]:cq[b + 1]], od[b, :, :lq[b]].transpose(0, 1)), b
+        assert torch.equal(l[:, cq[b]:cq[b + 1]], ld[b, :, :lq[b]]), b
+
+
+def test_fwd_varlen_rows_past_max_seqlen_untouched(ma):
+    # Rows of a sequence longer than max_seqlen_q are not written (the grid covers max_seqlen_q).
+    w = W.make_varlen([40, 300], [50, 60], 2, 64, seed=2)
+    q, k, v, cq, ck = (t.to(DEV) for t in (w.q, w.k, w.v, w.cu_q, w.cu_k))
+    out = torch.full_like(q, 7.0)
+    lse = torch.full((2, 340), 7.0, device=DEV)
+    ma.attn_fwd_varlen(q, k, v, cq, ck, 256, w.scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.attention_varlen(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale)
+    rows = list(range(0, 40 + 256))
+    check_attn(out[rows], lse[:, rows].t(), Oref[rows], Lref[:, rows].T, torch.bfloat16, "varlen truncated")
+    assert torch.all(out[40 + 256:] == 7.0) and torch.all(lse[:, 40 + 256:] == 7.0)
+
+
+def test_fwd_varlen_malformed_cu_stays_in_range(ma):
+    # Decreasing and out-of-range entries are clamped to [0, total]: results are defined by
+    # the clamped offsets and nothing outside the tensors is touched.
+    w = W.make_varlen([100, 100], [80, 80], 2, 64, seed=9)
+    q, k, v = (t.to(DEV) for t in (w.q, w.k, w.v))
+    cq = torch.tensor([0, 150, 120], dtype=torch.int32, device=DEV)     # end < start for b = 1
+    ck = torch.tensor([-5, 1000, 2000], dtype=torch.int32, device=DEV)
+    out = torch.zeros_like(q)
+    o, l = ma.attn_fwd_varlen(q, k, v, cq, ck, 200, w.scale, out=out)
+    torch.cuda.synchronize()
+    # clamped: sequence 0 = queries 0..149 vs keys 0..159; sequence 1 = no rows
+    Oref, Lref = oracle.attention_varlen(w.q[:150], w.k, w.v, [0, 150], [0, 160], w.scale)
+    check_attn(o[:150], l[:, :150].t(), Oref, Lref.T, torch.bfloat16, "varlen clamped")
+    assert torch.all(o[150:] == 0)
+
+
+def test_varlen_p1944_packed(ma):
+    w = W.varlen_p1944_packed()
+    o, l = run_varlen(ma, w)
+    rows = list(range(0, 3644, 37)) + [1943, 1944, 3643]
+    Oref, Lref = oracle.attention_varlen(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale)
+    check_attn(o[rows], l[:, rows].t(), Oref[rows], Lref[:, rows].T, torch.bfloat16, "varlen p1944")

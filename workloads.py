@@ -35,11 +35,11 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "Prefill", "Chunked", "Decode",
-    "make_prefill", "make_chunked", "make_decode",
+    "Prefill", "Chunked", "Decode", "Varlen",
+    "make_prefill", "make_chunked", "make_decode", "make_varlen", "cu_from_lengths",
     "mask_from_valid_lengths", "round_up",
     "fp32_masked_t512", "patch_p1944", "patch_p11616",
-    "chunked_kv_2x8192", "gqa_decode_b32",
+    "chunked_kv_2x8192", "gqa_decode_b32", "varlen_p1944_packed", "varlen_ring_hop_8192",
 ]
 
 
@@ -81,6 +81,26 @@ class Decode:
     lens: torch.Tensor     # int32 [B], cached length BEFORE the append
     scale: float
     name: str = ""
+
+
+@dataclass
+class Varlen:
+    q: torch.Tensor        # [total_q, H, D]
+    k: torch.Tensor        # [total_k, H, D]
+    v: torch.Tensor
+    cu_q: torch.Tensor     # int32 [B + 1], 0 .. total_q
+    cu_k: torch.Tensor     # int32 [B + 1], 0 .. total_k
+    max_q: int
+    scale: float
+    name: str = ""
+
+    @property
+    def lens_q(self):
+        return (self.cu_q[1:] - self.cu_q[:-1]).tolist()
+
+    @property
+    def lens_k(self):
+        return (self.cu_k[1:] - self.cu_k[:-1]).tolist()
 
 
 def _gen(seed: int) -> torch.Generator:
@@ -159,6 +179,30 @@ def make_decode(B, H_q, H_kv, D, len_lo, len_hi, dtype=torch.bfloat16, *, T_max=
     return Decode(q, kc, vc, kn, vn, lens.to(torch.int32), float(scale), name)
 
 
+def cu_from_lengths(lens: Sequence[int]) -> torch.Tensor:
+    """int32 [B + 1] running totals 0, l0, l0 + l1, ... of the sequence lengths."""
+    c = [0]
+    for n in lens:
+        assert int(n) >= 0
+        c.append(c[-1] + int(n))
+    return torch.tensor(c, dtype=torch.int32)
+
+
+def make_varlen(lens_q, lens_k, H, D, dtype=torch.bfloat16, *, amp=1.0, seed=0, scale=None,
+                name="") -> Varlen:
+    """Packed [total, H, D] Q, K, V for sequences of the given query / key lengths."""
+    assert len(lens_q) == len(lens_k) >= 1
+    g = _gen(seed)
+    cq, ck = cu_from_lengths(lens_q), cu_from_lengths(lens_k)
+    tq, tk = int(cq[-1]), int(ck[-1])
+    q = _randn(g, (tq, H, D), amp, dtype)
+    k = _randn(g, (tk, H, D), amp, dtype)
+    v = _randn(g, (tk, H, D), amp, dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return Varlen(q, k, v, cq, ck, max([int(n) for n in lens_q]), float(scale), name)
+
+
 # ---- the five named workloads -------------------------------------------------
 
 def fp32_masked_t512(seed=0) -> Prefill:
@@ -189,3 +233,16 @@ def gqa_decode_b32(seed=0) -> Decode:
     """bf16 GQA decode: B32, H_q 32 / H_kv 8, D128, cached len ~ U{512..8192}."""
     return make_decode(32, 32, 8, 128, 512, 8192, torch.bfloat16, seed=seed,
                        name="bf16 GQA decode B32 Hq32 Hkv8 D128, len U[512,8192] + 1 appended")
+
+
+def varlen_p1944_packed(seed=0) -> Varlen:
+    """bf16 packed patch self-attention: H16 D64, two sequences of 1,944 and 1,700 patches
+    (the P = 1,944 batch with its padding removed instead of masked)."""
+    return make_varlen([1944, 1700], [1944, 1700], 16, 64, seed=seed,
+                       name="bf16 packed varlen H16 D64, sequences 1944 + 1700")
+
+
+def varlen_ring_hop_8192(seed=0) -> Varlen:
+    """bf16 packed ring hop: one sequence, 8,192 queries against an 8,192-key chunk, H24 D128."""
+    return make_varlen([8192], [8192], 24, 128, seed=seed,
+                       name="bf16 packed varlen ring hop H24 D128, 8192 queries x 8192-key chunk")
