@@ -134,6 +134,23 @@ def cpu_model():
 SWEEP_P = (1944, 3952, 7776, 11616, 32122)   # the pages' patch counts, up to their OOM point
 
 
+def _time_call(torch, call, n=5, settle=0.3):
+    """Mean seconds per call over n calls, after `settle` seconds of untimed calls (the
+    clocks drop while the host prepares the next inputs and need ~30 ms of work to ramp)."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle:
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n / 1e3
+
+
 def p_sweep(torch, ma, dev):
     """Masked prefill with LSE, bf16, B1 H16 D64, last 16 keys padded, at each P:
     the call-level extra device bytes (the O and LSE the caller provides; the library
@@ -153,19 +170,11 @@ def p_sweep(torch, ma, dev):
         lse = torch.empty(1, H, P, dtype=torch.float32, device=dev)
         extra = torch.cuda.mem_get_info()[0]
         call = lambda: ma.attn_fwd_lse(q, k, v, mask, D ** -0.5, out=o, lse=lse)
-        for _ in range(3):
-            call()
+        call()
         torch.cuda.synchronize()
         free0 = torch.cuda.mem_get_info()[0]
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        n = 5
-        e0.record()
-        for _ in range(n):
-            call()
-        e1.record()
-        torch.cuda.synchronize()
+        t = _time_call(torch, call)
         free1 = torch.cuda.mem_get_info()[0]
-        t = e0.elapsed_time(e1) / n / 1e3
         flop = 4 * D * H * P * (P - 16)
         rows.append({"P": P, "us": round(t * 1e6, 1), "tflops": round(flop / t / 1e12, 1),
                      "call_extra_bytes": o.numel() * 2 + lse.numel() * 4,
@@ -182,19 +191,6 @@ def p_sweep(torch, ma, dev):
     c = my - a * mx
     return {"workload": "masked prefill with LSE, bf16, B1 H16 D64, last 16 keys padded, N(0,1)*0.5",
             "rows": rows, "linear_fit_bytes_per_P": round(a, 3), "linear_fit_intercept_bytes": round(c, 1)}
-
-
-def _time_call(torch, call, n=5, warm=3):
-    for _ in range(warm):
-        call()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(n):
-        call()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / n / 1e3
 
 
 def varlen_section(torch, ma, W, dev):

@@ -38,6 +38,7 @@ import numpy as np
 
 __all__ = [
     "scores", "masked_softmax", "attention", "attention_varlen", "merge_lse", "kv_append", "decode",
+    "gather_pages", "kv_append_paged", "decode_paged",
     "attention_flops", "score_matrix_bytes", "kv_bytes_per_token", "decode_kv_bytes",
 ]
 
@@ -240,6 +241,62 @@ def decode(q, k_cache, v_cache, lens, scale=None, heads=None):
         for h in range(Hq):
             O[b, h, 0], LSE[b, h] = one_head(b, h)
     return O, LSE
+
+
+# ---- paged KV cache ---------------------------------------------------------------
+# Paged layout (LLM inference memory accounting 2/10, section "15. Paged KV Cache가
+# 해결하는 것"): a sequence's logical KV blocks 0, 1, 2, ... live in physical blocks
+# block_table[b][0], block_table[b][1], ... of a shared pool, so token t of sequence b
+# is row t % page_size of physical block block_table[b][t // page_size].  The pool is
+# [num_pages, H_kv, page_size, D]: one physical block holds page_size tokens of every
+# KV head, each head's rows contiguous, like a slice of the contiguous cache.
+
+def gather_pages(pages, block_table, b, n):
+    """Tokens 0..n-1 of sequence b from the pool, in logical order: [H_kv, n, D]."""
+    pages = _f64(pages)
+    bt = np.asarray(_f64(block_table), dtype=np.int64)
+    ps = pages.shape[2]
+    rows = [pages[bt[b, t // ps], :, t % ps, :] for t in range(n)]
+    if not rows:
+        return np.zeros((pages.shape[1], 0, pages.shape[3]))
+    return np.stack(rows, axis=1)
+
+
+def kv_append_paged(k_pages, v_pages, block_table, lens, k_new, v_new):
+    """Write one token per sequence at logical position lens[b], i.e. row
+    lens[b] % page_size of physical block block_table[b][lens[b] // page_size];
+    return (k_pages, v_pages, lens + 1) as copies (bit copy, dtype kept)."""
+    kp = np.array(k_pages, copy=True)
+    vp = np.array(v_pages, copy=True)
+    bt = np.asarray(block_table).astype(np.int64)
+    lens = np.asarray(lens).astype(np.int64)
+    ps = kp.shape[2]
+    for b in range(bt.shape[0]):
+        t = int(lens[b])
+        assert 0 <= t < bt.shape[1] * ps, "cache full"
+        p = int(bt[b, t // ps])
+        kp[p, :, t % ps, :] = np.asarray(k_new)[b, :, 0, :]
+        vp[p, :, t % ps, :] = np.asarray(v_new)[b, :, 0, :]
+    return kp, vp, lens + 1
+
+
+def decode_paged(q, k_pages, v_pages, block_table, lens, scale=None, heads=None):
+    """``decode`` over a paged cache: each sequence's first lens[b] tokens are
+    gathered from the pool through its block-table row, then attended exactly
+    as in the contiguous cache.  Arguments and results as ``decode``."""
+    q = _f64(q)
+    B = q.shape[0]
+    kp, vp = _f64(k_pages), _f64(v_pages)
+    lens = np.asarray(lens).astype(np.int64)
+    H_kv, D = kp.shape[1], kp.shape[3]
+    T = max(1, int(lens.max()) if lens.size else 1)
+    kc = np.zeros((B, H_kv, T, D))
+    vc = np.zeros((B, H_kv, T, D))
+    for b in range(B):
+        n = int(lens[b])
+        kc[b, :, :n] = gather_pages(kp, block_table, b, n)
+        vc[b, :, :n] = gather_pages(vp, block_table, b, n)
+    return decode(q, kc, vc, lens, scale, heads)
 
 
 # ---- work and byte accounting --------------------------------------------------

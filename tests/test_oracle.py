@@ -433,3 +433,76 @@ def test_varlen_equals_padded_masked_dense():
     for b in range(B):
         assert np.allclose(O[cq[b]:cq[b + 1]], Od[b, :, :lq[b]].transpose(1, 0, 2), atol=1e-13, rtol=0)
         assert np.allclose(L[:, cq[b]:cq[b + 1]], Ld[b, :, :lq[b]], atol=1e-13, rtol=0)
+
+
+# ---- paged KV cache -----------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(3))
+def test_decode_paged_matches_brute_force(seed):
+    # Pure-Python walk of the page table: token t of sequence b is row t % ps of page bt[b][t // ps].
+    r = _rng(100 + seed)
+    B, Hkv, G, D, ps = 2, 2, 2, 4, 3
+    mp = 4
+    n_pages = B * mp + 2
+    kp = r.standard_normal((n_pages, Hkv, ps, D))
+    vp = r.standard_normal((n_pages, Hkv, ps, D))
+    bt = r.permutation(n_pages)[:B * mp].reshape(B, mp)
+    lens = [int(x) for x in r.integers(0, mp * ps + 1, B)]
+    q = r.standard_normal((B, Hkv * G, 1, D))
+    scale = 0.6
+    O, L = oracle.decode_paged(q, kp, vp, bt, lens, scale)
+    for b in range(B):
+        for h in range(Hkv * G):
+            g = h // G
+            keys = [kp[bt[b][t // ps], g, t % ps].tolist() for t in range(lens[b])]
+            vals = [vp[bt[b][t // ps], g, t % ps].tolist() for t in range(lens[b])]
+            o, l = brute.attend_row(q[b, h, 0].tolist(), keys, vals, [False] * len(keys), scale)
+            if l == -math.inf:
+                assert L[b, h] == -np.inf and np.all(O[b, h, 0] == 0)
+            else:
+                assert abs(L[b, h] - l) <= 1e-12
+                assert np.max(np.abs(O[b, h, 0] - np.array(o))) <= 1e-12
+
+
+def test_decode_paged_identity_table_equals_contiguous():
+    # With pages laid out in order (page b*mp + i = tokens i*ps.. of sequence b) the pool is a
+    # reshape of the contiguous cache, so the two definitions must agree exactly.
+    d = workloads.make_decode(3, 4, 2, 8, 0, 60, torch.float32, seed=6)
+    B, Hkv, T, D = d.k_cache.shape
+    ps = 16
+    mp = T // ps
+    kp = d.k_cache.reshape(B, Hkv, mp, ps, D).permute(0, 2, 1, 3, 4).reshape(B * mp, Hkv, ps, D)
+    vp = d.v_cache.reshape(B, Hkv, mp, ps, D).permute(0, 2, 1, 3, 4).reshape(B * mp, Hkv, ps, D)
+    bt = np.arange(B * mp).reshape(B, mp)
+    O, L = oracle.decode_paged(d.q, kp, vp, bt, d.lens, d.scale)
+    Oc, Lc = oracle.decode(d.q, d.k_cache, d.v_cache, d.lens, d.scale)
+    assert np.array_equal(O, Oc) and np.array_equal(L, Lc)
+
+
+def test_decode_paged_relabelling_pages_changes_nothing():
+    pg = workloads.to_paged(workloads.make_decode(2, 4, 2, 8, 10, 60, torch.float32, seed=7), 16)
+    O, L = oracle.decode_paged(pg.dec.q, pg.k_pages, pg.v_pages, pg.block_table, pg.dec.lens, pg.dec.scale)
+    n = pg.k_pages.shape[0]
+    pi = torch.randperm(n, generator=torch.Generator().manual_seed(3))
+    kp2, vp2 = torch.empty_like(pg.k_pages), torch.empty_like(pg.v_pages)
+    kp2[pi] = pg.k_pages
+    vp2[pi] = pg.v_pages
+    bt2 = pi[pg.block_table.long()]
+    O2, L2 = oracle.decode_paged(pg.dec.q, kp2, vp2, bt2, pg.dec.lens, pg.dec.scale)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2)
+
+
+def test_paged_append_then_decode_equals_contiguous():
+    d = workloads.make_decode(3, 4, 2, 8, 0, 47, torch.float32, seed=8)
+    pg = workloads.to_paged(d, 16)
+    kp, vp, lens = oracle.kv_append_paged(pg.k_pages, pg.v_pages, pg.block_table, d.lens, d.k_new, d.v_new)
+    kc, vc, lens_c = oracle.kv_append(d.k_cache, d.v_cache, d.lens, d.k_new, d.v_new)
+    assert np.array_equal(lens, lens_c)
+    O, L = oracle.decode_paged(d.q, kp, vp, pg.block_table, lens, d.scale)
+    Oc, Lc = oracle.decode(d.q, kc, vc, lens_c, d.scale)
+    assert np.array_equal(O, Oc) and np.array_equal(L, Lc)
+    # exactly one row of one page per sequence changed
+    diff = np.argwhere(np.any(kp != pg.k_pages.numpy(), axis=(1, 3)))
+    want = sorted((int(pg.block_table[b, int(d.lens[b]) // 16]), int(d.lens[b]) % 16) for b in range(3))
+    got = sorted({(int(p), int(r)) for p, _, r in np.argwhere(np.any(kp != pg.k_pages.numpy(), axis=3))})
+    assert got == want and len(diff) <= 3 * 2

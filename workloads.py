@@ -35,11 +35,12 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "Prefill", "Chunked", "Decode", "Varlen",
+    "Prefill", "Chunked", "Decode", "Varlen", "Paged", "to_paged",
     "make_prefill", "make_chunked", "make_decode", "make_varlen", "cu_from_lengths",
     "mask_from_valid_lengths", "round_up",
     "fp32_masked_t512", "patch_p1944", "patch_p11616",
     "chunked_kv_2x8192", "gqa_decode_b32", "varlen_p1944_packed", "varlen_ring_hop_8192",
+    "gqa_decode_b32_paged",
 ]
 
 
@@ -101,6 +102,16 @@ class Varlen:
     @property
     def lens_k(self):
         return (self.cu_k[1:] - self.cu_k[:-1]).tolist()
+
+
+@dataclass
+class Paged:
+    """A decode workload with its caches scattered into a pool of physical pages."""
+    dec: Decode
+    k_pages: torch.Tensor      # [num_pages, H_kv, page_size, D]
+    v_pages: torch.Tensor
+    block_table: torch.Tensor  # int32 [B, max_pages]: logical page i of b -> physical page
+    page_size: int
 
 
 def _gen(seed: int) -> torch.Generator:
@@ -203,6 +214,30 @@ def make_varlen(lens_q, lens_k, H, D, dtype=torch.bfloat16, *, amp=1.0, seed=0, 
     return Varlen(q, k, v, cq, ck, max([int(n) for n in lens_q]), float(scale), name)
 
 
+def to_paged(dec: Decode, page_size: int, *, seed=1, spare_pages=3) -> Paged:
+    """Scatter the contiguous caches of `dec` into shuffled physical pages.
+
+    Logical page i of sequence b (tokens i*page_size .. +page_size-1 of its T_max slots)
+    is copied to physical page block_table[b, i], a seeded random permutation of
+    B*max_pages + spare_pages pages (the spares hold random data and are never mapped).
+    A bit copy: the paged and contiguous caches hold the same values.
+    """
+    B, H_kv, T_max, D = dec.k_cache.shape
+    assert T_max % page_size == 0
+    mp = T_max // page_size
+    n = B * mp + spare_pages
+    g = _gen(seed)
+    perm = torch.randperm(n, generator=g)
+    bt = perm[:B * mp].reshape(B, mp).to(torch.int32).contiguous()
+    kp = _randn(g, (n, H_kv, page_size, D), 1.0, dec.k_cache.dtype)
+    vp = _randn(g, (n, H_kv, page_size, D), 1.0, dec.k_cache.dtype)
+    kc = dec.k_cache.reshape(B, H_kv, mp, page_size, D).permute(0, 2, 1, 3, 4)   # [B, mp, H_kv, ps, D]
+    vc = dec.v_cache.reshape(B, H_kv, mp, page_size, D).permute(0, 2, 1, 3, 4)
+    kp[bt.reshape(-1).long()] = kc.reshape(B * mp, H_kv, page_size, D)
+    vp[bt.reshape(-1).long()] = vc.reshape(B * mp, H_kv, page_size, D)
+    return Paged(dec, kp.contiguous(), vp.contiguous(), bt, page_size)
+
+
 # ---- the five named workloads -------------------------------------------------
 
 def fp32_masked_t512(seed=0) -> Prefill:
@@ -246,3 +281,8 @@ def varlen_ring_hop_8192(seed=0) -> Varlen:
     """bf16 packed ring hop: one sequence, 8,192 queries against an 8,192-key chunk, H24 D128."""
     return make_varlen([8192], [8192], 24, 128, seed=seed,
                        name="bf16 packed varlen ring hop H24 D128, 8192 queries x 8192-key chunk")
+
+
+def gqa_decode_b32_paged(page_size=16, seed=0) -> Paged:
+    """The GQA decode workload (B32, H_q 32 / H_kv 8, D128, len U[512, 8192]) in a paged cache."""
+    return to_paged(gqa_decode_b32(seed), page_size)
