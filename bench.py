@@ -52,7 +52,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-sweep", action="store_true",
                    help="skip the sections measured outside the step: the P-sweep of the prefill "
-                        "(memory and TFLOP/s at P = 1,944 .. 32,122) and the packed varlen calls")
+                        "(memory and TFLOP/s at P = 1,944 .. 32,122), the packed varlen calls and "
+                        "the paged decode")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -220,6 +221,32 @@ def varlen_section(torch, ma, W, dev):
     return res
 
 
+def paged_section(torch, ma, W, dev):
+    """The decode workload (B32, H_q 32 / H_kv 8, D128, len U[512, 8192] + 1) with its cache in a
+    shuffled page pool (attn_decode_paged), per page size, timed on its own; bytes as the
+    contiguous decode (K and V of every cached token, plus q and o)."""
+    res = {}
+    for ps in (16, 64):
+        pg = W.gqa_decode_b32_paged(ps)
+        w = pg.dec
+        kp, vp, bt = pg.k_pages.to(dev), pg.v_pages.to(dev), pg.block_table.to(dev)
+        lens = (w.lens + 1).to(dev)
+        q = w.q.to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        B, Hq, _, D = q.shape
+        Hkv = kp.shape[1]
+        ws = torch.empty(ma.attn_decode_workspace_bytes(B, Hq, Hkv, bt.shape[1] * ps, D), dtype=torch.uint8,
+                         device=dev)
+        t = _time_call(torch, lambda: ma.attn_decode_paged(q, kp, vp, bt, lens, w.scale, out=o, lse=lse,
+                                                           workspace=ws, want_lse=True), n=20)
+        nbytes = int((w.lens + 1).sum()) * 2 * Hkv * D * 2 + 2 * q.numel() * 2
+        res[f"page_{ps}"] = {"us": round(t * 1e6, 2), "gbps": round(nbytes / t / 1e9, 1),
+                             "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBPS, 4)}
+        del kp, vp, bt, lens, q, o, lse, ws
+    return res
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -383,6 +410,7 @@ def main():
     if not args.no_sweep:
         out["p_sweep"] = p_sweep(torch, ma, dev)
         out["varlen"] = varlen_section(torch, ma, W, dev)
+        out["paged_decode"] = paged_section(torch, ma, W, dev)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(pf, args.cpu_seconds)
         cb.pop("seconds", None)

@@ -188,8 +188,51 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 float scale, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace attn_decode needs for these sizes (0 on invalid sizes). */
+/* Bytes of workspace attn_decode needs for these sizes (0 on invalid sizes).
+ * attn_decode_paged needs the same with T_max = max_pages_per_seq · page_size. */
 size_t attn_decode_workspace_bytes(int B, int H_q, int H_kv, int T_max, int D);
+
+/*
+ * Paged KV cache.  A sequence's logical KV blocks live in non-contiguous
+ * physical blocks of a shared pool, found through its row of a block table
+ * (blog.ruahverce.com, LLM inference memory accounting 2/10, section
+ * "15. Paged KV Cache가 해결하는 것": logical block i of a request maps to
+ * physical block block_table[i]; the attention kernel must read that
+ * layout).  Conventions of the two paged calls:
+ *   k_pages, v_pages  [num_pages, H_kv, page_size, D] (dtype): a physical page
+ *       holds page_size consecutive tokens of every KV head, each head's
+ *       page_size rows contiguous
+ *   block_table  [B, max_pages_per_seq] int32 device array, owned by the
+ *       caller and only read: token t of sequence b is row t % page_size of
+ *       page block_table[b][t / page_size].  Only the entries covering
+ *       positions 0..len_b (decode: 0..len_b - 1) are read; an entry outside
+ *       [0, num_pages) is clamped into it (wrong values, no access outside
+ *       the pool).  Pages may be shared between sequences.
+ *   page_size  a power of two, 16 <= page_size <= 2^20
+ *   capacity   T_max = max_pages_per_seq · page_size <= 2^30 tokens; B ·
+ *       max_pages_per_seq <= 2^29
+ * Lengths, q, o, lse, scale, workspace and errors as the contiguous calls.
+ */
+
+/* kv_append_paged — kv_append into a paged cache: the new token of sequence
+ * b is written at row len_b % page_size of page block_table[b][len_b /
+ * page_size], then len_b is incremented; a length outside [0, T_max) leaves
+ * the sequence untouched.  k_new, v_new [B, H_kv, 1, D] (dtype). */
+int kv_append_paged(void* k_pages, void* v_pages, const int32_t* block_table,
+                    int32_t* cache_seqlens, const void* k_new, const void* v_new,
+                    int B, int H_kv, int num_pages, int page_size, int max_pages_per_seq,
+                    int D, int dtype, void* stream);
+
+/* attn_decode_paged — attn_decode over a paged cache (bf16 only, else
+ * ATTN_ERR_UNSUPPORTED): the same result as attn_decode over the contiguous
+ * cache that the block table describes.  workspace as attn_decode with
+ * T_max = max_pages_per_seq · page_size. */
+int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                      const int32_t* block_table, const int32_t* cache_seqlens,
+                      void* o, float* lse,
+                      int B, int H_q, int H_kv, int num_pages, int page_size,
+                      int max_pages_per_seq, int D, float scale, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(int status);

@@ -30,7 +30,8 @@ STATUS = {
 }
 
 EXPORTS = ("attn_fwd_masked", "attn_fwd_lse", "attn_fwd_varlen", "attn_merge_lse", "kv_append",
-           "attn_decode", "attn_decode_workspace_bytes", "attn_status_string")
+           "attn_decode", "attn_decode_workspace_bytes", "kv_append_paged", "attn_decode_paged",
+           "attn_status_string")
 
 _lib = None
 
@@ -57,12 +58,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_merge_lse.argtypes = [I, ctypes.POINTER(P), ctypes.POINTER(P), P, P, I, I, I, I, I, P]
     lib.kv_append.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
     lib.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, P, S, P]
+    lib.kv_append_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, S, P]
     lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.attn_decode_workspace_bytes.restype = S
     lib.attn_status_string.argtypes = [I]
     lib.attn_status_string.restype = ctypes.c_char_p
     for name in ("attn_fwd_masked", "attn_fwd_lse", "attn_fwd_varlen", "attn_merge_lse", "kv_append",
-                 "attn_decode"):
+                 "attn_decode", "kv_append_paged", "attn_decode_paged"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -274,4 +277,66 @@ def attn_decode(q, k_cache, v_cache, cache_seqlens, scale=None, out=None, lse=No
     _check("attn_decode", load().attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
                                              _ptr(out), _ptr(lse if want_lse else None), B, Hq, Hkv, Tmax, D,
                                              float(scale), code, _ptr(workspace), nbytes, _stream(q.device)))
+    return (out, lse) if want_lse else out
+
+
+def _paged_args(k_pages, v_pages, block_table, cache_seqlens, B):
+    for t, n in ((k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"),
+                 (cache_seqlens, "cache_seqlens")):
+        _dev(t, n)
+    if k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages / v_pages must be [num_pages, H_kv, page_size, D] of one shape")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages_per_seq]")
+    if cache_seqlens.shape != (B,) or cache_seqlens.dtype != torch.int32:
+        raise ValueError("cache_seqlens must be int32 [B]")
+    num_pages, Hkv, page_size, D = k_pages.shape
+    return num_pages, Hkv, page_size, D, block_table.shape[1]
+
+
+def kv_append_paged(k_pages, v_pages, block_table, cache_seqlens, k_new, v_new):
+    """kv_append into a paged pool [num_pages, H_kv, page_size, D] through block_table [B, max_pages]."""
+    B = k_new.shape[0]
+    _dev(k_new, "k_new")
+    _dev(v_new, "v_new")
+    num_pages, Hkv, ps, D, mp = _paged_args(k_pages, v_pages, block_table, cache_seqlens, B)
+    if k_new.shape != (B, Hkv, 1, D) or v_new.shape != (B, Hkv, 1, D):
+        raise ValueError("k_new / v_new must be [B, H_kv, 1, D]")
+    code = _dtype_code(k_pages)
+    for t in (v_pages, k_new, v_new):
+        if t.dtype != k_pages.dtype:
+            raise TypeError("pools and new tokens must share a dtype")
+    _check("kv_append_paged", load().kv_append_paged(
+        _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(cache_seqlens), _ptr(k_new), _ptr(v_new),
+        B, Hkv, num_pages, ps, mp, D, code, _stream(k_pages.device)))
+
+
+def attn_decode_paged(q, k_pages, v_pages, block_table, cache_seqlens, scale=None, out=None, lse=None,
+                      workspace=None, want_lse: bool = False):
+    """attn_decode over a paged pool: q [B, H_q, 1, D] (bf16), pools [num_pages, H_kv, page_size, D],
+    block_table int32 [B, max_pages]."""
+    _dev(q, "q")
+    B, Hq, one, D = q.shape
+    if one != 1:
+        raise ValueError("q must be [B, H_q, 1, D]")
+    num_pages, Hkv, ps, Dk, mp = _paged_args(k_pages, v_pages, block_table, cache_seqlens, B)
+    if Dk != D:
+        raise ValueError("pool head_dim does not match q")
+    if q.dtype != torch.bfloat16 or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise TypeError("attn_decode_paged takes bfloat16 q and pools")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, mp * ps, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("attn_decode_paged", load().attn_decode_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(cache_seqlens), _ptr(out),
+        _ptr(lse if want_lse else None), B, Hq, Hkv, num_pages, ps, mp, D, float(scale), ATTN_BF16,
+        _ptr(workspace), nbytes, _stream(q.device)))
     return (out, lse) if want_lse else out

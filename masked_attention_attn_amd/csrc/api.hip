@@ -132,6 +132,72 @@ int kv_append(void* k_cache, void* v_cache, int32_t* cache_seqlens, const void* 
     return finish(launch_kv_append(a));
 }
 
+// Shared checks of the paged pool geometry: page_size a power of two in [16, 2^20],
+// capacity max_pages * page_size within the contiguous decode's limits, and the
+// block table (B x max_pages int32) addressable with 32-bit byte offsets.
+static int paged_geometry(int B, int H_kv, int num_pages, int page_size, int max_pages, int D,
+                          int& T_max) {
+    if (num_pages < 1 || max_pages < 1 || page_size < 16 || page_size > (1 << 20) ||
+        (page_size & (page_size - 1)) != 0)
+        return ATTN_ERR_SHAPE;
+    const long long cap = (long long)max_pages * page_size;
+    if (cap > (1ll << 30) || (long long)B * max_pages > (1ll << 29) ||
+        !fits(num_pages, H_kv, page_size, D))
+        return ATTN_ERR_SHAPE;
+    T_max = (int)cap;
+    return ATTN_OK;
+}
+
+int kv_append_paged(void* k_pages, void* v_pages, const int32_t* block_table, int32_t* cache_seqlens,
+                    const void* k_new, const void* v_new, int B, int H_kv, int num_pages,
+                    int page_size, int max_pages_per_seq, int D, int dtype, void* stream) {
+    if (!k_pages || !v_pages || !block_table || !cache_seqlens || !k_new || !v_new) return ATTN_ERR_NULL;
+    if (!dtype_ok(dtype) || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+    int T_max = 0;
+    if (B < 1 || H_kv < 1 || B > (1 << 30)) return ATTN_ERR_SHAPE;
+    if (const int st = paged_geometry(B, H_kv, num_pages, page_size, max_pages_per_seq, D, T_max))
+        return st;
+    if (!aligned16(k_pages) || !aligned16(v_pages) || !aligned16(k_new) || !aligned16(v_new))
+        return ATTN_ERR_ALIGN;
+    if (k_pages == v_pages || k_new == k_pages || v_new == v_pages) return ATTN_ERR_ALIAS;
+    AppendArgs a{k_pages, v_pages, cache_seqlens, k_new, v_new, B, H_kv, T_max, D,
+                 elem_bytes(dtype), stream};
+    a.block_table = block_table;
+    a.page_size = page_size;
+    a.max_pages = max_pages_per_seq;
+    a.num_pages = num_pages;
+    return finish(launch_kv_append(a));
+}
+
+int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                      const int32_t* block_table, const int32_t* cache_seqlens, void* o, float* lse,
+                      int B, int H_q, int H_kv, int num_pages, int page_size, int max_pages_per_seq,
+                      int D, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+    if (!q || !k_pages || !v_pages || !block_table || !cache_seqlens || !o) return ATTN_ERR_NULL;
+    if (!dtype_ok(dtype) || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+    if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (H_kv <= 0 || H_q <= 0 || H_q % H_kv != 0) return ATTN_ERR_SHAPE;
+    if (!fits(B, H_q, 1, D) || (long long)B * H_q > (1 << 30)) return ATTN_ERR_SHAPE;
+    int T_max = 0;
+    if (const int st = paged_geometry(B, H_kv, num_pages, page_size, max_pages_per_seq, D, T_max))
+        return st;
+    if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
+    if (!workspace || workspace_bytes < decode_workspace_bytes(B, H_q, T_max, D))
+        return ATTN_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) ||
+        !aligned16(workspace))
+        return ATTN_ERR_ALIGN;
+    if (o == q || o == k_pages || o == v_pages) return ATTN_ERR_ALIAS;
+    DecodeArgs a{q, k_pages, v_pages, cache_seqlens, o, lse, B, H_q, H_kv, T_max, D, scale,
+                 workspace, stream};
+    a.block_table = block_table;
+    a.page_size = page_size;
+    a.max_pages = max_pages_per_seq;
+    a.num_pages = num_pages;
+    return finish(launch_decode_bf16(a));
+}
+
 size_t attn_decode_workspace_bytes(int B, int H_q, int H_kv, int T_max, int D) {
     if (B <= 0 || H_q <= 0 || H_kv <= 0 || T_max <= 0 || !head_dim_ok(D) || H_q % H_kv != 0)
         return 0;

@@ -87,15 +87,43 @@ __device__ __forceinline__ void dma_x4(i32x4_sgpr r, const uint32_t* m, const ui
         : "s"(m[0]), "s"(m[1]), "s"(m[2]), "s"(m[3]), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "s"(r)
         : "memory");
 }
+__device__ __forceinline__ void dma_x2(i32x4_sgpr r, const uint32_t* m, const uint32_t* vo) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %3, %5, 0 offen lds\n\t"
+        "s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %4, %5, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m[0]), "s"(m[1]), "v"(vo[0]), "v"(vo[1]), "s"(r)
+        : "memory");
+}
 template <int N>
 __device__ __forceinline__ void dma_n(i32x4_sgpr r, uint32_t lds_addr, const uint32_t* vo) {
-    static_assert(N % 4 == 0, "whole groups of four");
+    static_assert(N % 2 == 0, "whole pairs");
 #pragma unroll
-    for (int k = 0; k < N; k += 4) {
+    for (int k = 0; k + 4 <= N; k += 4) {
         const uint32_t m[4] = {lds_addr + (k + 0) * 1024u, lds_addr + (k + 1) * 1024u, lds_addr + (k + 2) * 1024u,
                                lds_addr + (k + 3) * 1024u};
         dma_x4(r, m, vo + k);
     }
+    if constexpr (N % 4 == 2) {
+        const uint32_t m[2] = {lds_addr + (N - 2) * 1024u, lds_addr + (N - 1) * 1024u};
+        dma_x2(r, m, vo + N - 2);
+    }
+}
+
+// Two dwords at byte offsets o0, o1 of a wavefront-uniform table (scalar loads: they
+// count in lgkmcnt, not vmcnt, so the vector-load accounting of the look-ahead is not
+// disturbed).  Both offsets must lie inside the table.
+__device__ __forceinline__ void sload2(const int32_t* p, uint32_t o0, uint32_t o1, int& a, int& b) {
+    asm volatile(
+        "s_load_dword %0, %2, %3\n\t"
+        "s_load_dword %1, %2, %4\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&s"(a), "=&s"(b)
+        : "s"(p), "s"(o0), "s"(o1)
+        : "memory");
 }
 
 // Stores written as inline assembly so that their number is exact: stores
@@ -257,13 +285,18 @@ __device__ __forceinline__ void advance(Cursor& c, const Lens& L, int HG, int n_
     }
 }
 
-template <int D>
+// PAGED: kc / vc are page pools [num_pages, H_kv, 2^lps, D]; token t of sequence b is
+// row t mod 2^lps of page bt[b * max_pages + (t >> lps)] (entries clamped to
+// [0, num_pages)), T_max = max_pages << lps.  A 32-token block is loaded as two
+// 16-token halves, each inside one page, each through its own buffer range.
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64)
 void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
                           const bf16* __restrict__ vc, const int32_t* __restrict__ lens,
                           float* __restrict__ ws_o, float* __restrict__ ws_ml,
                           int B, int H_q, int H_kv, int T_max, int G, int n_hg, int nsplit,
-                          int nwaves, int qb, float c) {
+                          int nwaves, int qb, float c,
+                          const int32_t* __restrict__ bt, int lps, int max_pages, int num_pages) {
     using Gm = Geo<D>;
     constexpr int RB = Gm::RB, BLK = Gm::BLK, NCH = Gm::NCH, R = Gm::R, QCH = Gm::QCH;
     constexpr int KSTEPS = D / 16;     // MFMA k-steps of K·Qᵀ
@@ -316,20 +349,68 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
     const i32x4_sgpr zrs = make_rsrc(kc, 0u);
     i32x4_sgpr krs, vrs;
     auto set_item = [&]() {
-        const size_t head = ((size_t)ic.b * H_kv + ic.g) * (size_t)T_max * D;
-        krs = make_rsrc(kc + head, (uint32_t)ic.t_end * RB);
-        vrs = make_rsrc(vc + head, (uint32_t)ic.t_end * RB);
+        if constexpr (!PAGED) {
+            const size_t head = ((size_t)ic.b * H_kv + ic.g) * (size_t)T_max * D;
+            krs = make_rsrc(kc + head, (uint32_t)ic.t_end * RB);
+            vrs = make_rsrc(vc + head, (uint32_t)ic.t_end * RB);
+        }
     };
     set_item();
-    auto issue = [&](bool live, bool first_of_item, int sl) {
-        const uint32_t row0 = (uint32_t)(ic.s * kDecodeSplit + ic.i * CK) * RB;
+    // Paged: a 32-token block is two 16-token halves; LDS chunks [0, NCH/2) hold keys
+    // 0..15 of the block and chunks [NCH/2, NCH) keys 16..31 (the K row permutation
+    // swaps bits 2 and 3 only, so it stays inside each half).
+    constexpr int HCH = NCH / 2;
+    auto issue_paged = [&](bool live, int sl) {
+        const int t0 = ic.s * kDecodeSplit + ic.i * CK;
+        i32x4_sgpr kh[2] = {zrs, zrs}, vh[2] = {zrs, zrs};
+        uint32_t roff[2] = {0u, 0u};
+        if (live) {
+            // table entries of the halves; a half past the item's end reuses the last
+            // valid token's entry (it is then read through the zero range)
+            const int last = ic.t_end - 1;
+            const int pi0 = t0 >> lps, pi1 = min(t0 + 16, last) >> lps;
+            const uint32_t rowb = (uint32_t)ic.b * (uint32_t)max_pages * 4u;
+            int e0, e1;
+            sload2(bt, __builtin_amdgcn_readfirstlane(rowb + (uint32_t)pi0 * 4u),
+                   __builtin_amdgcn_readfirstlane(rowb + (uint32_t)pi1 * 4u), e0, e1);
+            const int pe[2] = {e0, e1}, pidx[2] = {pi0, pi1};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int th = t0 + 16 * h;
+                if (th < ic.t_end) {
+                    const int page = min(max(pe[h], 0), num_pages - 1);
+                    const int pstart = pidx[h] << lps;
+                    const int rows = min(1 << lps, ic.t_end - pstart);
+                    const size_t head = (((size_t)page * H_kv + ic.g) << lps) * D;
+                    kh[h] = make_rsrc(kc + head, (uint32_t)rows * RB);
+                    vh[h] = make_rsrc(vc + head, (uint32_t)rows * RB);
+                    roff[h] = (uint32_t)(th - pstart) * RB;
+                }
+            }
+        }
         uint32_t vo[NCH];
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) vo[ch] = row0 + k_voff[ch];
-        dma_n<NCH>(live ? krs : zrs, lds0 + sl * 2 * BLK, vo);
+        for (int ch = 0; ch < NCH; ++ch) vo[ch] = roff[ch / HCH] + k_voff[ch] - (ch / HCH) * 16u * RB;
+        dma_n<HCH>(kh[0], lds0 + sl * 2 * BLK, vo);
+        dma_n<HCH>(kh[1], lds0 + sl * 2 * BLK + HCH * 1024, vo + HCH);
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) vo[ch] = row0 + v_voff[ch];
-        dma_n<NCH>(live ? vrs : zrs, lds0 + sl * 2 * BLK + BLK, vo);
+        for (int ch = 0; ch < NCH; ++ch) vo[ch] = roff[ch / HCH] + v_voff[ch] - (ch / HCH) * 16u * RB;
+        dma_n<HCH>(vh[0], lds0 + sl * 2 * BLK + BLK, vo);
+        dma_n<HCH>(vh[1], lds0 + sl * 2 * BLK + BLK + HCH * 1024, vo + HCH);
+    };
+    auto issue = [&](bool live, bool first_of_item, int sl) {
+        if constexpr (PAGED) {
+            issue_paged(live, sl);
+        } else {
+            const uint32_t row0 = (uint32_t)(ic.s * kDecodeSplit + ic.i * CK) * RB;
+            uint32_t vo[NCH];
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) vo[ch] = row0 + k_voff[ch];
+            dma_n<NCH>(live ? krs : zrs, lds0 + sl * 2 * BLK, vo);
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) vo[ch] = row0 + v_voff[ch];
+            dma_n<NCH>(live ? vrs : zrs, lds0 + sl * 2 * BLK + BLK, vo);
+        }
         if (live && first_of_item) {
             const int ncols = min(32, G - ic.hg * 32);
             const i32x4_sgpr qrs = make_rsrc(q + ((size_t)ic.b * H_q + ic.g * G + ic.hg * 32) * D,
@@ -564,14 +645,14 @@ void decode_stream_combine(const float* __restrict__ ws_o, const float* __restri
 
 // Wavefronts the split kernel runs at once (one round of the whole GPU) for
 // a given dynamic LDS size; the last query is cached.
-template <int D>
+template <int D, bool PAGED>
 int resident_waves(int lds_bytes) {
     static int cached_lds = -1, cached = 0;
     if (lds_bytes == cached_lds) return cached;
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_stream_kernel<D>, 64, lds_bytes) !=
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_stream_kernel<D, PAGED>, 64, lds_bytes) !=
             hipSuccess ||
         cus <= 0 || per_cu <= 0)
         return 256;
@@ -580,11 +661,11 @@ int resident_waves(int lds_bytes) {
     return cached;
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch(const DecodeArgs& a) {
     // the largest dynamic LDS any call uses: ring + R full 32-head Q slots
     static const hipError_t attr =
-        hipFuncSetAttribute((const void*)decode_stream_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        hipFuncSetAttribute((const void*)decode_stream_kernel<D, PAGED>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             Geo<D>::RING + Geo<D>::R * q_slot_bytes(32, D));
     if (attr != hipSuccess) return attr;
     const int G = a.H_q / a.H_kv;
@@ -592,12 +673,14 @@ hipError_t launch(const DecodeArgs& a) {
     const int nsplit = decode_nsplit(a.T_max);
     const int qb = q_slot_bytes(G, D);
     const int lds = Geo<D>::RING + Geo<D>::R * qb;
-    const int nwaves = resident_waves<D>(lds);
+    const int nwaves = resident_waves<D, PAGED>(lds);
     float* ws_o = static_cast<float*>(a.workspace);
     float* ws_ml = ws_o + (size_t)a.B * a.H_q * nsplit * 2 * D;
-    hipLaunchKernelGGL((decode_stream_kernel<D>), dim3(nwaves), dim3(64), lds, (hipStream_t)a.stream,
+    const int lps = PAGED ? __builtin_ctz((unsigned)a.page_size) : 0;
+    hipLaunchKernelGGL((decode_stream_kernel<D, PAGED>), dim3(nwaves), dim3(64), lds, (hipStream_t)a.stream,
                        (const bf16*)a.q, (const bf16*)a.k_cache, (const bf16*)a.v_cache, a.lens, ws_o, ws_ml,
-                       a.B, a.H_q, a.H_kv, a.T_max, G, n_hg, nsplit, nwaves, qb, a.scale * kLog2e);
+                       a.B, a.H_q, a.H_kv, a.T_max, G, n_hg, nsplit, nwaves, qb, a.scale * kLog2e,
+                       a.block_table, lps, a.max_pages, a.num_pages);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_stream_combine<D>), dim3(a.B * a.H_q), dim3(D), 0, (hipStream_t)a.stream,
@@ -608,7 +691,8 @@ hipError_t launch(const DecodeArgs& a) {
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeArgs& a) {
-    return a.D == 64 ? launch<64>(a) : launch<128>(a);
+    if (a.block_table) return a.D == 64 ? launch<64, true>(a) : launch<128, true>(a);
+    return a.D == 64 ? launch<64, false>(a) : launch<128, false>(a);
 }
 
 }  // namespace mattn

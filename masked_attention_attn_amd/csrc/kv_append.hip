@@ -11,6 +11,14 @@
 // K and V rows of all KV heads to slot len_b, then, after a barrier that
 // orders every read of len_b before the write, thread 0 increments it.  A
 // sequence whose length is outside [0, T_max) is left untouched.
+//
+// Paged cache (LLM inference memory accounting 2/10, section "15. Paged KV
+// Cache가 해결하는 것": logical blocks of a sequence map to physical blocks of a
+// shared pool through its block-table row): the pools are [num_pages, H_kv,
+// page_size, D], slot t is row t % page_size of page block_table[b][t /
+// page_size], and T_max = max_pages * page_size.  Table entries are clamped
+// to [0, num_pages), so a bad entry writes a wrong page but never outside
+// the pool.
 #include "common.cuh"
 #include "launch.h"
 
@@ -19,14 +27,28 @@ namespace {
 
 constexpr int NT = 256;
 
+template <bool PAGED>
 __global__ __launch_bounds__(NT)
 void kv_append_kernel(unsigned char* __restrict__ kc, unsigned char* __restrict__ vc,
                       int32_t* __restrict__ lens, const unsigned char* __restrict__ kn,
-                      const unsigned char* __restrict__ vn, int H_kv, int T_max, int row_bytes) {
+                      const unsigned char* __restrict__ vn, int H_kv, int T_max, int row_bytes,
+                      const int32_t* __restrict__ block_table, int page_size, int max_pages,
+                      int num_pages) {
     const int b = blockIdx.x;
     const int t = lens[b];
     const bool ok = t >= 0 && t < T_max;
     if (ok) {
+        // element offset of slot t of head 0 and the stride between heads, in rows
+        size_t row0, head_rows;
+        if constexpr (PAGED) {
+            const int e = block_table[(size_t)b * max_pages + t / page_size];
+            const int page = min(max(e, 0), num_pages - 1);
+            row0 = (size_t)page * H_kv * page_size + t % page_size;
+            head_rows = (size_t)page_size;
+        } else {
+            row0 = (size_t)b * H_kv * T_max + t;
+            head_rows = (size_t)T_max;
+        }
         const int chunks = row_bytes / 16;            // per head
         const int total = 2 * H_kv * chunks;          // K then V
         for (int idx = threadIdx.x; idx < total; idx += NT) {
@@ -34,7 +56,7 @@ void kv_append_kernel(unsigned char* __restrict__ kc, unsigned char* __restrict_
             const int rem = idx - which * H_kv * chunks;
             const int g = rem / chunks, ch = rem - g * chunks;
             const size_t src = ((size_t)b * H_kv + g) * row_bytes + (size_t)ch * 16;
-            const size_t dst = (((size_t)b * H_kv + g) * T_max + t) * row_bytes + (size_t)ch * 16;
+            const size_t dst = (row0 + g * head_rows) * row_bytes + (size_t)ch * 16;
             if (which == 0) stg128(kc + dst, ldg128(kn + src));
             else stg128(vc + dst, ldg128(vn + src));
         }
@@ -47,10 +69,17 @@ void kv_append_kernel(unsigned char* __restrict__ kc, unsigned char* __restrict_
 
 hipError_t launch_kv_append(const AppendArgs& a) {
     const int row_bytes = a.D * a.elem_bytes;
-    hipLaunchKernelGGL(kv_append_kernel, dim3(a.B), dim3(NT), 0, (hipStream_t)a.stream,
-                       (unsigned char*)a.k_cache, (unsigned char*)a.v_cache, a.lens,
-                       (const unsigned char*)a.k_new, (const unsigned char*)a.v_new,
-                       a.H_kv, a.T_max, row_bytes);
+    if (a.block_table)
+        hipLaunchKernelGGL(kv_append_kernel<true>, dim3(a.B), dim3(NT), 0, (hipStream_t)a.stream,
+                           (unsigned char*)a.k_cache, (unsigned char*)a.v_cache, a.lens,
+                           (const unsigned char*)a.k_new, (const unsigned char*)a.v_new,
+                           a.H_kv, a.T_max, row_bytes, a.block_table, a.page_size, a.max_pages,
+                           a.num_pages);
+    else
+        hipLaunchKernelGGL(kv_append_kernel<false>, dim3(a.B), dim3(NT), 0, (hipStream_t)a.stream,
+                           (unsigned char*)a.k_cache, (unsigned char*)a.v_cache, a.lens,
+                           (const unsigned char*)a.k_new, (const unsigned char*)a.v_new,
+                           a.H_kv, a.T_max, row_bytes, nullptr, 0, 0, 0);
     return hipGetLastError();
 }
 

@@ -39,6 +39,11 @@ struct AppendArgs {
     const void* k_new; const void* v_new;
     int B, H_kv, T_max, D, elem_bytes;
     void* stream;
+    // paged cache: k_cache / v_cache are pools [num_pages, H_kv, page_size, D] and token t
+    // of sequence b sits at row t % page_size of page block_table[b * max_pages + t / page_size]
+    // (T_max = max_pages * page_size)
+    const int32_t* block_table = nullptr;
+    int page_size = 0, max_pages = 0, num_pages = 0;
 };
 
 struct DecodeArgs {
@@ -49,6 +54,9 @@ struct DecodeArgs {
     float scale;
     void* workspace;
     void* stream;
+    // paged cache, as in AppendArgs (page_size a power of two >= 16 here)
+    const int32_t* block_table = nullptr;
+    int page_size = 0, max_pages = 0, num_pages = 0;
 };
 
 hipError_t launch_fwd_bf16_d64(const FwdArgs& a);

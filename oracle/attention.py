@@ -74,6 +74,9 @@ def masked_softmax(S, padded):
     with no unpadded key get weights 0, m = -inf, l = 0.
     """
     S = np.where(padded[None, :], NEG_INF, S)
+    if S.shape[1] == 0:                             # no keys at all: as if all were padded
+        z = np.zeros(S.shape[0])
+        return np.zeros_like(S), np.full(S.shape[0], NEG_INF), z
     m = S.max(axis=1)
     live = np.isfinite(m)
     E = np.zeros_like(S)

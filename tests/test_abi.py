@@ -160,3 +160,44 @@ def test_varlen_validation(lib):
     assert vl(lse=C) == 8
     assert vl(tq=0, mq=0) == 0          # nothing to do: no launch, no pointer touched
     assert vl(mq=0) == 0
+
+
+def test_paged_validation(lib):
+    BT, W = 0x70000, 0x60000
+    ws = lib.attn_decode_workspace_bytes(4, 8, 2, 64 * 16, 128)
+
+    def dp(**kw):
+        a = dict(q=A, k=B_, v=C, bt=BT, lens=L, o=O, lse=0, B=4, Hq=8, Hkv=2, npg=100, ps=16, mp=64, D=128,
+                 scale=0.088, dtype=1, ws=W, wsb=ws)
+        a.update(kw)
+        return lib.attn_decode_paged(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["o"], a["lse"], a["B"],
+                                     a["Hq"], a["Hkv"], a["npg"], a["ps"], a["mp"], a["D"], a["scale"],
+                                     a["dtype"], a["ws"], a["wsb"], None)
+    assert dp(bt=0) == 1
+    assert dp(lens=0) == 1
+    assert dp(dtype=0) == 3           # bf16 only
+    assert dp(D=96) == 3
+    assert dp(ps=24) == 2             # not a power of two
+    assert dp(ps=8) == 2              # below 16
+    assert dp(npg=0) == 2
+    assert dp(mp=0) == 2
+    assert dp(mp=1 << 27) == 2        # capacity above 2^30 tokens
+    assert dp(Hq=5) == 2
+    assert dp(scale=-1.0) == 6
+    assert dp(wsb=ws - 1) == 4
+    assert dp(ws=0) == 4
+    assert dp(k=B_ + 8) == 7
+    assert dp(o=B_) == 8
+
+    def ap(**kw):
+        a = dict(k=A, v=B_, bt=BT, lens=L, kn=C, vn=O, B=4, Hkv=2, npg=100, ps=16, mp=64, D=128, dtype=1)
+        a.update(kw)
+        return lib.kv_append_paged(a["k"], a["v"], a["bt"], a["lens"], a["kn"], a["vn"], a["B"], a["Hkv"],
+                                   a["npg"], a["ps"], a["mp"], a["D"], a["dtype"], None)
+    assert ap(bt=0) == 1
+    assert ap(kn=0) == 1
+    assert ap(D=80) == 3
+    assert ap(ps=48) == 2
+    assert ap(B=0) == 2
+    assert ap(v=A) == 8
+    assert ap(kn=C + 4) == 7

@@ -506,3 +506,17 @@ def test_paged_append_then_decode_equals_contiguous():
     want = sorted((int(pg.block_table[b, int(d.lens[b]) // 16]), int(d.lens[b]) % 16) for b in range(3))
     got = sorted({(int(p), int(r)) for p, _, r in np.argwhere(np.any(kp != pg.k_pages.numpy(), axis=3))})
     assert got == want and len(diff) <= 3 * 2
+
+
+def test_decode_zero_length_has_no_keys():
+    # len 0: the empty key set, O = 0 and LSE = -inf like a fully padded row (brute force agrees)
+    d = workloads.make_decode(3, 4, 2, 8, 0, 5, torch.float32, lens=[0, 3, 0], seed=9)
+    O, L = oracle.decode(d.q, d.k_cache, d.v_cache, d.lens, d.scale)
+    o, l = brute.attend_row(d.q[0, 0, 0].tolist(), [], [], [], d.scale)
+    assert l == -math.inf
+    for b in (0, 2):
+        assert np.all(O[b] == 0) and np.all(np.isneginf(L[b]))
+    assert np.all(np.isfinite(L[1]))
+    pg = workloads.to_paged(d, 16)
+    Op, Lp = oracle.decode_paged(d.q, pg.k_pages, pg.v_pages, pg.block_table, d.lens, d.scale)
+    assert np.array_equal(Op, O) and np.array_equal(Lp, L)

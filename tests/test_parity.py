@@ -399,3 +399,98 @@ def test_varlen_p1944_packed(ma):
     rows = list(range(0, 3644, 37)) + [1943, 1944, 3643]
     Oref, Lref = oracle.attention_varlen(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale)
     check_attn(o[rows], l[:, rows].t(), Oref[rows], Lref[:, rows].T, torch.bfloat16, "varlen p1944")
+
+
+# ---- paged KV cache (block table) -------------------------------------------------------
+
+PAGED_CASES = [(shape, ps) for shape in DEC_SHAPES for ps in (16, 64)] + [
+    ((4, 8, 2, 128, 1, 1500, 1536), 512),
+    ((4, 8, 8, 128, 1023, 1023, 1024), 1024),
+    ((3, 16, 4, 64, 900, 4000, 4096), 2048),      # pages longer than a split
+    ((2, 32, 8, 128, 10, 3000, 3072), 32),
+]
+
+
+def _paged_dev(pg):
+    return (pg.k_pages.to(DEV), pg.v_pages.to(DEV), pg.block_table.to(DEV))
+
+
+@pytest.mark.parametrize("case", PAGED_CASES)
+def test_paged_append_then_decode(ma, case):
+    (B, Hq, Hkv, D, lo, hi, Tm), ps = case
+    w = W.make_decode(B, Hq, Hkv, D, lo, hi, torch.bfloat16, T_max=Tm, seed=B * 100 + Hq + ps)
+    pg = W.to_paged(w, ps, seed=ps)
+    kp, vp, bt = _paged_dev(pg)
+    lens = w.lens.to(DEV)
+    ma.kv_append_paged(kp, vp, bt, lens, w.k_new.to(DEV), w.v_new.to(DEV))
+    o, l = ma.attn_decode_paged(w.q.to(DEV), kp, vp, bt, lens, w.scale, want_lse=True)
+    torch.cuda.synchronize()
+    ek, ev, el = oracle.kv_append_paged(pg.k_pages.float().numpy(), pg.v_pages.float().numpy(),
+                                        pg.block_table.numpy(), w.lens.numpy(),
+                                        w.k_new.float().numpy(), w.v_new.float().numpy())
+    assert lens.cpu().tolist() == el.tolist()
+    # the append is a bit copy into exactly the pages the oracle wrote
+    assert np.array_equal(kp.cpu().float().numpy(), ek) and np.array_equal(vp.cpu().float().numpy(), ev)
+    Or, Lr = oracle.decode_paged(w.q, ek, ev, pg.block_table, el, w.scale)
+    check_attn(o, l, Or, Lr, torch.bfloat16, f"paged decode {case}")
+
+
+@pytest.mark.parametrize("ps", [16, 32, 128])
+@pytest.mark.parametrize("D", [64, 128])
+def test_paged_decode_bitwise_equals_contiguous(ma, ps, D):
+    # Same values, same block order: the paged call must reproduce the contiguous call bit for bit.
+    w = W.make_decode(5, 16, 4, D, 0, 2500, torch.bfloat16, T_max=2560, seed=ps + D)
+    pg = W.to_paged(w, ps, seed=3)
+    kp, vp, bt = _paged_dev(pg)
+    lens = w.lens.to(DEV)
+    o1, l1 = ma.attn_decode_paged(w.q.to(DEV), kp, vp, bt, lens, w.scale, want_lse=True)
+    o2, l2 = ma.attn_decode(w.q.to(DEV), w.k_cache.to(DEV), w.v_cache.to(DEV), lens, w.scale, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_paged_decode_shared_and_bad_entries(ma):
+    # Two sequences share their first pages (a shared prefix); entries past a sequence's
+    # length are garbage (never read); out-of-range entries inside the length are clamped.
+    w = W.make_decode(3, 8, 2, 128, 10, 200, torch.bfloat16, T_max=256, lens=[100, 70, 40], seed=4)
+    pg = W.to_paged(w, 16, seed=5)
+    bt = pg.block_table.clone()
+    n = pg.k_pages.shape[0]
+    bt[1, :4] = bt[0, :4]                 # shared prefix pages
+    bt[0, 7:] = 10 ** 6                   # past len 100 (pages 0..6 used): never read
+    bt[2, 2] = -7                         # inside len 40: clamped to page 0
+    bt[2, 1] = n + 5                      # clamped to the last page
+    kp, vp, _ = _paged_dev(pg)
+    o, l = ma.attn_decode_paged(w.q.to(DEV), kp, vp, bt.to(DEV), w.lens.to(DEV), w.scale, want_lse=True)
+    torch.cuda.synchronize()
+    eff = bt.clamp(0, n - 1)
+    Or, Lr = oracle.decode_paged(w.q, pg.k_pages, pg.v_pages, eff, w.lens, w.scale)
+    check_attn(o, l, Or, Lr, torch.bfloat16, "paged shared / clamped")
+
+
+def test_paged_decode_zero_lengths(ma):
+    w = W.make_decode(5, 8, 2, 64, 0, 10, torch.bfloat16, T_max=1024, lens=[0, 513, 0, 0, 31], seed=6)
+    pg = W.to_paged(w, 16, seed=7)
+    kp, vp, bt = _paged_dev(pg)
+    o, l = ma.attn_decode_paged(w.q.to(DEV), kp, vp, bt, w.lens.to(DEV), w.scale, want_lse=True)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.decode_paged(w.q, pg.k_pages, pg.v_pages, pg.block_table, w.lens, w.scale)
+    check_attn(o, l, Or, Lr, torch.bfloat16, "paged zero lengths")
+
+
+def test_gqa_decode_b32_paged_sampled_heads(ma):
+    """The full decode workload in 16-token pages: append, decode, sampled (b, h) against the oracle."""
+    pg = W.gqa_decode_b32_paged(16)
+    w = pg.dec
+    kp, vp, bt = _paged_dev(pg)
+    lens = w.lens.to(DEV)
+    ma.kv_append_paged(kp, vp, bt, lens, w.k_new.to(DEV), w.v_new.to(DEV))
+    o, l = ma.attn_decode_paged(w.q.to(DEV), kp, vp, bt, lens, w.scale, want_lse=True)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(6)
+    heads = [(int(b), int(h)) for b, h in zip(g.integers(0, 32, 16), g.integers(0, 32, 16))]
+    heads += [(int(np.argmax(w.lens)), 3)]
+    Or, Lr = oracle.decode_paged(w.q, kp.cpu(), vp.cpu(), pg.block_table, lens.cpu().numpy(), w.scale,
+                                 heads=heads)
+    check_attn(torch.stack([o[b, h, 0] for b, h in heads]), torch.stack([l[b, h] for b, h in heads]),
+               Or, Lr, torch.bfloat16, "paged decode sampled heads")
