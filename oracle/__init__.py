@@ -6,6 +6,6 @@ with the HIP path.
 """
 from .attention import (  # noqa: F401
     scores, masked_softmax, attention, attention_varlen, merge_lse, kv_append, decode,
-    gather_pages, kv_append_paged, decode_paged,
+    gather_pages, kv_append_paged, decode_paged, allowed_keys, prefill, prefill_varlen,
     attention_flops, score_matrix_bytes, kv_bytes_per_token, decode_kv_bytes,
 )

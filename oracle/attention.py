@@ -38,6 +38,7 @@ import numpy as np
 
 __all__ = [
     "scores", "masked_softmax", "attention", "attention_varlen", "merge_lse", "kv_append", "decode",
+    "allowed_keys", "prefill", "prefill_varlen",
     "gather_pages", "kv_append_paged", "decode_paged",
     "attention_flops", "score_matrix_bytes", "kv_bytes_per_token", "decode_kv_bytes",
 ]
@@ -158,6 +159,99 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale=None):
         ks = k[k0:k1].transpose(1, 0, 2)[None]
         vs = v[k0:k1].transpose(1, 0, 2)[None]
         Ob, Lb = attention(qs, ks, vs, None, scale)
+        O[q0:q1] = Ob[0].transpose(1, 0, 2)
+        LSE[:, q0:q1] = Lb[0]
+    return O, LSE
+
+
+# ---- GQA and causal prefill ----------------------------------------------------------
+# The prompt pass of a grouped-query-attention language model (nanoVLM-KV page, sections
+# "1. 어텐션 블록 업데이트" (LanguageModelGroupedAttention) and "3. 생성 루프 분리" (the
+# prefill phase encodes the whole prompt and fills the cache)): query head h reads KV head
+# h // (H_q / H_kv), and an autoregressive model's position i sees positions <= i only.
+# With Tk >= Tq the Tq queries are the LAST Tq positions of the Tk keys (a prompt chunk
+# after a cached prefix), so query i sees keys j <= i + (Tk - Tq); with Tq = Tk that is
+# j <= i, and a single query (Tq = 1) sees every key, which is the decode step.
+
+def allowed_keys(Tq, Tk, causal, padded=None):
+    """Boolean [Tq, Tk]: True where query i may attend key j (unpadded and, if causal,
+    j <= i + Tk - Tq)."""
+    ok = np.ones((Tq, Tk), dtype=bool)
+    if causal:
+        i = np.arange(Tq)[:, None]
+        j = np.arange(Tk)[None, :]
+        ok &= j <= i + (Tk - Tq)
+    if padded is not None:
+        ok &= ~np.asarray(padded, dtype=bool)[None, :]
+    return ok
+
+
+def _softmax_allowed(S, ok):
+    """Row softmax of S over the allowed entries: (W, m, l) as masked_softmax, a row
+    with no allowed entry giving W = 0, m = -inf, l = 0."""
+    S = np.where(ok, S, NEG_INF)
+    if S.shape[1] == 0:
+        return np.zeros_like(S), np.full(S.shape[0], NEG_INF), np.zeros(S.shape[0])
+    m = S.max(axis=1)
+    live = np.isfinite(m)
+    E = np.zeros_like(S)
+    E[live] = np.exp(S[live] - m[live, None])
+    l = E.sum(axis=1)
+    W = np.zeros_like(S)
+    W[live] = E[live] / l[live, None]
+    return W, m, l
+
+
+def prefill(q, k, v, key_padding_mask=None, causal=False, scale=None, rows=None):
+    """GQA (optionally causal, optionally key-padded) attention and its LSE.
+
+    q [B, H_q, Tq, D], k and v [B, H_kv, Tk, D] with H_q a multiple of H_kv; query head
+    h uses KV head h // (H_q / H_kv).  ``rows`` restricts to a subset of query indices
+    (the causal limit still uses each row's own index).  Returns O [B, H_q, R, D] and
+    LSE [B, H_q, R] in float64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Tq, D = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    assert k.shape == (B, Hkv, Tk, D) and v.shape == k.shape and Hq % Hkv == 0
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    padded = _mask_bool(key_padding_mask, B, Tk)
+    ridx = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = ridx.size
+    O = np.zeros((B, Hq, R, D))
+    LSE = np.full((B, Hq, R), NEG_INF)
+    for b in range(B):
+        ok = allowed_keys(Tq, Tk, causal, padded[b])[ridx]
+        for h in range(Hq):
+            S = scores(q[b, h, ridx], k[b, h // G], scale)
+            W, m, l = _softmax_allowed(S, ok)
+            O[b, h] = W @ v[b, h // G]
+            live = np.isfinite(m)
+            LSE[b, h, live] = m[live] + np.log(l[live])
+    return O, LSE
+
+
+def prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, causal=False, scale=None):
+    """``prefill`` on packed sequences: q [total_q, H_q, D], k and v [total_k, H_kv, D],
+    sequences as in ``attention_varlen`` (the causal limit uses each sequence's own
+    lengths).  Returns O [total_q, H_q, D] and LSE [H_q, total_q]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cq = np.asarray(_f64(cu_seqlens_q), dtype=np.int64)
+    ck = np.asarray(_f64(cu_seqlens_k), dtype=np.int64)
+    total_q, Hq, D = q.shape
+    Hkv = k.shape[1]
+    assert k.shape[2] == D and v.shape == k.shape and Hq % Hkv == 0
+    assert cq[0] == 0 and ck[0] == 0 and cq[-1] == total_q and ck[-1] == k.shape[0]
+    O = np.zeros((total_q, Hq, D))
+    LSE = np.full((Hq, total_q), NEG_INF)
+    for b in range(cq.size - 1):
+        q0, q1, k0, k1 = int(cq[b]), int(cq[b + 1]), int(ck[b]), int(ck[b + 1])
+        if q1 == q0:
+            continue
+        Ob, Lb = prefill(q[q0:q1].transpose(1, 0, 2)[None], k[k0:k1].transpose(1, 0, 2)[None],
+                         v[k0:k1].transpose(1, 0, 2)[None], None, causal, scale)
         O[q0:q1] = Ob[0].transpose(1, 0, 2)
         LSE[:, q0:q1] = Lb[0]
     return O, LSE

@@ -520,3 +520,97 @@ def test_decode_zero_length_has_no_keys():
     pg = workloads.to_paged(d, 16)
     Op, Lp = oracle.decode_paged(d.q, pg.k_pages, pg.v_pages, pg.block_table, d.lens, d.scale)
     assert np.array_equal(Op, O) and np.array_equal(Lp, L)
+
+
+# ---- GQA + causal prefill ------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(6))
+def test_prefill_gqa_causal_matches_brute_force(seed):
+    r = _rng(200 + seed)
+    B, Hkv, G = int(r.integers(1, 3)), int(r.integers(1, 3)), int(r.integers(1, 4))
+    Tq, Tk, D = int(r.integers(1, 9)), int(r.integers(1, 9)), int(r.integers(1, 7))
+    q = r.standard_normal((B, Hkv * G, Tq, D)) * 1.4
+    k = r.standard_normal((B, Hkv, Tk, D))
+    v = r.standard_normal((B, Hkv, Tk, D))
+    mask = (r.random((B, Tk)) < 0.25).astype(np.uint8) if seed % 2 else None
+    causal = seed != 4
+    scale = float(r.uniform(0.3, 1.2))
+    O, L = oracle.prefill(q, k, v, mask, causal, scale)
+    off = Tk - Tq
+    for b in range(B):
+        for h in range(Hkv * G):
+            g = h // G
+            for i in range(Tq):
+                pad = [(mask is not None and mask[b, j] != 0) or (causal and j > i + off) for j in range(Tk)]
+                o, l = brute.attend_row(q[b, h, i].tolist(), k[b, g].tolist(), v[b, g].tolist(), pad, scale)
+                if l == -math.inf:
+                    assert L[b, h, i] == -np.inf and np.all(O[b, h, i] == 0)
+                else:
+                    assert abs(L[b, h, i] - l) <= 1e-12
+                    assert np.max(np.abs(O[b, h, i] - np.array(o))) <= 1e-12
+
+
+def test_prefill_single_query_causal_is_decode():
+    # the last position sees every key: Tq = 1 causal prefill = the decode step over the cache
+    d = workloads.make_decode(3, 8, 2, 16, 5, 40, torch.float32, seed=10)
+    n = int(d.lens.max())
+    kc, vc = d.k_cache[:, :, :n], d.v_cache[:, :, :n]
+    for b in range(3):
+        lb = int(d.lens[b])
+        Op, Lp = oracle.prefill(d.q[b:b + 1], kc[b:b + 1, :, :lb], vc[b:b + 1, :, :lb], None, True, d.scale)
+        Od, Ld = oracle.decode(d.q[b:b + 1], kc[b:b + 1], vc[b:b + 1], d.lens[b:b + 1], d.scale)
+        assert np.allclose(Op, Od, atol=1e-13, rtol=0) and np.allclose(Lp[..., 0], Ld, atol=1e-13, rtol=0)
+
+
+def test_prefill_causal_row_is_attention_over_its_prefix():
+    w = workloads.make_prefill(1, 2, 6, 9, 8, torch.float32, seed=11)
+    O, L = oracle.prefill(w.q, w.k, w.v, None, True, w.scale)
+    for i in range(6):
+        n = i + 3 + 1                      # keys 0 .. i + (Tk - Tq)
+        Oi, Li = oracle.attention(w.q[:, :, i:i + 1], w.k[:, :, :n], w.v[:, :, :n], None, w.scale)
+        assert np.allclose(O[:, :, i:i + 1], Oi, atol=1e-13, rtol=0)
+        assert np.allclose(L[:, :, i:i + 1], Li, atol=1e-13, rtol=0)
+
+
+def test_prefill_gqa_equals_mha_on_repeated_kv_and_g1_is_attention():
+    w = workloads.make_prefill(2, 2, 7, 11, 8, torch.float32, valid=[11, 6], seed=12)
+    q6 = torch.cat([w.q, w.q * 0.5, -w.q], dim=1)          # 6 query heads over 2 KV heads
+    O, L = oracle.prefill(q6, w.k, w.v, w.mask, False, w.scale)
+    kr, vr = w.k.repeat_interleave(3, dim=1), w.v.repeat_interleave(3, dim=1)
+    Om, Lm = oracle.attention(q6, kr, vr, w.mask, w.scale)
+    assert np.allclose(O, Om, atol=1e-13, rtol=0) and np.allclose(L, Lm, atol=1e-13, rtol=0)
+    O1, L1 = oracle.prefill(w.q, w.k, w.v, w.mask, False, w.scale)
+    Oa, La = oracle.attention(w.q, w.k, w.v, w.mask, w.scale)
+    assert np.array_equal(O1, Oa) and np.array_equal(L1, La)
+
+
+def test_prefill_causal_rows_before_the_keys_are_empty():
+    # Tq > Tk: queries i < Tq - Tk precede every key, so they attend nothing
+    w = workloads.make_prefill(1, 1, 7, 4, 8, torch.float32, seed=13)
+    O, L = oracle.prefill(w.q, w.k, w.v, None, True, w.scale)
+    assert np.all(np.isneginf(L[0, 0, :3])) and np.all(O[0, 0, :3] == 0)
+    assert np.all(np.isfinite(L[0, 0, 3:]))
+
+
+def test_prefill_varlen_causal_gqa_matches_brute_force():
+    r = _rng(14)
+    lq, lk = [3, 0, 5, 2], [3, 4, 2, 6]
+    Hkv, G, D = 2, 2, 4
+    cq, ck = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q = r.standard_normal((cq[-1], Hkv * G, D))
+    k = r.standard_normal((ck[-1], Hkv, D))
+    v = r.standard_normal((ck[-1], Hkv, D))
+    O, L = oracle.prefill_varlen(q, k, v, cq, ck, True, 0.8)
+    for b in range(4):
+        off = lk[b] - lq[b]
+        for i in range(lq[b]):
+            for h in range(Hkv * G):
+                keys = list(range(ck[b], ck[b + 1]))
+                pad = [j - ck[b] > i + off for j in keys]
+                o, l = brute.attend_row(q[cq[b] + i, h].tolist(), [k[j, h // G].tolist() for j in keys],
+                                        [v[j, h // G].tolist() for j in keys], pad, 0.8)
+                row = cq[b] + i
+                if l == -math.inf:
+                    assert L[h, row] == -np.inf and np.all(O[row, h] == 0)
+                else:
+                    assert abs(L[h, row] - l) <= 1e-12 and np.max(np.abs(O[row, h] - np.array(o))) <= 1e-12
