@@ -52,8 +52,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-sweep", action="store_true",
                    help="skip the sections measured outside the step: the P-sweep of the prefill "
-                        "(memory and TFLOP/s at P = 1,944 .. 32,122), the packed varlen calls and "
-                        "the paged decode")
+                        "(memory and TFLOP/s at P = 1,944 .. 32,122), the packed varlen calls, "
+                        "the paged decode and the causal GQA prefill")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -247,6 +247,32 @@ def paged_section(torch, ma, W, dev):
     return res
 
 
+def causal_section(torch, ma, W, dev):
+    """Causal GQA prompt passes (attn_prefill / attn_prefill_varlen, H_q 32 / H_kv 8, D128), each
+    timed on its own: one 8,192-token prompt, and 8 packed prompts of 1,024 .. 4,096 tokens.
+    FLOP are algorithmic: 4·D·H_q per (query, visible key) pair, T(T+1)/2 pairs per prompt."""
+    res = {}
+    w = W.gqa_causal_prefill_8192()
+    q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    t = _time_call(torch, lambda: ma.attn_prefill(q, k, v, None, True, w.scale, out=o, lse=lse))
+    B, Hq, T, D = q.shape
+    flop = 4 * D * Hq * B * T * (T + 1) // 2
+    res["prompt_8192"] = {"workload": w.name, "us": round(t * 1e6, 1), "tflops": round(flop / t / 1e12, 1),
+                          "frac_mfma": round(flop / t / 1e12 / PEAK_BF16_TFLOPS, 4), "algorithmic_flop": flop}
+    del q, k, v, o, lse
+    w = W.gqa_causal_prompts_packed()
+    q, k, v, cq, ck = (t_.to(dev) for t_ in (w.q, w.k, w.v, w.cu_q, w.cu_k))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=dev)
+    t = _time_call(torch, lambda: ma.attn_prefill_varlen(q, k, v, cq, ck, w.max_q, True, w.scale, out=o, lse=lse))
+    flop = 4 * 128 * 32 * sum(n * (n + 1) // 2 for n in w.lens_q)
+    res["packed_prompts"] = {"workload": w.name, "us": round(t * 1e6, 1), "tflops": round(flop / t / 1e12, 1),
+                             "frac_mfma": round(flop / t / 1e12 / PEAK_BF16_TFLOPS, 4), "algorithmic_flop": flop}
+    return res
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -411,6 +437,7 @@ def main():
         out["p_sweep"] = p_sweep(torch, ma, dev)
         out["varlen"] = varlen_section(torch, ma, W, dev)
         out["paged_decode"] = paged_section(torch, ma, W, dev)
+        out["causal_gqa_prefill"] = causal_section(torch, ma, W, dev)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(pf, args.cpu_seconds)
         cb.pop("seconds", None)

@@ -125,6 +125,47 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v,
                     float scale, int dtype, void* stream);
 
 /*
+ * attn_prefill — grouped-query, optionally causal attention (the prompt pass).
+ *
+ * The prefill phase of a grouped-query-attention language model: the whole
+ * prompt is encoded once and its K/V fill the cache (nanoVLM-KV page,
+ * agentlenshq.com "nanoVLM에서 KV 캐시 구현", sections "1. 어텐션 블록
+ * 업데이트" and "3. 생성 루프 분리"); query heads share KV heads (LLM
+ * inference memory accounting 2/10, "11. 계산 예시: GQA Decoder").
+ *   q, o  [B, H_q, Tq, D] bf16      k, v  [B, H_kv, Tk, D] bf16
+ *   query head h reads KV head h / (H_q / H_kv); H_q must be a multiple of H_kv
+ *   causal  nonzero: query i sees keys j <= i + (Tk - Tq) only, i.e. the Tq
+ *       queries are the last Tq of the Tk positions (Tq = Tk: j <= i; Tq = 1:
+ *       every key).  A query that sees no key gets O = 0, LSE = -inf.
+ *   key_padding_mask  [B, Tk] uint8 or NULL, as attn_fwd_masked (combined
+ *       with the causal limit)
+ *   lse  [B, H_q, Tq] float32 or NULL
+ * bf16 only when causal or H_kv != H_q (ATTN_ERR_UNSUPPORTED otherwise; with
+ * neither it is attn_fwd_masked / attn_fwd_lse and takes float32 too).  Other
+ * rules as attn_fwd_masked.
+ */
+int attn_prefill(const void* q, const void* k, const void* v,
+                 const uint8_t* key_padding_mask, void* o, float* lse,
+                 int B, int H_q, int H_kv, int Tq, int Tk, int D, int causal,
+                 float scale, int dtype, void* stream);
+
+/*
+ * attn_prefill_varlen — attn_prefill on packed sequences.
+ *
+ * The varlen call with its causal flag (sglang PR 49078 analysis, section
+ * "1. aiter.py": flash_attn_varlen_func takes cu_seqlens and causal; the
+ * ring hop passes causal = false).  Layouts, cu_seqlens, LSE [H_q, total_q]
+ * and max_seqlen_q as attn_fwd_varlen, with k, v [total_k, H_kv, D]; the
+ * causal limit uses each sequence's own lengths.  bf16 only; H_q·D <= 2^22,
+ * total_k·H_kv·D < 2^30, total_q·H_q·D < 2^31.
+ */
+int attn_prefill_varlen(const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        void* o, float* lse,
+                        int B, int H_q, int H_kv, int total_q, int total_k, int max_seqlen_q,
+                        int D, int causal, float scale, int dtype, void* stream);
+
+/*
  * attn_merge_lse — combine n partial results over disjoint KV chunks.
  *
  * out = sum_i exp(lse_i - lse)·out_i with lse = log sum_i exp(lse_i), the

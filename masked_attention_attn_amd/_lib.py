@@ -31,7 +31,7 @@ STATUS = {
 
 EXPORTS = ("attn_fwd_masked", "attn_fwd_lse", "attn_fwd_varlen", "attn_merge_lse", "kv_append",
            "attn_decode", "attn_decode_workspace_bytes", "kv_append_paged", "attn_decode_paged",
-           "attn_status_string")
+           "attn_prefill", "attn_prefill_varlen", "attn_status_string")
 
 _lib = None
 
@@ -58,6 +58,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_merge_lse.argtypes = [I, ctypes.POINTER(P), ctypes.POINTER(P), P, P, I, I, I, I, I, P]
     lib.kv_append.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
     lib.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, P, S, P]
+    lib.attn_prefill.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
+    lib.attn_prefill_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P]
     lib.kv_append_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
     lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, S, P]
     lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -65,7 +67,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_status_string.argtypes = [I]
     lib.attn_status_string.restype = ctypes.c_char_p
     for name in ("attn_fwd_masked", "attn_fwd_lse", "attn_fwd_varlen", "attn_merge_lse", "kv_append",
-                 "attn_decode", "kv_append_paged", "attn_decode_paged"):
+                 "attn_decode", "kv_append_paged", "attn_decode_paged", "attn_prefill", "attn_prefill_varlen"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -339,4 +341,86 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, cache_seqlens, scale=Non
         _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(cache_seqlens), _ptr(out),
         _ptr(lse if want_lse else None), B, Hq, Hkv, num_pages, ps, mp, D, float(scale), ATTN_BF16,
         _ptr(workspace), nbytes, _stream(q.device)))
+    return (out, lse) if want_lse else out
+
+
+def attn_prefill(q, k, v, key_padding_mask=None, causal=False, scale=None, out=None, lse=None,
+                 want_lse: bool = True):
+    """GQA / causal attention: q [B, H_q, Tq, D], k/v [B, H_kv, Tk, D]; query head h reads KV
+    head h // (H_q / H_kv); causal lets query i see keys j <= i + Tk - Tq."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, T, D]")
+    B, Hq, Tq, D = q.shape
+    _, Hkv, Tk, _ = k.shape
+    if k.shape != (B, Hkv, Tk, D) or v.shape != k.shape:
+        raise ValueError("k/v must be [B, H_kv, Tk, D] with q's B and D")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    code = _dtype_code(q)
+    if key_padding_mask is not None:
+        _dev(key_padding_mask, "key_padding_mask")
+        if key_padding_mask.shape != (B, Tk):
+            raise ValueError(f"key_padding_mask must be [B, Tk] = {(B, Tk)}")
+        if key_padding_mask.dtype == torch.bool:
+            key_padding_mask = key_padding_mask.view(torch.uint8)
+        if key_padding_mask.dtype != torch.uint8:
+            raise TypeError("key_padding_mask must be uint8 or bool (nonzero/True = padded)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out")
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    if want_lse:
+        _dev(lse, "lse")
+        if lse.shape != (B, Hq, Tq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [B, H_q, Tq]")
+    _check("attn_prefill", load().attn_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(key_padding_mask), _ptr(out), _ptr(lse if want_lse else None),
+        B, Hq, Hkv, Tq, Tk, D, 1 if causal else 0, float(scale), code, _stream(q.device)))
+    return (out, lse) if want_lse else out
+
+
+def attn_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=False, scale=None,
+                        out=None, lse=None, want_lse: bool = True):
+    """Packed GQA / causal attention: q/o [total_q, H_q, D], k/v [total_k, H_kv, D] (bf16),
+    cu_seqlens_* int32 [B+1]; returns O (and the LSE [H_q, total_q])."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
+        _dev(t, n)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [total, H, D]")
+    total_q, Hq, D = q.shape
+    total_k, Hkv, Dk = k.shape
+    if Dk != D or v.shape != k.shape:
+        raise ValueError("k/v must be [total_k, H_kv, D] with q's D")
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("attn_prefill_varlen takes bfloat16 q, k, v")
+    if (cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32 or cu_seqlens_q.dim() != 1
+            or cu_seqlens_q.shape != cu_seqlens_k.shape):
+        raise ValueError("cu_seqlens_q / cu_seqlens_k must be int32 [B+1] of equal length")
+    B = cu_seqlens_q.shape[0] - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out")
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    if want_lse and lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    if want_lse:
+        _dev(lse, "lse")
+        if lse.shape != (Hq, total_q) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [H_q, total_q]")
+    _check("attn_prefill_varlen", load().attn_prefill_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(out),
+        _ptr(lse if want_lse else None), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), D,
+        1 if causal else 0, float(scale), ATTN_BF16, _stream(q.device)))
     return (out, lse) if want_lse else out

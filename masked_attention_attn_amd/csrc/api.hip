@@ -30,11 +30,14 @@ bool fits(long long a, long long b, long long c, long long d) {
 int finish(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
 
 int fwd_common(const void* q, const void* k, const void* v, const uint8_t* mask, void* o,
-               float* lse, bool need_lse, int B, int H, int Tq, int Tk, int D, float scale,
-               int dtype, void* stream) {
+               float* lse, bool need_lse, int B, int H, int H_kv, int Tq, int Tk, int D,
+               bool causal, float scale, int dtype, void* stream) {
     if (!q || !k || !v || !o || (need_lse && !lse)) return ATTN_ERR_NULL;
     if (!dtype_ok(dtype) || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
-    if (!fits(B, H, Tq, D) || !fits(B, H, Tk, D) || (long long)B * H > (1ll << 24) ||
+    // grouped-query and causal attention run in the bf16 kernel only
+    if ((causal || H_kv != H) && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (H_kv < 1 || H < 1 || H % H_kv != 0) return ATTN_ERR_SHAPE;
+    if (!fits(B, H, Tq, D) || !fits(B, H_kv, Tk, D) || (long long)B * H > (1ll << 24) ||
         (long long)B * H * ((Tq + 127) / 128) > (1ll << 31) - 64)
         return ATTN_ERR_SHAPE;
     if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
@@ -44,7 +47,41 @@ int fwd_common(const void* q, const void* k, const void* v, const uint8_t* mask,
     // the bf16 kernel addresses one head's K/V through a 32-bit buffer range
     if (dtype == ATTN_BF16 && (long long)Tk * D * 2 > (1ll << 31) - 1) return ATTN_ERR_SHAPE;
     FwdArgs a{q, k, v, mask, o, lse, B, H, Tq, Tk, D, scale, stream};
+    a.H_kv = H_kv;
+    a.causal = causal;
     if (dtype == ATTN_F32) return finish(launch_fwd_f32(a));
+    return finish(D == 64 ? launch_fwd_bf16_d64(a) : launch_fwd_bf16_d128(a));
+}
+
+int varlen_common(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                  const int32_t* cu_seqlens_k, void* o, float* lse, int B, int H, int H_kv,
+                  int total_q, int total_k, int max_seqlen_q, int D, bool causal, float scale,
+                  int dtype, void* stream) {
+    if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL;
+    if (!dtype_ok(dtype) || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+    if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0 || total_q < 0 || total_k < 0 ||
+        max_seqlen_q < 0 || max_seqlen_q > total_q)
+        return ATTN_ERR_SHAPE;
+    // One packed row is H·D elements; tile offsets of 64 rows must fit the 32-bit buffer offset.
+    if ((long long)H * D > (1ll << 22) || (long long)total_q * H * D > (1ll << 31) - 1 ||
+        (long long)total_k * H_kv * D > (1ll << 30) - 1 ||
+        (long long)B * H * ((max_seqlen_q + 127) / 128) > (1ll << 31) - 64)
+        return ATTN_ERR_SHAPE;
+    if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
+    if (o == q || o == k || o == v || (lse && ((void*)lse == q || (void*)lse == k || (void*)lse == v ||
+                                               (void*)lse == o)))
+        return ATTN_ERR_ALIAS;
+    if (total_q == 0 || max_seqlen_q == 0) return ATTN_OK;      // no query rows: nothing to write
+    FwdArgs a{q, k, v, nullptr, o, lse, B, H, max_seqlen_q, 0, D, scale, stream};
+    a.H_kv = H_kv;
+    a.causal = causal;
+    a.varlen = true;
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.total_q = total_q;
+    a.total_k = total_k;
     return finish(D == 64 ? launch_fwd_bf16_d64(a) : launch_fwd_bf16_d128(a));
 }
 
@@ -55,43 +92,37 @@ extern "C" {
 int attn_fwd_masked(const void* q, const void* k, const void* v, const uint8_t* key_padding_mask,
                     void* o, int B, int H, int Tq, int Tk, int D, float scale, int dtype,
                     void* stream) {
-    return fwd_common(q, k, v, key_padding_mask, o, nullptr, false, B, H, Tq, Tk, D, scale, dtype,
-                      stream);
+    return fwd_common(q, k, v, key_padding_mask, o, nullptr, false, B, H, H, Tq, Tk, D, false, scale,
+                      dtype, stream);
 }
 
 int attn_fwd_lse(const void* q, const void* k, const void* v, const uint8_t* key_padding_mask,
                  void* o, float* lse, int B, int H, int Tq, int Tk, int D, float scale, int dtype,
                  void* stream) {
-    return fwd_common(q, k, v, key_padding_mask, o, lse, true, B, H, Tq, Tk, D, scale, dtype,
-                      stream);
+    return fwd_common(q, k, v, key_padding_mask, o, lse, true, B, H, H, Tq, Tk, D, false, scale,
+                      dtype, stream);
+}
+
+int attn_prefill(const void* q, const void* k, const void* v, const uint8_t* key_padding_mask,
+                 void* o, float* lse, int B, int H_q, int H_kv, int Tq, int Tk, int D, int causal,
+                 float scale, int dtype, void* stream) {
+    return fwd_common(q, k, v, key_padding_mask, o, lse, false, B, H_q, H_kv, Tq, Tk, D,
+                      causal != 0, scale, dtype, stream);
+}
+
+int attn_prefill_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, void* o, float* lse, int B, int H_q, int H_kv,
+                        int total_q, int total_k, int max_seqlen_q, int D, int causal, float scale,
+                        int dtype, void* stream) {
+    return varlen_common(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, B, H_q, H_kv, total_q, total_k,
+                         max_seqlen_q, D, causal != 0, scale, dtype, stream);
 }
 
 int attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                     const int32_t* cu_seqlens_k, void* o, float* lse, int B, int H, int total_q,
                     int total_k, int max_seqlen_q, int D, float scale, int dtype, void* stream) {
-    if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL;
-    if (!dtype_ok(dtype) || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
-    if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-    if (B < 1 || H < 1 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_q > total_q)
-        return ATTN_ERR_SHAPE;
-    // One packed row is H·D elements; tile offsets of 64 rows must fit the 32-bit buffer offset.
-    if ((long long)H * D > (1ll << 22) || (long long)total_q * H * D > (1ll << 31) - 1 ||
-        (long long)total_k * H * D > (1ll << 30) - 1 ||
-        (long long)B * H * ((max_seqlen_q + 127) / 128) > (1ll << 31) - 64)
-        return ATTN_ERR_SHAPE;
-    if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
-    if (o == q || o == k || o == v || (lse && ((void*)lse == q || (void*)lse == k || (void*)lse == v ||
-                                               (void*)lse == o)))
-        return ATTN_ERR_ALIAS;
-    if (total_q == 0 || max_seqlen_q == 0) return ATTN_OK;      // no query rows: nothing to write
-    FwdArgs a{q, k, v, nullptr, o, lse, B, H, max_seqlen_q, 0, D, scale, stream};
-    a.varlen = true;
-    a.cu_q = cu_seqlens_q;
-    a.cu_k = cu_seqlens_k;
-    a.total_q = total_q;
-    a.total_k = total_k;
-    return finish(D == 64 ? launch_fwd_bf16_d64(a) : launch_fwd_bf16_d128(a));
+    return varlen_common(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, B, H, H, total_q, total_k,
+                         max_seqlen_q, D, false, scale, dtype, stream);
 }
 
 int attn_merge_lse(int n_chunks, const void* const* outs, const float* const* lses, void* out,

@@ -100,16 +100,22 @@ struct Lds {
     static constexpr int BYTES = ELEMS * (int)sizeof(bf16);
 };
 
-// VARLEN = false: q/k/v/o [B, H, T, D], mask [B, Tk] (or none), lse [B, H, Tq].
-// VARLEN = true: packed q/o [total_q, H, D], k/v [total_k, H, D] holding the
+// VARLEN = false: q/o [B, H, Tq, D], k/v [B, H_kv, Tk, D], mask [B, Tk] (or
+// none), lse [B, H, Tq].
+// VARLEN = true: packed q/o [total_q, H, D], k/v [total_k, H_kv, D] holding the
 // sequences back to back at the offsets cu_q / cu_k (B+1 entries, clamped to
 // [0, total]); lse [H, total_q]; no mask; Tq = the longest sequence (grid).
-template <int D, bool WRITE_LSE, bool VARLEN>
+// Query head h reads KV head h / (H / H_kv).
+// CAUSAL: query i of a sequence sees keys j <= i + (Tk - Tq) only.  A workgroup's
+// key range ends at its last query's limit, the per-query limit is applied on
+// the key blocks that cross a wave's diagonal, and q-tiles run last-first
+// (the longest first, for the balance of the grid).
+template <int D, bool WRITE_LSE, bool VARLEN, bool CAUSAL>
 __global__ __launch_bounds__(64 * Cfg<D>::NWAVE, 1)
 void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                      const bf16* __restrict__ v, const uint8_t* __restrict__ mask,
                      bf16* __restrict__ o, float* __restrict__ lse,
-                     int H, int Tq, int Tk, float c, int n_qt, int total,
+                     int H, int H_kv, int Tq, int Tk, float c, int n_qt, int total, int nparts, int tpp,
                      const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                      int total_q, int total_k) {
     using L = Lds<D>;
@@ -131,40 +137,65 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     bf16* smem = reinterpret_cast<bf16*>(smem_raw);
     __shared__ int red_s[3 * NWAVE];
 
-    const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
-    if (logical >= total) return;
-    const int bh = logical / n_qt;
-    const int qt = logical - bh * n_qt;
-    const int b = bh / H;
+    // Workgroup -> (b, h, q-tile).  Workgroup i runs on XCD i % 8.
+    int b, h, qt;
+    if constexpr (!VARLEN) {
+        // Equal work per (b, h): XCD x takes the x-th eighth of the (b, h, q-tile) order, so a
+        // head's q-tiles share one L2.
+        const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
+        if (logical >= total) return;
+        const int bh = logical / n_qt;
+        const int r = logical - bh * n_qt;
+        qt = CAUSAL ? n_qt - 1 - r : r;
+        b = bh / H;
+        h = bh - b * H;
+    } else {
+        // Sequences differ in length, so eighths of the grid would not balance.  The tiles of a
+        // (sequence, KV head) group (its G query heads x n_qt q-tiles, q-tile-major, last q-tile
+        // first when causal) form a chunk; each chunk is cut into nparts parts that take every
+        // nparts-th tile (so each part mixes long and short causal tiles), and the parts are
+        // dealt to the XCDs in turn: XCD x runs parts x, x+8, ..., one after the other, tpp
+        // workgroup slots each.  The G heads of a group share the group's K/V in that L2.
+        const int G = H / H_kv;
+        const int x = blockIdx.x % kNumXcd, k = blockIdx.x / kNumXcd;
+        const int part = (k / tpp) * kNumXcd + x;
+        const int chunk = part / nparts;
+        const int r = part - chunk * nparts + nparts * (k % tpp);
+        if (chunk >= total / (G * n_qt) || r >= G * n_qt) return;
+        const int qr = r / G;
+        qt = CAUSAL ? n_qt - 1 - qr : qr;
+        b = chunk / H_kv;
+        h = (chunk - b * H_kv) * G + (r - qr * G);
+    }
+    const int bh = b * H + h;
+    const int hk = h / (H / H_kv);        // KV head
     // This (b, h)'s rows: lengths, first rows and row strides (elements).
-    int Tq_, Tk_, rs;                     // rows of Q/O and K/V, row stride
+    int Tq_, Tk_, rsq, rsk;               // rows of Q/O and K/V, their row strides
     size_t q_row0, k_row0, l_row0;        // element offset of row 0 (LSE: index of row 0)
-    size_t l_rs;                          // LSE stride between rows
     if constexpr (VARLEN) {
-        const int h = bh - b * H;
         const int sq = min(max(cu_q[b], 0), total_q), eq = min(max(cu_q[b + 1], sq), total_q);
         const int sk = min(max(cu_k[b], 0), total_k), ek = min(max(cu_k[b + 1], sk), total_k);
         Tq_ = __builtin_amdgcn_readfirstlane(eq - sq);
         Tk_ = __builtin_amdgcn_readfirstlane(ek - sk);
-        rs = H * D;
+        rsq = H * D;
+        rsk = H_kv * D;
         q_row0 = ((size_t)sq * H + h) * D;
-        k_row0 = ((size_t)sk * H + h) * D;
+        k_row0 = ((size_t)sk * H_kv + hk) * D;
         l_row0 = (size_t)h * total_q + sq;
-        l_rs = 1;
     } else {
         Tq_ = Tq;
         Tk_ = Tk;
-        rs = D;
+        rsq = D;
+        rsk = D;
         q_row0 = (size_t)bh * Tq * D;
-        k_row0 = (size_t)bh * Tk * D;
+        k_row0 = ((size_t)b * H_kv + hk) * Tk * D;
         l_row0 = (size_t)bh * Tq;
-        l_rs = 1;
     }
     if (qt * BM >= Tq_) return;           // whole workgroup: past this sequence's queries
     const bf16* qp = q + q_row0;
     const uint8_t* mp = VARLEN ? nullptr : mask ? mask + (size_t)b * Tk_ : nullptr;
     // K/V buffer range ends after the last row, so rows >= Tk_ read as zero.
-    const uint32_t kv_bytes = Tk_ > 0 ? (uint32_t)((Tk_ - 1) * rs + D) * (uint32_t)sizeof(bf16) : 0u;
+    const uint32_t kv_bytes = Tk_ > 0 ? (uint32_t)((Tk_ - 1) * rsk + D) * (uint32_t)sizeof(bf16) : 0u;
     const i32x4_sgpr krs = make_rsrc(k + k_row0, kv_bytes);
     const i32x4_sgpr vrs = make_rsrc(v + k_row0, kv_bytes);
 
@@ -226,6 +257,9 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         last = __builtin_amdgcn_readfirstlane(last);
         holes = __builtin_amdgcn_readfirstlane(holes);
     }
+    // Causal: no query of this workgroup sees a key past its last query's limit.
+    const int coff = Tk_ - Tq_;           // query i sees keys <= i + coff
+    if constexpr (CAUSAL) last = min(last, min(Tq_ - 1, qt * BM + BM - 1) + coff);
     // Visited key blocks: [u_first, u_last] in units of CK keys; LDS tiles of TK keys.
     const int t_first = first / TK;
     const int u_first = t_first * HALVES;                  // steps start on a tile boundary
@@ -241,7 +275,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const int row = min(q0 + nb * 32 + l32, Tq_ - 1);
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk)
-            qreg[nb][kk] = as_bf16x8(ldg128(qp + (size_t)row * rs + kk * 16 + hl * 8));
+            qreg[nb][kk] = as_bf16x8(ldg128(qp + (size_t)row * rsq + kk * 16 + hl * 8));
     }
 
     // ---- tile loads straight into LDS: a tile is 8 KiB = 8 chunks of 1 KiB, wave w
@@ -259,8 +293,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const int o = (CPW * wave + i) * 1024 + lane * 16;
         const int r = o / L::RB, pch = (o % L::RB) / 16;
         const int kr = (r & ~31) | swap_bits23(r & 31);
-        k_voff[i] = (uint32_t)(kr * rs + (pch ^ k_swz<D>(r)) * 8) * 2u;
-        v_voff[i] = (uint32_t)(r * rs + (pch ^ v_swz<D>(r)) * 8) * 2u;
+        k_voff[i] = (uint32_t)(kr * rsk + (pch ^ k_swz<D>(r)) * 8) * 2u;
+        v_voff[i] = (uint32_t)(r * rsk + (pch ^ v_swz<D>(r)) * 8) * 2u;
     }
     // Ring slots are counted from the first visited tile: tile t sits in K slot
     // (t - t_first) % K_RING and V slot (t - t_first) % V_RING; kcur / vcur
@@ -272,12 +306,12 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     auto dma_k = [&](int t, int sl) {
 #pragma unroll
         for (int i = 0; i < CPW; ++i)
-            dma16(krs, kslot_b(sl) + (CPW * wave + i) * 1024, k_voff[i] + (uint32_t)t * TK * rs * 2u, 0u);
+            dma16(krs, kslot_b(sl) + (CPW * wave + i) * 1024, k_voff[i] + (uint32_t)t * TK * rsk * 2u, 0u);
     };
     auto dma_v = [&](int t, int sl) {
 #pragma unroll
         for (int i = 0; i < CPW; ++i)
-            dma16(vrs, vslot_b(sl) + (CPW * wave + i) * 1024, v_voff[i] + (uint32_t)t * TK * rs * 2u, 0u);
+            dma16(vrs, vslot_b(sl) + (CPW * wave + i) * 1024, v_voff[i] + (uint32_t)t * TK * rsk * 2u, 0u);
     };
     int kcur = 0, vcur = 0;
     static_assert(L::K_RING == 3 && L::V_RING == 2, "slot arithmetic below");
@@ -389,13 +423,29 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 }
             }
         }
+        if constexpr (CAUSAL) {
+            // key e of the block is past the limit of this lane's query nb iff
+            // e > lim0 + nb*32 + l32; wave-uniform test on the wave's first query
+            const int lim0 = q0 + coff - u * CK;
+            if (lim0 < CK - 1) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int lim = lim0 + nb * 32 + l32;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if ((i >> 3) * 16 + hl * 8 + (i & 7) > lim) S[nb][i] = kNegInf;
+                }
+            }
+        }
         if (!mc_set && pm != ~0u) {   // once: first block with an unpadded key
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 float m = S[nb][0];
 #pragma unroll
                 for (int i = 1; i < 16; ++i) m = fmaxf(m, S[nb][i]);
-                mc[nb] = pair_max(m) * c;
+                // a causal row may have no key at all (then any finite reference serves)
+                m = pair_max(m);
+                mc[nb] = m == kNegInf ? 0.f : m * c;
             }
             mc_set = true;
         }
@@ -604,7 +654,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const float inv = lt > 0.f ? 1.0f / lt : 0.f;
         const int qi = q0 + nb * 32 + l32;
         if (qi < Tq_) {
-            bf16* orow = o + q_row0 + (size_t)qi * rs;
+            bf16* orow = o + q_row0 + (size_t)qi * rsq;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -615,15 +665,15 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     *reinterpret_cast<u32x2*>(orow + db * 32 + g * 8 + hl * 4) = w;
                 }
             if (WRITE_LSE && hl == 0)
-                lse[l_row0 + (size_t)qi * l_rs] = lt > 0.f ? (mc[nb] + __log2f(lt)) * kLn2 : kNegInf;
+                lse[l_row0 + (size_t)qi] = lt > 0.f ? (mc[nb] + __log2f(lt)) * kLn2 : kNegInf;
         }
     }
 }
 
-template <int D, bool WRITE_LSE, bool VARLEN>
+template <int D, bool WRITE_LSE, bool VARLEN, bool CAUSAL>
 hipError_t launch_one(const FwdArgs& a) {
     using L = Lds<D>;
-    auto kern = fwd_bf16_kernel<D, WRITE_LSE, VARLEN>;
+    auto kern = fwd_bf16_kernel<D, WRITE_LSE, VARLEN, CAUSAL>;
     // LDS above 64 KiB must be opted into once per kernel (thread-safe static init).
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
@@ -631,13 +681,35 @@ hipError_t launch_one(const FwdArgs& a) {
     constexpr int BM = kBM<D>;
     const int n_qt = (a.Tq + BM - 1) / BM;       // varlen: Tq = the longest sequence
     const int total = a.B * a.H * n_qt;
-    const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
+    int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
+    int nparts = 1, tpp = 0;
+    if (VARLEN) {   // chunk parts dealt to the XCDs in turn (see the kernel)
+        const int H_kv = a.H_kv > 0 ? a.H_kv : a.H;
+        const int chunks = a.B * H_kv, S = (a.H / H_kv) * n_qt;
+        int g = kNumXcd, x = chunks;
+        while (x % g) g /= 2;                     // gcd(chunks, 8): 8 is a power of two
+        nparts = kNumXcd / g;
+        tpp = (S + nparts - 1) / nparts;
+        grid = chunks * nparts * tpp;             // chunks * nparts is a multiple of 8
+    }
     const float c = a.scale * kLog2e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * Cfg<D>::NWAVE), L::BYTES, (hipStream_t)a.stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.mask,
-                       (bf16*)a.o, a.lse, a.H, a.Tq, a.Tk, c, n_qt, total,
+                       (bf16*)a.o, a.lse, a.H, a.H_kv > 0 ? a.H_kv : a.H, a.Tq, a.Tk, c, n_qt, total, nparts, tpp,
                        a.cu_q, a.cu_k, a.total_q, a.total_k);
     return hipGetLastError();
+}
+
+template <int D, bool WRITE_LSE>
+hipError_t launch_lse(const FwdArgs& a) {
+    if (a.varlen)
+        return a.causal ? launch_one<D, WRITE_LSE, true, true>(a) : launch_one<D, WRITE_LSE, true, false>(a);
+    return a.causal ? launch_one<D, WRITE_LSE, false, true>(a) : launch_one<D, WRITE_LSE, false, false>(a);
+}
+
+template <int D>
+hipError_t launch(const FwdArgs& a) {
+    return a.lse ? launch_lse<D, true>(a) : launch_lse<D, false>(a);
 }
 
 }  // namespace fwdk

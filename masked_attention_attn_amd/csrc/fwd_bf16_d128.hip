@@ -3,9 +3,5 @@
 #include "fwd_bf16.cuh"
 
 namespace mattn {
-hipError_t launch_fwd_bf16_d128(const FwdArgs& a) {
-    if (a.varlen)
-        return a.lse ? fwdk::launch_one<128, true, true>(a) : fwdk::launch_one<128, false, true>(a);
-    return a.lse ? fwdk::launch_one<128, true, false>(a) : fwdk::launch_one<128, false, false>(a);
-}
+hipError_t launch_fwd_bf16_d128(const FwdArgs& a) { return fwdk::launch<128>(a); }
 }  // namespace mattn

@@ -4,9 +4,5 @@
 #include "fwd_bf16.cuh"
 
 namespace mattn {
-hipError_t launch_fwd_bf16_d64(const FwdArgs& a) {
-    if (a.varlen)
-        return a.lse ? fwdk::launch_one<64, true, true>(a) : fwdk::launch_one<64, false, true>(a);
-    return a.lse ? fwdk::launch_one<64, true, false>(a) : fwdk::launch_one<64, false, false>(a);
-}
+hipError_t launch_fwd_bf16_d64(const FwdArgs& a) { return fwdk::launch<64>(a); }
 }  // namespace mattn

@@ -16,6 +16,10 @@ struct FwdArgs {
     int B, H, Tq, Tk, D;          // varlen: B sequences, Tq = the longest query sequence
     float scale;
     void* stream;
+    // grouped-query attention: K/V have H_kv heads (0 = H); query head h reads h / (H / H_kv)
+    int H_kv = 0;
+    // causal: query i sees keys j <= i + (Tk - Tq) of its sequence (bf16 only)
+    bool causal = false;
     // packed variable-length layout ([total, H, D], offsets in cu_q / cu_k)
     bool varlen = false;
     const int32_t* cu_q = nullptr;

@@ -201,3 +201,37 @@ def test_paged_validation(lib):
     assert ap(B=0) == 2
     assert ap(v=A) == 8
     assert ap(kn=C + 4) == 7
+
+
+def test_prefill_validation(lib):
+    def pf(**kw):
+        a = dict(q=A, k=B_, v=C, m=0, o=O, lse=0, B=1, Hq=8, Hkv=2, Tq=64, Tk=64, D=64, causal=1, scale=0.125,
+                 dtype=1)
+        a.update(kw)
+        return lib.attn_prefill(a["q"], a["k"], a["v"], a["m"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                a["Tq"], a["Tk"], a["D"], a["causal"], a["scale"], a["dtype"], None)
+    assert pf(q=0) == 1
+    assert pf(dtype=0) == 3                   # causal needs bf16
+    assert pf(dtype=0, causal=0) == 3         # so does GQA
+    assert pf(Hq=6, Hkv=4) == 2
+    assert pf(Hkv=0) == 2
+    assert pf(D=80) == 3
+    assert pf(Tk=0) == 2
+    assert pf(scale=0.0) == 6
+    assert pf(v=C + 2) == 7
+    assert pf(lse=O) == 8
+    CQ, CK = 0x70000, 0x80000
+
+    def pv(**kw):
+        a = dict(q=A, k=B_, v=C, cq=CQ, ck=CK, o=O, lse=L, B=2, Hq=8, Hkv=2, tq=100, tk=90, mq=60, D=128,
+                 causal=1, scale=0.088, dtype=1)
+        a.update(kw)
+        return lib.attn_prefill_varlen(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["o"], a["lse"], a["B"],
+                                       a["Hq"], a["Hkv"], a["tq"], a["tk"], a["mq"], a["D"], a["causal"],
+                                       a["scale"], a["dtype"], None)
+    assert pv(cq=0) == 1
+    assert pv(dtype=0) == 3
+    assert pv(Hq=8, Hkv=3) == 2
+    assert pv(mq=101) == 2
+    assert pv(o=A) == 8
+    assert pv(tq=0, mq=0) == 0

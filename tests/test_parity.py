@@ -494,3 +494,83 @@ def test_gqa_decode_b32_paged_sampled_heads(ma):
                                  heads=heads)
     check_attn(torch.stack([o[b, h, 0] for b, h in heads]), torch.stack([l[b, h] for b, h in heads]),
                Or, Lr, torch.bfloat16, "paged decode sampled heads")
+
+
+# ---- GQA + causal prefill ------------------------------------------------------------------
+
+PREFILL = [
+    # B, H_q, H_kv, Tq, Tk, D, causal, valid key lengths (None = no mask)
+    (1, 1, 1, 1, 1, 64, True, None),
+    (1, 2, 1, 31, 31, 128, True, None),
+    (1, 4, 1, 300, 300, 64, True, None),
+    (2, 8, 2, 257, 257, 128, True, None),
+    (1, 2, 2, 100, 700, 64, True, None),          # a chunk after a cached prefix
+    (1, 2, 1, 600, 200, 128, True, None),         # more queries than keys: early rows see nothing
+    (2, 6, 3, 513, 513, 64, True, [513, 300]),    # causal and key padding together
+    (1, 4, 2, 333, 333, 64, False, [333]),        # GQA, not causal
+    (2, 4, 4, 1000, 1000, 64, True, None),
+    (1, 8, 1, 600, 900, 128, False, [850]),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL)
+def test_prefill_gqa_causal(ma, case):
+    B, Hq, Hkv, Tq, Tk, D, causal, valid = case
+    w = W.make_gqa_prefill(B, Hq, Hkv, Tq, Tk, D, valid=valid, seed=Tq + Hq)
+    m = w.mask.to(DEV) if w.mask is not None else None
+    o, l = ma.attn_prefill(w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), m, causal, w.scale)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.prefill(w.q, w.k, w.v, w.mask, causal, w.scale)
+    check_attn(o, l, Or, Lr, torch.bfloat16, f"prefill {case}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_gqa_bitwise_equals_mha_on_repeated_kv(ma, D):
+    w = W.make_gqa_prefill(2, 8, 2, 300, 450, D, valid=[450, 200], seed=3)
+    q, k, v, m = w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), w.mask.to(DEV)
+    o1, l1 = ma.attn_prefill(q, k, v, m, False, w.scale)
+    o2, l2 = ma.attn_fwd_lse(q, k.repeat_interleave(4, dim=1).contiguous(),
+                             v.repeat_interleave(4, dim=1).contiguous(), m, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_causal_single_query_bitwise_equals_noncausal(ma, D):
+    # one query is the last position: it sees every key, exactly the non-causal call
+    w = W.make_gqa_prefill(2, 4, 4, 1, 777, D, valid=[777, 500], seed=4)
+    q, k, v, m = w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), w.mask.to(DEV)
+    o1, l1 = ma.attn_prefill(q, k, v, m, True, w.scale)
+    o2, l2 = ma.attn_fwd_lse(q, k, v, m, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+VARLEN_CAUSAL = [
+    # lens_q, lens_k, H_q, H_kv, D, causal
+    ([300, 0, 513, 64], [300, 10, 513, 100], 4, 2, 64, True),
+    ([1, 257, 40], [1, 257, 600], 8, 2, 128, True),
+    ([700, 129], [700, 129], 2, 1, 64, False),
+    ([100, 300], [40, 300], 4, 4, 128, True),       # Tq > Tk in the first sequence
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CAUSAL)
+def test_prefill_varlen_gqa_causal(ma, case):
+    lq, lk, Hq, Hkv, D, causal = case
+    w = W.make_varlen(lq, lk, Hq, D, H_kv=Hkv, seed=len(lq) * 10 + Hq)
+    q, k, v, cq, ck = (t.to(DEV) for t in (w.q, w.k, w.v, w.cu_q, w.cu_k))
+    o, l = ma.attn_prefill_varlen(q, k, v, cq, ck, w.max_q, causal, w.scale)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.prefill_varlen(w.q, w.k, w.v, w.cu_q, w.cu_k, causal, w.scale)
+    check_attn(o, l.t(), Or, Lr.T, torch.bfloat16, f"varlen prefill {case}")
+
+
+def test_gqa_causal_prefill_8192_sampled_rows(ma):
+    """The 8,192-token causal GQA prompt (H_q 32 / H_kv 8, D128) on sampled rows of every head."""
+    w = W.gqa_causal_prefill_8192()
+    o, l = ma.attn_prefill(w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), None, True, w.scale)
+    torch.cuda.synchronize()
+    rows = [0, 1, 31, 32, 255, 256, 4095, 4096, 8191] + list(range(7, 8192, 613))
+    Or, Lr = oracle.prefill(w.q, w.k, w.v, None, True, w.scale, rows=rows)
+    check_attn(o[:, :, rows], l[:, :, rows], Or, Lr, torch.bfloat16, "causal 8192 sampled rows")

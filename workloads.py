@@ -40,7 +40,7 @@ __all__ = [
     "mask_from_valid_lengths", "round_up",
     "fp32_masked_t512", "patch_p1944", "patch_p11616",
     "chunked_kv_2x8192", "gqa_decode_b32", "varlen_p1944_packed", "varlen_ring_hop_8192",
-    "gqa_decode_b32_paged",
+    "gqa_decode_b32_paged", "make_gqa_prefill", "gqa_causal_prefill_8192", "gqa_causal_prompts_packed",
 ]
 
 
@@ -199,16 +199,18 @@ def cu_from_lengths(lens: Sequence[int]) -> torch.Tensor:
     return torch.tensor(c, dtype=torch.int32)
 
 
-def make_varlen(lens_q, lens_k, H, D, dtype=torch.bfloat16, *, amp=1.0, seed=0, scale=None,
+def make_varlen(lens_q, lens_k, H, D, dtype=torch.bfloat16, *, H_kv=None, amp=1.0, seed=0, scale=None,
                 name="") -> Varlen:
-    """Packed [total, H, D] Q, K, V for sequences of the given query / key lengths."""
+    """Packed [total, H, D] Q and [total, H_kv, D] K, V (H_kv defaults to H) for sequences of
+    the given query / key lengths."""
     assert len(lens_q) == len(lens_k) >= 1
+    H_kv = H if H_kv is None else H_kv
     g = _gen(seed)
     cq, ck = cu_from_lengths(lens_q), cu_from_lengths(lens_k)
     tq, tk = int(cq[-1]), int(ck[-1])
     q = _randn(g, (tq, H, D), amp, dtype)
-    k = _randn(g, (tk, H, D), amp, dtype)
-    v = _randn(g, (tk, H, D), amp, dtype)
+    k = _randn(g, (tk, H_kv, D), amp, dtype)
+    v = _randn(g, (tk, H_kv, D), amp, dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     return Varlen(q, k, v, cq, ck, max([int(n) for n in lens_q]), float(scale), name)
@@ -236,6 +238,19 @@ def to_paged(dec: Decode, page_size: int, *, seed=1, spare_pages=3) -> Paged:
     kp[bt.reshape(-1).long()] = kc.reshape(B * mp, H_kv, page_size, D)
     vp[bt.reshape(-1).long()] = vc.reshape(B * mp, H_kv, page_size, D)
     return Paged(dec, kp.contiguous(), vp.contiguous(), bt, page_size)
+
+
+def make_gqa_prefill(B, H_q, H_kv, Tq, Tk, D, dtype=torch.bfloat16, *, valid=None, amp=1.0, seed=0,
+                     scale=None, name="") -> Prefill:
+    """Q [B, H_q, Tq, D] and K/V [B, H_kv, Tk, D] (grouped-query layout), drawn Q, K, V."""
+    g = _gen(seed)
+    q = _randn(g, (B, H_q, Tq, D), amp, dtype)
+    k = _randn(g, (B, H_kv, Tk, D), amp, dtype)
+    v = _randn(g, (B, H_kv, Tk, D), amp, dtype)
+    mask = mask_from_valid_lengths(valid, Tk) if valid is not None else None
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return Prefill(q, k, v, mask, float(scale), name)
 
 
 # ---- the five named workloads -------------------------------------------------
@@ -286,3 +301,24 @@ def varlen_ring_hop_8192(seed=0) -> Varlen:
 def gqa_decode_b32_paged(page_size=16, seed=0) -> Paged:
     """The GQA decode workload (B32, H_q 32 / H_kv 8, D128, len U[512, 8192]) in a paged cache."""
     return to_paged(gqa_decode_b32(seed), page_size)
+
+
+
+def gqa_causal_prefill_8192(seed=0) -> Prefill:
+    """bf16 causal GQA prompt pass: B1, H_q 32 / H_kv 8, D128, an 8,192-token prompt."""
+    return make_gqa_prefill(1, 32, 8, 8192, 8192, 128, seed=seed,
+                            name="bf16 causal GQA prefill B1 Hq32 Hkv8 D128, 8192-token prompt")
+
+
+def gqa_causal_prompts_packed(seed=0) -> Varlen:
+    """bf16 packed causal GQA prompts: 4 x 1,024 + 2 x 2,048 + 2 x 4,096 tokens, H_q 32 / H_kv 8,
+    D128 (queries and keys of each prompt are the same positions)."""
+    lens = [1024, 4096, 1024, 2048, 1024, 4096, 2048, 1024]
+    g = _gen(seed)
+    cq = cu_from_lengths(lens)
+    n = int(cq[-1])
+    q = _randn(g, (n, 32, 128), 1.0, torch.bfloat16)
+    k = _randn(g, (n, 8, 128), 1.0, torch.bfloat16)
+    v = _randn(g, (n, 8, 128), 1.0, torch.bfloat16)
+    return Varlen(q, k, v, cq, cq.clone(), max(lens), 1.0 / math.sqrt(128),
+                  "bf16 packed causal GQA prompts Hq32 Hkv8 D128, 4x1024 + 2x2048 + 2x4096")
