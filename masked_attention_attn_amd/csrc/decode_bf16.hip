@@ -610,37 +610,78 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
     wait_vmem_le<0>();     // drain the zero-range look-ahead loads before exit
 }
 
-// Merge the parts of every split of (b, query head) and normalise.  Every
-// (split, part) slot was written by the split kernel; an absent part 1
-// carries reference -inf and weight sum 0.
+// Merge the parts of every split of (b, query head) and normalise: one
+// wavefront per (b, query head), lane l holding elements l*E .. l*E+E-1 of the
+// output row.  The (reference, sum) of the parts (lane k: part k) and the O rows
+// of the first 16 parts are loaded in one round, so the merge costs one memory
+// latency for caches up to 8 splits; parts beyond are merged 16 at a time with
+// a running reference.  Every (split, part) slot was written by the split
+// kernel; an absent part 1 carries reference -inf and weight sum 0, and its O
+// slot (never written) is read but not used.
 template <int D>
-__global__ __launch_bounds__(D)
+__global__ __launch_bounds__(256)
 void decode_stream_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
                            const int32_t* __restrict__ lens, bf16* __restrict__ o,
-                           float* __restrict__ lse, int H_q, int T_max, int nsplit) {
-    const int bh = blockIdx.x;
+                           float* __restrict__ lse, int H_q, int T_max, int nsplit, int n_bh) {
+    constexpr int E = D / 64;
+    constexpr int PG = 16;                       // parts per load round
+    const int lane = threadIdx.x & 63;
+    const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (bh >= n_bh) return;
     const int b = bh / H_q;
-    const int d = threadIdx.x;
     const int len = seq_len(lens, b, T_max);
     const int np = (len + kDecodeSplit - 1) / kDecodeSplit * 2;    // (split, part) slots
     const size_t base = (size_t)bh * nsplit * 2;
-    float M = kNegInf;
-    for (int k = 0; k < np; ++k) M = fmaxf(M, ws_ml[(base + k) * 2]);
-    if (np == 0 || M == kNegInf) {
-        o[(size_t)bh * D + d] = (bf16)0.f;
-        if (lse && d == 0) lse[bh] = kNegInf;
+    const float* orow_ws = ws_o + base * D + lane * E;
+    float M = kNegInf, lsum = 0.f;
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    for (int k0 = 0; k0 < np; k0 += PG) {
+        // one round: (m, l) of parts k0 .. k0+PG-1 in lanes 0..PG-1, and their O elements
+        const int k = k0 + lane;
+        const bool mine = lane < PG && k < np;
+        const float m = mine ? ws_ml[(base + k) * 2] : kNegInf;
+        const float l = mine ? ws_ml[(base + k) * 2 + 1] : 0.f;
+        float ov[PG][E];
+#pragma unroll
+        for (int i = 0; i < PG; ++i)
+#pragma unroll
+            for (int e = 0; e < E; ++e) ov[i][e] = k0 + i < np ? orow_ws[(size_t)(k0 + i) * D + e] : 0.f;
+        float mg = m;
+#pragma unroll
+        for (int sh = 8; sh >= 1; sh >>= 1) mg = fmaxf(mg, __shfl_xor(mg, sh));
+        mg = __shfl(mg, 0);
+        const float Mn = fmaxf(M, mg);
+        if (Mn == kNegInf) continue;             // nothing present yet
+        const float alpha = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+        M = Mn;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] *= alpha;
+        lsum *= alpha;
+        const float w = m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m - M);
+        float lw = w * l;
+#pragma unroll
+        for (int sh = 8; sh >= 1; sh >>= 1) lw += __shfl_xor(lw, sh);
+        lsum += __shfl(lw, 0);
+#pragma unroll
+        for (int i = 0; i < PG; ++i) {
+            const float wi = __shfl(w, i);
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] = wi != 0.f ? __builtin_fmaf(ov[i][e], wi, acc[e]) : acc[e];
+        }
+    }
+    bf16* orow = o + (size_t)bh * D + lane * E;
+    if (M == kNegInf) {                          // no cached token
+#pragma unroll
+        for (int e = 0; e < E; ++e) orow[e] = (bf16)0.f;
+        if (lse && lane == 0) lse[bh] = kNegInf;
         return;
     }
-    float acc = 0.f, Lsum = 0.f;
-    for (int k = 0; k < np; ++k) {
-        const float m = ws_ml[(base + k) * 2];
-        if (m == kNegInf) continue;              // absent part: its O slot is not written
-        const float wgt = __builtin_amdgcn_exp2f(m - M);
-        acc = __builtin_fmaf(ws_o[(base + k) * D + d], wgt, acc);
-        Lsum = __builtin_fmaf(ws_ml[(base + k) * 2 + 1], wgt, Lsum);
-    }
-    o[(size_t)bh * D + d] = (bf16)(acc / Lsum);
-    if (lse && d == 0) lse[bh] = (M + __log2f(Lsum)) * kLn2;
+    const float inv = 1.0f / lsum;
+#pragma unroll
+    for (int e = 0; e < E; ++e) orow[e] = (bf16)(acc[e] * inv);
+    if (lse && lane == 0) lse[bh] = (M + __log2f(lsum)) * kLn2;
 }
 
 // Wavefronts the split kernel runs at once (one round of the whole GPU) for
@@ -683,8 +724,9 @@ hipError_t launch(const DecodeArgs& a) {
                        a.block_table, lps, a.max_pages, a.num_pages);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_stream_combine<D>), dim3(a.B * a.H_q), dim3(D), 0, (hipStream_t)a.stream,
-                       ws_o, ws_ml, a.lens, (bf16*)a.o, a.lse, a.H_q, a.T_max, nsplit);
+    const int n_bh = a.B * a.H_q;
+    hipLaunchKernelGGL((decode_stream_combine<D>), dim3((n_bh + 3) / 4), dim3(256), 0, (hipStream_t)a.stream,
+                       ws_o, ws_ml, a.lens, (bf16*)a.o, a.lse, a.H_q, a.T_max, nsplit, n_bh);
     return hipGetLastError();
 }
 
