@@ -22,16 +22,21 @@
 // merge (sglang PR 49078 analysis, "1. aiter.py").
 //
 // Per block, on the matrix cores, with the query heads as the 32 columns:
-//   Sᵀ[key, head] = K·Qᵀ   (A = 32 K rows from LDS, B = Q from registers)
+//   Sᵀ[key, head] = K·Qᵀ   (A = 32 K rows from registers, B = Q from registers)
 //   Oᵀ[d, head]  += Vᵀ·Pᵀ  (A = Vᵀ via the transposing LDS read, B = P)
-// (lane l owns head column l%32 and 16 of the block's keys; K rows are
-// stored with bits 2 and 3 of the row index swapped so a lane's P values are
-// consecutive accumulator elements).  K, V and each item's Q reach LDS by
-// direct buffer->LDS loads issued R-1 blocks ahead; buffer ranges end at the
-// item's last token, so look-ahead past it reads zeros without touching
-// memory.  Softmax per head column: weights 2^(S·c - mc), mc from the exact
-// max of the item's first block here, raised only when a 16-key chunk's
-// per-lane sum passes 2^8 (then l and O are rescaled).
+// (lane l owns head column l%32 and 16 of the block's keys; K rows are taken
+// with bits 2 and 3 of the row index swapped so a lane's P values are
+// consecutive accumulator elements).  The look-ahead lives in registers as
+// well as LDS, so that it is not capped by the LDS size: K of a block is
+// loaded straight into the A-operand layout two blocks ahead, V by
+// buffer->LDS loads into a ring of four slots three blocks ahead (each slot
+// its own LDS array), and each item's Q into an LDS slot with the V of its
+// first block.  The loads are compiler builtins, so the compiler derives the
+// waits for K and Q; only the V slot reads carry an explicit wait.  Buffer
+// ranges end at the item's last token, so look-ahead past it reads zeros
+// without touching memory.  Softmax per head column: weights 2^(S·c - mc),
+// mc from the exact max of the item's first block here, raised only when a
+// 16-key chunk's per-lane sum passes 2^8 (then l and O are rescaled).
 #include "common.cuh"
 #include "launch.h"
 #include "mfma_lds.cuh"
@@ -49,9 +54,9 @@ template <int D> struct Geo {
     static constexpr int RB = D * 2;               // bytes per cache row
     static constexpr int BLK = CK * RB;            // bytes of one K (or V) block
     static constexpr int NCH = BLK / 1024;         // 1 KiB loads per block
-    static constexpr int R = D == 64 ? 4 : 3;      // ring depth in blocks
+    static constexpr int RV = 4;                   // V ring slots (look-ahead RV - 1 blocks)
+    static constexpr int LK = 2;                   // K look-ahead in blocks (in registers)
     static constexpr int QCH = 32 * RB / 1024;     // 1 KiB loads of a full 32-head Q slot
-    static constexpr int RING = R * 2 * BLK;       // LDS bytes of the K/V ring
 };
 // Q slot bytes: the group's heads (at most 32) rounded up to whole 1 KiB loads.
 inline int q_slot_bytes(int G, int D) { return (min(G, 32) * D * 2 + 1023) / 1024 * 1024; }
@@ -71,48 +76,6 @@ __device__ __forceinline__ int wave_scan(int x) {
     return x;
 }
 
-// N loads of 16 bytes per lane straight into LDS: load k writes LDS bytes
-// [m[k] + 16*lane, +16) from buffer offset vo[k] (per lane).  One statement
-// per block keeps the M0 save / restore to once per N loads.
-__device__ __forceinline__ void dma_x4(i32x4_sgpr r, const uint32_t* m, const uint32_t* vo) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %5, %9, 0 offen lds\n\t"
-        "s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %6, %9, 0 offen lds\n\t"
-        "s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %7, %9, 0 offen lds\n\t"
-        "s_mov_b32 m0, %4\n\tbuffer_load_dwordx4 %8, %9, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(m[0]), "s"(m[1]), "s"(m[2]), "s"(m[3]), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "s"(r)
-        : "memory");
-}
-__device__ __forceinline__ void dma_x2(i32x4_sgpr r, const uint32_t* m, const uint32_t* vo) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %3, %5, 0 offen lds\n\t"
-        "s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %4, %5, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(m[0]), "s"(m[1]), "v"(vo[0]), "v"(vo[1]), "s"(r)
-        : "memory");
-}
-template <int N>
-__device__ __forceinline__ void dma_n(i32x4_sgpr r, uint32_t lds_addr, const uint32_t* vo) {
-    static_assert(N % 2 == 0, "whole pairs");
-#pragma unroll
-    for (int k = 0; k + 4 <= N; k += 4) {
-        const uint32_t m[4] = {lds_addr + (k + 0) * 1024u, lds_addr + (k + 1) * 1024u, lds_addr + (k + 2) * 1024u,
-                               lds_addr + (k + 3) * 1024u};
-        dma_x4(r, m, vo + k);
-    }
-    if constexpr (N % 4 == 2) {
-        const uint32_t m[2] = {lds_addr + (N - 2) * 1024u, lds_addr + (N - 1) * 1024u};
-        dma_x2(r, m, vo + N - 2);
-    }
-}
-
 // Two dwords at byte offsets o0, o1 of a wavefront-uniform table (scalar loads: they
 // count in lgkmcnt, not vmcnt, so the vector-load accounting of the look-ahead is not
 // disturbed).  Both offsets must lie inside the table.
@@ -126,34 +89,18 @@ __device__ __forceinline__ void sload2(const int32_t* p, uint32_t o0, uint32_t o
         : "memory");
 }
 
-// Stores written as inline assembly so that their number is exact: stores
-// count in vmcnt like loads, and the waits of the look-ahead stream allow for
-// the partial-result stores issued since a block's loads.  Every lane issues
-// them (offsets past the buffer range are dropped); the trailing s_nop keeps
-// the data registers unmodified for the cycle after the last store.
-__device__ __forceinline__ void store_x4x4(i32x4_sgpr r, uint32_t o0, u32x4 a, uint32_t o1, u32x4 b,
-                                           uint32_t o2, u32x4 c2, uint32_t o3, u32x4 d2) {
-    asm volatile(
-        "buffer_store_dwordx4 %0, %1, %8, 0 offen\n\t"
-        "buffer_store_dwordx4 %2, %3, %8, 0 offen\n\t"
-        "buffer_store_dwordx4 %4, %5, %8, 0 offen\n\t"
-        "buffer_store_dwordx4 %6, %7, %8, 0 offen\n\t"
-        "s_nop 1"
-        :
-        : "v"(a), "v"(o0), "v"(b), "v"(o1), "v"(c2), "v"(o2), "v"(d2), "v"(o3), "s"(r)
-        : "memory");
-}
-__device__ __forceinline__ void store_x2(i32x4_sgpr r, uint32_t o, u32x2 v) {
-    asm volatile("buffer_store_dwordx2 %0, %1, %2, 0 offen\n\ts_nop 1" : : "v"(v), "v"(o), "s"(r) : "memory");
-}
-
 // Clamped sequence lengths as seen by one wavefront: with at most 64
 // sequences lane b holds len_b in a register (read back with readlane, no
 // memory round trip); beyond that they are read from memory.
 struct Lens {
     const int32_t* p;
     int B, T_max, reg;
-    __device__ int get(int b) const { return B <= 64 ? __builtin_amdgcn_readlane(reg, b) : seq_len(p, b, T_max); }
+    __device__ int get(int b) const {
+        if (B <= 64) return __builtin_amdgcn_readlane(reg, b);
+        int v, u;              // scalar load: no wait on the wavefront's vector loads
+        sload2(p, __builtin_amdgcn_readfirstlane((uint32_t)b * 4u), __builtin_amdgcn_readfirstlane((uint32_t)b * 4u), v, u);
+        return min(max(v, 0), T_max);
+    }
 };
 __device__ __forceinline__ Lens load_lens(const int32_t* lens, int B, int T_max) {
     const int lane = threadIdx.x & 63;
@@ -289,6 +236,74 @@ __device__ __forceinline__ void advance(Cursor& c, const Lens& L, int HG, int n_
 // row t mod 2^lps of page bt[b * max_pages + (t >> lps)] (entries clamped to
 // [0, num_pages)), T_max = max_pages << lps.  A 32-token block is loaded as two
 // 16-token halves, each inside one page, each through its own buffer range.
+// Buffer descriptor for the compiler's buffer-load builtins: `bytes` from p are
+// addressable, offsets past them read as zero without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds_chunk, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_chunk, 16, voff,
+                                             0, 0, 0);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+// The transposing LDS reads of one V block's operands (2 k-steps x DB row blocks x
+// lo/hi), written as one asm statement ending in lgkmcnt(0).  They are asm so
+// that the compiler inserts no wait of its own for the block's LDS loads (it
+// cannot tell the ring slots apart for these reads and would wait for the most
+// recent one); the caller waits for the slot explicitly.  addr[db]: this lane's
+// LDS byte address of row block db for k-step 0, lo half.
+template <int D>
+__device__ __forceinline__ void v_operands(const uint32_t* addr, u32x4 (&va)[2][D / 32]) {
+    constexpr int K2 = 16 * D * 2;     // bytes between the k-steps (16 rows)
+    constexpr int HI = 4 * D * 2;      // bytes between the lo and hi 4-row groups
+    u32x2 r[2][D / 32][2];
+    if constexpr (D == 128) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %16\n\tds_read_b64_tr_b16 %1, %16 offset:%20\n\t"
+            "ds_read_b64_tr_b16 %2, %17\n\tds_read_b64_tr_b16 %3, %17 offset:%20\n\t"
+            "ds_read_b64_tr_b16 %4, %18\n\tds_read_b64_tr_b16 %5, %18 offset:%20\n\t"
+            "ds_read_b64_tr_b16 %6, %19\n\tds_read_b64_tr_b16 %7, %19 offset:%20\n\t"
+            "ds_read_b64_tr_b16 %8, %16 offset:%21\n\tds_read_b64_tr_b16 %9, %16 offset:%22\n\t"
+            "ds_read_b64_tr_b16 %10, %17 offset:%21\n\tds_read_b64_tr_b16 %11, %17 offset:%22\n\t"
+            "ds_read_b64_tr_b16 %12, %18 offset:%21\n\tds_read_b64_tr_b16 %13, %18 offset:%22\n\t"
+            "ds_read_b64_tr_b16 %14, %19 offset:%21\n\tds_read_b64_tr_b16 %15, %19 offset:%22\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0][0][0]), "=&v"(r[0][0][1]), "=&v"(r[0][1][0]), "=&v"(r[0][1][1]),
+              "=&v"(r[0][2][0]), "=&v"(r[0][2][1]), "=&v"(r[0][3][0]), "=&v"(r[0][3][1]),
+              "=&v"(r[1][0][0]), "=&v"(r[1][0][1]), "=&v"(r[1][1][0]), "=&v"(r[1][1][1]),
+              "=&v"(r[1][2][0]), "=&v"(r[1][2][1]), "=&v"(r[1][3][0]), "=&v"(r[1][3][1])
+            : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "n"(HI), "n"(K2), "n"(K2 + HI)
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
+            "ds_read_b64_tr_b16 %2, %9\n\tds_read_b64_tr_b16 %3, %9 offset:%10\n\t"
+            "ds_read_b64_tr_b16 %4, %8 offset:%11\n\tds_read_b64_tr_b16 %5, %8 offset:%12\n\t"
+            "ds_read_b64_tr_b16 %6, %9 offset:%11\n\tds_read_b64_tr_b16 %7, %9 offset:%12\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0][0][0]), "=&v"(r[0][0][1]), "=&v"(r[0][1][0]), "=&v"(r[0][1][1]),
+              "=&v"(r[1][0][0]), "=&v"(r[1][0][1]), "=&v"(r[1][1][0]), "=&v"(r[1][1][1])
+            : "v"(addr[0]), "v"(addr[1]), "n"(HI), "n"(K2), "n"(K2 + HI)
+            : "memory");
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+            va[k2][db] = u32x4{r[k2][db][0][0], r[k2][db][0][1], r[k2][db][1][0], r[k2][db][1][1]};
+}
+
+// One persistent wavefront per resident slot.  Every load is a compiler
+// builtin, so the compiler derives each wait from the loads issued after the
+// one a use needs: K of a block goes straight into registers in the layout of
+// the A operand of K·Qᵀ (lane l: key perm(l % 32), 16 bytes at d = 16·kk +
+// 8·(l / 32)), LK blocks ahead; V goes by buffer->LDS loads into a ring of RV
+// slots, RV - 1 blocks ahead, each slot its own LDS array so that a read of
+// one slot waits only for that slot's loads; an item's Q goes by buffer->LDS
+// loads into one of RV Q slots together with the V of its first block.
 template <int D, bool PAGED>
 __global__ __launch_bounds__(64)
 void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
@@ -298,13 +313,16 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
                           int nwaves, int qb, float c,
                           const int32_t* __restrict__ bt, int lps, int max_pages, int num_pages) {
     using Gm = Geo<D>;
-    constexpr int RB = Gm::RB, BLK = Gm::BLK, NCH = Gm::NCH, R = Gm::R, QCH = Gm::QCH;
+    constexpr int RB = Gm::RB, BLK = Gm::BLK, NCH = Gm::NCH, QCH = Gm::QCH;
+    constexpr int RV = Gm::RV, LK = Gm::LK;
     constexpr int KSTEPS = D / 16;     // MFMA k-steps of K·Qᵀ
     constexpr int DB = D / 32;         // 32-row blocks of Oᵀ
-    constexpr int NWAIT = (R - 1) * 2 * NCH;   // loads younger than a block's own
-    constexpr int NST = 4 * DB + 1;            // stores of one partial result (per lane)
-    static_assert(NWAIT + (R - 1) * QCH <= 63, "vmcnt range");
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    constexpr int HCH = NCH / 2;       // 1 KiB V loads per 16-token half
+    static_assert(RV == 4 && LK >= 1 && LK < RV, "ring geometry");
+    __shared__ __attribute__((aligned(16))) unsigned char vs0[BLK], vs1[BLK], vs2[BLK], vs3[BLK];
+    extern __shared__ __attribute__((aligned(16))) unsigned char qlds[];   // RV Q slots of qb bytes
+    auto vslot = [&](int s) -> unsigned char* { return s == 0 ? vs0 : s == 1 ? vs1 : s == 2 ? vs2 : vs3; };
+    auto qslot = [&](int s) -> unsigned char* { return qlds + s * qb; };
 
     const int HG = H_kv * n_hg;
     const Lens L = load_lens(lens, B, T_max);
@@ -321,128 +339,139 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
     const int lane = threadIdx.x;
     const int hl = lane >> 5, l32 = lane & 31;
 
-    // LDS byte o of a block: row r = o / RB, chunk position p.  K row r holds
-    // key swap_bits23(r), chunk p = global chunk p ^ k_swz(r); V row r holds key r,
-    // chunk p = global chunk p ^ v_swz(r).  A Q slot holds the group's heads as
-    // rows in order.
-    uint32_t k_voff[NCH], v_voff[NCH];
+    // K: lane offsets of the operand layout within a block (bytes).  V: LDS byte o =
+    // 1 KiB load ch at lane*16 holds row r = o / RB, chunk position p = global chunk
+    // p ^ v_swz(r) (conflict-free transposing reads).
+    uint32_t k_off[KSTEPS], v_voff[NCH];
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) k_off[kk] = (uint32_t)(swap_bits23(l32) * RB + (kk * 16 + hl * 8) * 2);
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
         const int o = ch * 1024 + lane * 16;
         const int r = o / RB, p = (o % RB) / 16;
-        k_voff[ch] = (uint32_t)(swap_bits23(r) * RB + (p ^ k_swz<D>(r)) * 16);
         v_voff[ch] = (uint32_t)(r * RB + (p ^ v_swz<D>(r)) * 16);
     }
-    auto kblk = [&](int sl) { return lds + sl * 2 * BLK; };
-    auto vblk = [&](int sl) { return lds + sl * 2 * BLK + BLK; };
-    auto qslot = [&](int sl) { return lds + Gm::RING + sl * qb; };
-    // LDS byte address of the dynamic area (a constant of the launch)
-    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)lds));
+    const __amdgpu_buffer_rsrc_t zrs = brsrc(kc, 0u);
+    constexpr uint32_t kOob = 0x7FFFFFF0u;      // past every buffer range: reads zero
 
-    // Issue side: K, V (and, at an item's first block, its Q) of the block at
-    // cursor ic into ring slot sl; past the wavefront's range, zero-range loads
-    // keep the count of loads per block fixed without touching memory.  The
-    // buffer descriptors are rebuilt only when the cursor enters a new item.
-    Cursor ic = cursor_at(L, HG, n_hg, b0, a0 - before);
-    int qs_issue = 0;            // Q slot of the item the issue cursor is in
-    const i32x4_sgpr zrs = make_rsrc(kc, 0u);
-    i32x4_sgpr krs, vrs;
-    auto set_item = [&]() {
-        if constexpr (!PAGED) {
-            const size_t head = ((size_t)ic.b * H_kv + ic.g) * (size_t)T_max * D;
-            krs = make_rsrc(kc + head, (uint32_t)ic.t_end * RB);
-            vrs = make_rsrc(vc + head, (uint32_t)ic.t_end * RB);
-        }
-    };
-    set_item();
-    // Paged: a 32-token block is two 16-token halves; LDS chunks [0, NCH/2) hold keys
-    // 0..15 of the block and chunks [NCH/2, NCH) keys 16..31 (the K row permutation
-    // swaps bits 2 and 3 only, so it stays inside each half).
-    constexpr int HCH = NCH / 2;
-    auto issue_paged = [&](bool live, int sl) {
-        const int t0 = ic.s * kDecodeSplit + ic.i * CK;
-        i32x4_sgpr kh[2] = {zrs, zrs}, vh[2] = {zrs, zrs};
-        uint32_t roff[2] = {0u, 0u};
-        if (live) {
-            // table entries of the halves; a half past the item's end reuses the last
-            // valid token's entry (it is then read through the zero range)
-            const int last = ic.t_end - 1;
-            const int pi0 = t0 >> lps, pi1 = min(t0 + 16, last) >> lps;
-            const uint32_t rowb = (uint32_t)ic.b * (uint32_t)max_pages * 4u;
-            int e0, e1;
-            sload2(bt, __builtin_amdgcn_readfirstlane(rowb + (uint32_t)pi0 * 4u),
-                   __builtin_amdgcn_readfirstlane(rowb + (uint32_t)pi1 * 4u), e0, e1);
-            const int pe[2] = {e0, e1}, pidx[2] = {pi0, pi1};
+    // Paged: the buffer ranges of the two 16-token halves of block (cursor) x, each
+    // inside one page (pages are powers of two >= 16 tokens, blocks start at
+    // multiples of 32): kh/vh and the row offset of the half within its range.
+    auto page_halves = [&](const Cursor& x, __amdgpu_buffer_rsrc_t* kh, __amdgpu_buffer_rsrc_t* vh,
+                           uint32_t* roff) {
+        const int t0 = x.s * kDecodeSplit + x.i * CK;
+        const int last = x.t_end - 1;
+        const int pi0 = t0 >> lps, pi1 = min(t0 + 16, last) >> lps;
+        const uint32_t rowb = (uint32_t)x.b * (uint32_t)max_pages * 4u;
+        int e0, e1;
+        sload2(bt, __builtin_amdgcn_readfirstlane(rowb + (uint32_t)pi0 * 4u),
+               __builtin_amdgcn_readfirstlane(rowb + (uint32_t)pi1 * 4u), e0, e1);
+        const int pe[2] = {e0, e1}, pidx[2] = {pi0, pi1};
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int th = t0 + 16 * h;
-                if (th < ic.t_end) {
-                    const int page = min(max(pe[h], 0), num_pages - 1);
-                    const int pstart = pidx[h] << lps;
-                    const int rows = min(1 << lps, ic.t_end - pstart);
-                    const size_t head = (((size_t)page * H_kv + ic.g) << lps) * D;
-                    kh[h] = make_rsrc(kc + head, (uint32_t)rows * RB);
-                    vh[h] = make_rsrc(vc + head, (uint32_t)rows * RB);
-                    roff[h] = (uint32_t)(th - pstart) * RB;
-                }
+        for (int h = 0; h < 2; ++h) {
+            if (kh) kh[h] = zrs;
+            if (vh) vh[h] = zrs;
+            roff[h] = 0u;
+            const int th = t0 + 16 * h;
+            if (th < x.t_end) {
+                const int page = min(max(pe[h], 0), num_pages - 1);
+                const int pstart = pidx[h] << lps;
+                const int rows = min(1 << lps, x.t_end - pstart);
+                const size_t head = (((size_t)page * H_kv + x.g) << lps) * D;
+                if (kh) kh[h] = brsrc(kc + head, (uint32_t)rows * RB);
+                if (vh) vh[h] = brsrc(vc + head, (uint32_t)rows * RB);
+                roff[h] = (uint32_t)(th - pstart) * RB;
             }
         }
-        uint32_t vo[NCH];
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) vo[ch] = roff[ch / HCH] + k_voff[ch] - (ch / HCH) * 16u * RB;
-        dma_n<HCH>(kh[0], lds0 + sl * 2 * BLK, vo);
-        dma_n<HCH>(kh[1], lds0 + sl * 2 * BLK + HCH * 1024, vo + HCH);
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) vo[ch] = roff[ch / HCH] + v_voff[ch] - (ch / HCH) * 16u * RB;
-        dma_n<HCH>(vh[0], lds0 + sl * 2 * BLK + BLK, vo);
-        dma_n<HCH>(vh[1], lds0 + sl * 2 * BLK + BLK + HCH * 1024, vo + HCH);
     };
-    auto issue = [&](bool live, bool first_of_item, int sl) {
+
+    // ---- issue side: V (+ Q) cursor RV-1 blocks ahead of the compute, K cursor LK ahead
+    Cursor icv = cursor_at(L, HG, n_hg, b0, a0 - before);
+    Cursor ick = icv;
+    int nv = 0, nk = 0, qs_issue = 0;
+    __amdgpu_buffer_rsrc_t vrs = zrs, krs = zrs;
+    auto item_rsrc = [&](const Cursor& x, const bf16* base) {
+        const size_t head = ((size_t)x.b * H_kv + x.g) * (size_t)T_max * D;
+        return brsrc(base + head, (uint32_t)x.t_end * RB);
+    };
+    if constexpr (!PAGED) {
+        vrs = item_rsrc(icv, vc);
+        krs = item_rsrc(ick, kc);
+    }
+    auto issue_v = [&](int s) {
+        const bool live = nv < nblk;
+        unsigned char* dst = vslot(s);
         if constexpr (PAGED) {
-            issue_paged(live, sl);
+            __amdgpu_buffer_rsrc_t vh[2] = {zrs, zrs};
+            uint32_t roff[2] = {0u, 0u};
+            if (live) page_halves(icv, nullptr, vh, roff);
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch)
+                lds_dma16(vh[ch / HCH], dst + ch * 1024, roff[ch / HCH] + v_voff[ch] - (ch / HCH) * 16u * RB);
         } else {
-            const uint32_t row0 = (uint32_t)(ic.s * kDecodeSplit + ic.i * CK) * RB;
-            uint32_t vo[NCH];
+            const uint32_t row0 = (uint32_t)(icv.s * kDecodeSplit + icv.i * CK) * RB;
 #pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) vo[ch] = row0 + k_voff[ch];
-            dma_n<NCH>(live ? krs : zrs, lds0 + sl * 2 * BLK, vo);
-#pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) vo[ch] = row0 + v_voff[ch];
-            dma_n<NCH>(live ? vrs : zrs, lds0 + sl * 2 * BLK + BLK, vo);
+            for (int ch = 0; ch < NCH; ++ch) lds_dma16(live ? vrs : zrs, dst + ch * 1024, row0 + v_voff[ch]);
         }
-        if (live && first_of_item) {
-            const int ncols = min(32, G - ic.hg * 32);
-            const i32x4_sgpr qrs = make_rsrc(q + ((size_t)ic.b * H_q + ic.g * G + ic.hg * 32) * D,
-                                             (uint32_t)(ncols * RB));
+        if (!live) return;
+        if (icv.i == 0 || nv == 0) {     // the item's Q (also for a range that starts inside it)
+            const int ncols = min(32, G - icv.hg * 32);
+            const __amdgpu_buffer_rsrc_t qrs =
+                brsrc(q + ((size_t)icv.b * H_q + icv.g * G + icv.hg * 32) * D, (uint32_t)(ncols * RB));
 #pragma unroll
             for (int ch = 0; ch < QCH; ++ch)
-                if (ch * 1024 < ncols * RB)
-                    dma16(qrs, qslot(qs_issue) + ch * 1024, (uint32_t)(ch * 1024 + lane * 16), 0u);
+                if (ch * 1024 < ncols * RB) lds_dma16(qrs, qslot(qs_issue) + ch * 1024, (uint32_t)(ch * 1024 + lane * 16));
+        }
+        ++nv;
+        advance(icv, L, HG, n_hg);
+        if (icv.i == 0) {
+            qs_issue = qs_issue == RV - 1 ? 0 : qs_issue + 1;
+            if constexpr (!PAGED) vrs = item_rsrc(icv, vc);
         }
     };
-    // the issue cursor's step: the next block, a new descriptor pair on a new item
-    auto issue_advance = [&]() {
-        advance(ic, L, HG, n_hg);
-        if (ic.i == 0) {
-            qs_issue = qs_issue == R - 1 ? 0 : qs_issue + 1;
-            set_item();
-        }
-    };
-    // Q of the wavefront's first item (loaded at its first block even when the
-    // range starts inside the item).
-    int issued = 0;
+    u32x4 kr[RV][KSTEPS];
+    auto issue_k = [&](int s) {
+        const bool live = nk < nblk;
+        if constexpr (PAGED) {
+            // one global load per k-step from a per-lane address: lane l reads key perm(l % 32)
+            // of the block from the page of its half; a key past the item's end (its score is
+            // masked) and a block past the wavefront's range read row 0 of a valid page
+            const bf16* src = kc;
+            if (live) {
+                const int t0 = ick.s * kDecodeSplit + ick.i * CK;
+                const int last = ick.t_end - 1;
+                const int pi0 = t0 >> lps, pi1 = min(t0 + 16, last) >> lps;
+                const uint32_t rowb = (uint32_t)ick.b * (uint32_t)max_pages * 4u;
+                int e0, e1;
+                sload2(bt, __builtin_amdgcn_readfirstlane(rowb + (uint32_t)pi0 * 4u),
+                       __builtin_amdgcn_readfirstlane(rowb + (uint32_t)pi1 * 4u), e0, e1);
+                const int key = swap_bits23(l32);
+                const int t = t0 + key <= last ? t0 + key : t0;       // t0 <= last: a live block
+                const bool h1 = t - t0 >= 16;
+                const int page = min(max(h1 ? e1 : e0, 0), num_pages - 1);
+                const int pstart = (h1 ? pi1 : pi0) << lps;
+                src = kc + ((((size_t)page * H_kv + ick.g) << lps) + (size_t)(t - pstart)) * D;
+            }
 #pragma unroll
-    for (int j = 0; j < R - 1; ++j) {
-        const bool live = issued < nblk;
-        issue(live, live && (ic.i == 0 || issued == 0), j);
-        if (live) {
-            ++issued;
-            issue_advance();
+            for (int kk = 0; kk < KSTEPS; ++kk)
+                kr[s][kk] = *reinterpret_cast<const u32x4*>(src + kk * 16 + hl * 8);
+        } else {
+            const uint32_t row0 = (uint32_t)(ick.s * kDecodeSplit + ick.i * CK) * RB;
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk) kr[s][kk] = bload16(live ? krs : zrs, row0 + k_off[kk]);
         }
-    }
+        if (!live) return;
+        ++nk;
+        advance(ick, L, HG, n_hg);
+        if constexpr (!PAGED)
+            if (ick.i == 0) krs = item_rsrc(ick, kc);
+    };
+#pragma unroll
+    for (int s = 0; s < RV - 1; ++s) issue_v(s);
+#pragma unroll
+    for (int s = 0; s < LK; ++s) issue_k(s);
 
-    // Compute side.
+    // ---- compute side
     Cursor cc = cursor_at(L, HG, n_hg, b0, a0 - before);
     int part = cc.i == 0 ? 0 : 1;
     int qs = 0;
@@ -462,34 +491,16 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
     const int vfv = v_swz<D>(vrow);
     const int vc0 = 2 * (vg & 1) + ((vm & 3) >> 1);
     const int vin = (vm & 1) * 4;
-    auto v_opnd = [&](int sl, int k2, int db) -> u32x4 {
-        const bf16* base = reinterpret_cast<const bf16*>(vblk(sl)) + (k2 * 16 + vrow) * D +
-                           (((db * 4 + vc0) ^ vfv) * 8) + vin;
-        const u32x2 lo = ds_read_tr(base);
-        const u32x2 hi = ds_read_tr(base + 4 * D);
-        return u32x4{lo[0], lo[1], hi[0], hi[1]};
-    };
+    uint32_t v_lane[DB];           // this lane's byte offset of row block db in a V slot
+#pragma unroll
+    for (int db = 0; db < DB; ++db) v_lane[db] = (uint32_t)((vrow * D + (((db * 4 + vc0) ^ vfv) * 8) + vin) * 2);
+    // V of block j lands before the loads of the three blocks issued after it
+    // (3 x (NCH + KSTEPS) loads, plus any Q loads and partial stores): waiting for
+    // at most that many outstanding makes slot j's V complete.
+    constexpr int NV_AFTER = (RV - 1) * (NCH + KSTEPS);
+    static_assert(NV_AFTER <= 63, "vmcnt range");
 
-    int sl = 0;
-    unsigned st_hist = 0;        // bit k: partial stores issued at the end of iteration j-1-k
-    for (int j = 0; j < nblk; ++j) {
-        {
-            const bool live = issued < nblk;
-            issue(live, live && ic.i == 0, sl == 0 ? R - 1 : sl - 1);   // the slot block j-1 left
-            if (live) {
-                ++issued;
-                issue_advance();
-            }
-        }
-        // block j (and its item's Q) has landed: allow for the loads of the R-1
-        // younger blocks and for the partial stores issued since block j's loads
-        {
-            const int k = __builtin_popcount(st_hist);
-            if (k == 0) wait_vmem_le<NWAIT>();
-            else if (k == 1) wait_vmem_le<(NWAIT + NST > 63 ? 63 : NWAIT + NST)>();
-            else if (k == 2) wait_vmem_le<(NWAIT + 2 * NST > 63 ? 63 : NWAIT + 2 * NST)>();
-            else wait_vmem_le<(NWAIT + 3 * NST > 63 ? 63 : NWAIT + 3 * NST)>();
-        }
+    auto compute = [&](int j, int s) {
         const int g = cc.g, hg = cc.hg;
         const int col = hg * 32 + l32;
         const bool col_ok = col < G;
@@ -503,13 +514,10 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
             }
             need_q = false;
         }
-        const bf16* krow = reinterpret_cast<const bf16*>(kblk(sl)) + l32 * D;
         f32x16 S = {};
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (((2 * kk + hl) ^ k_swz<D>(l32)) * 8));
-            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], S, 0, 0, 0);
-        }
+        for (int kk = 0; kk < KSTEPS; ++kk)
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[s][kk]), qreg[kk], S, 0, 0, 0);
         const int nvalid = cc.t_end - (cc.s * kDecodeSplit + cc.i * CK);   // keys before the item's end
         if (nvalid < CK) {
 #pragma unroll
@@ -556,45 +564,43 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
 #pragma unroll
             for (int e = 0; e < 4; ++e) pw[k2][e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
         }
+        u32x4 va[2][DB];
+        {
+            const uint32_t sb = (uint32_t)reinterpret_cast<uintptr_t>(
+                (__attribute__((address_space(3))) unsigned char*)vslot(s));
+            uint32_t addr[DB];
+#pragma unroll
+            for (int db = 0; db < DB; ++db) addr[db] = sb + v_lane[db];
+            wait_vmem_le<NV_AFTER>();
+            v_operands<D>(addr, va);
+        }
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
             for (int db = 0; db < DB; ++db)
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, v_opnd(sl, k2, db)), __builtin_bit_cast(bf16x8, pw[k2]),
+                    __builtin_bit_cast(bf16x8, va[k2][db]), __builtin_bit_cast(bf16x8, pw[k2]),
                     oacc[db], 0, 0, 0);
-        sl = sl == R - 1 ? 0 : sl + 1;
 
         // end of this wavefront's part of the item: write the partial
-        const bool item_end = cc.i == cc.nb - 1 || j == nblk - 1;
-        st_hist = (st_hist << 1 | (item_end ? 1u : 0u)) & ((1u << (R - 1)) - 1u);
-        if (item_end) {
+        if (cc.i == cc.nb - 1 || j == nblk - 1) {
             const float Lsum = pair_sum(lsum);
-            // the group's (split, part) slots: head column col, slot (col*nsplit + s)*2 + part
-            const int ncols = min(32, G - hg * 32);
-            const size_t grp = ((size_t)cc.b * H_q + g * G + hg * 32) * nsplit * 2;
-            const i32x4_sgpr ors = make_rsrc(ws_o + grp * D, (uint32_t)(ncols * nsplit * 2 * D * 4));
-            const i32x4_sgpr mrs = make_rsrc(ws_ml + grp * 2, (uint32_t)(ncols * nsplit * 2 * 8));
-            const uint32_t slot = (uint32_t)((l32 * nsplit + cc.s) * 2 + part);
-            const uint32_t oob = 0xFFFFFFF0u;            // dropped by the range check
-            auto ooff = [&](int db, int g4) -> uint32_t {
-                return col_ok ? (slot * D + db * 32 + g4 * 8 + hl * 4) * 4u : oob;
-            };
-            auto o4 = [&](int db, int g4) -> u32x4 {
-                return u32x4{__float_as_uint(oacc[db][4 * g4]), __float_as_uint(oacc[db][4 * g4 + 1]),
-                             __float_as_uint(oacc[db][4 * g4 + 2]), __float_as_uint(oacc[db][4 * g4 + 3])};
-            };
+            if (col_ok) {
+                // the group's (split, part) slots: head column col, slot (col*nsplit + s)*2 + part
+                const size_t slot = ((size_t)(cc.b * H_q + g * G + col) * nsplit + cc.s) * 2 + part;
+                float* orow = ws_o + slot * D;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-                store_x4x4(ors, ooff(db, 0), o4(db, 0), ooff(db, 1), o4(db, 1), ooff(db, 2), o4(db, 2),
-                           ooff(db, 3), o4(db, 3));
-            // lanes of the first half store (reference, sum); lanes of the second half the
-            // empty part 1 of an item finished by the wavefront that began it
-            const bool mark = part == 0 && cc.i == cc.nb - 1;
-            const uint32_t moff = !col_ok ? oob : hl == 0 ? slot * 8u : mark ? (slot + 1) * 8u : oob;
-            const u32x2 mv = hl == 0 ? u32x2{__float_as_uint(mc), __float_as_uint(Lsum)}
-                                     : u32x2{__float_as_uint(kNegInf), 0u};
-            store_x2(mrs, moff, mv);
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4)
+                        *reinterpret_cast<f32x4*>(orow + db * 32 + g4 * 8 + hl * 4) =
+                            f32x4{oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]};
+                // lanes of the first half store (reference, sum); lanes of the second half
+                // the empty part 1 of an item finished by the wavefront that began it
+                if (hl == 0) *reinterpret_cast<f32x2*>(ws_ml + slot * 2) = f32x2{mc, Lsum};
+                else if (part == 0 && cc.i == cc.nb - 1)
+                    *reinterpret_cast<f32x2*>(ws_ml + (slot + 1) * 2) = f32x2{kNegInf, 0.f};
+            }
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -603,11 +609,24 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
             mc_set = false;
             need_q = true;
             part = 0;
-            qs = qs == R - 1 ? 0 : qs + 1;
+            qs = qs == RV - 1 ? 0 : qs + 1;
         }
         advance(cc, L, HG, n_hg);
+    };
+
+    // block j sits in V slot j % RV and K slot j % RV; the loop is unrolled RV times so
+    // every slot index is a constant
+    for (int j0 = 0; j0 < nblk; j0 += RV) {
+#pragma unroll
+        for (int r = 0; r < RV; ++r) {
+            const int j = j0 + r;
+            if (j >= nblk) break;
+            issue_v((r + RV - 1) % RV);       // block j + RV - 1, into the slot block j - 1 left
+            issue_k((r + LK) % RV);           // block j + LK
+            compute(j, r);
+        }
     }
-    wait_vmem_le<0>();     // drain the zero-range look-ahead loads before exit
+    wait_vmem_le<0>();     // the look-ahead's LDS loads land before the wavefront ends
 }
 
 // Merge the parts of every split of (b, query head) and normalise: one
@@ -704,16 +723,16 @@ int resident_waves(int lds_bytes) {
 
 template <int D, bool PAGED>
 hipError_t launch(const DecodeArgs& a) {
-    // the largest dynamic LDS any call uses: ring + R full 32-head Q slots
+    // the largest dynamic LDS any call uses: RV full 32-head Q slots
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)decode_stream_kernel<D, PAGED>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            Geo<D>::RING + Geo<D>::R * q_slot_bytes(32, D));
+                            Geo<D>::RV * q_slot_bytes(32, D));
     if (attr != hipSuccess) return attr;
     const int G = a.H_q / a.H_kv;
     const int n_hg = (G + 31) / 32;
     const int nsplit = decode_nsplit(a.T_max);
     const int qb = q_slot_bytes(G, D);
-    const int lds = Geo<D>::RING + Geo<D>::R * qb;
+    const int lds = Geo<D>::RV * qb;
     const int nwaves = resident_waves<D, PAGED>(lds);
     float* ws_o = static_cast<float*>(a.workspace);
     float* ws_ml = ws_o + (size_t)a.B * a.H_q * nsplit * 2 * D;
