@@ -1,0 +1,294 @@
+// Shared machinery of the single-token decode kernels (bf16 and FP8 caches):
+// the block order of the work split, cursors over it, the lengths, buffer
+// descriptors for the load builtins, and the combine kernel.
+//
+// Work decomposition ("stream" split).  The cache is cut into blocks of 32
+// tokens of one item = (sequence b, split s of kDecodeSplit tokens, KV head
+// g, group hg of up to 32 of g's query heads), in the global order b, s,
+// (g, hg), block.  Every wavefront derives the same order from the lengths
+// on the device and takes one contiguous range of bpw blocks (bpw >= the
+// blocks of a split, so an item is shared by at most two wavefronts).  A
+// wavefront streams its range without draining at item boundaries and
+// writes one unnormalised partial (O, reference, weight sum) per item it
+// touches: part 0 from the wavefront that holds the item's first block,
+// part 1 from the next one.  The combine kernel recomputes the same order
+// to find the parts and merges them with the log-sum-exp rule of the chunk
+// merge (sglang PR 49078 analysis, "1. aiter.py").
+#pragma once
+
+#include "common.cuh"
+#include "launch.h"
+#include "mfma_lds.cuh"
+
+namespace mattn {
+namespace {
+using namespace mattn::mfma;
+
+constexpr int CK = 32;                         // tokens per block
+constexpr int SB = kDecodeSplit / CK;          // blocks of a full split
+constexpr float kRescaleSum = 256.0f;          // 2^8
+static_assert(kDecodeSplit % CK == 0, "splits are whole blocks");
+
+// Q slot bytes: the group's heads (at most 32) rounded up to whole 1 KiB loads.
+inline int q_slot_bytes(int G, int D) { return (min(G, 32) * D * 2 + 1023) / 1024 * 1024; }
+
+__device__ __forceinline__ int seq_len(const int32_t* lens, int b, int T_max) {
+    return min(max(lens[b], 0), T_max);
+}
+
+// inclusive prefix sum over the 64 lanes of the wavefront
+__device__ __forceinline__ int wave_scan(int x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// Two dwords at byte offsets o0, o1 of a wavefront-uniform table (scalar loads: they
+// count in lgkmcnt, not vmcnt, so the vector-load accounting of the look-ahead is not
+// disturbed).  Both offsets must lie inside the table.
+__device__ __forceinline__ void sload2(const int32_t* p, uint32_t o0, uint32_t o1, int& a, int& b) {
+    asm volatile(
+        "s_load_dword %0, %2, %3\n\t"
+        "s_load_dword %1, %2, %4\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&s"(a), "=&s"(b)
+        : "s"(p), "s"(o0), "s"(o1)
+        : "memory");
+}
+
+// Clamped sequence lengths as seen by one wavefront: with at most 64
+// sequences lane b holds len_b in a register (read back with readlane, no
+// memory round trip); beyond that they are read from memory.
+struct Lens {
+    const int32_t* p;
+    int B, T_max, reg;
+    __device__ int get(int b) const {
+        if (B <= 64) return __builtin_amdgcn_readlane(reg, b);
+        int v, u;              // scalar load: no wait on the wavefront's vector loads
+        sload2(p, __builtin_amdgcn_readfirstlane((uint32_t)b * 4u), __builtin_amdgcn_readfirstlane((uint32_t)b * 4u), v, u);
+        return min(max(v, 0), T_max);
+    }
+};
+__device__ __forceinline__ Lens load_lens(const int32_t* lens, int B, int T_max) {
+    const int lane = threadIdx.x & 63;
+    Lens L;
+    L.p = lens;
+    L.B = B;
+    L.T_max = T_max;
+    L.reg = lane < B ? seq_len(lens, lane, T_max) : 0;
+    return L;
+}
+
+struct Plan {
+    int total;   // blocks over all items
+    int bpw;     // blocks per wavefront
+};
+
+// The block order: the plan and the sequence holding global block w*bpw (b0,
+// with `before` blocks ahead of it).  Identical in every wavefront.
+__device__ void make_plan(const Lens& L, int HG, int nwaves, int w, Plan& P, int& b0, int& before) {
+    const int lane = threadIdx.x & 63;
+    auto nblocks = [&](int len) { return (len + CK - 1) / CK * HG; };
+    if (L.B <= 64) {
+        const int n = nblocks(L.reg);
+        const int inc = wave_scan(n);
+        P.total = __builtin_amdgcn_readlane(inc, 63);
+        P.bpw = max(SB, (P.total + nwaves - 1) / nwaves);
+        const int a = w * P.bpw;
+        const uint64_t m = __ballot(lane < L.B && inc > a);
+        b0 = m ? __builtin_ctzll(m) : L.B;
+        before = m ? __builtin_amdgcn_readlane(inc - n, b0) : P.total;
+        return;
+    }
+    int total = 0;
+    for (int base = 0; base < L.B; base += 64) {
+        const int b = base + lane;
+        total += __builtin_amdgcn_readlane(wave_scan(b < L.B ? nblocks(seq_len(L.p, b, L.T_max)) : 0), 63);
+    }
+    P.total = total;
+    P.bpw = max(SB, (total + nwaves - 1) / nwaves);
+    const int a = w * P.bpw;
+    int carry = 0;
+    b0 = L.B;
+    before = total;
+    for (int base = 0; base < L.B; base += 64) {
+        const int b = base + lane;
+        const int n = b < L.B ? nblocks(seq_len(L.p, b, L.T_max)) : 0;
+        const int inc = wave_scan(n) + carry;
+        const uint64_t m = __ballot(b < L.B && inc > a);
+        if (m) {
+            const int f = __builtin_ctzll(m);
+            b0 = base + f;
+            before = __builtin_amdgcn_readlane(inc - n, f);
+            return;
+        }
+        carry = __builtin_amdgcn_readlane(inc, 63);
+    }
+}
+
+// Position in the global block order (all fields wavefront-uniform).
+struct Cursor {
+    int b, len, full, nsplit;   // sequence, its length, full splits, splits
+    int s, it, i, nb, t_end;    // split, item within the split, block within the item, blocks, item end
+    int g, hg;                  // KV head and query-head group of the item (it = g*n_hg + hg)
+};
+
+__device__ __forceinline__ void set_split(Cursor& c) {
+    if (c.s < c.full) {
+        c.nb = SB;
+        c.t_end = (c.s + 1) * kDecodeSplit;
+    } else {
+        c.nb = (c.len - c.full * kDecodeSplit + CK - 1) / CK;
+        c.t_end = c.len;
+    }
+}
+__device__ __forceinline__ void set_seq(Cursor& c, int len) {
+    c.len = len;
+    c.full = len / kDecodeSplit;
+    c.nsplit = (len + kDecodeSplit - 1) / kDecodeSplit;
+}
+// Cursor at local block lb of sequence b.
+__device__ Cursor cursor_at(const Lens& L, int HG, int n_hg, int b, int lb) {
+    Cursor c;
+    c.b = b;
+    set_seq(c, L.get(b));
+    const int fb = c.full * HG * SB;
+    if (lb < fb) {
+        c.s = lb / (HG * SB);
+        const int q = lb - c.s * HG * SB;
+        c.it = q / SB;
+        c.i = q - c.it * SB;
+    } else {
+        c.s = c.full;
+        set_split(c);
+        const int q = lb - fb;
+        c.it = q / c.nb;
+        c.i = q - c.it * c.nb;
+    }
+    set_split(c);
+    c.g = c.it / n_hg;
+    c.hg = c.it - c.g * n_hg;
+    return c;
+}
+// Next block in the global order.
+__device__ __forceinline__ void advance(Cursor& c, const Lens& L, int HG, int n_hg) {
+    if (++c.i < c.nb) return;
+    c.i = 0;
+    if (++c.it < HG) {
+        if (++c.hg == n_hg) {
+            c.hg = 0;
+            ++c.g;
+        }
+        return;
+    }
+    c.it = 0;
+    c.g = 0;
+    c.hg = 0;
+    if (++c.s < c.nsplit) {
+        set_split(c);
+        return;
+    }
+    c.s = 0;
+    int len = 0;
+    do {
+        ++c.b;
+    } while (c.b < L.B && (len = L.get(c.b)) == 0);
+    if (c.b < L.B) {
+        set_seq(c, len);
+        set_split(c);
+    }
+}
+
+// Buffer descriptor for the compiler's buffer-load builtins: `bytes` from p are
+// addressable, offsets past them read as zero without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds_chunk, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_chunk, 16, voff,
+                                             0, 0, 0);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+// Merge the parts of every split of (b, query head) and normalise: one
+// wavefront per (b, query head), lane l holding elements l*E .. l*E+E-1 of the
+// output row.  The (reference, sum) of the parts (lane k: part k) and the O rows
+// of the first 16 parts are loaded in one round, so the merge costs one memory
+// latency for caches up to 8 splits; parts beyond are merged 16 at a time with
+// a running reference.  Every (split, part) slot was written by the split
+// kernel; an absent part 1 carries reference -inf and weight sum 0, and its O
+// slot (never written) is read but not used.
+template <int D>
+__global__ __launch_bounds__(256)
+void decode_stream_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
+                           const int32_t* __restrict__ lens, bf16* __restrict__ o,
+                           float* __restrict__ lse, int H_q, int T_max, int nsplit, int n_bh) {
+    constexpr int E = D / 64;
+    constexpr int PG = 16;                       // parts per load round
+    const int lane = threadIdx.x & 63;
+    const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (bh >= n_bh) return;
+    const int b = bh / H_q;
+    const int len = seq_len(lens, b, T_max);
+    const int np = (len + kDecodeSplit - 1) / kDecodeSplit * 2;    // (split, part) slots
+    const size_t base = (size_t)bh * nsplit * 2;
+    const float* orow_ws = ws_o + base * D + lane * E;
+    float M = kNegInf, lsum = 0.f;
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    for (int k0 = 0; k0 < np; k0 += PG) {
+        // one round: (m, l) of parts k0 .. k0+PG-1 in lanes 0..PG-1, and their O elements
+        const int k = k0 + lane;
+        const bool mine = lane < PG && k < np;
+        const float m = mine ? ws_ml[(base + k) * 2] : kNegInf;
+        const float l = mine ? ws_ml[(base + k) * 2 + 1] : 0.f;
+        float ov[PG][E];
+#pragma unroll
+        for (int i = 0; i < PG; ++i)
+#pragma unroll
+            for (int e = 0; e < E; ++e) ov[i][e] = k0 + i < np ? orow_ws[(size_t)(k0 + i) * D + e] : 0.f;
+        float mg = m;
+#pragma unroll
+        for (int sh = 8; sh >= 1; sh >>= 1) mg = fmaxf(mg, __shfl_xor(mg, sh));
+        mg = __shfl(mg, 0);
+        const float Mn = fmaxf(M, mg);
+        if (Mn == kNegInf) continue;             // nothing present yet
+        const float alpha = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+        M = Mn;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] *= alpha;
+        lsum *= alpha;
+        const float w = m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m - M);
+        float lw = w * l;
+#pragma unroll
+        for (int sh = 8; sh >= 1; sh >>= 1) lw += __shfl_xor(lw, sh);
+        lsum += __shfl(lw, 0);
+#pragma unroll
+        for (int i = 0; i < PG; ++i) {
+            const float wi = __shfl(w, i);
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] = wi != 0.f ? __builtin_fmaf(ov[i][e], wi, acc[e]) : acc[e];
+        }
+    }
+    bf16* orow = o + (size_t)bh * D + lane * E;
+    if (M == kNegInf) {                          // no cached token
+#pragma unroll
+        for (int e = 0; e < E; ++e) orow[e] = (bf16)0.f;
+        if (lse && lane == 0) lse[bh] = kNegInf;
+        return;
+    }
+    const float inv = 1.0f / lsum;
+#pragma unroll
+    for (int e = 0; e < E; ++e) orow[e] = (bf16)(acc[e] * inv);
+    if (lse && lane == 0) lse[bh] = (M + __log2f(lsum)) * kLn2;
+}
+
+}  // namespace
+}  // namespace mattn

@@ -9,3 +9,6 @@ from .attention import (  # noqa: F401
     gather_pages, kv_append_paged, decode_paged, allowed_keys, prefill, prefill_varlen,
     attention_flops, score_matrix_bytes, kv_bytes_per_token, decode_kv_bytes,
 )
+from .fp8 import (  # noqa: F401
+    E4M3_MAX, e4m3_values, quantize_e4m3, dequantize_e4m3, kv_append_fp8, decode_fp8kv,
+)

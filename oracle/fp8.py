@@ -1,0 +1,113 @@
+"""CPU oracle for the FP8 (E4M3) key/value cache.
+
+TEST INFRASTRUCTURE ONLY, like the rest of this package: the library never
+imports it and it shares no code with the HIP path.
+
+KV-cache quantisation stores each cached K/V element in fewer bytes plus scale
+metadata, and the attention kernel must dequantise on the fly (LLM inference
+memory accounting 2/10, section "18. KV Cache Quantization": lower-precision
+KV halves or quarters the bytes per token and brings scales and a dequant
+step with it).  The pages fix neither the 8-bit format nor the scale
+granularity; the readings taken here (also listed in the design doc):
+  * format: OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent bits with bias 7,
+    3 mantissa bits, subnormals, no infinities, S.1111.111 = NaN, largest
+    finite magnitude 448;
+  * one float32 scale per (sequence, KV head) for K and one for V: the cached
+    value of element x is q(x) * scale;
+  * quantising x: y = x / scale in float32 (IEEE division), clamped to
+    [-448, 448], rounded to the nearest E4M3 value, ties to the even mantissa.
+Decoding against the quantised cache is exactly ``decode`` applied to the
+dequantised caches.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import decode, _f64
+
+__all__ = ["E4M3_MAX", "e4m3_values", "quantize_e4m3", "dequantize_e4m3", "kv_append_fp8", "decode_fp8kv"]
+
+E4M3_MAX = 448.0
+
+
+def e4m3_values():
+    """float64 [256]: the value of every byte under E4M3 (NaN for the two NaN codes)."""
+    out = np.empty(256)
+    for byte in range(256):
+        s = -1.0 if byte & 0x80 else 1.0
+        e = (byte >> 3) & 0xF
+        m = byte & 0x7
+        if e == 0xF and m == 0x7:
+            out[byte] = np.nan
+        elif e == 0:
+            out[byte] = s * (m / 8.0) * 2.0 ** (1 - 7)          # subnormal
+        else:
+            out[byte] = s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return out
+
+
+_VALS = e4m3_values()
+# non-negative finite codes in increasing value order (0x00 .. 0x7E)
+_POS_CODES = np.arange(0x7F)
+_POS_VALS = _VALS[:0x7F]
+
+
+def _round_e4m3_magnitude(a):
+    """Codes (0..0x7E) of the nearest E4M3 magnitudes to a >= 0 (a <= 448), ties to even."""
+    a = np.asarray(a, dtype=np.float64)
+    hi = np.searchsorted(_POS_VALS, a, side="left")          # first value >= a
+    hi = np.clip(hi, 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    dlo = a - _POS_VALS[lo]
+    dhi = _POS_VALS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (_POS_CODES[hi] % 2 == 0) & (hi != lo))
+    return np.where(pick_hi, _POS_CODES[hi], _POS_CODES[lo])
+
+
+def quantize_e4m3(x, scale):
+    """uint8 codes of x / scale (float32 division, clamped to +-448, nearest, ties to even).
+
+    x: any shape (its values are taken as float32); scale broadcasts against x.
+    """
+    x32 = np.asarray(_f64(x), dtype=np.float32)
+    s32 = np.asarray(_f64(scale), dtype=np.float32)
+    y = (x32 / s32).astype(np.float64)                       # IEEE float32 division
+    y = np.clip(y, -E4M3_MAX, E4M3_MAX)
+    code = _round_e4m3_magnitude(np.abs(y))
+    neg = (y < 0) | ((y == 0) & np.signbit(y))
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def dequantize_e4m3(codes, scale):
+    """float64 values code_value * scale (exact: both factors are exact in float64)."""
+    codes = np.asarray(codes.detach().cpu().numpy() if hasattr(codes, "detach") else codes, dtype=np.uint8)
+    return _VALS[codes] * np.asarray(_f64(scale))
+
+
+def kv_append_fp8(k_cache, v_cache, k_scale, v_scale, lens, k_new, v_new):
+    """Quantise one new token per sequence into slot lens[b] of the uint8 caches.
+
+    k_cache/v_cache uint8 [B, H_kv, T_max, D]; k_scale/v_scale [B, H_kv];
+    k_new/v_new [B, H_kv, 1, D] (any float dtype).  Returns copies of the
+    caches and lens + 1.
+    """
+    kc = np.array(k_cache, dtype=np.uint8, copy=True)
+    vc = np.array(v_cache, dtype=np.uint8, copy=True)
+    lens = np.asarray(lens).astype(np.int64)
+    ks, vs = _f64(k_scale), _f64(v_scale)
+    kn, vn = _f64(k_new), _f64(v_new)
+    for b in range(kc.shape[0]):
+        t = int(lens[b])
+        assert 0 <= t < kc.shape[2], "cache full"
+        kc[b, :, t, :] = quantize_e4m3(kn[b, :, 0, :], ks[b][:, None])
+        vc[b, :, t, :] = quantize_e4m3(vn[b, :, 0, :], vs[b][:, None])
+    return kc, vc, lens + 1
+
+
+def decode_fp8kv(q, k_cache, v_cache, k_scale, v_scale, lens, scale=None, heads=None):
+    """``decode`` against the dequantised caches (code value x per-(b, KV head) scale)."""
+    ks = _f64(k_scale)[:, :, None, None]
+    vs = _f64(v_scale)[:, :, None, None]
+    kd = dequantize_e4m3(k_cache, ks)
+    vd = dequantize_e4m3(v_cache, vs)
+    return decode(q, kd, vd, lens, scale, heads)
