@@ -614,3 +614,85 @@ def test_prefill_varlen_causal_gqa_matches_brute_force():
                     assert L[h, row] == -np.inf and np.all(O[row, h] == 0)
                 else:
                     assert abs(L[h, row] - l) <= 1e-12 and np.max(np.abs(O[row, h] - np.array(o))) <= 1e-12
+
+
+# ---- FP8 (E4M3) key/value cache ---------------------------------------------------------
+
+def test_e4m3_table_known_codes_and_library():
+    v = oracle.e4m3_values()
+    # format definition: 1.0 = 0 0111 000, 448 = 0 1111 110, smallest subnormal 2^-9, NaN codes
+    assert v[0x38] == 1.0 and v[0x7E] == 448.0 and v[0x01] == 2.0 ** -9 and v[0x08] == 2.0 ** -6
+    assert v[0xBE] == -1.75 and v[0xC6] == -3.5 and np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert v[0x00] == 0.0 and v[0x80] == 0.0 and np.signbit(v[0x80])
+    assert np.nanmax(np.abs(v)) == oracle.E4M3_MAX
+    # library cross-check: torch's float8_e4m3fn decoding
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(v), np.isnan(t)) and np.array_equal(v[~np.isnan(v)], t[~np.isnan(t)])
+
+
+def test_quantize_e4m3_rounding_saturation_and_library():
+    q = oracle.quantize_e4m3
+    one = np.float32(1.0)
+    # ties to the even mantissa: 1 + 1/16 lies halfway between 1 and 1.125
+    assert q(np.float32(1.0625), one) == 0x38 and q(np.float32(1.1875), one) == 0x3A
+    assert q(np.float32(-1.0625), one) == 0xB8
+    # saturation at 448 (never the NaN code); halfway to the subnormal step rounds to even (0)
+    assert q(np.float32(1e6), one) == 0x7E and q(np.float32(-1e6), one) == 0xFE
+    assert q(np.float32(2.0 ** -10), one) == 0x00 and q(np.float32(3 * 2.0 ** -11), one) == 0x01
+    # the scale divides: x = 3.5 * s quantises to 3.5
+    s = np.float32(0.0371)
+    assert q(np.float32(3.5) * s, s) == 0x46 or oracle.e4m3_values()[q(np.float32(3.5) * s, s)] == 3.5
+    # every finite code survives a round trip through its value times a power-of-two scale
+    v = oracle.e4m3_values()
+    codes = np.array([c for c in range(256) if not np.isnan(v[c]) and c != 0x80], dtype=np.uint8)
+    assert np.array_equal(q(v[codes] * 4.0, np.float32(4.0)), codes)
+    # library cross-check on random values: torch's float8 cast of the clamped quotient
+    x = np.random.default_rng(3).standard_normal(50000).astype(np.float32) * 300
+    s = np.float32(0.77)
+    ref = torch.from_numpy(np.clip(x / s, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q(x, s), ref)
+
+
+def test_decode_fp8kv_is_decode_of_dequantised_cache_and_brute_force():
+    r = _rng(21)
+    B, Hkv, G, D, T = 2, 2, 2, 4, 9
+    k8 = r.integers(0, 256, (B, Hkv, T, D)).astype(np.uint8)
+    v8 = r.integers(0, 256, (B, Hkv, T, D)).astype(np.uint8)
+    vals = oracle.e4m3_values()
+    k8[np.isnan(vals[k8])] = 0x38                       # no NaN codes in a cache
+    v8[np.isnan(vals[v8])] = 0x30
+    ks = r.uniform(0.01, 0.1, (B, Hkv))
+    vs = r.uniform(0.5, 2.0, (B, Hkv))
+    q = r.standard_normal((B, Hkv * G, 1, D))
+    lens = [7, 0]
+    O, L = oracle.decode_fp8kv(q, k8, v8, ks, vs, lens, 0.9)
+    for b in range(B):
+        for h in range(Hkv * G):
+            g = h // G
+            keys = [[vals[k8[b, g, t, d]] * ks[b, g] for d in range(D)] for t in range(lens[b])]
+            vv = [[vals[v8[b, g, t, d]] * vs[b, g] for d in range(D)] for t in range(lens[b])]
+            o, l = brute.attend_row(q[b, h, 0].tolist(), keys, vv, [False] * len(keys), 0.9)
+            if l == -math.inf:
+                assert L[b, h] == -np.inf and np.all(O[b, h, 0] == 0)
+            else:
+                assert abs(L[b, h] - l) <= 1e-12 and np.max(np.abs(O[b, h, 0] - np.array(o))) <= 1e-12
+
+
+def test_kv_append_fp8_writes_only_the_quantised_slot():
+    r = _rng(22)
+    B, Hkv, T, D = 3, 2, 8, 8
+    kc = r.integers(0, 0x70, (B, Hkv, T, D)).astype(np.uint8)
+    vc = r.integers(0, 0x70, (B, Hkv, T, D)).astype(np.uint8)
+    ks = r.uniform(0.05, 0.2, (B, Hkv)).astype(np.float32)
+    vs = r.uniform(0.05, 0.2, (B, Hkv)).astype(np.float32)
+    kn = r.standard_normal((B, Hkv, 1, D)).astype(np.float32)
+    vn = r.standard_normal((B, Hkv, 1, D)).astype(np.float32)
+    lens = np.array([0, 5, 7])
+    kc2, vc2, l2 = oracle.kv_append_fp8(kc, vc, ks, vs, lens, kn, vn)
+    assert l2.tolist() == [1, 6, 8]
+    for b in range(B):
+        t = lens[b]
+        assert np.array_equal(kc2[b, :, t], oracle.quantize_e4m3(kn[b, :, 0], ks[b][:, None]))
+        assert np.array_equal(vc2[b, :, t], oracle.quantize_e4m3(vn[b, :, 0], vs[b][:, None]))
+        other = [i for i in range(T) if i != t]
+        assert np.array_equal(kc2[b, :, other], kc[b, :, other]) and np.array_equal(vc2[b, :, other], vc[b, :, other])
