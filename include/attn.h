@@ -275,6 +275,40 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
                       int max_pages_per_seq, int D, float scale, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * FP8 (E4M3) KV cache.  KV-cache quantisation stores each cached element in
+ * fewer bytes plus scale metadata and dequantises inside the attention kernel
+ * (blog.ruahverce.com, LLM inference memory accounting 2/10, section "18. KV
+ * Cache Quantization").  Layout and conventions of the two FP8 calls:
+ *   k_cache, v_cache  [B, H_kv, T_max, D] uint8: OCP E4M3 codes (1 sign, 4
+ *       exponent bits with bias 7, 3 mantissa bits, subnormals, largest
+ *       magnitude 448, S.1111.111 = NaN; no infinities)
+ *   k_scale, v_scale  [B, H_kv] float32 device arrays, owned by the caller and
+ *       only read: the cached element is code value x scale of its (sequence,
+ *       KV head); scales must be finite and > 0
+ *   q, o bf16 as in attn_decode; lengths, lse, workspace (attn_decode_workspace_bytes
+ *   with the same sizes) and errors as attn_decode.
+ */
+
+/* kv_append_fp8 — quantise one token per sequence into slot cache_seqlens[b]:
+ * code = E4M3(clamp(x / scale, -448, 448)) with x the new element as float32,
+ * an IEEE float32 division and rounding to nearest, ties to even; then
+ * cache_seqlens[b] += 1 (a length outside [0, T_max) leaves the sequence
+ * untouched).  k_new, v_new [B, H_kv, 1, D] of new_dtype (ATTN_BF16 or ATTN_F32). */
+int kv_append_fp8(void* k_cache, void* v_cache, const float* k_scale, const float* v_scale,
+                  int32_t* cache_seqlens, const void* k_new, const void* v_new,
+                  int B, int H_kv, int T_max, int D, int new_dtype, void* stream);
+
+/* attn_decode_fp8kv — attn_decode against the FP8 cache: the same result as
+ * attn_decode over the dequantised cache (codes are converted exactly to bf16,
+ * the K scale multiplies the scores and the V scale the output).  T_max·D must
+ * stay below 2^31. */
+int attn_decode_fp8kv(const void* q, const void* k_cache, const void* v_cache,
+                      const float* k_scale, const float* v_scale,
+                      const int32_t* cache_seqlens, void* o, float* lse,
+                      int B, int H_q, int H_kv, int T_max, int D, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(int status);
 

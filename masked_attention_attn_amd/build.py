@@ -36,6 +36,7 @@ EXTRA = {
     "fwd_bf16_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
     "fwd_bf16_d128.hip": ["-fno-honor-nans"],
     "decode_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+    "decode_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
 }
 
 

@@ -229,6 +229,41 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
     return finish(launch_decode_bf16(a));
 }
 
+int kv_append_fp8(void* k_cache, void* v_cache, const float* k_scale, const float* v_scale,
+                  int32_t* cache_seqlens, const void* k_new, const void* v_new, int B, int H_kv, int T_max,
+                  int D, int new_dtype, void* stream) {
+    if (!k_cache || !v_cache || !k_scale || !v_scale || !cache_seqlens || !k_new || !v_new) return ATTN_ERR_NULL;
+    if (!dtype_ok(new_dtype) || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+    if (!fits(B, H_kv, T_max, D) || B > (1 << 30)) return ATTN_ERR_SHAPE;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+        return ATTN_ERR_ALIGN;
+    if (k_cache == v_cache || k_new == k_cache || v_new == v_cache) return ATTN_ERR_ALIAS;
+    AppendFp8Args a{k_cache, v_cache, k_scale, v_scale, cache_seqlens, k_new, v_new,
+                    new_dtype == ATTN_BF16, B, H_kv, T_max, D, stream};
+    return finish(launch_kv_append_fp8(a));
+}
+
+int attn_decode_fp8kv(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                      const float* v_scale, const int32_t* cache_seqlens, void* o, float* lse, int B,
+                      int H_q, int H_kv, int T_max, int D, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !cache_seqlens || !o) return ATTN_ERR_NULL;
+    if (!head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+    if (H_kv <= 0 || H_q <= 0 || H_q % H_kv != 0) return ATTN_ERR_SHAPE;
+    if (!fits(B, H_kv, T_max, D) || !fits(B, H_q, 1, D) || (long long)B * H_q > (1 << 30))
+        return ATTN_ERR_SHAPE;
+    // one (sequence, KV head) of codes is addressed through a 32-bit buffer range
+    if ((long long)T_max * D > (1ll << 31) - 1) return ATTN_ERR_SHAPE;
+    if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
+    if (!workspace || workspace_bytes < decode_workspace_bytes(B, H_q, T_max, D)) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(workspace))
+        return ATTN_ERR_ALIGN;
+    if (o == q || o == k_cache || o == v_cache) return ATTN_ERR_ALIAS;
+    DecodeFp8Args a{q, k_cache, v_cache, k_scale, v_scale, cache_seqlens, o, lse, B, H_q, H_kv, T_max, D,
+                    scale, workspace, stream};
+    return finish(launch_decode_fp8kv(a));
+}
+
 size_t attn_decode_workspace_bytes(int B, int H_q, int H_kv, int T_max, int D) {
     if (B <= 0 || H_q <= 0 || H_kv <= 0 || T_max <= 0 || !head_dim_ok(D) || H_q % H_kv != 0)
         return 0;

@@ -39,53 +39,6 @@ template <int D> struct Geo {
     static constexpr int LK = 2;                   // K look-ahead in blocks (in registers)
     static constexpr int QCH = 32 * RB / 1024;     // 1 KiB loads of a full 32-head Q slot
 };
-// The transposing LDS reads of one V block's operands (2 k-steps x DB row blocks x
-// lo/hi), written as one asm statement ending in lgkmcnt(0).  They are asm so
-// that the compiler inserts no wait of its own for the block's LDS loads (it
-// cannot tell the ring slots apart for these reads and would wait for the most
-// recent one); the caller waits for the slot explicitly.  addr[db]: this lane's
-// LDS byte address of row block db for k-step 0, lo half.
-template <int D>
-__device__ __forceinline__ void v_operands(const uint32_t* addr, u32x4 (&va)[2][D / 32]) {
-    constexpr int K2 = 16 * D * 2;     // bytes between the k-steps (16 rows)
-    constexpr int HI = 4 * D * 2;      // bytes between the lo and hi 4-row groups
-    u32x2 r[2][D / 32][2];
-    if constexpr (D == 128) {
-        asm volatile(
-            "ds_read_b64_tr_b16 %0, %16\n\tds_read_b64_tr_b16 %1, %16 offset:%20\n\t"
-            "ds_read_b64_tr_b16 %2, %17\n\tds_read_b64_tr_b16 %3, %17 offset:%20\n\t"
-            "ds_read_b64_tr_b16 %4, %18\n\tds_read_b64_tr_b16 %5, %18 offset:%20\n\t"
-            "ds_read_b64_tr_b16 %6, %19\n\tds_read_b64_tr_b16 %7, %19 offset:%20\n\t"
-            "ds_read_b64_tr_b16 %8, %16 offset:%21\n\tds_read_b64_tr_b16 %9, %16 offset:%22\n\t"
-            "ds_read_b64_tr_b16 %10, %17 offset:%21\n\tds_read_b64_tr_b16 %11, %17 offset:%22\n\t"
-            "ds_read_b64_tr_b16 %12, %18 offset:%21\n\tds_read_b64_tr_b16 %13, %18 offset:%22\n\t"
-            "ds_read_b64_tr_b16 %14, %19 offset:%21\n\tds_read_b64_tr_b16 %15, %19 offset:%22\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(r[0][0][0]), "=&v"(r[0][0][1]), "=&v"(r[0][1][0]), "=&v"(r[0][1][1]),
-              "=&v"(r[0][2][0]), "=&v"(r[0][2][1]), "=&v"(r[0][3][0]), "=&v"(r[0][3][1]),
-              "=&v"(r[1][0][0]), "=&v"(r[1][0][1]), "=&v"(r[1][1][0]), "=&v"(r[1][1][1]),
-              "=&v"(r[1][2][0]), "=&v"(r[1][2][1]), "=&v"(r[1][3][0]), "=&v"(r[1][3][1])
-            : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "n"(HI), "n"(K2), "n"(K2 + HI)
-            : "memory");
-    } else {
-        asm volatile(
-            "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
-            "ds_read_b64_tr_b16 %2, %9\n\tds_read_b64_tr_b16 %3, %9 offset:%10\n\t"
-            "ds_read_b64_tr_b16 %4, %8 offset:%11\n\tds_read_b64_tr_b16 %5, %8 offset:%12\n\t"
-            "ds_read_b64_tr_b16 %6, %9 offset:%11\n\tds_read_b64_tr_b16 %7, %9 offset:%12\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(r[0][0][0]), "=&v"(r[0][0][1]), "=&v"(r[0][1][0]), "=&v"(r[0][1][1]),
-              "=&v"(r[1][0][0]), "=&v"(r[1][0][1]), "=&v"(r[1][1][0]), "=&v"(r[1][1][1])
-            : "v"(addr[0]), "v"(addr[1]), "n"(HI), "n"(K2), "n"(K2 + HI)
-            : "memory");
-    }
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-            va[k2][db] = u32x4{r[k2][db][0][0], r[k2][db][0][1], r[k2][db][1][0], r[k2][db][1][1]};
-}
-
 // One persistent wavefront per resident slot.  Every load is a compiler
 // builtin, so the compiler derives each wait from the loads issued after the
 // one a use needs: K of a block goes straight into registers in the layout of
@@ -414,11 +367,12 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
     for (int j0 = 0; j0 < nblk; j0 += RV) {
 #pragma unroll
         for (int r = 0; r < RV; ++r) {
+            // past the range the issues are zero-range loads and the compute is skipped;
+            // the loop is never left mid-body (no register copies on extra exits)
             const int j = j0 + r;
-            if (j >= nblk) break;
             issue_v((r + RV - 1) % RV);       // block j + RV - 1, into the slot block j - 1 left
             issue_k((r + LK) % RV);           // block j + LK
-            compute(j, r);
+            if (j < nblk) compute(j, r);
         }
     }
     wait_vmem_le<0>();     // the look-ahead's LDS loads land before the wavefront ends

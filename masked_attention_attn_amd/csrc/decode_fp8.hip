@@ -1,0 +1,356 @@
+// Single-token decode against an FP8 (E4M3) key/value cache.
+//
+// KV-cache quantisation stores each cached element in fewer bytes plus scale
+// metadata, and the attention kernel dequantises on the fly (blog.ruahverce.com,
+// LLM inference memory accounting 2/10, section "18. KV Cache Quantization").
+// Here the cache holds OCP E4M3 codes with one float32 scale per (sequence,
+// KV head) for K and one for V: a cached element is code value x scale.  Every
+// E4M3 value is exact in bf16, so codes are converted to bf16 (conversion
+// scale 1) and the bf16 decode's matrix-core block runs unchanged; the scales
+// act outside the products: the K scale multiplies the score multiplier, the V
+// scale the partial O of an item.  The work split, cursors and combine are
+// those of the bf16 decode (decode_common.cuh); the cache bytes per token are
+// half of bf16's.
+//
+// Look-ahead, all in registers: K of a block is loaded in the A-operand layout
+// of K·Qᵀ (8 codes per lane and k-step: key perm(l % 32), d = 16·kk +
+// 8·(l / 32)) LK blocks ahead; V rows (16 codes per lane and 1 KiB load) RV - 1
+// blocks ahead.  At its block, V is converted and written to a bf16 LDS tile in
+// the bf16 kernel's swizzled layout and read back with the transposing LDS
+// read.  Every global load is a compiler builtin, so the compiler derives the
+// waits; each item's Q (bf16) reaches an LDS slot by buffer->LDS loads.
+#include "decode_common.cuh"
+
+namespace mattn {
+namespace {
+
+template <int D> struct Geo8 {
+    static constexpr int RB = D;                   // bytes per cache row (one byte per element)
+    static constexpr int BLK = CK * RB;            // bytes of one K (or V) block
+    static constexpr int NV = BLK / 1024;          // 1 KiB V loads per block (16 bytes per lane)
+    static constexpr int RV = 8;                   // V register ring (look-ahead RV - 1 blocks)
+    static constexpr int LK = 4;                   // K look-ahead in blocks
+    static constexpr int QCH = 32 * D * 2 / 1024;  // 1 KiB loads of a full 32-head bf16 Q slot
+};
+
+__device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
+}
+
+// Four E4M3 codes (one dword, element i in byte i) -> four bf16 (two dwords), exact.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    const bf2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const bf2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
+template <int D>
+__global__ __launch_bounds__(64)
+void decode_fp8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc,
+                       const uint8_t* __restrict__ vc, const float* __restrict__ kscale,
+                       const float* __restrict__ vscale, const int32_t* __restrict__ lens,
+                       float* __restrict__ ws_o, float* __restrict__ ws_ml,
+                       int B, int H_q, int H_kv, int T_max, int G, int n_hg, int nsplit,
+                       int nwaves, int qb, float c) {
+    using Gm = Geo8<D>;
+    constexpr int RB = Gm::RB, NV = Gm::NV, QCH = Gm::QCH, RV = Gm::RV, LK = Gm::LK;
+    constexpr int KSTEPS = D / 16;     // MFMA k-steps of K·Qᵀ
+    constexpr int DB = D / 32;         // 32-row blocks of Oᵀ
+    constexpr int RB16 = D * 2;        // bytes per row of the bf16 V tile
+    static_assert(LK >= 1 && LK < RV, "ring geometry");
+    __shared__ __attribute__((aligned(16))) unsigned char vtile[CK * RB16];
+    extern __shared__ __attribute__((aligned(16))) unsigned char qlds[];   // RV Q slots of qb bytes
+    auto qslot = [&](int s) -> unsigned char* { return qlds + s * qb; };
+
+    const int HG = H_kv * n_hg;
+    const Lens L = load_lens(lens, B, T_max);
+    Plan P;
+    int b0, before;
+    const int w = blockIdx.x;
+    make_plan(L, HG, nwaves, w, P, b0, before);
+    const int a0 = w * P.bpw;
+    if (a0 >= P.total) return;
+    const int nblk = min(P.total, a0 + P.bpw) - a0;
+    b0 = __builtin_amdgcn_readfirstlane(b0);
+    before = __builtin_amdgcn_readfirstlane(before);
+
+    const int lane = threadIdx.x;
+    const int hl = lane >> 5, l32 = lane & 31;
+
+    // K: byte offsets of the operand layout within a block.  V: load i of a lane holds
+    // block bytes i*1024 + 16*lane .. +15 = row r, codes of columns col .. col+15, i.e.
+    // bf16 chunks g0 = col/8 and g0+1 of row r, which sit at LDS chunk positions
+    // g0 ^ v_swz(r) and the next one (v_swz is even).
+    uint32_t k_off[KSTEPS], v_off[NV], v_dst[NV];
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) k_off[kk] = (uint32_t)(swap_bits23(l32) * RB + kk * 16 + hl * 8);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int o = i * 1024 + lane * 16;
+        const int r = o / RB, g0 = (o % RB) / 8;
+        v_off[i] = (uint32_t)o;
+        v_dst[i] = (uint32_t)(r * RB16 + (g0 ^ v_swz<D>(r)) * 16);
+    }
+    const __amdgpu_buffer_rsrc_t zrs = brsrc(kc, 0u);
+
+    // ---- issue side: V (+ Q) cursor RV-1 blocks ahead of the compute, K cursor LK ahead
+    Cursor icv = cursor_at(L, HG, n_hg, b0, a0 - before);
+    Cursor ick = icv;
+    int nv = 0, nk = 0, qs_issue = 0;
+    auto item_rsrc = [&](const Cursor& x, const uint8_t* base) {
+        const size_t head = ((size_t)x.b * H_kv + x.g) * (size_t)T_max * D;
+        return brsrc(base + head, (uint32_t)x.t_end * RB);
+    };
+    __amdgpu_buffer_rsrc_t vrs = item_rsrc(icv, vc), krs = item_rsrc(ick, kc);
+    u32x4 vr[RV][NV];
+    u32x2 kr[RV][KSTEPS];
+    auto issue_v = [&](int s) {
+        const bool live = nv < nblk;
+        const uint32_t row0 = (uint32_t)(icv.s * kDecodeSplit + icv.i * CK) * RB;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) vr[s][i] = bload16(live ? vrs : zrs, row0 + v_off[i]);
+        if (!live) return;
+        if (icv.i == 0 || nv == 0) {     // the item's Q (also for a range that starts inside it)
+            const int ncols = min(32, G - icv.hg * 32);
+            const __amdgpu_buffer_rsrc_t qrs =
+                brsrc(q + ((size_t)icv.b * H_q + icv.g * G + icv.hg * 32) * D, (uint32_t)(ncols * RB16));
+#pragma unroll
+            for (int ch = 0; ch < QCH; ++ch)
+                if (ch * 1024 < ncols * RB16)
+                    lds_dma16(qrs, qslot(qs_issue) + ch * 1024, (uint32_t)(ch * 1024 + lane * 16));
+        }
+        ++nv;
+        advance(icv, L, HG, n_hg);
+        if (icv.i == 0) {
+            qs_issue = qs_issue == RV - 1 ? 0 : qs_issue + 1;
+            vrs = item_rsrc(icv, vc);
+        }
+    };
+    auto issue_k = [&](int s) {
+        const bool live = nk < nblk;
+        const uint32_t row0 = (uint32_t)(ick.s * kDecodeSplit + ick.i * CK) * RB;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) kr[s][kk] = bload8(live ? krs : zrs, row0 + k_off[kk]);
+        if (!live) return;
+        ++nk;
+        advance(ick, L, HG, n_hg);
+        if (ick.i == 0) krs = item_rsrc(ick, kc);
+    };
+#pragma unroll
+    for (int s = 0; s < RV - 1; ++s) issue_v(s);
+#pragma unroll
+    for (int s = 0; s < LK; ++s) issue_k(s);
+
+    // ---- compute side
+    Cursor cc = cursor_at(L, HG, n_hg, b0, a0 - before);
+    int part = cc.i == 0 ? 0 : 1;
+    int qs = 0;
+    bf16x8 qreg[KSTEPS];
+    bool need_q = true;
+    float ci = c, vsc = 1.f;           // this item's score multiplier and V scale
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    float mc = 0.f, lsum = 0.f;
+    bool mc_set = false;
+
+    const int vg = lane >> 4, vm = lane & 15;
+    const int vrow = (vg >> 1) * 8 + (vm >> 2);
+    const int vfv = v_swz<D>(vrow);
+    const int vc0 = 2 * (vg & 1) + ((vm & 3) >> 1);
+    const int vin = (vm & 1) * 4;
+    uint32_t vaddr[DB];                // this lane's LDS byte address of row block db in the tile
+    {
+        const uint32_t tb = (uint32_t)reinterpret_cast<uintptr_t>(
+            (__attribute__((address_space(3))) unsigned char*)vtile);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            vaddr[db] = tb + (uint32_t)((vrow * D + (((db * 4 + vc0) ^ vfv) * 8) + vin) * 2);
+    }
+
+    auto compute = [&](int j, int s) {
+        const int g = cc.g, hg = cc.hg;
+        const int col = hg * 32 + l32;
+        const bool col_ok = col < G;
+        if (need_q) {                    // first block of an item: Q and the scales
+            const bf16* qrow = reinterpret_cast<const bf16*>(qslot(qs)) + (col_ok ? l32 : 0) * D;
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hl * 8);
+                qreg[kk] = __builtin_bit_cast(bf16x8, col_ok ? v : u32x4{0u, 0u, 0u, 0u});
+            }
+            const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)(cc.b * H_kv + g) * 4u);
+            int kb, vb;
+            sload2(reinterpret_cast<const int32_t*>(kscale), so, so, kb, vb);
+            ci = c * __int_as_float(kb);
+            sload2(reinterpret_cast<const int32_t*>(vscale), so, so, vb, kb);
+            vsc = __int_as_float(vb);
+            need_q = false;
+        }
+        f32x16 S = {};
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            const u32x2 a0 = e4m3x4_to_bf16(kr[s][kk][0]), a1 = e4m3x4_to_bf16(kr[s][kk][1]);
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]}),
+                                                        qreg[kk], S, 0, 0, 0);
+        }
+        const int nvalid = cc.t_end - (cc.s * kDecodeSplit + cc.i * CK);   // keys before the item's end
+        if (nvalid < CK) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if ((i >> 3) * 16 + hl * 8 + (i & 7) >= nvalid) S[i] = kNegInf;
+        }
+        if (!mc_set) {                   // reference from this item's first block here
+            float m = S[0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) m = fmaxf(m, S[i]);
+            mc = pair_max(m) * ci;
+            mc_set = true;
+        }
+        u32x4 pw[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            float p[8];
+            float cs = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[k2 * 8 + e], ci, -mc));
+                cs += p[e];
+            }
+            if (__ballot(cs > kRescaleSum)) {     // rare: raise the reference
+                float m = S[k2 * 8];
+#pragma unroll
+                for (int e = 1; e < 8; ++e) m = fmaxf(m, S[k2 * 8 + e]);
+                const float mn = fmaxf(mc, pair_max(m) * ci);
+                const float alpha = __builtin_amdgcn_exp2f(mc - mn);
+                mc = mn;
+                lsum *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+                cs = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[k2 * 8 + e], ci, -mc));
+                    cs += p[e];
+                }
+            }
+            lsum += cs;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pw[k2][e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+        }
+        // V of this block: codes -> bf16 tile -> transposing operand reads
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const u32x4 v = vr[s][i];
+            const u32x2 c0 = e4m3x4_to_bf16(v[0]), c1 = e4m3x4_to_bf16(v[1]);
+            const u32x2 c2 = e4m3x4_to_bf16(v[2]), c3 = e4m3x4_to_bf16(v[3]);
+            *reinterpret_cast<u32x4*>(vtile + v_dst[i]) = u32x4{c0[0], c0[1], c1[0], c1[1]};
+            *reinterpret_cast<u32x4*>(vtile + v_dst[i] + 16) = u32x4{c2[0], c2[1], c3[0], c3[1]};
+        }
+        u32x4 va[2][DB];
+        v_operands<D>(vaddr, va);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, va[k2][db]), __builtin_bit_cast(bf16x8, pw[k2]),
+                    oacc[db], 0, 0, 0);
+
+        // end of this wavefront's part of the item: write the partial (O times the V scale)
+        if (cc.i == cc.nb - 1 || j == nblk - 1) {
+            const float Lsum = pair_sum(lsum);
+            if (col_ok) {
+                const size_t slot = ((size_t)(cc.b * H_q + g * G + col) * nsplit + cc.s) * 2 + part;
+                float* orow = ws_o + slot * D;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4)
+                        *reinterpret_cast<f32x4*>(orow + db * 32 + g4 * 8 + hl * 4) =
+                            f32x4{oacc[db][4 * g4] * vsc, oacc[db][4 * g4 + 1] * vsc,
+                                  oacc[db][4 * g4 + 2] * vsc, oacc[db][4 * g4 + 3] * vsc};
+                if (hl == 0) *reinterpret_cast<f32x2*>(ws_ml + slot * 2) = f32x2{mc, Lsum};
+                else if (part == 0 && cc.i == cc.nb - 1)
+                    *reinterpret_cast<f32x2*>(ws_ml + (slot + 1) * 2) = f32x2{kNegInf, 0.f};
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+            lsum = 0.f;
+            mc_set = false;
+            need_q = true;
+            part = 0;
+            qs = qs == RV - 1 ? 0 : qs + 1;
+        }
+        advance(cc, L, HG, n_hg);
+    };
+
+    // block j sits in V slot j % RV and K slot j % RV; unrolled RV times so every slot
+    // index is a constant
+    for (int j0 = 0; j0 < nblk; j0 += RV) {
+#pragma unroll
+        for (int r = 0; r < RV; ++r) {
+            // past the range the issues are zero-range loads and the compute is skipped;
+            // the loop is never left mid-body (no register copies on extra exits)
+            const int j = j0 + r;
+            issue_v((r + RV - 1) % RV);       // block j + RV - 1, into the slot block j - 1 left
+            issue_k((r + LK) % RV);           // block j + LK
+            if (j < nblk) compute(j, r);
+        }
+    }
+    wait_vmem_le<0>();     // the Q loads into LDS land before the wavefront ends
+}
+
+template <int D>
+int resident_waves8(int lds_bytes) {
+    static int cached_lds = -1, cached = 0;
+    if (lds_bytes == cached_lds) return cached;
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_fp8_kernel<D>, 64, lds_bytes) != hipSuccess ||
+        cus <= 0 || per_cu <= 0)
+        return 256;
+    cached = cus * per_cu;
+    cached_lds = lds_bytes;
+    return cached;
+}
+
+template <int D>
+hipError_t launch8(const DecodeFp8Args& a) {
+    static const hipError_t attr =
+        hipFuncSetAttribute((const void*)decode_fp8_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            Geo8<D>::RV * q_slot_bytes(32, D));
+    if (attr != hipSuccess) return attr;
+    const int G = a.H_q / a.H_kv;
+    const int n_hg = (G + 31) / 32;
+    const int nsplit = decode_nsplit(a.T_max);
+    const int qb = q_slot_bytes(G, D);
+    const int lds = Geo8<D>::RV * qb;
+    const int nwaves = resident_waves8<D>(lds);
+    float* ws_o = static_cast<float*>(a.workspace);
+    float* ws_ml = ws_o + (size_t)a.B * a.H_q * nsplit * 2 * D;
+    hipLaunchKernelGGL((decode_fp8_kernel<D>), dim3(nwaves), dim3(64), lds, (hipStream_t)a.stream,
+                       (const bf16*)a.q, (const uint8_t*)a.k_cache, (const uint8_t*)a.v_cache, a.k_scale,
+                       a.v_scale, a.lens, ws_o, ws_ml, a.B, a.H_q, a.H_kv, a.T_max, G, n_hg, nsplit, nwaves, qb,
+                       a.scale * kLog2e);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int n_bh = a.B * a.H_q;
+    hipLaunchKernelGGL((decode_stream_combine<D>), dim3((n_bh + 3) / 4), dim3(256), 0, (hipStream_t)a.stream,
+                       ws_o, ws_ml, a.lens, (bf16*)a.o, a.lse, a.H_q, a.T_max, nsplit, n_bh);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_fp8kv(const DecodeFp8Args& a) { return a.D == 64 ? launch8<64>(a) : launch8<128>(a); }
+
+}  // namespace mattn

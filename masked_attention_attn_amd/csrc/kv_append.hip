@@ -65,7 +65,54 @@ void kv_append_kernel(unsigned char* __restrict__ kc, unsigned char* __restrict_
     if (ok && threadIdx.x == 0) lens[b] = t + 1;
 }
 
+// FP8 (E4M3) cache: the new token's elements are quantised with the (b, KV head)
+// scale as code = E4M3(clamp(x / scale, -448, 448)) (IEEE float32 division,
+// round to nearest, ties to even) and written as bytes; four elements per
+// thread become one dword of codes (element i in byte i).
+__global__ __launch_bounds__(NT)
+void kv_append_fp8_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                          const float* __restrict__ ks, const float* __restrict__ vs,
+                          int32_t* __restrict__ lens, const void* __restrict__ kn,
+                          const void* __restrict__ vn, int new_bf16, int H_kv, int T_max, int D) {
+    const int b = blockIdx.x;
+    const int t = lens[b];
+    const bool ok = t >= 0 && t < T_max;
+    if (ok) {
+        const int quads = D / 4;
+        const int total = 2 * H_kv * quads;          // K then V
+        for (int idx = threadIdx.x; idx < total; idx += NT) {
+            const int which = idx / (H_kv * quads);
+            const int rem = idx - which * H_kv * quads;
+            const int g = rem / quads, qd = rem - g * quads;
+            const float s = (which ? vs : ks)[b * H_kv + g];
+            const size_t e0 = ((size_t)b * H_kv + g) * D + (size_t)qd * 4;
+            const void* src = which ? vn : kn;
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                x[e] = new_bf16 ? (float)reinterpret_cast<const bf16*>(src)[e0 + e]
+                                : reinterpret_cast<const float*>(src)[e0 + e];
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf(__fdiv_rn(x[e], s), -448.0f), 448.0f);
+            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+            wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], wd, true);
+            uint8_t* dst = (which ? vc : kc) + (((size_t)b * H_kv + g) * T_max + t) * D + (size_t)qd * 4;
+            *reinterpret_cast<uint32_t*>(dst) = (uint32_t)wd;
+        }
+    }
+    __syncthreads();
+    if (ok && threadIdx.x == 0) lens[b] = t + 1;
+}
+
 }  // namespace
+
+hipError_t launch_kv_append_fp8(const AppendFp8Args& a) {
+    hipLaunchKernelGGL(kv_append_fp8_kernel, dim3(a.B), dim3(NT), 0, (hipStream_t)a.stream,
+                       (uint8_t*)a.k_cache, (uint8_t*)a.v_cache, a.k_scale, a.v_scale, a.lens, a.k_new,
+                       a.v_new, a.new_bf16 ? 1 : 0, a.H_kv, a.T_max, a.D);
+    return hipGetLastError();
+}
 
 hipError_t launch_kv_append(const AppendArgs& a) {
     const int row_bytes = a.D * a.elem_bytes;

@@ -63,6 +63,29 @@ struct DecodeArgs {
     int page_size = 0, max_pages = 0, num_pages = 0;
 };
 
+// FP8 (E4M3) cache: codes [B, H_kv, T_max, D] uint8, one float32 scale per (b, KV head)
+// for K and for V; q, o bf16.
+struct DecodeFp8Args {
+    const void* q; const void* k_cache; const void* v_cache;
+    const float* k_scale; const float* v_scale;
+    const int32_t* lens;
+    void* o; float* lse;          // lse may be null
+    int B, H_q, H_kv, T_max, D;
+    float scale;
+    void* workspace;
+    void* stream;
+};
+
+struct AppendFp8Args {
+    void* k_cache; void* v_cache;
+    const float* k_scale; const float* v_scale;
+    int32_t* lens;
+    const void* k_new; const void* v_new;   // [B, H_kv, 1, D], bf16 or float32
+    bool new_bf16;
+    int B, H_kv, T_max, D;
+    void* stream;
+};
+
 hipError_t launch_fwd_bf16_d64(const FwdArgs& a);
 hipError_t launch_fwd_bf16_d128(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
@@ -71,6 +94,8 @@ hipError_t launch_merge_f32(const MergeArgs& a);
 hipError_t launch_kv_append(const AppendArgs& a);
 hipError_t launch_decode_bf16(const DecodeArgs& a);
 hipError_t launch_decode_f32(const DecodeArgs& a);
+hipError_t launch_decode_fp8kv(const DecodeFp8Args& a);
+hipError_t launch_kv_append_fp8(const AppendFp8Args& a);
 
 // Split-K geometry of the decode path (shared by the workspace-size query
 // and the launcher).

@@ -235,3 +235,28 @@ def test_prefill_validation(lib):
     assert pv(mq=101) == 2
     assert pv(o=A) == 8
     assert pv(tq=0, mq=0) == 0
+
+
+def test_fp8_validation(lib):
+    KS, VS, W = 0x70000, 0x80000, 0x60000
+    ws = lib.attn_decode_workspace_bytes(4, 8, 2, 1000, 128)
+
+    def dec(**kw):
+        a = dict(q=A, k=B_, v=C, ks=KS, vs=VS, lens=L, o=O, lse=0, B=4, Hq=8, Hkv=2, Tmax=1000, D=128,
+                 scale=0.088, ws=W, wsb=ws)
+        a.update(kw)
+        return lib.attn_decode_fp8kv(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["lens"], a["o"], a["lse"], a["B"],
+                                     a["Hq"], a["Hkv"], a["Tmax"], a["D"], a["scale"], a["ws"], a["wsb"], None)
+    assert dec(ks=0) == 1
+    assert dec(vs=0) == 1
+    assert dec(D=96) == 3
+    assert dec(Hq=6, Hkv=4) == 2
+    assert dec(Tmax=(1 << 24) + 1) == 2          # T_max·D beyond the 32-bit range of one head
+    assert dec(scale=0.0) == 6
+    assert dec(wsb=ws - 1) == 4
+    assert dec(k=B_ + 8) == 7
+    assert dec(o=A) == 8
+    assert lib.kv_append_fp8(A, B_, KS, 0, L, C, O, 2, 2, 16, 64, 1, None) == 1
+    assert lib.kv_append_fp8(A, B_, KS, VS, L, C, O, 2, 2, 16, 64, 7, None) == 3
+    assert lib.kv_append_fp8(A, B_, KS, VS, L, C, O, 2, 2, 0, 64, 1, None) == 2
+    assert lib.kv_append_fp8(A, A, KS, VS, L, C, O, 2, 2, 16, 64, 1, None) == 8

@@ -574,3 +574,87 @@ def test_gqa_causal_prefill_8192_sampled_rows(ma):
     rows = [0, 1, 31, 32, 255, 256, 4095, 4096, 8191] + list(range(7, 8192, 613))
     Or, Lr = oracle.prefill(w.q, w.k, w.v, None, True, w.scale, rows=rows)
     check_attn(o[:, :, rows], l[:, :, rows], Or, Lr, torch.bfloat16, "causal 8192 sampled rows")
+
+
+# ---- FP8 (E4M3) KV cache ----------------------------------------------------------------
+
+FP8_DEC = [
+    # B, Hq, Hkv, D, len_lo, len_hi, T_max
+    (3, 4, 4, 64, 1, 40, 64),
+    (4, 8, 2, 128, 1, 1500, 1536),
+    (2, 32, 8, 128, 500, 1100, 1152),
+    (3, 6, 2, 64, 0, 600, 640),
+    (2, 40, 1, 64, 100, 900, 960),
+    (70, 8, 4, 128, 1, 300, 320),
+    (4, 8, 8, 128, 1023, 1023, 1024),
+    (1, 1, 1, 128, 0, 0, 64),
+]
+
+
+def _fp8_dev(w):
+    return (w.k_cache.to(DEV), w.v_cache.to(DEV), w.k_scale.to(DEV), w.v_scale.to(DEV), w.lens.to(DEV))
+
+
+@pytest.mark.parametrize("shape", FP8_DEC)
+def test_fp8_append_then_decode(ma, shape):
+    B, Hq, Hkv, D, lo, hi, Tm = shape
+    w = W.make_decode_fp8(B, Hq, Hkv, D, lo, hi, T_max=Tm, seed=B * 10 + Hq)
+    kc, vc, ks, vs, lens = _fp8_dev(w)
+    ma.kv_append_fp8(kc, vc, ks, vs, lens, w.k_new.to(DEV), w.v_new.to(DEV))
+    o, l = ma.attn_decode_fp8kv(w.q.to(DEV), kc, vc, ks, vs, lens, w.scale, want_lse=True)
+    torch.cuda.synchronize()
+    ek, ev, el = oracle.kv_append_fp8(w.k_cache.numpy(), w.v_cache.numpy(), w.k_scale, w.v_scale, w.lens.numpy(),
+                                      w.k_new, w.v_new)
+    assert lens.cpu().tolist() == el.tolist()
+    assert np.array_equal(kc.cpu().numpy(), ek) and np.array_equal(vc.cpu().numpy(), ev)   # bytes, exact
+    Or, Lr = oracle.decode_fp8kv(w.q, ek, ev, w.k_scale, w.v_scale, el, w.scale)
+    check_attn(o, l, Or, Lr, torch.bfloat16, f"fp8 decode {shape}")
+
+
+@pytest.mark.parametrize("new_dtype", [torch.bfloat16, torch.float32])
+def test_fp8_append_quantisation_edges(ma, new_dtype):
+    # ties to even, saturation, the subnormal boundary, zeros and signs, in both input dtypes
+    B, Hkv, D, Tm = 2, 2, 64, 64
+    w = W.make_decode_fp8(B, 2, Hkv, D, 3, 10, T_max=Tm, seed=5)
+    special = torch.tensor([1.0625, 1.1875, -1.0625, 1e6, -1e6, 2.0 ** -10, 3 * 2.0 ** -11, 0.0, -0.0,
+                            448.0, 464.0, 0.0009765625, 240.0, 232.0, -3.5, 17.0])
+    g = torch.Generator().manual_seed(9)
+    kn = torch.randn(B, Hkv, 1, D, generator=g) * 40
+    vn = torch.randn(B, Hkv, 1, D, generator=g) * 0.01
+    kn[0, 0, 0, :16] = special
+    vn[1, 1, 0, :16] = special
+    kn, vn = kn.to(new_dtype).contiguous(), vn.to(new_dtype).contiguous()
+    ks = torch.tensor([[1.0, 0.75], [0.3, 2.0]], dtype=torch.float32)
+    vs = torch.tensor([[0.001, 0.25], [1.5, 1.0]], dtype=torch.float32)
+    kc, vc = w.k_cache.to(DEV), w.v_cache.to(DEV)
+    lens = w.lens.to(DEV)
+    ma.kv_append_fp8(kc, vc, ks.to(DEV), vs.to(DEV), lens, kn.to(DEV), vn.to(DEV))
+    torch.cuda.synchronize()
+    ek, ev, el = oracle.kv_append_fp8(w.k_cache.numpy(), w.v_cache.numpy(), ks, vs, w.lens.numpy(), kn, vn)
+    assert np.array_equal(kc.cpu().numpy(), ek) and np.array_equal(vc.cpu().numpy(), ev)
+    assert lens.cpu().tolist() == el.tolist()
+
+
+def test_fp8_decode_zero_lengths(ma):
+    w = W.make_decode_fp8(5, 8, 2, 128, 0, 10, T_max=1024, lens=[0, 513, 0, 0, 31], seed=6)
+    kc, vc, ks, vs, lens = _fp8_dev(w)
+    o, l = ma.attn_decode_fp8kv(w.q.to(DEV), kc, vc, ks, vs, lens, w.scale, want_lse=True)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.decode_fp8kv(w.q, w.k_cache, w.v_cache, w.k_scale, w.v_scale, w.lens, w.scale)
+    check_attn(o, l, Or, Lr, torch.bfloat16, "fp8 decode zero lengths")
+
+
+def test_gqa_decode_b32_fp8_sampled_heads(ma):
+    """The B32 GQA decode workload with an E4M3 cache: append, decode, sampled (b, h)."""
+    w = W.gqa_decode_b32_fp8()
+    kc, vc, ks, vs, lens = _fp8_dev(w)
+    ma.kv_append_fp8(kc, vc, ks, vs, lens, w.k_new.to(DEV), w.v_new.to(DEV))
+    o, l = ma.attn_decode_fp8kv(w.q.to(DEV), kc, vc, ks, vs, lens, w.scale, want_lse=True)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(8)
+    heads = [(int(b), int(h)) for b, h in zip(g.integers(0, 32, 16), g.integers(0, 32, 16))]
+    heads += [(int(np.argmax(w.lens)), 5)]
+    Or, Lr = oracle.decode_fp8kv(w.q, kc.cpu().numpy(), vc.cpu().numpy(), w.k_scale, w.v_scale,
+                                 lens.cpu().numpy(), w.scale, heads=heads)
+    check_attn(torch.stack([o[b, h, 0] for b, h in heads]), torch.stack([l[b, h] for b, h in heads]),
+               Or, Lr, torch.bfloat16, "fp8 decode sampled heads")

@@ -40,7 +40,7 @@ __all__ = [
     "mask_from_valid_lengths", "round_up",
     "fp32_masked_t512", "patch_p1944", "patch_p11616",
     "chunked_kv_2x8192", "gqa_decode_b32", "varlen_p1944_packed", "varlen_ring_hop_8192",
-    "gqa_decode_b32_paged", "make_gqa_prefill", "gqa_causal_prefill_8192", "gqa_causal_prompts_packed",
+    "gqa_decode_b32_paged", "DecodeFp8", "make_decode_fp8", "gqa_decode_b32_fp8", "make_gqa_prefill", "gqa_causal_prefill_8192", "gqa_causal_prompts_packed",
 ]
 
 
@@ -112,6 +112,21 @@ class Paged:
     v_pages: torch.Tensor
     block_table: torch.Tensor  # int32 [B, max_pages]: logical page i of b -> physical page
     page_size: int
+
+
+@dataclass
+class DecodeFp8:
+    """Decode inputs with an E4M3 cache: codes (uint8) and float32 scales per (b, KV head)."""
+    q: torch.Tensor        # [B, H_q, 1, D] bf16
+    k_cache: torch.Tensor  # [B, H_kv, T_max, D] uint8 (E4M3 codes)
+    v_cache: torch.Tensor
+    k_scale: torch.Tensor  # [B, H_kv] float32
+    v_scale: torch.Tensor
+    k_new: torch.Tensor    # [B, H_kv, 1, D] bf16
+    v_new: torch.Tensor
+    lens: torch.Tensor     # int32 [B], cached length BEFORE the append
+    scale: float
+    name: str = ""
 
 
 def _gen(seed: int) -> torch.Generator:
@@ -240,6 +255,30 @@ def to_paged(dec: Decode, page_size: int, *, seed=1, spare_pages=3) -> Paged:
     return Paged(dec, kp.contiguous(), vp.contiguous(), bt, page_size)
 
 
+def make_decode_fp8(B, H_q, H_kv, D, len_lo, len_hi, *, T_max=None, seed=0, scale=None, lens=None,
+                    name="") -> DecodeFp8:
+    """E4M3 caches drawn as N(0,1) cast to float8_e4m3fn (round to nearest even), scales
+    2^U{-6..-2} per (b, KV head), new tokens N(0,1) times their head's scale in bf16 (so they
+    quantise into the bulk of the code range), Q N(0,1) bf16.  Draw order: lengths, K cache,
+    V cache, K scale exponents, V scale exponents, k_new, v_new, Q."""
+    g = _gen(seed)
+    if lens is None:
+        lens = torch.randint(len_lo, len_hi + 1, (B,), generator=g, dtype=torch.int64)
+    lens = torch.as_tensor(lens, dtype=torch.int64)
+    if T_max is None:
+        T_max = round_up(len_hi + 1, 64)
+    kc = torch.randn(B, H_kv, T_max, D, generator=g).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    vc = torch.randn(B, H_kv, T_max, D, generator=g).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    ks = torch.exp2(torch.randint(-6, -1, (B, H_kv), generator=g).float()).contiguous()
+    vs = torch.exp2(torch.randint(-6, -1, (B, H_kv), generator=g).float()).contiguous()
+    kn = (torch.randn(B, H_kv, 1, D, generator=g) * ks[:, :, None, None]).to(torch.bfloat16).contiguous()
+    vn = (torch.randn(B, H_kv, 1, D, generator=g) * vs[:, :, None, None]).to(torch.bfloat16).contiguous()
+    q = torch.randn(B, H_q, 1, D, generator=g).to(torch.bfloat16).contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return DecodeFp8(q, kc, vc, ks, vs, kn, vn, lens.to(torch.int32), float(scale), name)
+
+
 def make_gqa_prefill(B, H_q, H_kv, Tq, Tk, D, dtype=torch.bfloat16, *, valid=None, amp=1.0, seed=0,
                      scale=None, name="") -> Prefill:
     """Q [B, H_q, Tq, D] and K/V [B, H_kv, Tk, D] (grouped-query layout), drawn Q, K, V."""
@@ -322,3 +361,9 @@ def gqa_causal_prompts_packed(seed=0) -> Varlen:
     v = _randn(g, (n, 8, 128), 1.0, torch.bfloat16)
     return Varlen(q, k, v, cq, cq.clone(), max(lens), 1.0 / math.sqrt(128),
                   "bf16 packed causal GQA prompts Hq32 Hkv8 D128, 4x1024 + 2x2048 + 2x4096")
+
+
+def gqa_decode_b32_fp8(seed=0) -> DecodeFp8:
+    """The GQA decode workload (B32, H_q 32 / H_kv 8, D128, len U[512, 8192]) with an E4M3 cache."""
+    return make_decode_fp8(32, 32, 8, 128, 512, 8192, seed=seed,
+                           name="E4M3-cache GQA decode B32 Hq32 Hkv8 D128, len U[512,8192] + 1 appended")
