@@ -53,7 +53,7 @@ def parse():
     p.add_argument("--no-sweep", action="store_true",
                    help="skip the sections measured outside the step: the P-sweep of the prefill "
                         "(memory and TFLOP/s at P = 1,944 .. 32,122), the packed varlen calls, "
-                        "the paged decode and the causal GQA prefill")
+                        "the paged decode, the causal GQA prefill and the FP8-cache decode")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -247,6 +247,25 @@ def paged_section(torch, ma, W, dev):
     return res
 
 
+def fp8_section(torch, ma, W, dev):
+    """The decode workload with an E4M3 cache (attn_decode_fp8kv; per-(sequence, KV head) scales),
+    timed on its own after the append; bytes: one byte per cached K and V element, plus q and o."""
+    w = W.gqa_decode_b32_fp8()
+    kc, vc, ks, vs = w.k_cache.to(dev), w.v_cache.to(dev), w.k_scale.to(dev), w.v_scale.to(dev)
+    lens = (w.lens + 1).to(dev)
+    q = w.q.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    B, Hq, _, D = q.shape
+    Hkv, Tm = kc.shape[1], kc.shape[2]
+    ws = torch.empty(ma.attn_decode_workspace_bytes(B, Hq, Hkv, Tm, D), dtype=torch.uint8, device=dev)
+    t = _time_call(torch, lambda: ma.attn_decode_fp8kv(q, kc, vc, ks, vs, lens, w.scale, out=o, lse=lse,
+                                                       workspace=ws, want_lse=True), n=20)
+    nbytes = int((w.lens + 1).sum()) * 2 * Hkv * D + 2 * q.numel() * 2
+    return {"workload": w.name, "us": round(t * 1e6, 2), "gbps": round(nbytes / t / 1e9, 1),
+            "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBPS, 4), "algorithmic_bytes": nbytes}
+
+
 def causal_section(torch, ma, W, dev):
     """Causal GQA prompt passes (attn_prefill / attn_prefill_varlen, H_q 32 / H_kv 8, D128), each
     timed on its own: one 8,192-token prompt, and 8 packed prompts of 1,024 .. 4,096 tokens.
@@ -438,6 +457,7 @@ def main():
         out["varlen"] = varlen_section(torch, ma, W, dev)
         out["paged_decode"] = paged_section(torch, ma, W, dev)
         out["causal_gqa_prefill"] = causal_section(torch, ma, W, dev)
+        out["fp8_kv_decode"] = fp8_section(torch, ma, W, dev)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(pf, args.cpu_seconds)
         cb.pop("seconds", None)
