@@ -11,4 +11,5 @@ from .attention import (  # noqa: F401
 )
 from .fp8 import (  # noqa: F401
     E4M3_MAX, e4m3_values, quantize_e4m3, dequantize_e4m3, kv_append_fp8, decode_fp8kv,
+    prefill_fp8,
 )

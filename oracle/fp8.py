@@ -18,14 +18,23 @@ granularity; the readings taken here (also listed in the design doc):
     [-448, 448], rounded to the nearest E4M3 value, ties to the even mantissa.
 Decoding against the quantised cache is exactly ``decode`` applied to the
 dequantised caches.
+
+FP8 prefill with LSE: the aiter ring-attention analysis (sglang PR 49078
+analysis, section "1. aiter.py") notes that the FP8 prefill kernel there
+returns no LSE, so a ring hop that needs the LSE falls back to BF16.  The
+FP8 prefill here keeps the LSE.  Reading taken: Q, K and V all arrive as E4M3
+codes, with one float32 scale per (sequence, query head) for Q and one per
+(sequence, KV head) for K and for V; the result is exactly ``prefill`` (GQA,
+optional key padding, optional causal limit) on the dequantised tensors.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .attention import decode, _f64
+from .attention import decode, prefill, _f64
 
-__all__ = ["E4M3_MAX", "e4m3_values", "quantize_e4m3", "dequantize_e4m3", "kv_append_fp8", "decode_fp8kv"]
+__all__ = ["E4M3_MAX", "e4m3_values", "quantize_e4m3", "dequantize_e4m3", "kv_append_fp8", "decode_fp8kv",
+           "prefill_fp8"]
 
 E4M3_MAX = 448.0
 
@@ -111,3 +120,17 @@ def decode_fp8kv(q, k_cache, v_cache, k_scale, v_scale, lens, scale=None, heads=
     kd = dequantize_e4m3(k_cache, ks)
     vd = dequantize_e4m3(v_cache, vs)
     return decode(q, kd, vd, lens, scale, heads)
+
+
+def prefill_fp8(q, k, v, q_scale, k_scale, v_scale, key_padding_mask=None, causal=False, scale=None,
+                rows=None):
+    """``prefill`` on dequantised E4M3 inputs.
+
+    q uint8 [B, H_q, Tq, D], k and v uint8 [B, H_kv, Tk, D]; q_scale [B, H_q],
+    k_scale and v_scale [B, H_kv].  Element x of Q stands for value(x) * q_scale[b, h]
+    (K and V likewise with their KV head's scale).  Returns O and LSE as ``prefill``.
+    """
+    qd = dequantize_e4m3(q, _f64(q_scale)[:, :, None, None])
+    kd = dequantize_e4m3(k, _f64(k_scale)[:, :, None, None])
+    vd = dequantize_e4m3(v, _f64(v_scale)[:, :, None, None])
+    return prefill(qd, kd, vd, key_padding_mask, causal, scale, rows)

@@ -696,3 +696,72 @@ def test_kv_append_fp8_writes_only_the_quantised_slot():
         assert np.array_equal(vc2[b, :, t], oracle.quantize_e4m3(vn[b, :, 0], vs[b][:, None]))
         other = [i for i in range(T) if i != t]
         assert np.array_equal(kc2[b, :, other], kc[b, :, other]) and np.array_equal(vc2[b, :, other], vc[b, :, other])
+
+
+# ---- FP8 prefill with LSE ---------------------------------------------------------------
+
+def _e4m3_codes(r, shape):
+    c = r.integers(0, 256, shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x3C                         # no NaN codes in an input
+    return c
+
+
+def _torch_e4m3(c):
+    """Values of E4M3 codes by torch's float8_e4m3fn decoding (independent of the oracle's table)."""
+    return torch.from_numpy(np.ascontiguousarray(c)).view(torch.float8_e4m3fn).double().numpy()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefill_fp8_matches_brute_force(seed):
+    r = _rng(300 + seed)
+    B, Hkv, G = int(r.integers(1, 3)), int(r.integers(1, 3)), int(r.integers(1, 3))
+    Tq, Tk, D = int(r.integers(1, 7)), int(r.integers(1, 8)), int(r.integers(1, 6))
+    q8 = _e4m3_codes(r, (B, Hkv * G, Tq, D))
+    k8 = _e4m3_codes(r, (B, Hkv, Tk, D))
+    v8 = _e4m3_codes(r, (B, Hkv, Tk, D))
+    qs = r.uniform(2 ** -8, 2 ** -5, (B, Hkv * G))
+    ks = r.uniform(2 ** -8, 2 ** -5, (B, Hkv))
+    vs = r.uniform(0.5, 2.0, (B, Hkv))
+    mask = (r.random((B, Tk)) < 0.3).astype(np.uint8) if seed % 2 else None
+    causal = seed >= 2
+    scale = float(r.uniform(0.3, 1.2))
+    O, L = oracle.prefill_fp8(q8, k8, v8, qs, ks, vs, mask, causal, scale)
+    qv, kv, vv = _torch_e4m3(q8), _torch_e4m3(k8), _torch_e4m3(v8)
+    off = Tk - Tq
+    for b in range(B):
+        for h in range(Hkv * G):
+            g = h // G
+            keys = [[kv[b, g, t, d] * ks[b, g] for d in range(D)] for t in range(Tk)]
+            vals = [[vv[b, g, t, d] * vs[b, g] for d in range(D)] for t in range(Tk)]
+            for i in range(Tq):
+                qrow = [qv[b, h, i, d] * qs[b, h] for d in range(D)]
+                pad = [(mask is not None and mask[b, j] != 0) or (causal and j > i + off) for j in range(Tk)]
+                o, l = brute.attend_row(qrow, keys, vals, pad, scale)
+                if l == -math.inf:
+                    assert L[b, h, i] == -np.inf and np.all(O[b, h, i] == 0)
+                else:
+                    assert abs(L[b, h, i] - l) <= 1e-12
+                    assert np.max(np.abs(O[b, h, i] - np.array(o))) <= 1e-12
+
+
+def test_prefill_fp8_scale_roles():
+    # the Q and K scales only multiply the scores (a factor on `scale`); the V scale only
+    # multiplies O (the LSE ignores it): a swapped or dropped scale fails one of these
+    r = _rng(310)
+    B, Hkv, G, T, D = 2, 2, 2, 9, 8
+    q8, k8, v8 = _e4m3_codes(r, (B, Hkv * G, T, D)), _e4m3_codes(r, (B, Hkv, T, D)), _e4m3_codes(r, (B, Hkv, T, D))
+    ones_q, ones_kv = np.ones((B, Hkv * G)), np.ones((B, Hkv))
+    O1, L1 = oracle.prefill_fp8(q8, k8, v8, ones_q, ones_kv, ones_kv, None, False, 0.01)
+    O2, L2 = oracle.prefill_fp8(q8, k8, v8, ones_q * 0.5, ones_kv * 0.25, ones_kv * 3.0, None, False, 0.08)
+    np.testing.assert_allclose(L2, L1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(O2, 3.0 * O1, rtol=1e-12, atol=1e-12)
+    # per-head scales act on their own head only
+    qs = ones_q.copy()
+    qs[1, 3] = 2.0
+    O3, L3 = oracle.prefill_fp8(q8, k8, v8, qs, ones_kv, ones_kv, None, False, 0.01)
+    O4, L4 = oracle.prefill_fp8(q8, k8, v8, ones_q, ones_kv, ones_kv, None, False, 0.02)
+    np.testing.assert_allclose(O3[1, 3], O4[1, 3], atol=1e-12)
+    np.testing.assert_allclose(L3[1, 3], L4[1, 3], atol=1e-12)
+    keep = np.ones((B, Hkv * G), bool)
+    keep[1, 3] = False
+    assert np.array_equal(O3[keep], O1[keep]) and np.array_equal(L3[keep], L1[keep])
