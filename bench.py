@@ -37,6 +37,10 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E (published)
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 matrix peak (published)
+# The E4M3 prefill runs Q·Kᵀ (half its FLOP) at the fp8 rate and P·V (the other half) at
+# the bf16 rate: its matrix-core bound is 1 / (0.5 / fp8 peak + 0.5 / bf16 peak).
+PEAK_FP8_PREFILL_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PREFILL_SRCS = [os.path.join(ROOT, "masked_attention_attn_amd", "csrc", f)
                 for f in ("fwd_bf16.cuh", "fwd_bf16_d64.hip", "mfma_lds.cuh")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_p11616_traffic.json")
@@ -266,6 +270,32 @@ def fp8_section(torch, ma, W, dev):
             "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBPS, 4), "algorithmic_bytes": nbytes}
 
 
+def fp8_prefill_section(torch, ma, W, dev):
+    """E4M3-input prefill with LSE (attn_prefill_fp8), each timed on its own: the P = 11,616 patch
+    shape (non-causal, padded keys) and the causal GQA 8,192-token prompt.  FLOP are algorithmic
+    as for the bf16 calls; frac_mfma is against the split fp8 / bf16 matrix-core bound."""
+    res = {}
+    for key, w, causal in (("p11616", W.patch_p11616_fp8(), False),
+                           ("causal_prompt_8192", W.gqa_causal_prefill_8192_fp8(), True)):
+        q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
+        qs, ks, vs = w.q_scale.to(dev), w.k_scale.to(dev), w.v_scale.to(dev)
+        m = w.mask.to(dev) if w.mask is not None else None
+        B, Hq, T, D = q.shape
+        o = torch.empty((B, Hq, T, D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+        t = _time_call(torch, lambda: ma.attn_prefill_fp8(q, k, v, qs, ks, vs, m, causal, w.scale, out=o, lse=lse))
+        if causal:
+            flop = 4 * D * Hq * B * T * (T + 1) // 2
+        else:
+            n_valid = [int((w.mask[b] == 0).sum()) if w.mask is not None else T for b in range(B)]
+            flop = 4 * D * Hq * T * sum(n_valid)
+        res[key] = {"workload": w.name, "us": round(t * 1e6, 1), "tflops": round(flop / t / 1e12, 1),
+                    "frac_mfma": round(flop / t / 1e12 / PEAK_FP8_PREFILL_TFLOPS, 4),
+                    "peak_tflops": round(PEAK_FP8_PREFILL_TFLOPS, 1), "algorithmic_flop": flop}
+        del q, k, v, o, lse
+    return res
+
+
 def causal_section(torch, ma, W, dev):
     """Causal GQA prompt passes (attn_prefill / attn_prefill_varlen, H_q 32 / H_kv 8, D128), each
     timed on its own: one 8,192-token prompt, and 8 packed prompts of 1,024 .. 4,096 tokens.
@@ -458,6 +488,7 @@ def main():
         out["paged_decode"] = paged_section(torch, ma, W, dev)
         out["causal_gqa_prefill"] = causal_section(torch, ma, W, dev)
         out["fp8_kv_decode"] = fp8_section(torch, ma, W, dev)
+        out["fp8_prefill"] = fp8_prefill_section(torch, ma, W, dev)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(pf, args.cpu_seconds)
         cb.pop("seconds", None)

@@ -309,6 +309,31 @@ int attn_decode_fp8kv(const void* q, const void* k_cache, const void* v_cache,
                       int B, int H_q, int H_kv, int T_max, int D, float scale,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * attn_prefill_fp8 — attn_prefill on E4M3 inputs, with the LSE.
+ *
+ * The aiter ring-attention analysis (sglang PR 49078 analysis, section
+ * "1. aiter.py") notes that the FP8 prefill kernel there has no LSE output, so
+ * a ring hop that needs the LSE stays in BF16; this call returns it.  The
+ * result is attn_prefill (GQA, optional key padding, optional causal limit)
+ * on the dequantised inputs:
+ *   q  [B, H_q, Tq, D] uint8      k, v  [B, H_kv, Tk, D] uint8: E4M3 codes as
+ *       in the FP8 cache above (NaN codes are not valid input)
+ *   q_scale [B, H_q], k_scale and v_scale [B, H_kv] float32 device arrays,
+ *       owned by the caller and only read: an element stands for code value x
+ *       the scale of its (sequence, head); scales must be finite and > 0
+ *   o  [B, H_q, Tq, D] bf16        lse  [B, H_q, Tq] float32 or NULL
+ *   key_padding_mask, causal, scale  as attn_prefill
+ * Q·Kᵀ runs on the E4M3 matrix cores (exact products, float32 sums); the
+ * softmax weights and P·V are bf16 as in attn_prefill.  Tk·D must stay below
+ * 2^31; other rules and errors as attn_prefill.
+ */
+int attn_prefill_fp8(const void* q, const void* k, const void* v,
+                     const float* q_scale, const float* k_scale, const float* v_scale,
+                     const uint8_t* key_padding_mask, void* o, float* lse,
+                     int B, int H_q, int H_kv, int Tq, int Tk, int D, int causal,
+                     float scale, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(int status);
 

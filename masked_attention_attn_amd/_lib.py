@@ -31,7 +31,8 @@ STATUS = {
 
 EXPORTS = ("attn_fwd_masked", "attn_fwd_lse", "attn_fwd_varlen", "attn_merge_lse", "kv_append",
            "attn_decode", "attn_decode_workspace_bytes", "kv_append_paged", "attn_decode_paged",
-           "attn_prefill", "attn_prefill_varlen", "kv_append_fp8", "attn_decode_fp8kv", "attn_status_string")
+           "attn_prefill", "attn_prefill_varlen", "kv_append_fp8", "attn_decode_fp8kv", "attn_prefill_fp8",
+           "attn_status_string")
 
 _lib = None
 
@@ -63,6 +64,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kv_append_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
     lib.kv_append_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
     lib.attn_decode_fp8kv.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, S, P]
+    lib.attn_prefill_fp8.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
     lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, S, P]
     lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.attn_decode_workspace_bytes.restype = S
@@ -70,7 +72,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_status_string.restype = ctypes.c_char_p
     for name in ("attn_fwd_masked", "attn_fwd_lse", "attn_fwd_varlen", "attn_merge_lse", "kv_append",
                  "attn_decode", "kv_append_paged", "attn_decode_paged", "attn_prefill", "attn_prefill_varlen",
-                 "kv_append_fp8", "attn_decode_fp8kv"):
+                 "kv_append_fp8", "attn_decode_fp8kv", "attn_prefill_fp8"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -480,5 +482,54 @@ def attn_decode_fp8kv(q, k_cache, v_cache, k_scale, v_scale, cache_seqlens, scal
     _check("attn_decode_fp8kv", load().attn_decode_fp8kv(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(cache_seqlens), _ptr(out),
         _ptr(lse if want_lse else None), B, Hq, Hkv, Tmax, D, float(scale), _ptr(workspace), nbytes,
+        _stream(q.device)))
+    return (out, lse) if want_lse else out
+
+
+def attn_prefill_fp8(q, k, v, q_scale, k_scale, v_scale, key_padding_mask=None, causal=False, scale=None,
+                     out=None, lse=None, want_lse: bool = True):
+    """attn_prefill on E4M3 codes: q uint8 [B, H_q, Tq, D], k/v uint8 [B, H_kv, Tk, D] (or
+    torch.float8_e4m3fn, passed as its bytes); q_scale [B, H_q], k_scale / v_scale [B, H_kv]
+    float32.  Returns O bf16 [B, H_q, Tq, D] (and the LSE [B, H_q, Tq] float32)."""
+    q, k, v = (t.view(torch.uint8) if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn else t
+               for t in (q, k, v))
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _dev(t, n)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, T, D]")
+    if q.dtype != torch.uint8 or k.dtype != torch.uint8 or v.dtype != torch.uint8:
+        raise TypeError("q, k, v must be E4M3 codes (uint8 or float8_e4m3fn)")
+    B, Hq, Tq, D = q.shape
+    _, Hkv, Tk, _ = k.shape
+    if k.shape != (B, Hkv, Tk, D) or v.shape != k.shape:
+        raise ValueError("k/v must be [B, H_kv, Tk, D] with q's B and D")
+    for t, n, shp in ((q_scale, "q_scale", (B, Hq)), (k_scale, "k_scale", (B, Hkv)), (v_scale, "v_scale", (B, Hkv))):
+        if t.shape != shp or t.dtype != torch.float32:
+            raise ValueError(f"{n} must be float32 {list(shp)}")
+    if key_padding_mask is not None:
+        _dev(key_padding_mask, "key_padding_mask")
+        if key_padding_mask.shape != (B, Tk):
+            raise ValueError(f"key_padding_mask must be [B, Tk] = {(B, Tk)}")
+        if key_padding_mask.dtype == torch.bool:
+            key_padding_mask = key_padding_mask.view(torch.uint8)
+        if key_padding_mask.dtype != torch.uint8:
+            raise TypeError("key_padding_mask must be uint8 or bool (nonzero/True = padded)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, Tq, D), dtype=torch.bfloat16, device=q.device)
+    else:
+        _dev(out, "out")
+        if out.shape != (B, Hq, Tq, D) or out.dtype != torch.bfloat16:
+            raise ValueError("out must be bfloat16 [B, H_q, Tq, D]")
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    if want_lse:
+        _dev(lse, "lse")
+        if lse.shape != (B, Hq, Tq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [B, H_q, Tq]")
+    _check("attn_prefill_fp8", load().attn_prefill_fp8(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(key_padding_mask),
+        _ptr(out), _ptr(lse if want_lse else None), B, Hq, Hkv, Tq, Tk, D, 1 if causal else 0, float(scale),
         _stream(q.device)))
     return (out, lse) if want_lse else out

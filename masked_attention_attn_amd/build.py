@@ -32,9 +32,15 @@ FLAGS = [
 #    results instead of canonicalise-then-max.
 #  * VGPR-form MFMAs at D = 64 keep the score blocks in VGPRs for the vector
 #    unit (no AGPR<->VGPR copies).
+#  * the E4M3 kernels turn off machine sinking: it moves the E4M3 score MFMAs
+#    of the next key block (used only by the next step) past the rescale
+#    branches to the end of the step, where the next step's exponentials
+#    would wait for them, instead of the slots the step gives them.
 EXTRA = {
     "fwd_bf16_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
     "fwd_bf16_d128.hip": ["-fno-honor-nans"],
+    "fwd_fp8_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans", "-mllvm", "-disable-machine-sink"],
+    "fwd_fp8_d128.hip": ["-fno-honor-nans", "-mllvm", "-disable-machine-sink"],
     "decode_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
     "decode_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
 }

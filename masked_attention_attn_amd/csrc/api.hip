@@ -264,6 +264,32 @@ int attn_decode_fp8kv(const void* q, const void* k_cache, const void* v_cache, c
     return finish(launch_decode_fp8kv(a));
 }
 
+int attn_prefill_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                     const float* k_scale, const float* v_scale, const uint8_t* key_padding_mask, void* o,
+                     float* lse, int B, int H_q, int H_kv, int Tq, int Tk, int D, int causal, float scale,
+                     void* stream) {
+    if (!q || !k || !v || !q_scale || !k_scale || !v_scale || !o) return ATTN_ERR_NULL;
+    if (!head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+    if (H_kv < 1 || H_q < 1 || H_q % H_kv != 0) return ATTN_ERR_SHAPE;
+    if (!fits(B, H_q, Tq, D) || !fits(B, H_kv, Tk, D) || (long long)B * H_q > (1ll << 24) ||
+        (long long)B * H_q * ((Tq + 127) / 128) > (1ll << 31) - 64)
+        return ATTN_ERR_SHAPE;
+    // one (sequence, KV head) of codes is addressed through a 32-bit buffer range
+    if ((long long)Tk * D > (1ll << 31) - 1) return ATTN_ERR_SHAPE;
+    if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
+    if (o == q || o == k || o == v || (lse && ((void*)lse == q || (void*)lse == k || (void*)lse == v ||
+                                               (void*)lse == o)))
+        return ATTN_ERR_ALIAS;
+    FwdArgs a{q, k, v, key_padding_mask, o, lse, B, H_q, Tq, Tk, D, scale, stream};
+    a.H_kv = H_kv;
+    a.causal = causal != 0;
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    return finish(D == 64 ? launch_fwd_fp8_d64(a) : launch_fwd_fp8_d128(a));
+}
+
 size_t attn_decode_workspace_bytes(int B, int H_q, int H_kv, int T_max, int D) {
     if (B <= 0 || H_q <= 0 || H_kv <= 0 || T_max <= 0 || !head_dim_ok(D) || H_q % H_kv != 0)
         return 0;

@@ -203,17 +203,9 @@ __device__ __forceinline__ void advance(Cursor& c, const Lens& L, int HG, int n_
     }
 }
 
-// Buffer descriptor for the compiler's buffer-load builtins: `bytes` from p are
-// addressable, offsets past them read as zero without touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds_chunk, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_chunk, 16, voff,
                                              0, 0, 0);
-}
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
 // The transposing LDS reads of one V block's operands (2 k-steps x DB row blocks x

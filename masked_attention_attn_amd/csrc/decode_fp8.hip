@@ -37,13 +37,6 @@ __device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff)
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
 }
 
-// Four E4M3 codes (one dword, element i in byte i) -> four bf16 (two dwords), exact.
-__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
-    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-    const bf2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-    const bf2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
-    return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-}
 
 template <int D>
 __global__ __launch_bounds__(64)

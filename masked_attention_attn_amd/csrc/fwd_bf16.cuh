@@ -62,6 +62,19 @@
 // 2^(old - new) and the chunk redone.  Every weight used is therefore at most
 // 2^TAU.  Final O = acc / l and LSE = (mc + log2 l)·ln 2 are exact for any
 // reference, so this changes rounding only.
+//
+// FP8 variant (FP8 = true): Q, K and V arrive as E4M3 codes with one float32
+// scale per (sequence, head) (K and V: per KV head); the result is the
+// attention of the dequantised tensors, O in bf16 plus the LSE, which the
+// FP8 prefill the aiter ring-attention analysis describes does not return
+// (sglang PR 49078 analysis, section "1. aiter.py").  Sᵀ = K·Qᵀ runs on the
+// E4M3 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales:
+// exact products, fp32 sums) straight from the codes, K tiles staged in LDS as
+// codes (half the bytes); the Q and K scales fold into the softmax constant c.
+// V is converted to bf16 on its way into LDS (every E4M3 value is a bf16
+// value), so the P·V product, the softmax and the rescale logic are those of
+// the bf16 kernel; the V scale multiplies O in the epilogue.  The weights stay
+// bf16: E4M3 weights would cost more accuracy than the output tolerance.
 #pragma once
 
 #include "common.cuh"
@@ -89,16 +102,27 @@ template <int D> struct Tile;
 template <> struct Tile<64> { static constexpr int TK = 64; };
 template <> struct Tile<128> { static constexpr int TK = 64; };
 
-template <int D>
+template <int D, bool FP8>
 struct Lds {
     static constexpr int TK = Tile<D>::TK;
-    static constexpr int RB = D * 2;      // bytes per K or V row (unpadded, swizzled)
-    static constexpr int K_TILE = TK * D; // elements
-    static constexpr int V_TILE = TK * D;
+    static constexpr int RBK = FP8 ? D : D * 2;   // bytes per K row (E4M3 codes or bf16; unpadded, swizzled)
+    static constexpr int RBV = D * 2;             // bytes per V row (bf16 either way)
+    static constexpr int K_TILE = TK * RBK;       // bytes
+    static constexpr int V_TILE = TK * RBV;
     static constexpr int K_RING = 3, V_RING = 2;
-    static constexpr int ELEMS = K_RING * K_TILE + V_RING * V_TILE;
-    static constexpr int BYTES = ELEMS * (int)sizeof(bf16);
+    static constexpr int BYTES = K_RING * K_TILE + V_RING * V_TILE;
 };
+
+// Element type of Q, K and V in HBM.
+template <bool FP8> struct ElemT { typedef bf16 type; };
+template <> struct ElemT<true> { typedef uint8_t type; };
+template <bool FP8> using Elem = typename ElemT<FP8>::type;
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+// E4M3 x E4M3 32x32x64 product (format codes 0) with unit block scales (exponent 127 = 2^0).
+__device__ __forceinline__ f32x16 mfma_e4m3(i32x8 a, i32x8 b, f32x16 acc) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
+}
 
 // VARLEN = false: q/o [B, H, Tq, D], k/v [B, H_kv, Tk, D], mask [B, Tk] (or
 // none), lse [B, H, Tq].
@@ -106,19 +130,24 @@ struct Lds {
 // sequences back to back at the offsets cu_q / cu_k (B+1 entries, clamped to
 // [0, total]); lse [H, total_q]; no mask; Tq = the longest sequence (grid).
 // Query head h reads KV head h / (H / H_kv).
+// FP8 (dense layout only): q, k, v are E4M3 codes; qsc [B, H], ksc and vsc [B, H_kv].
 // CAUSAL: query i of a sequence sees keys j <= i + (Tk - Tq) only.  A workgroup's
 // key range ends at its last query's limit, the per-query limit is applied on
 // the key blocks that cross a wave's diagonal, and q-tiles run last-first
 // (the longest first, for the balance of the grid).
-template <int D, bool WRITE_LSE, bool VARLEN, bool CAUSAL>
+template <int D, bool WRITE_LSE, bool VARLEN, bool CAUSAL, bool FP8>
 __global__ __launch_bounds__(64 * Cfg<D>::NWAVE, 1)
-void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                     const bf16* __restrict__ v, const uint8_t* __restrict__ mask,
+void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restrict__ k,
+                     const Elem<FP8>* __restrict__ v, const uint8_t* __restrict__ mask,
                      bf16* __restrict__ o, float* __restrict__ lse,
-                     int H, int H_kv, int Tq, int Tk, float c, int n_qt, int total, int nparts, int tpp,
+                     int H, int H_kv, int Tq, int Tk, float c_in, int n_qt, int total, int nparts, int tpp,
                      const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
-                     int total_q, int total_k) {
-    using L = Lds<D>;
+                     int total_q, int total_k, const float* __restrict__ qsc,
+                     const float* __restrict__ ksc, const float* __restrict__ vsc) {
+    static_assert(!(FP8 && VARLEN), "the FP8 variant takes the dense layout");
+    using L = Lds<D, FP8>;
+    using ET = Elem<FP8>;
+    constexpr int ES = (int)sizeof(ET);   // bytes per Q/K/V element in HBM
     constexpr int NWAVE = Cfg<D>::NWAVE;
     constexpr int NT = 64 * NWAVE;        // threads per workgroup
     constexpr int NB = Cfg<D>::NB;        // 32-query column blocks per wave
@@ -128,13 +157,13 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     constexpr int CP = 4 * NB;            // pairs per 16-key chunk
     constexpr int TK = L::TK;             // keys per LDS tile
     constexpr int HALVES = TK / CK;       // compute steps per tile
-    constexpr int KSTEPS = D / 16;        // MFMA k-steps of K·Qᵀ
+    constexpr int KSTEPS = D / 16;        // MFMA k-steps of K·Qᵀ (bf16)
+    constexpr int KS8 = D / 64;           // MFMA k-steps of K·Qᵀ (E4M3)
     constexpr int PSTEPS = CK / 16;       // MFMA k-steps of Vᵀ·Pᵀ per step (2)
     constexpr int DB = D / 32;            // 32-row blocks of Oᵀ
     constexpr uint64_t TILE_BITS = TK == 64 ? ~0ull : ((1ull << TK) - 1);
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-    bf16* smem = reinterpret_cast<bf16*>(smem_raw);
     __shared__ int red_s[3 * NWAVE];
 
     // Workgroup -> (b, h, q-tile).  Workgroup i runs on XCD i % 8.
@@ -192,12 +221,20 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         l_row0 = (size_t)bh * Tq;
     }
     if (qt * BM >= Tq_) return;           // whole workgroup: past this sequence's queries
-    const bf16* qp = q + q_row0;
+    // Softmax constant (log2 units) and output factor: FP8 scores are those of the codes,
+    // times the Q and K scales; O is times the V scale.
+    float c = c_in, osc = 1.f;
+    if constexpr (FP8) {
+        c = c_in * qsc[bh] * ksc[b * H_kv + hk];
+        osc = vsc[b * H_kv + hk];
+    }
+    const ET* qp = q + q_row0;
     const uint8_t* mp = VARLEN ? nullptr : mask ? mask + (size_t)b * Tk_ : nullptr;
     // K/V buffer range ends after the last row, so rows >= Tk_ read as zero.
-    const uint32_t kv_bytes = Tk_ > 0 ? (uint32_t)((Tk_ - 1) * rsk + D) * (uint32_t)sizeof(bf16) : 0u;
+    const uint32_t kv_bytes = Tk_ > 0 ? (uint32_t)((Tk_ - 1) * rsk + D) * (uint32_t)ES : 0u;
     const i32x4_sgpr krs = make_rsrc(k + k_row0, kv_bytes);
     const i32x4_sgpr vrs = make_rsrc(v + k_row0, kv_bytes);
+    const __amdgpu_buffer_rsrc_t vrs8 = brsrc(v + k_row0, kv_bytes);    // FP8: V through registers
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -269,13 +306,25 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
     // ---- Q as the B operand of Sᵀ = K·Qᵀ: lane holds query (l%32), d = kk*16 + hl*8 + 0..7.
     // Rows past Tq are clamped to a valid row; their results are never stored.
+    // FP8: lane holds query (l%32), d = s*64 + hl*32 + 0..31 (E4M3 operand layout).
     bf16x8 qreg[NB][KSTEPS];
+    i32x8 q8[NB][KS8];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int row = min(q0 + nb * 32 + l32, Tq_ - 1);
+        if constexpr (FP8) {
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk)
-            qreg[nb][kk] = as_bf16x8(ldg128(qp + (size_t)row * rsq + kk * 16 + hl * 8));
+            for (int s = 0; s < KS8; ++s) {
+                const ET* p = qp + (size_t)row * rsq + s * 64 + hl * 32;
+                const u32x4 a = ldg128(p), a1 = ldg128(p + 16);
+                q8[nb][s] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3],
+                                  (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk)
+                qreg[nb][kk] = as_bf16x8(ldg128(qp + (size_t)row * rsq + kk * 16 + hl * 8));
+        }
     }
 
     // ---- tile loads straight into LDS: a tile is 8 KiB = 8 chunks of 1 KiB, wave w
@@ -284,35 +333,60 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // chunk p ^ k_swz(r); V takes key r, chunk p ^ v_swz(r).  Keys past Tk read
     // as zeros (the buffer range check covers the per-lane offset, which is why the
     // tile offset is added there and not to the scalar offset; they are masked).
-    constexpr int NCHUNK = TK * D * 2 / 1024;   // 1 KiB chunks per tile
-    constexpr int CPW = NCHUNK / NWAVE;         // chunks per wave and tile
-    static_assert(CPW * NWAVE == NCHUNK, "whole chunks per wave");
-    uint32_t k_voff[CPW], v_voff[CPW];
+    // FP8: K tiles are codes (k8_swz); V does not use these loads (see vload below).
+    constexpr int CPW = L::K_TILE / 1024 / NWAVE;    // K chunks per wave and tile
+    constexpr int CPWV = L::V_TILE / 1024 / NWAVE;   // V chunks per wave and tile
+    static_assert(CPW * NWAVE * 1024 == L::K_TILE && CPWV * NWAVE * 1024 == L::V_TILE,
+                  "whole chunks per wave");
+    uint32_t k_voff[CPW], v_voff[CPWV];
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
         const int o = (CPW * wave + i) * 1024 + lane * 16;
-        const int r = o / L::RB, pch = (o % L::RB) / 16;
+        const int r = o / L::RBK, pch = (o % L::RBK) / 16;
         const int kr = (r & ~31) | swap_bits23(r & 31);
-        k_voff[i] = (uint32_t)(kr * rsk + (pch ^ k_swz<D>(r)) * 8) * 2u;
+        if constexpr (FP8) k_voff[i] = (uint32_t)(kr * rsk + (pch ^ k8_swz<D>(r)) * 16);
+        else k_voff[i] = (uint32_t)(kr * rsk + (pch ^ k_swz<D>(r)) * 8) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < CPWV; ++i) {
+        const int o = (CPWV * wave + i) * 1024 + lane * 16;
+        const int r = o / L::RBV, pch = (o % L::RBV) / 16;
         v_voff[i] = (uint32_t)(r * rsk + (pch ^ v_swz<D>(r)) * 8) * 2u;
     }
     // Ring slots are counted from the first visited tile: tile t sits in K slot
     // (t - t_first) % K_RING and V slot (t - t_first) % V_RING; kcur / vcur
     // track the slots of the current tile.
-    auto kslot_b = [&](int sl) -> unsigned char* { return smem_raw + sl * L::K_TILE * 2; };
-    auto vslot_b = [&](int sl) -> unsigned char* { return smem_raw + (L::K_RING * L::K_TILE + sl * L::V_TILE) * 2; };
+    auto kslot_b = [&](int sl) -> unsigned char* { return smem_raw + sl * L::K_TILE; };
+    auto vslot_b = [&](int sl) -> unsigned char* { return smem_raw + L::K_RING * L::K_TILE + sl * L::V_TILE; };
     auto kslot = [&](int sl) -> const bf16* { return reinterpret_cast<const bf16*>(kslot_b(sl)); };
     auto vslot = [&](int sl) -> const bf16* { return reinterpret_cast<const bf16*>(vslot_b(sl)); };
     auto dma_k = [&](int t, int sl) {
 #pragma unroll
         for (int i = 0; i < CPW; ++i)
-            dma16(krs, kslot_b(sl) + (CPW * wave + i) * 1024, k_voff[i] + (uint32_t)t * TK * rsk * 2u, 0u);
+            dma16(krs, kslot_b(sl) + (CPW * wave + i) * 1024, k_voff[i] + (uint32_t)t * TK * rsk * (uint32_t)ES, 0u);
     };
     auto dma_v = [&](int t, int sl) {
 #pragma unroll
-        for (int i = 0; i < CPW; ++i)
-            dma16(vrs, vslot_b(sl) + (CPW * wave + i) * 1024, v_voff[i] + (uint32_t)t * TK * rsk * 2u, 0u);
+        for (int i = 0; i < CPWV; ++i)
+            dma16(vrs, vslot_b(sl) + (CPWV * wave + i) * 1024, v_voff[i] + (uint32_t)t * TK * rsk * 2u, 0u);
     };
+    // FP8 V: thread tid loads codes 16*vt_j .. +15 of tile row vt_r into registers a tile
+    // ahead and stores them, as bf16, as chunks 2*vt_j and 2*vt_j + 1 of that row of a bf16
+    // V tile (the layout dma_v gives), so the Vᵀ reads are those of the bf16 kernel.
+    constexpr int VJ = D / 16;
+    static_assert(!FP8 || NT == TK * VJ, "one 16-byte V load per thread and tile");
+    const int vt_r = tid / VJ, vt_j = tid % VJ;
+    const uint32_t v8_off = (uint32_t)(vt_r * rsk + vt_j * 16);
+    const int vw0 = vt_r * L::RBV + ((2 * vt_j) ^ v_swz<D>(vt_r)) * 16;
+    const int vw1 = vt_r * L::RBV + ((2 * vt_j + 1) ^ v_swz<D>(vt_r)) * 16;
+    auto vload = [&](int t) -> u32x4 { return bload16(vrs8, v8_off + (uint32_t)t * TK * rsk); };
+    auto vstore = [&](const u32x4& w, int sl) {
+        const u32x2 a0 = e4m3x4_to_bf16(w[0]), a1 = e4m3x4_to_bf16(w[1]);
+        const u32x2 a2 = e4m3x4_to_bf16(w[2]), a3 = e4m3x4_to_bf16(w[3]);
+        *reinterpret_cast<u32x4*>(vslot_b(sl) + vw0) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+        *reinterpret_cast<u32x4*>(vslot_b(sl) + vw1) = u32x4{a2[0], a2[1], a3[0], a3[1]};
+    };
+    u32x4 vraw = {};     // FP8: codes of the V tile two ahead of the current one
     int kcur = 0, vcur = 0;
     static_assert(L::K_RING == 3 && L::V_RING == 2, "slot arithmetic below");
     // Per-lane LDS offsets of the operand reads.
@@ -354,7 +428,24 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     auto k_opnd = [&](const bf16* krow, int kk) -> bf16x8 {
         return *reinterpret_cast<const bf16x8*>(krow + ((kk * 2) ^ kx) * 8);
     };
+    // FP8: K operand of k-step s (d = s*64 + hl*32 + 0..31) of key block hb in slot sl
+    const int kf8 = k8_swz<D>(l32);
+    auto k8_opnd = [&](int sl, int hb, int s) -> i32x8 {
+        const unsigned char* row = kslot_b(sl) + (hb * 32 + l32) * L::RBK;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(row + ((4 * s + 2 * hl) ^ kf8) * 16);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(row + ((4 * s + 2 * hl + 1) ^ kf8) * 16);
+        return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    };
     auto qk_full = [&](f32x16 (&S)[NB]) {     // first block of slot 0
+        if constexpr (FP8) {
+#pragma unroll
+            for (int s = 0; s < KS8; ++s) {
+                const i32x8 a = k8_opnd(0, 0, s);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) S[nb] = mfma_e4m3(a, q8[nb][s], s == 0 ? f32x16{} : S[nb]);
+            }
+            return;
+        }
         const bf16* kp_ = kblock(0, 0);
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
@@ -404,6 +495,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // they are read from LDS during the step before, so no step starts by
     // waiting on LDS.
     bf16x8 ka[KSTEPS];
+    i32x8 ka8[KS8];
     auto step = [&](int j, const int hf, f32x16 (&S)[NB], f32x16 (&Sn)[NB]) {
         const int u = u_first + j;
         const int T = u / HALVES;
@@ -466,6 +558,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         float cs[NB][PSTEPS];
         float xs[16][2], ps[16][2];
         auto rd_k = [&](int kk) { ka[kk] = k_opnd(kblock(knext, hf), kk); };
+        auto rd_k8 = [&](int s) { ka8[s] = k8_opnd(knext, hf, s); };
         auto rd_v = [&](int db) { va[db] = v_opnd(hf, 0, db); };
         auto rd_v1 = [&](int db) { va1[db] = v_opnd(hf, 1, db); };
         // pair pp: chunk k2 = pp / (4*NB), query block nb, elements i, i+1
@@ -534,6 +627,10 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) lsum[nb] += cs[nb][k2];
         };
+        auto qk8_one = [&](int qi) {    // FP8: qi = s*NB + nb
+            const int nb = qi % NB, s = qi / NB;
+            Sn[nb] = mfma_e4m3(ka8[s], q8[nb][s], s == 0 ? f32x16{} : Sn[nb]);
+        };
         auto qk_one = [&](int qi) {     // qi = kk*NB + nb
             const int nb = qi % NB, kk = qi / NB;
             if (kk == 0) {
@@ -553,15 +650,21 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
         if constexpr (D == 64) {
             // 22 slots: 0-7 QK(u+1), 10-13 PV(u,0) (chunk 0 packed by slot 9),
-            // 18-21 PV(u,1) (chunk 1 packed by slot 17); softmax in 0-17.
+            // 18-21 PV(u,1) (chunk 1 packed by slot 17); softmax in 0-17.  FP8: QK(u+1)
+            // is two E4M3 MFMAs, in slots 0 and 2.
 #pragma unroll
             for (int sl = 0; sl < 22; ++sl) {
                 if (sl == 4) { rd_v(0); rd_v(1); }
                 if (sl == 12) { rd_v1(0); rd_v1(1); }
-                if (sl == 14) { rd_k(0); rd_k(1); }      // QK(u+2) operands: after QK(u+1) issued
-                if (sl == 15) { rd_k(2); rd_k(3); }
-                if (sl < 8) qk_one(sl);
-                else if (sl >= 10 && sl < 14) pv_one(0, sl - 10);
+                if constexpr (FP8) {
+                    if (sl == 14) rd_k8(0);
+                    if (sl == 0 || sl == 2) qk8_one(sl / 2);
+                } else {
+                    if (sl == 14) { rd_k(0); rd_k(1); }      // QK(u+2) operands: after QK(u+1) issued
+                    if (sl == 15) { rd_k(2); rd_k(3); }
+                    if (sl < 8) qk_one(sl);
+                }
+                if (sl >= 10 && sl < 14) pv_one(0, sl - 10);
                 else if (sl >= 18) pv_one(1, sl - 18);
                 if (sl < NPP + 2) softmax_slot(sl);
                 fence();
@@ -572,22 +675,29 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             // D=128, one query block: 16 slots.  QK(u+1) is one chain of 8 MFMAs
             // (slots 0-5, 7, 9); PV(u,0) in 6, 8, 10, 11 once chunk 0 is packed
             // (slot 5); PV(u,1) in 12-15 once chunk 1 is packed (slot 9);
-            // softmax in 0-9.
+            // softmax in 0-9.  FP8: QK(u+1) is a chain of two E4M3 MFMAs (slots 0, 4).
 #pragma unroll
             for (int sl = 0; sl < 16; ++sl) {
                 if (sl == 1) { rd_v(0); rd_v(1); }
                 if (sl == 2) { rd_v(2); rd_v(3); }
                 if (sl == 7) { rd_v1(0); rd_v1(1); }
                 if (sl == 8) { rd_v1(2); rd_v1(3); }
-                if constexpr (HALVES == 2) {          // QK(u+2) operands, after QK(u+1) issued
-                    if (sl == 10) { rd_k(0); rd_k(1); }
-                    if (sl == 11) { rd_k(2); rd_k(3); }
-                    if (sl == 12) { rd_k(4); rd_k(5); }
-                    if (sl == 13) { rd_k(6); rd_k(7); }
+                if constexpr (FP8) {
+                    static_assert(HALVES == 2, "K of block u+2 is in the next tile");
+                    if (sl == 10) rd_k8(0);
+                    if (sl == 11) rd_k8(1);
+                    if (sl == 0 || sl == 4) qk8_one(sl / 4);
+                } else {
+                    if constexpr (HALVES == 2) {          // QK(u+2) operands, after QK(u+1) issued
+                        if (sl == 10) { rd_k(0); rd_k(1); }
+                        if (sl == 11) { rd_k(2); rd_k(3); }
+                        if (sl == 12) { rd_k(4); rd_k(5); }
+                        if (sl == 13) { rd_k(6); rd_k(7); }
+                    }
+                    if (sl < 6) qk_one(sl);
+                    else if (sl == 7) qk_one(6);
+                    else if (sl == 9) qk_one(7);
                 }
-                if (sl < 6) qk_one(sl);
-                else if (sl == 7) qk_one(6);
-                else if (sl == 9) qk_one(7);
                 if (sl == 6) pv_one(0, 0);
                 else if (sl == 8) pv_one(0, 1);
                 else if (sl == 10) pv_one(0, 2);
@@ -606,10 +716,15 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             wait_vmem();            // this wave's part of K_{T+2} and V_{T+1} has landed
             __syncthreads();
             if (T + 3 <= t_last) dma_k(T + 3, kcur);     // into the slot tile T leaves
-            if (T + 2 <= t_last) dma_v(T + 2, vcur);
+            if constexpr (FP8) {
+                if (T + 2 <= t_last) vstore(vraw, vcur);   // codes loaded during tile T-1
+                if (T + 3 <= t_last) vraw = vload(T + 3);
+            } else {
+                if (T + 2 <= t_last) dma_v(T + 2, vcur);
+            }
             kcur = knext;
             vcur ^= 1;
-            if constexpr (HALVES == 1) {    // D = 128: K of block u+2 = tile T+2, just published
+            if constexpr (HALVES == 1 && !FP8) {    // K of block u+2 = tile T+2, just published
 #pragma unroll
                 for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = k_opnd(kblock(kcur == 2 ? 0 : kcur + 1, 0), kk);
             }
@@ -622,23 +737,39 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
     if (nsteps > 0) {
         f32x16 sA[NB], sB[NB];
+        u32x4 vraw1 = {};
         dma_k(t_first, 0);
-        dma_v(t_first, 0);
+        if constexpr (FP8) vraw = vload(t_first);
+        else dma_v(t_first, 0);
         if (t_first + 1 <= t_last) {
             dma_k(t_first + 1, 1);
-            dma_v(t_first + 1, 1);
+            if constexpr (FP8) vraw1 = vload(t_first + 1);
+            else dma_v(t_first + 1, 1);
         }
         if (holes) {
             padf = pad_flag(t_first);
             padf_nxt = pad_flag(min(t_first + 1, t_last));
         }
         wait_vmem();
+        if constexpr (FP8) {
+            vstore(vraw, 0);
+            if (t_first + 1 <= t_last) vstore(vraw1, 1);
+        }
         __syncthreads();
-        if (t_first + 2 <= t_last) dma_k(t_first + 2, 2);   // waited for at the end of tile t_first
+        if (t_first + 2 <= t_last) {     // waited for at the end of tile t_first
+            dma_k(t_first + 2, 2);
+            if constexpr (FP8) vraw = vload(t_first + 2);
+        }
         qk_full(sA);
+        if constexpr (FP8) {
+            static_assert(!FP8 || HALVES == 2, "K of block u_first + 1 is in slot 0");
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk)     // K of block u_first + 1
-            ka[kk] = HALVES == 1 ? k_opnd(kblock(1, 0), kk) : k_opnd(kblock(0, 1), kk);
+            for (int s = 0; s < KS8; ++s) ka8[s] = k8_opnd(0, 1, s);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk)     // K of block u_first + 1
+                ka[kk] = HALVES == 1 ? k_opnd(kblock(1, 0), kk) : k_opnd(kblock(0, 1), kk);
+        }
         int j = 0;
         for (; j + 1 < nsteps; j += 2) {
             step(j, 0, sA, sB);
@@ -651,7 +782,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const float lt = pair_sum(lsum[nb]);
-        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        const float inv = lt > 0.f ? osc / lt : 0.f;
         const int qi = q0 + nb * 32 + l32;
         if (qi < Tq_) {
             bf16* orow = o + q_row0 + (size_t)qi * rsq;
@@ -670,10 +801,11 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
 }
 
-template <int D, bool WRITE_LSE, bool VARLEN, bool CAUSAL>
+template <int D, bool WRITE_LSE, bool VARLEN, bool CAUSAL, bool FP8 = false>
 hipError_t launch_one(const FwdArgs& a) {
-    using L = Lds<D>;
-    auto kern = fwd_bf16_kernel<D, WRITE_LSE, VARLEN, CAUSAL>;
+    using L = Lds<D, FP8>;
+    using ET = Elem<FP8>;
+    auto kern = fwd_bf16_kernel<D, WRITE_LSE, VARLEN, CAUSAL, FP8>;
     // LDS above 64 KiB must be opted into once per kernel (thread-safe static init).
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
@@ -694,9 +826,9 @@ hipError_t launch_one(const FwdArgs& a) {
     }
     const float c = a.scale * kLog2e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * Cfg<D>::NWAVE), L::BYTES, (hipStream_t)a.stream,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.mask,
+                       (const ET*)a.q, (const ET*)a.k, (const ET*)a.v, a.mask,
                        (bf16*)a.o, a.lse, a.H, a.H_kv > 0 ? a.H_kv : a.H, a.Tq, a.Tk, c, n_qt, total, nparts, tpp,
-                       a.cu_q, a.cu_k, a.total_q, a.total_k);
+                       a.cu_q, a.cu_k, a.total_q, a.total_k, a.q_scale, a.k_scale, a.v_scale);
     return hipGetLastError();
 }
 
@@ -710,6 +842,14 @@ hipError_t launch_lse(const FwdArgs& a) {
 template <int D>
 hipError_t launch(const FwdArgs& a) {
     return a.lse ? launch_lse<D, true>(a) : launch_lse<D, false>(a);
+}
+
+// E4M3 inputs, dense layout (GQA, padding and causal as in the bf16 kernel).
+template <int D>
+hipError_t launch_fp8(const FwdArgs& a) {
+    if (a.lse)
+        return a.causal ? launch_one<D, true, false, true, true>(a) : launch_one<D, true, false, false, true>(a);
+    return a.causal ? launch_one<D, false, false, true, true>(a) : launch_one<D, false, false, false, true>(a);
 }
 
 }  // namespace fwdk

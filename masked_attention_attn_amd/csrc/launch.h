@@ -25,6 +25,11 @@ struct FwdArgs {
     const int32_t* cu_q = nullptr;
     const int32_t* cu_k = nullptr;
     int total_q = 0, total_k = 0;
+    // E4M3 inputs (launch_fwd_fp8_*): q, k, v are codes; q_scale [B, H], k_scale and
+    // v_scale [B, H_kv] float32
+    const float* q_scale = nullptr;
+    const float* k_scale = nullptr;
+    const float* v_scale = nullptr;
 };
 
 constexpr int kMaxMergeChunks = 32;
@@ -88,6 +93,8 @@ struct AppendFp8Args {
 
 hipError_t launch_fwd_bf16_d64(const FwdArgs& a);
 hipError_t launch_fwd_bf16_d128(const FwdArgs& a);
+hipError_t launch_fwd_fp8_d64(const FwdArgs& a);
+hipError_t launch_fwd_fp8_d128(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_merge_bf16(const MergeArgs& a);
 hipError_t launch_merge_f32(const MergeArgs& a);

@@ -21,6 +21,10 @@ __device__ __forceinline__ int swap_bits23(int r) {
 // 64-bank model prefers.
 template <int D> __device__ __forceinline__ int k_swz(int r) { return D == 64 ? (r & 7) : (r & 15); }
 template <int D> __device__ __forceinline__ int v_swz(int r) { return D == 64 ? 2 * (r & 3) : 4 * (r & 3); }
+// E4M3 K rows (D bytes, D/16 chunks): lane l reads chunks 4s + 2(l/32) and the next one of
+// row l%32, two 16-byte reads per MFMA operand; chunk c of row r sits at c ^ k8_swz(r), which
+// leaves both reads free of bank conflicts.
+template <int D> __device__ __forceinline__ int k8_swz(int r) { return D == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -64,6 +68,24 @@ __device__ __forceinline__ void dma16(i32x4_sgpr r, unsigned char* lds_base, uin
                  : "s"(m0), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
                  : "memory");
 }
+// Buffer descriptor for the compiler's buffer-load builtins: `bytes` from p are
+// addressable, offsets past them read as zero without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+// Four E4M3 codes (one dword, element i in byte i) -> four bf16 (two dwords), exact: every
+// E4M3 value is a bf16 value.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    const bf2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const bf2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
 // Wait for this wave's outstanding global loads (including LDS-direct ones).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

@@ -260,3 +260,28 @@ def test_fp8_validation(lib):
     assert lib.kv_append_fp8(A, B_, KS, VS, L, C, O, 2, 2, 16, 64, 7, None) == 3
     assert lib.kv_append_fp8(A, B_, KS, VS, L, C, O, 2, 2, 0, 64, 1, None) == 2
     assert lib.kv_append_fp8(A, A, KS, VS, L, C, O, 2, 2, 16, 64, 1, None) == 8
+
+
+def test_prefill_fp8_validation(lib):
+    QS, KS, VS = 0x70000, 0x80000, 0x90000
+
+    def pf(**kw):
+        a = dict(q=A, k=B_, v=C, qs=QS, ks=KS, vs=VS, m=0, o=O, lse=L, B=2, Hq=8, Hkv=2, Tq=100, Tk=130, D=128,
+                 causal=1, scale=0.088)
+        a.update(kw)
+        return lib.attn_prefill_fp8(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["m"], a["o"], a["lse"],
+                                    a["B"], a["Hq"], a["Hkv"], a["Tq"], a["Tk"], a["D"], a["causal"], a["scale"],
+                                    None)
+    assert pf(qs=0) == 1
+    assert pf(ks=0) == 1
+    assert pf(vs=0) == 1
+    assert pf(o=0) == 1
+    assert pf(D=96) == 3
+    assert pf(Hq=6, Hkv=4) == 2
+    assert pf(Hkv=0) == 2
+    assert pf(Tq=0) == 2
+    assert pf(Tk=(1 << 24) + 1) == 2           # Tk·D beyond the 32-bit range of one head
+    assert pf(scale=float("nan")) == 6
+    assert pf(k=B_ + 4) == 7
+    assert pf(o=A) == 8
+    assert pf(lse=C) == 8

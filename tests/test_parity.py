@@ -658,3 +658,69 @@ def test_gqa_decode_b32_fp8_sampled_heads(ma):
                                  lens.cpu().numpy(), w.scale, heads=heads)
     check_attn(torch.stack([o[b, h, 0] for b, h in heads]), torch.stack([l[b, h] for b, h in heads]),
                Or, Lr, torch.bfloat16, "fp8 decode sampled heads")
+
+
+# ---- FP8 (E4M3) prefill with LSE ------------------------------------------------------------
+
+PREFILL_FP8 = [
+    # B, H_q, H_kv, Tq, Tk, D, causal, valid key lengths (None = no mask)
+    (1, 1, 1, 1, 1, 64, False, None),
+    (1, 2, 1, 31, 31, 128, True, None),
+    (2, 4, 2, 300, 333, 64, False, [333, 200]),
+    (2, 8, 2, 257, 257, 128, True, None),
+    (1, 2, 2, 100, 700, 64, True, None),          # a chunk after a cached prefix
+    (1, 2, 1, 600, 200, 128, True, None),         # more queries than keys: early rows see nothing
+    (2, 6, 3, 513, 513, 64, True, [513, 300]),    # causal and key padding together
+    (1, 8, 1, 600, 900, 128, False, [850]),
+    (2, 4, 4, 1000, 1000, 64, False, [1000, 0]),  # a fully padded sequence
+    (1, 4, 2, 64, 4000, 128, False, [3990]),      # long key range, one q-tile
+]
+
+
+def _fp8_prefill(ma, w, causal, **kw):
+    m = w.mask.to(DEV) if w.mask is not None else None
+    r = ma.attn_prefill_fp8(w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), w.q_scale.to(DEV), w.k_scale.to(DEV),
+                            w.v_scale.to(DEV), m, causal, w.scale, **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+@pytest.mark.parametrize("case", PREFILL_FP8)
+def test_prefill_fp8(ma, case):
+    B, Hq, Hkv, Tq, Tk, D, causal, valid = case
+    w = W.make_prefill_fp8(B, Hq, Hkv, Tq, Tk, D, valid=valid, seed=Tq + Hq + D)
+    o, l = _fp8_prefill(ma, w, causal)
+    Or, Lr = oracle.prefill_fp8(w.q, w.k, w.v, w.q_scale, w.k_scale, w.v_scale, w.mask, causal, w.scale)
+    check_attn(o, l, Or, Lr, torch.bfloat16, f"fp8 prefill {case}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_fp8_lse_flag_and_v_scale_bitwise(ma, D):
+    # O does not depend on whether the LSE is written; doubling the V scale doubles O exactly
+    # (a power-of-two factor on the final reciprocal) and leaves the LSE bit-identical
+    w = W.make_prefill_fp8(2, 4, 2, 300, 450, D, valid=[450, 200], seed=3)
+    o1, l1 = _fp8_prefill(ma, w, True)
+    o2 = _fp8_prefill(ma, w, True, want_lse=False)
+    w.v_scale = w.v_scale * 2
+    o3, l3 = _fp8_prefill(ma, w, True)
+    assert torch.equal(o1, o2)
+    assert torch.equal(o3, o1 * 2) and torch.equal(l3, l1)
+
+
+def test_prefill_fp8_p11616_sampled_rows(ma):
+    """The P = 11,616 patch shape with E4M3 inputs, sampled rows of every head."""
+    w = W.patch_p11616_fp8()
+    o, l = _fp8_prefill(ma, w, False)
+    rows = [0, 1, 63, 64, 255, 256, 5807, 11599, 11600, 11615] + list(range(11, 11616, 997))
+    Or, Lr = oracle.prefill_fp8(w.q, w.k, w.v, w.q_scale, w.k_scale, w.v_scale, w.mask, False, w.scale,
+                                rows=rows)
+    check_attn(o[:, :, rows], l[:, :, rows], Or, Lr, torch.bfloat16, "fp8 P11616 sampled rows")
+
+
+def test_gqa_causal_prefill_8192_fp8_sampled_rows(ma):
+    """The causal GQA 8,192-token prompt with E4M3 inputs, sampled rows of every head."""
+    w = W.gqa_causal_prefill_8192_fp8()
+    o, l = _fp8_prefill(ma, w, True)
+    rows = [0, 1, 31, 32, 255, 256, 4095, 4096, 8191] + list(range(7, 8192, 613))
+    Or, Lr = oracle.prefill_fp8(w.q, w.k, w.v, w.q_scale, w.k_scale, w.v_scale, None, True, w.scale, rows=rows)
+    check_attn(o[:, :, rows], l[:, :, rows], Or, Lr, torch.bfloat16, "fp8 causal 8192 sampled rows")

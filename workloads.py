@@ -129,6 +129,20 @@ class DecodeFp8:
     name: str = ""
 
 
+@dataclass
+class PrefillFp8:
+    """Prefill inputs as E4M3 codes with float32 scales per (b, head)."""
+    q: torch.Tensor        # [B, H_q, Tq, D] uint8 (E4M3 codes)
+    k: torch.Tensor        # [B, H_kv, Tk, D] uint8
+    v: torch.Tensor
+    q_scale: torch.Tensor  # [B, H_q] float32
+    k_scale: torch.Tensor  # [B, H_kv] float32
+    v_scale: torch.Tensor
+    mask: Optional[torch.Tensor]  # uint8 [B, Tk], nonzero = padded; None = no padding
+    scale: float
+    name: str = ""
+
+
 def _gen(seed: int) -> torch.Generator:
     g = torch.Generator()
     g.manual_seed(seed)
@@ -292,6 +306,31 @@ def make_gqa_prefill(B, H_q, H_kv, Tq, Tk, D, dtype=torch.bfloat16, *, valid=Non
     return Prefill(q, k, v, mask, float(scale), name)
 
 
+def make_prefill_fp8(B, H_q, H_kv, Tq, Tk, D, *, valid=None, amp=1.0, seed=0, scale=None,
+                     name="") -> PrefillFp8:
+    """E4M3 prefill inputs whose dequantised values are about N(0, amp^2): each (b, head) of Q, K
+    and V gets a scale amp * 2^-e with e ~ U{2..6}, and its codes are N(0,1) * 2^e cast to
+    float8_e4m3fn (round to nearest even; |N * 2^e| stays far below 448).  Draw order: Q, K, V
+    scale exponents, then Q, K, V."""
+    g = _gen(seed)
+    eq = torch.randint(2, 7, (B, H_q), generator=g)
+    ek = torch.randint(2, 7, (B, H_kv), generator=g)
+    ev = torch.randint(2, 7, (B, H_kv), generator=g)
+
+    def codes(shape, e):
+        x = torch.randn(*shape, generator=g) * torch.exp2(e.float())[:, :, None, None]
+        return x.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+
+    q = codes((B, H_q, Tq, D), eq)
+    k = codes((B, H_kv, Tk, D), ek)
+    v = codes((B, H_kv, Tk, D), ev)
+    sc = lambda e: (amp * torch.exp2(-e.float())).contiguous()
+    mask = mask_from_valid_lengths(valid, Tk) if valid is not None else None
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return PrefillFp8(q, k, v, sc(eq), sc(ek), sc(ev), mask, float(scale), name)
+
+
 # ---- the five named workloads -------------------------------------------------
 
 def fp32_masked_t512(seed=0) -> Prefill:
@@ -367,3 +406,16 @@ def gqa_decode_b32_fp8(seed=0) -> DecodeFp8:
     """The GQA decode workload (B32, H_q 32 / H_kv 8, D128, len U[512, 8192]) with an E4M3 cache."""
     return make_decode_fp8(32, 32, 8, 128, 512, 8192, seed=seed,
                            name="E4M3-cache GQA decode B32 Hq32 Hkv8 D128, len U[512,8192] + 1 appended")
+
+
+def patch_p11616_fp8(seed=0) -> PrefillFp8:
+    """The P = 11,616 patch self-attention shape (B1 H16 D64, last 16 keys padded, values about
+    N(0,1)*0.5) with E4M3 inputs."""
+    return make_prefill_fp8(1, 16, 16, 11616, 11616, 64, valid=[11616 - 16], amp=0.5, seed=seed,
+                            name="E4M3 patch self-attention B1 H16 P11616 D64, 16 padded keys")
+
+
+def gqa_causal_prefill_8192_fp8(seed=0) -> PrefillFp8:
+    """The causal GQA prompt pass (B1, H_q 32 / H_kv 8, D128, 8,192 tokens) with E4M3 inputs."""
+    return make_prefill_fp8(1, 32, 8, 8192, 8192, 128, seed=seed,
+                            name="E4M3 causal GQA prefill B1 Hq32 Hkv8 D128, 8192-token prompt")
