@@ -765,3 +765,66 @@ def test_prefill_fp8_scale_roles():
     keep = np.ones((B, Hkv * G), bool)
     keep[1, 3] = False
     assert np.array_equal(O3[keep], O1[keep]) and np.array_equal(L3[keep], L1[keep])
+
+
+# ---- INT8 KV cache ------------------------------------------------------------------------
+
+def test_quantize_int8_ties_saturation_and_library():
+    q = oracle.quantize_int8
+    s = np.float32(1.0)
+    vals = np.array([0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5, 127.4, 127.5, 300.0, -300.0, 0.49999997,
+                     -0.0, 3.0, -126.5], dtype=np.float32)
+    assert q(vals, s).tolist() == [0, 2, 2, 0, -2, -2, 126, 127, 127, 127, -127, 0, 0, 3, -126]
+    # every code round-trips through a power-of-two scale (exact products)
+    codes = np.arange(-127, 128).astype(np.int8)
+    assert np.array_equal(q(oracle.dequantize_int8(codes, 0.125), np.float32(0.125)), codes)
+    # library cross-check: torch.round rounds half to even, on the float32 quotient
+    x = np.random.default_rng(4).standard_normal(50000).astype(np.float32) * 90
+    sc = np.float32(0.61)
+    ref = torch.round(torch.from_numpy(x) / torch.tensor(sc)).clamp(-127, 127).to(torch.int8).numpy()
+    assert np.array_equal(q(x, sc), ref)
+
+
+def test_decode_int8kv_is_decode_of_dequantised_cache_and_brute_force():
+    r = _rng(23)
+    B, Hkv, G, D, T = 2, 2, 3, 4, 10
+    k8 = r.integers(-128, 128, (B, Hkv, T, D)).astype(np.int8)
+    v8 = r.integers(-128, 128, (B, Hkv, T, D)).astype(np.int8)
+    ks = r.uniform(0.002, 0.02, (B, Hkv))
+    vs = r.uniform(0.005, 0.05, (B, Hkv))
+    q = r.standard_normal((B, Hkv * G, 1, D))
+    lens = [0, 9]
+    O, L = oracle.decode_int8kv(q, k8, v8, ks, vs, lens, 0.7)
+    for b in range(B):
+        for h in range(Hkv * G):
+            g = h // G
+            keys = [[int(k8[b, g, t, d]) * ks[b, g] for d in range(D)] for t in range(lens[b])]
+            vv = [[int(v8[b, g, t, d]) * vs[b, g] for d in range(D)] for t in range(lens[b])]
+            o, l = brute.attend_row(q[b, h, 0].tolist(), keys, vv, [False] * len(keys), 0.7)
+            if l == -math.inf:
+                assert L[b, h] == -np.inf and np.all(O[b, h, 0] == 0)
+            else:
+                assert abs(L[b, h] - l) <= 1e-12 and np.max(np.abs(O[b, h, 0] - np.array(o))) <= 1e-12
+
+
+def test_kv_append_int8_writes_only_the_quantised_slot():
+    r = _rng(24)
+    B, Hkv, T, D = 3, 2, 8, 8
+    kc = r.integers(-128, 128, (B, Hkv, T, D)).astype(np.int8)
+    vc = r.integers(-128, 128, (B, Hkv, T, D)).astype(np.int8)
+    ks = r.uniform(0.01, 0.05, (B, Hkv)).astype(np.float32)
+    vs = r.uniform(0.01, 0.05, (B, Hkv)).astype(np.float32)
+    kn = r.standard_normal((B, Hkv, 1, D)).astype(np.float32)
+    vn = r.standard_normal((B, Hkv, 1, D)).astype(np.float32)
+    lens = np.array([0, 5, 7])
+    kc2, vc2, l2 = oracle.kv_append_int8(kc, vc, ks, vs, lens, kn, vn)
+    assert l2.tolist() == [1, 6, 8]
+    for b in range(B):
+        t = lens[b]
+        # written codes: within half a step of x, x clamped to the +-127 steps
+        for c2, xn, sc in ((kc2, kn, ks), (vc2, vn, vs)):
+            lim = 127.0 * sc[b][:, None].astype(np.float64)
+            err = np.abs(c2[b, :, t].astype(np.float64) * sc[b][:, None] - np.clip(xn[b, :, 0], -lim, lim))
+            assert np.all(err <= sc[b][:, None] * 0.5 + 1e-7)
+        other = [i for i in range(T) if i != t]
+        assert np.array_equal(kc2[b, :, other], kc[b, :, other]) and np.array_equal(vc2[b, :, other], vc[b, :, other])
