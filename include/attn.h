@@ -310,6 +310,29 @@ int attn_decode_fp8kv(const void* q, const void* k_cache, const void* v_cache,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * INT8 KV cache: the two FP8 calls above with symmetric INT8 codes, another of
+ * the cache formats LLM inference memory accounting 2/10 lists (section
+ * "18. KV Cache Quantization").
+ *   k_cache, v_cache  [B, H_kv, T_max, D] int8: code q stands for q x scale
+ *   k_scale, v_scale  as for the FP8 cache
+ * kv_append_int8 writes code = clamp(rint(x / scale), -127, 127): an IEEE
+ * float32 division, the nearest integer with ties to even, the symmetric range
+ * (-128 is never written; a -128 in the cache decodes as -128).
+ * attn_decode_int8kv returns attn_decode over the dequantised cache (codes are
+ * converted exactly to bf16).  Lengths, lse, workspace, sizes and errors as
+ * the FP8 calls.
+ */
+int kv_append_int8(void* k_cache, void* v_cache, const float* k_scale, const float* v_scale,
+                   int32_t* cache_seqlens, const void* k_new, const void* v_new,
+                   int B, int H_kv, int T_max, int D, int new_dtype, void* stream);
+
+int attn_decode_int8kv(const void* q, const void* k_cache, const void* v_cache,
+                       const float* k_scale, const float* v_scale,
+                       const int32_t* cache_seqlens, void* o, float* lse,
+                       int B, int H_q, int H_kv, int T_max, int D, float scale,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_prefill_fp8 — attn_prefill on E4M3 inputs, with the LSE.
  *
  * The aiter ring-attention analysis (sglang PR 49078 analysis, section

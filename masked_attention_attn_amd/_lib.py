@@ -32,7 +32,7 @@ STATUS = {
 EXPORTS = ("attn_fwd_masked", "attn_fwd_lse", "attn_fwd_varlen", "attn_merge_lse", "kv_append",
            "attn_decode", "attn_decode_workspace_bytes", "kv_append_paged", "attn_decode_paged",
            "attn_prefill", "attn_prefill_varlen", "kv_append_fp8", "attn_decode_fp8kv", "attn_prefill_fp8",
-           "attn_status_string")
+           "kv_append_int8", "attn_decode_int8kv", "attn_status_string")
 
 _lib = None
 
@@ -64,6 +64,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kv_append_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
     lib.kv_append_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
     lib.attn_decode_fp8kv.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, S, P]
+    lib.kv_append_int8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
+    lib.attn_decode_int8kv.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, S, P]
     lib.attn_prefill_fp8.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
     lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, S, P]
     lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -72,7 +74,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_status_string.restype = ctypes.c_char_p
     for name in ("attn_fwd_masked", "attn_fwd_lse", "attn_fwd_varlen", "attn_merge_lse", "kv_append",
                  "attn_decode", "kv_append_paged", "attn_decode_paged", "attn_prefill", "attn_prefill_varlen",
-                 "kv_append_fp8", "attn_decode_fp8kv", "attn_prefill_fp8"):
+                 "kv_append_fp8", "attn_decode_fp8kv", "attn_prefill_fp8", "kv_append_int8",
+                 "attn_decode_int8kv"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -431,13 +434,13 @@ def attn_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causa
     return (out, lse) if want_lse else out
 
 
-def _fp8_cache_args(k_cache, v_cache, k_scale, v_scale, cache_seqlens):
+def _q8_cache_args(k_cache, v_cache, k_scale, v_scale, cache_seqlens, code_dtype, what):
     for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (k_scale, "k_scale"), (v_scale, "v_scale"),
                  (cache_seqlens, "cache_seqlens")):
         _dev(t, n)
-    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8 or k_cache.dim() != 4 \
+    if k_cache.dtype != code_dtype or v_cache.dtype != code_dtype or k_cache.dim() != 4 \
             or v_cache.shape != k_cache.shape:
-        raise ValueError("k_cache / v_cache must be uint8 [B, H_kv, T_max, D] (E4M3 codes) of one shape")
+        raise ValueError(f"k_cache / v_cache must be {code_dtype} [B, H_kv, T_max, D] ({what}) of one shape")
     B, Hkv, Tmax, D = k_cache.shape
     if k_scale.shape != (B, Hkv) or v_scale.shape != (B, Hkv) or k_scale.dtype != torch.float32 \
             or v_scale.dtype != torch.float32:
@@ -447,24 +450,21 @@ def _fp8_cache_args(k_cache, v_cache, k_scale, v_scale, cache_seqlens):
     return B, Hkv, Tmax, D
 
 
-def kv_append_fp8(k_cache, v_cache, k_scale, v_scale, cache_seqlens, k_new, v_new):
-    """Quantise k_new/v_new [B, H_kv, 1, D] (bf16 or float32) into slot cache_seqlens[b] of the
-    E4M3 caches, then increment cache_seqlens (in place)."""
-    B, Hkv, Tmax, D = _fp8_cache_args(k_cache, v_cache, k_scale, v_scale, cache_seqlens)
+def _q8_append(fn, code_dtype, what, k_cache, v_cache, k_scale, v_scale, cache_seqlens, k_new, v_new):
+    B, Hkv, Tmax, D = _q8_cache_args(k_cache, v_cache, k_scale, v_scale, cache_seqlens, code_dtype, what)
     _dev(k_new, "k_new")
     _dev(v_new, "v_new")
     if k_new.shape != (B, Hkv, 1, D) or v_new.shape != (B, Hkv, 1, D) or v_new.dtype != k_new.dtype:
         raise ValueError("k_new / v_new must be [B, H_kv, 1, D] of one dtype")
-    _check("kv_append_fp8", load().kv_append_fp8(
+    _check(fn, getattr(load(), fn)(
         _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(cache_seqlens), _ptr(k_new),
         _ptr(v_new), B, Hkv, Tmax, D, _dtype_code(k_new), _stream(k_cache.device)))
 
 
-def attn_decode_fp8kv(q, k_cache, v_cache, k_scale, v_scale, cache_seqlens, scale=None, out=None, lse=None,
-                      workspace=None, want_lse: bool = False):
-    """attn_decode against E4M3 caches with per-(sequence, KV head) scales; q [B, H_q, 1, D] bf16."""
+def _q8_decode(fn, code_dtype, what, q, k_cache, v_cache, k_scale, v_scale, cache_seqlens, scale, out, lse,
+               workspace, want_lse):
     _dev(q, "q")
-    B, Hkv, Tmax, D = _fp8_cache_args(k_cache, v_cache, k_scale, v_scale, cache_seqlens)
+    B, Hkv, Tmax, D = _q8_cache_args(k_cache, v_cache, k_scale, v_scale, cache_seqlens, code_dtype, what)
     if q.dim() != 4 or q.shape[0] != B or q.shape[2] != 1 or q.shape[3] != D or q.dtype != torch.bfloat16:
         raise ValueError("q must be bfloat16 [B, H_q, 1, D]")
     Hq = q.shape[1]
@@ -479,11 +479,39 @@ def attn_decode_fp8kv(q, k_cache, v_cache, k_scale, v_scale, cache_seqlens, scal
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace")
     nbytes = workspace.numel() * workspace.element_size()
-    _check("attn_decode_fp8kv", load().attn_decode_fp8kv(
+    _check(fn, getattr(load(), fn)(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(cache_seqlens), _ptr(out),
         _ptr(lse if want_lse else None), B, Hq, Hkv, Tmax, D, float(scale), _ptr(workspace), nbytes,
         _stream(q.device)))
     return (out, lse) if want_lse else out
+
+
+def kv_append_fp8(k_cache, v_cache, k_scale, v_scale, cache_seqlens, k_new, v_new):
+    """Quantise k_new/v_new [B, H_kv, 1, D] (bf16 or float32) into slot cache_seqlens[b] of the
+    E4M3 caches (uint8 codes), then increment cache_seqlens (in place)."""
+    _q8_append("kv_append_fp8", torch.uint8, "E4M3 codes", k_cache, v_cache, k_scale, v_scale, cache_seqlens,
+               k_new, v_new)
+
+
+def attn_decode_fp8kv(q, k_cache, v_cache, k_scale, v_scale, cache_seqlens, scale=None, out=None, lse=None,
+                      workspace=None, want_lse: bool = False):
+    """attn_decode against E4M3 caches with per-(sequence, KV head) scales; q [B, H_q, 1, D] bf16."""
+    return _q8_decode("attn_decode_fp8kv", torch.uint8, "E4M3 codes", q, k_cache, v_cache, k_scale, v_scale,
+                      cache_seqlens, scale, out, lse, workspace, want_lse)
+
+
+def kv_append_int8(k_cache, v_cache, k_scale, v_scale, cache_seqlens, k_new, v_new):
+    """Quantise k_new/v_new [B, H_kv, 1, D] (bf16 or float32) into slot cache_seqlens[b] of the
+    symmetric INT8 caches (int8 codes), then increment cache_seqlens (in place)."""
+    _q8_append("kv_append_int8", torch.int8, "INT8 codes", k_cache, v_cache, k_scale, v_scale, cache_seqlens,
+               k_new, v_new)
+
+
+def attn_decode_int8kv(q, k_cache, v_cache, k_scale, v_scale, cache_seqlens, scale=None, out=None, lse=None,
+                       workspace=None, want_lse: bool = False):
+    """attn_decode against INT8 caches with per-(sequence, KV head) scales; q [B, H_q, 1, D] bf16."""
+    return _q8_decode("attn_decode_int8kv", torch.int8, "INT8 codes", q, k_cache, v_cache, k_scale, v_scale,
+                      cache_seqlens, scale, out, lse, workspace, want_lse)
 
 
 def attn_prefill_fp8(q, k, v, q_scale, k_scale, v_scale, key_padding_mask=None, causal=False, scale=None,

@@ -42,7 +42,7 @@ EXTRA = {
     "fwd_fp8_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans", "-mllvm", "-disable-machine-sink"],
     "fwd_fp8_d128.hip": ["-fno-honor-nans", "-mllvm", "-disable-machine-sink"],
     "decode_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
-    "decode_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+    "decode_q8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
 }
 
 

@@ -85,6 +85,44 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* cu
     return finish(D == 64 ? launch_fwd_bf16_d64(a) : launch_fwd_bf16_d128(a));
 }
 
+// 8-bit caches (E4M3 codes, or INT8 codes when int8): shared checks of the append and decode calls.
+int q8_append(void* k_cache, void* v_cache, const float* k_scale, const float* v_scale,
+              int32_t* cache_seqlens, const void* k_new, const void* v_new, int B, int H_kv, int T_max,
+              int D, int new_dtype, void* stream, bool int8) {
+    if (!k_cache || !v_cache || !k_scale || !v_scale || !cache_seqlens || !k_new || !v_new) return ATTN_ERR_NULL;
+    if (!dtype_ok(new_dtype) || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+    if (!fits(B, H_kv, T_max, D) || B > (1 << 30)) return ATTN_ERR_SHAPE;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+        return ATTN_ERR_ALIGN;
+    if (k_cache == v_cache || k_new == k_cache || v_new == v_cache) return ATTN_ERR_ALIAS;
+    AppendFp8Args a{k_cache, v_cache, k_scale, v_scale, cache_seqlens, k_new, v_new,
+                    new_dtype == ATTN_BF16, B, H_kv, T_max, D, stream};
+    a.int8 = int8;
+    return finish(launch_kv_append_fp8(a));
+}
+
+int q8_decode(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+              const float* v_scale, const int32_t* cache_seqlens, void* o, float* lse, int B,
+              int H_q, int H_kv, int T_max, int D, float scale, void* workspace,
+              size_t workspace_bytes, void* stream, bool int8) {
+    if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !cache_seqlens || !o) return ATTN_ERR_NULL;
+    if (!head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+    if (H_kv <= 0 || H_q <= 0 || H_q % H_kv != 0) return ATTN_ERR_SHAPE;
+    if (!fits(B, H_kv, T_max, D) || !fits(B, H_q, 1, D) || (long long)B * H_q > (1 << 30))
+        return ATTN_ERR_SHAPE;
+    // one (sequence, KV head) of codes is addressed through a 32-bit buffer range
+    if ((long long)T_max * D > (1ll << 31) - 1) return ATTN_ERR_SHAPE;
+    if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
+    if (!workspace || workspace_bytes < decode_workspace_bytes(B, H_q, T_max, D)) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(workspace))
+        return ATTN_ERR_ALIGN;
+    if (o == q || o == k_cache || o == v_cache) return ATTN_ERR_ALIAS;
+    DecodeFp8Args a{q, k_cache, v_cache, k_scale, v_scale, cache_seqlens, o, lse, B, H_q, H_kv, T_max, D,
+                    scale, workspace, stream};
+    a.int8 = int8;
+    return finish(launch_decode_fp8kv(a));
+}
+
 }  // namespace
 
 extern "C" {
@@ -232,37 +270,33 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
 int kv_append_fp8(void* k_cache, void* v_cache, const float* k_scale, const float* v_scale,
                   int32_t* cache_seqlens, const void* k_new, const void* v_new, int B, int H_kv, int T_max,
                   int D, int new_dtype, void* stream) {
-    if (!k_cache || !v_cache || !k_scale || !v_scale || !cache_seqlens || !k_new || !v_new) return ATTN_ERR_NULL;
-    if (!dtype_ok(new_dtype) || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
-    if (!fits(B, H_kv, T_max, D) || B > (1 << 30)) return ATTN_ERR_SHAPE;
-    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
-        return ATTN_ERR_ALIGN;
-    if (k_cache == v_cache || k_new == k_cache || v_new == v_cache) return ATTN_ERR_ALIAS;
-    AppendFp8Args a{k_cache, v_cache, k_scale, v_scale, cache_seqlens, k_new, v_new,
-                    new_dtype == ATTN_BF16, B, H_kv, T_max, D, stream};
-    return finish(launch_kv_append_fp8(a));
+    return q8_append(k_cache, v_cache, k_scale, v_scale, cache_seqlens, k_new, v_new, B, H_kv, T_max, D,
+                     new_dtype, stream, false);
+}
+
+int kv_append_int8(void* k_cache, void* v_cache, const float* k_scale, const float* v_scale,
+                   int32_t* cache_seqlens, const void* k_new, const void* v_new, int B, int H_kv, int T_max,
+                   int D, int new_dtype, void* stream) {
+    return q8_append(k_cache, v_cache, k_scale, v_scale, cache_seqlens, k_new, v_new, B, H_kv, T_max, D,
+                     new_dtype, stream, true);
 }
 
 int attn_decode_fp8kv(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
                       const float* v_scale, const int32_t* cache_seqlens, void* o, float* lse, int B,
                       int H_q, int H_kv, int T_max, int D, float scale, void* workspace,
                       size_t workspace_bytes, void* stream) {
-    if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !cache_seqlens || !o) return ATTN_ERR_NULL;
-    if (!head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
-    if (H_kv <= 0 || H_q <= 0 || H_q % H_kv != 0) return ATTN_ERR_SHAPE;
-    if (!fits(B, H_kv, T_max, D) || !fits(B, H_q, 1, D) || (long long)B * H_q > (1 << 30))
-        return ATTN_ERR_SHAPE;
-    // one (sequence, KV head) of codes is addressed through a 32-bit buffer range
-    if ((long long)T_max * D > (1ll << 31) - 1) return ATTN_ERR_SHAPE;
-    if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
-    if (!workspace || workspace_bytes < decode_workspace_bytes(B, H_q, T_max, D)) return ATTN_ERR_WORKSPACE;
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(workspace))
-        return ATTN_ERR_ALIGN;
-    if (o == q || o == k_cache || o == v_cache) return ATTN_ERR_ALIAS;
-    DecodeFp8Args a{q, k_cache, v_cache, k_scale, v_scale, cache_seqlens, o, lse, B, H_q, H_kv, T_max, D,
-                    scale, workspace, stream};
-    return finish(launch_decode_fp8kv(a));
+    return q8_decode(q, k_cache, v_cache, k_scale, v_scale, cache_seqlens, o, lse, B, H_q, H_kv, T_max, D, scale,
+                     workspace, workspace_bytes, stream, false);
 }
+
+int attn_decode_int8kv(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                       const float* v_scale, const int32_t* cache_seqlens, void* o, float* lse, int B,
+                       int H_q, int H_kv, int T_max, int D, float scale, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    return q8_decode(q, k_cache, v_cache, k_scale, v_scale, cache_seqlens, o, lse, B, H_q, H_kv, T_max, D, scale,
+                     workspace, workspace_bytes, stream, true);
+}
+
 
 int attn_prefill_fp8(const void* q, const void* k, const void* v, const float* q_scale,
                      const float* k_scale, const float* v_scale, const uint8_t* key_padding_mask, void* o,

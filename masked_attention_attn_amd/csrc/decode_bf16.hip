@@ -25,7 +25,8 @@
 // ranges end at the item's last token, so look-ahead past it reads zeros
 // without touching memory.  Softmax per head column: weights 2^(S·c - mc),
 // mc from the exact max of the item's first block here, raised only when a
-// 16-key chunk's per-lane sum passes 2^8 (then l and O are rescaled).
+// lane's weights of one 32-key block sum past 2^8 (then l and O are rescaled
+// and the block's weights redone against the new reference).
 #include "decode_common.cuh"
 
 namespace mattn {
@@ -279,39 +280,42 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
             mc = pair_max(m) * c;
             mc_set = true;
         }
-        u32x4 pw[2];
+        // Weights of the block's 16 keys in this lane.  If their sum passes 2^8 (rare), the
+        // reference is raised to the block's row max where that is higher, O and l are scaled
+        // by 2^(old - new) and all 16 weights are redone, before any of them is packed: the
+        // P operand of both k-steps then uses one reference, the one O and l are kept in.
+        float p[16];
+        float cs = 0.f;
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            float p[8];
-            float cs = 0.f;
+        for (int e = 0; e < 16; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], c, -mc));
+            cs += p[e];
+        }
+        if (__ballot(cs > kRescaleSum)) {
+            float m = S[0];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[k2 * 8 + e], c, -mc));
+            for (int e = 1; e < 16; ++e) m = fmaxf(m, S[e]);
+            const float mn = fmaxf(mc, pair_max(m) * c);
+            const float alpha = __builtin_amdgcn_exp2f(mc - mn);
+            mc = mn;
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+            cs = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], c, -mc));
                 cs += p[e];
             }
-            if (__ballot(cs > kRescaleSum)) {     // rare: raise the reference
-                float m = S[k2 * 8];
-#pragma unroll
-                for (int e = 1; e < 8; ++e) m = fmaxf(m, S[k2 * 8 + e]);
-                const float mn = fmaxf(mc, pair_max(m) * c);
-                const float alpha = __builtin_amdgcn_exp2f(mc - mn);
-                mc = mn;
-                lsum *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-                cs = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[k2 * 8 + e], c, -mc));
-                    cs += p[e];
-                }
-            }
-            lsum += cs;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pw[k2][e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
         }
+        lsum += cs;
+        u32x4 pw[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pw[k2][e] = pack_bf16x2(p[k2 * 8 + 2 * e], p[k2 * 8 + 2 * e + 1]);
         u32x4 va[2][DB];
         {
             const uint32_t sb = (uint32_t)reinterpret_cast<uintptr_t>(

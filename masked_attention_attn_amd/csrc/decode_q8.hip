@@ -1,12 +1,15 @@
-// Single-token decode against an FP8 (E4M3) key/value cache.
+// Single-token decode against an 8-bit key/value cache: FP8 (E4M3) codes, or
+// symmetric INT8 codes when INT8.
 //
 // KV-cache quantisation stores each cached element in fewer bytes plus scale
 // metadata, and the attention kernel dequantises on the fly (blog.ruahverce.com,
 // LLM inference memory accounting 2/10, section "18. KV Cache Quantization").
-// Here the cache holds OCP E4M3 codes with one float32 scale per (sequence,
-// KV head) for K and one for V: a cached element is code value x scale.  Every
-// E4M3 value is exact in bf16, so codes are converted to bf16 (conversion
-// scale 1) and the bf16 decode's matrix-core block runs unchanged; the scales
+// Here the cache holds OCP E4M3 codes (or INT8 integers) with one float32 scale
+// per (sequence, KV head) for K and one for V: a cached element is code value x
+// scale.  Every E4M3 value and every integer in [-128, 127] is exact in bf16, so
+// codes are converted to bf16 (v_cvt_scalef32_pk_bf16_fp8 with scale 1, or a
+// byte-to-float convert and a pack) and the bf16 decode's matrix-core block runs
+// unchanged; the scales
 // act outside the products: the K scale multiplies the score multiplier, the V
 // scale the partial O of an item.  The work split, cursors and combine are
 // those of the bf16 decode (decode_common.cuh); the cache bytes per token are
@@ -24,11 +27,13 @@
 namespace mattn {
 namespace {
 
-template <int D> struct Geo8 {
+template <int D, bool INT8> struct Geo8 {
     static constexpr int RB = D;                   // bytes per cache row (one byte per element)
     static constexpr int BLK = CK * RB;            // bytes of one K (or V) block
     static constexpr int NV = BLK / 1024;          // 1 KiB V loads per block (16 bytes per lane)
-    static constexpr int RV = 8;                   // V register ring (look-ahead RV - 1 blocks)
+    // V register ring (look-ahead RV - 1 blocks); the INT8 conversion needs more temporaries,
+    // and at D = 128 a ring of 7 keeps the excess in accumulation registers (8 spills to memory)
+    static constexpr int RV = (INT8 && D == 128) ? 7 : 8;
     static constexpr int LK = 4;                   // K look-ahead in blocks
     static constexpr int QCH = 32 * D * 2 / 1024;  // 1 KiB loads of a full 32-head bf16 Q slot
 };
@@ -38,15 +43,17 @@ __device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff)
 }
 
 
-template <int D>
-__global__ __launch_bounds__(64)
-void decode_fp8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc,
+// At D = 128 the K and V register rings alone fill 256 registers: one wavefront per SIMD,
+// with the accumulation registers as well (no spills).
+template <int D, bool INT8>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, D == 128 ? 1 : 8)))
+void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc,
                        const uint8_t* __restrict__ vc, const float* __restrict__ kscale,
                        const float* __restrict__ vscale, const int32_t* __restrict__ lens,
                        float* __restrict__ ws_o, float* __restrict__ ws_ml,
                        int B, int H_q, int H_kv, int T_max, int G, int n_hg, int nsplit,
                        int nwaves, int qb, float c) {
-    using Gm = Geo8<D>;
+    using Gm = Geo8<D, INT8>;
     constexpr int RB = Gm::RB, NV = Gm::NV, QCH = Gm::QCH, RV = Gm::RV, LK = Gm::LK;
     constexpr int KSTEPS = D / 16;     // MFMA k-steps of K·Qᵀ
     constexpr int DB = D / 32;         // 32-row blocks of Oᵀ
@@ -186,7 +193,7 @@ void decode_fp8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ k
         f32x16 S = {};
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-            const u32x2 a0 = e4m3x4_to_bf16(kr[s][kk][0]), a1 = e4m3x4_to_bf16(kr[s][kk][1]);
+            const u32x2 a0 = codes4_to_bf16<INT8>(kr[s][kk][0]), a1 = codes4_to_bf16<INT8>(kr[s][kk][1]);
             S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]}),
                                                         qreg[kk], S, 0, 0, 0);
         }
@@ -203,45 +210,48 @@ void decode_fp8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ k
             mc = pair_max(m) * ci;
             mc_set = true;
         }
-        u32x4 pw[2];
+        // Weights of the block's 16 keys in this lane.  If their sum passes 2^8 (rare), the
+        // reference is raised to the block's row max where that is higher, O and l are scaled
+        // by 2^(old - new) and all 16 weights are redone, before any of them is packed: the
+        // P operand of both k-steps then uses one reference, the one O and l are kept in.
+        float p[16];
+        float cs = 0.f;
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            float p[8];
-            float cs = 0.f;
+        for (int e = 0; e < 16; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], ci, -mc));
+            cs += p[e];
+        }
+        if (__ballot(cs > kRescaleSum)) {
+            float m = S[0];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[k2 * 8 + e], ci, -mc));
+            for (int e = 1; e < 16; ++e) m = fmaxf(m, S[e]);
+            const float mn = fmaxf(mc, pair_max(m) * ci);
+            const float alpha = __builtin_amdgcn_exp2f(mc - mn);
+            mc = mn;
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+            cs = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], ci, -mc));
                 cs += p[e];
             }
-            if (__ballot(cs > kRescaleSum)) {     // rare: raise the reference
-                float m = S[k2 * 8];
-#pragma unroll
-                for (int e = 1; e < 8; ++e) m = fmaxf(m, S[k2 * 8 + e]);
-                const float mn = fmaxf(mc, pair_max(m) * ci);
-                const float alpha = __builtin_amdgcn_exp2f(mc - mn);
-                mc = mn;
-                lsum *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-                cs = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[k2 * 8 + e], ci, -mc));
-                    cs += p[e];
-                }
-            }
-            lsum += cs;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pw[k2][e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
         }
+        lsum += cs;
+        u32x4 pw[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pw[k2][e] = pack_bf16x2(p[k2 * 8 + 2 * e], p[k2 * 8 + 2 * e + 1]);
         // V of this block: codes -> bf16 tile -> transposing operand reads
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const u32x4 v = vr[s][i];
-            const u32x2 c0 = e4m3x4_to_bf16(v[0]), c1 = e4m3x4_to_bf16(v[1]);
-            const u32x2 c2 = e4m3x4_to_bf16(v[2]), c3 = e4m3x4_to_bf16(v[3]);
+            const u32x2 c0 = codes4_to_bf16<INT8>(v[0]), c1 = codes4_to_bf16<INT8>(v[1]);
+            const u32x2 c2 = codes4_to_bf16<INT8>(v[2]), c3 = codes4_to_bf16<INT8>(v[3]);
             *reinterpret_cast<u32x4*>(vtile + v_dst[i]) = u32x4{c0[0], c0[1], c1[0], c1[1]};
             *reinterpret_cast<u32x4*>(vtile + v_dst[i] + 16) = u32x4{c2[0], c2[1], c3[0], c3[1]};
         }
@@ -301,14 +311,14 @@ void decode_fp8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ k
     wait_vmem_le<0>();     // the Q loads into LDS land before the wavefront ends
 }
 
-template <int D>
+template <int D, bool INT8>
 int resident_waves8(int lds_bytes) {
     static int cached_lds = -1, cached = 0;
     if (lds_bytes == cached_lds) return cached;
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_fp8_kernel<D>, 64, lds_bytes) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_q8_kernel<D, INT8>, 64, lds_bytes) != hipSuccess ||
         cus <= 0 || per_cu <= 0)
         return 256;
     cached = cus * per_cu;
@@ -316,21 +326,21 @@ int resident_waves8(int lds_bytes) {
     return cached;
 }
 
-template <int D>
+template <int D, bool INT8>
 hipError_t launch8(const DecodeFp8Args& a) {
     static const hipError_t attr =
-        hipFuncSetAttribute((const void*)decode_fp8_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            Geo8<D>::RV * q_slot_bytes(32, D));
+        hipFuncSetAttribute((const void*)decode_q8_kernel<D, INT8>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            Geo8<D, INT8>::RV * q_slot_bytes(32, D));
     if (attr != hipSuccess) return attr;
     const int G = a.H_q / a.H_kv;
     const int n_hg = (G + 31) / 32;
     const int nsplit = decode_nsplit(a.T_max);
     const int qb = q_slot_bytes(G, D);
-    const int lds = Geo8<D>::RV * qb;
-    const int nwaves = resident_waves8<D>(lds);
+    const int lds = Geo8<D, INT8>::RV * qb;
+    const int nwaves = resident_waves8<D, INT8>(lds);
     float* ws_o = static_cast<float*>(a.workspace);
     float* ws_ml = ws_o + (size_t)a.B * a.H_q * nsplit * 2 * D;
-    hipLaunchKernelGGL((decode_fp8_kernel<D>), dim3(nwaves), dim3(64), lds, (hipStream_t)a.stream,
+    hipLaunchKernelGGL((decode_q8_kernel<D, INT8>), dim3(nwaves), dim3(64), lds, (hipStream_t)a.stream,
                        (const bf16*)a.q, (const uint8_t*)a.k_cache, (const uint8_t*)a.v_cache, a.k_scale,
                        a.v_scale, a.lens, ws_o, ws_ml, a.B, a.H_q, a.H_kv, a.T_max, G, n_hg, nsplit, nwaves, qb,
                        a.scale * kLog2e);
@@ -344,6 +354,9 @@ hipError_t launch8(const DecodeFp8Args& a) {
 
 }  // namespace
 
-hipError_t launch_decode_fp8kv(const DecodeFp8Args& a) { return a.D == 64 ? launch8<64>(a) : launch8<128>(a); }
+hipError_t launch_decode_fp8kv(const DecodeFp8Args& a) {
+    if (a.int8) return a.D == 64 ? launch8<64, true>(a) : launch8<128, true>(a);
+    return a.D == 64 ? launch8<64, false>(a) : launch8<128, false>(a);
+}
 
 }  // namespace mattn

@@ -65,12 +65,16 @@ void kv_append_kernel(unsigned char* __restrict__ kc, unsigned char* __restrict_
     if (ok && threadIdx.x == 0) lens[b] = t + 1;
 }
 
-// FP8 (E4M3) cache: the new token's elements are quantised with the (b, KV head)
-// scale as code = E4M3(clamp(x / scale, -448, 448)) (IEEE float32 division,
-// round to nearest, ties to even) and written as bytes; four elements per
-// thread become one dword of codes (element i in byte i).
+// 8-bit caches: the new token's elements are quantised with the (b, KV head)
+// scale, after an IEEE float32 division y = x / scale: E4M3 codes as
+// E4M3(clamp(y, -448, 448)) (round to nearest, ties to even), INT8 codes as
+// clamp(rint(y), -127, 127) (nearest integer, ties to even; symmetric INT8 is
+// one of the cache formats of LLM inference memory accounting 2/10, section
+// "18. KV Cache Quantization").  Four elements per thread become one dword of
+// codes (element i in byte i).
+template <bool INT8>
 __global__ __launch_bounds__(NT)
-void kv_append_fp8_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+void kv_append_q8_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
                           const float* __restrict__ ks, const float* __restrict__ vs,
                           int32_t* __restrict__ lens, const void* __restrict__ kn,
                           const void* __restrict__ vn, int new_bf16, int H_kv, int T_max, int D) {
@@ -92,11 +96,22 @@ void kv_append_fp8_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
             for (int e = 0; e < 4; ++e)
                 x[e] = new_bf16 ? (float)reinterpret_cast<const bf16*>(src)[e0 + e]
                                 : reinterpret_cast<const float*>(src)[e0 + e];
-            float y[4];
+            int wd;
+            if constexpr (INT8) {       // nearest integer (ties to even), clamped to +-127
+                uint32_t u = 0u;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf(__fdiv_rn(x[e], s), -448.0f), 448.0f);
-            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-            wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], wd, true);
+                for (int e = 0; e < 4; ++e) {
+                    const float y = fminf(fmaxf(__builtin_rintf(__fdiv_rn(x[e], s)), -127.0f), 127.0f);
+                    u |= ((uint32_t)(int)y & 0xFFu) << (8 * e);
+                }
+                wd = (int)u;
+            } else {                    // clamped to +-448, nearest E4M3 value (ties to even)
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf(__fdiv_rn(x[e], s), -448.0f), 448.0f);
+                wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+                wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], wd, true);
+            }
             uint8_t* dst = (which ? vc : kc) + (((size_t)b * H_kv + g) * T_max + t) * D + (size_t)qd * 4;
             *reinterpret_cast<uint32_t*>(dst) = (uint32_t)wd;
         }
@@ -108,7 +123,8 @@ void kv_append_fp8_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
 }  // namespace
 
 hipError_t launch_kv_append_fp8(const AppendFp8Args& a) {
-    hipLaunchKernelGGL(kv_append_fp8_kernel, dim3(a.B), dim3(NT), 0, (hipStream_t)a.stream,
+    auto kern = a.int8 ? kv_append_q8_kernel<true> : kv_append_q8_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3(a.B), dim3(NT), 0, (hipStream_t)a.stream,
                        (uint8_t*)a.k_cache, (uint8_t*)a.v_cache, a.k_scale, a.v_scale, a.lens, a.k_new,
                        a.v_new, a.new_bf16 ? 1 : 0, a.H_kv, a.T_max, a.D);
     return hipGetLastError();

@@ -68,8 +68,8 @@ struct DecodeArgs {
     int page_size = 0, max_pages = 0, num_pages = 0;
 };
 
-// FP8 (E4M3) cache: codes [B, H_kv, T_max, D] uint8, one float32 scale per (b, KV head)
-// for K and for V; q, o bf16.
+// 8-bit cache: E4M3 codes (or INT8 when int8) [B, H_kv, T_max, D], one float32 scale per
+// (b, KV head) for K and for V; q, o bf16.
 struct DecodeFp8Args {
     const void* q; const void* k_cache; const void* v_cache;
     const float* k_scale; const float* v_scale;
@@ -79,6 +79,7 @@ struct DecodeFp8Args {
     float scale;
     void* workspace;
     void* stream;
+    bool int8 = false;
 };
 
 struct AppendFp8Args {
@@ -89,6 +90,7 @@ struct AppendFp8Args {
     bool new_bf16;
     int B, H_kv, T_max, D;
     void* stream;
+    bool int8 = false;            // symmetric INT8 codes instead of E4M3
 };
 
 hipError_t launch_fwd_bf16_d64(const FwdArgs& a);

@@ -86,6 +86,22 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
     return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
+// Four INT8 codes (one dword, element i in byte i) -> four bf16 (two dwords), exact: every
+// integer in [-128, 127] is a bf16 value.
+__device__ __forceinline__ u32x2 i8x4_to_bf16(uint32_t w) {
+    const float f0 = (float)(int)(int8_t)(w & 0xFFu);
+    const float f1 = (float)(int)(int8_t)((w >> 8) & 0xFFu);
+    const float f2 = (float)(int)(int8_t)((w >> 16) & 0xFFu);
+    const float f3 = (float)((int)w >> 24);
+    return u32x2{pack_bf16x2(f0, f1), pack_bf16x2(f2, f3)};
+}
+// Four 8-bit cache codes (E4M3, or INT8 when INT8) -> four bf16, exact.
+template <bool INT8>
+__device__ __forceinline__ u32x2 codes4_to_bf16(uint32_t w) {
+    if constexpr (INT8) return i8x4_to_bf16(w);
+    else return e4m3x4_to_bf16(w);
+}
+
 // Wait for this wave's outstanding global loads (including LDS-direct ones).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

@@ -285,3 +285,28 @@ def test_prefill_fp8_validation(lib):
     assert pf(k=B_ + 4) == 7
     assert pf(o=A) == 8
     assert pf(lse=C) == 8
+
+
+def test_int8_validation(lib):
+    KS, VS, W = 0x70000, 0x80000, 0x60000
+    ws = lib.attn_decode_workspace_bytes(4, 8, 2, 1000, 128)
+
+    def dec(**kw):
+        a = dict(q=A, k=B_, v=C, ks=KS, vs=VS, lens=L, o=O, lse=0, B=4, Hq=8, Hkv=2, Tmax=1000, D=128,
+                 scale=0.088, ws=W, wsb=ws)
+        a.update(kw)
+        return lib.attn_decode_int8kv(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["lens"], a["o"], a["lse"],
+                                      a["B"], a["Hq"], a["Hkv"], a["Tmax"], a["D"], a["scale"], a["ws"], a["wsb"],
+                                      None)
+    assert dec(ks=0) == 1
+    assert dec(D=96) == 3
+    assert dec(Hq=6, Hkv=4) == 2
+    assert dec(Tmax=(1 << 24) + 1) == 2
+    assert dec(scale=-1.0) == 6
+    assert dec(wsb=ws - 1) == 4
+    assert dec(v=C + 8) == 7
+    assert dec(o=B_) == 8
+    assert lib.kv_append_int8(A, B_, 0, VS, L, C, O, 2, 2, 16, 64, 1, None) == 1
+    assert lib.kv_append_int8(A, B_, KS, VS, L, C, O, 2, 2, 16, 64, 5, None) == 3
+    assert lib.kv_append_int8(A, B_, KS, VS, L, C, O, 2, 0, 16, 64, 1, None) == 2
+    assert lib.kv_append_int8(A, A, KS, VS, L, C, O, 2, 2, 16, 64, 1, None) == 8

@@ -724,3 +724,140 @@ def test_gqa_causal_prefill_8192_fp8_sampled_rows(ma):
     rows = [0, 1, 31, 32, 255, 256, 4095, 4096, 8191] + list(range(7, 8192, 613))
     Or, Lr = oracle.prefill_fp8(w.q, w.k, w.v, w.q_scale, w.k_scale, w.v_scale, None, True, w.scale, rows=rows)
     check_attn(o[:, :, rows], l[:, :, rows], Or, Lr, torch.bfloat16, "fp8 causal 8192 sampled rows")
+
+
+# ---- INT8 KV cache ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", FP8_DEC)
+def test_int8_append_then_decode(ma, shape):
+    B, Hq, Hkv, D, lo, hi, Tm = shape
+    w = W.make_decode_int8(B, Hq, Hkv, D, lo, hi, T_max=Tm, seed=B * 10 + Hq + 1)
+    kc, vc, ks, vs, lens = _fp8_dev(w)
+    ma.kv_append_int8(kc, vc, ks, vs, lens, w.k_new.to(DEV), w.v_new.to(DEV))
+    o, l = ma.attn_decode_int8kv(w.q.to(DEV), kc, vc, ks, vs, lens, w.scale, want_lse=True)
+    torch.cuda.synchronize()
+    ek, ev, el = oracle.kv_append_int8(w.k_cache.numpy(), w.v_cache.numpy(), w.k_scale, w.v_scale,
+                                       w.lens.numpy(), w.k_new, w.v_new)
+    assert lens.cpu().tolist() == el.tolist()
+    assert np.array_equal(kc.cpu().numpy(), ek) and np.array_equal(vc.cpu().numpy(), ev)   # bytes, exact
+    Or, Lr = oracle.decode_int8kv(w.q, ek, ev, w.k_scale, w.v_scale, el, w.scale)
+    check_attn(o, l, Or, Lr, torch.bfloat16, f"int8 decode {shape}")
+
+
+@pytest.mark.parametrize("new_dtype", [torch.bfloat16, torch.float32])
+def test_int8_append_quantisation_edges(ma, new_dtype):
+    # ties to even, saturation at +-127, signed zero, and the full code range
+    B, Hkv, D, Tm = 2, 2, 64, 64
+    w = W.make_decode_int8(B, 2, Hkv, D, 3, 10, T_max=Tm, seed=5)
+    special = torch.tensor([0.5, 1.5, 2.5, -0.5, -2.5, 126.5, 127.5, 1e6, -1e6, -0.0, 0.0, 3.25, -127.0,
+                            100.5, -99.5, 127.49])
+    g = torch.Generator().manual_seed(9)
+    kn = torch.randn(B, Hkv, 1, D, generator=g) * 60
+    vn = torch.randn(B, Hkv, 1, D, generator=g) * 0.05
+    kn[0, 0, 0, :16] = special
+    vn[1, 1, 0, :16] = special * 0.25
+    kn, vn = kn.to(new_dtype).contiguous(), vn.to(new_dtype).contiguous()
+    ks = torch.tensor([[1.0, 0.75], [0.3, 2.0]], dtype=torch.float32)
+    vs = torch.tensor([[0.001, 0.25], [1.5, 0.25]], dtype=torch.float32)
+    kc, vc = w.k_cache.to(DEV), w.v_cache.to(DEV)
+    lens = w.lens.to(DEV)
+    ma.kv_append_int8(kc, vc, ks.to(DEV), vs.to(DEV), lens, kn.to(DEV), vn.to(DEV))
+    torch.cuda.synchronize()
+    ek, ev, el = oracle.kv_append_int8(w.k_cache.numpy(), w.v_cache.numpy(), ks, vs, w.lens.numpy(), kn, vn)
+    assert np.array_equal(kc.cpu().numpy(), ek) and np.array_equal(vc.cpu().numpy(), ev)
+    assert lens.cpu().tolist() == el.tolist()
+
+
+def test_int8_decode_v_scale_doubles_o_exactly(ma):
+    # the V scale multiplies each partial O (a power-of-two factor is exact) and not the weights:
+    # doubling it doubles O bit for bit and leaves the LSE unchanged.  Unit K scales (scores of
+    # codes up to +-127: peaky rows, many raised references) against the oracle, with V at 1/64
+    # (O of order one, the scale of the tolerance)
+    w = W.make_decode_int8(4, 8, 2, 128, 1, 1500, T_max=1536, seed=12)
+    kc, vc, lens = w.k_cache.to(DEV), w.v_cache.to(DEV), (w.lens + 1).to(DEV)
+    ks = torch.ones(4, 2, dtype=torch.float32, device=DEV)
+    vs = ks / 64
+    q = w.q.to(DEV)
+    o1, l1 = ma.attn_decode_int8kv(q, kc, vc, ks, vs, lens, w.scale, want_lse=True)
+    o2, l2 = ma.attn_decode_int8kv(q, kc, vc, ks, vs * 2, lens, w.scale, want_lse=True)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.decode_int8kv(w.q, w.k_cache, w.v_cache, np.ones((4, 2)), np.full((4, 2), 1 / 64),
+                                  w.lens + 1, w.scale)
+    check_attn(o1, l1, Or, Lr, torch.bfloat16, "int8 decode, unit K scales")
+    assert torch.equal(o2, o1 * 2) and torch.equal(l2, l1)
+
+
+def test_gqa_decode_b32_int8_sampled_heads(ma):
+    """The B32 GQA decode workload with an INT8 cache: append, decode, sampled (b, h)."""
+    w = W.gqa_decode_b32_int8()
+    kc, vc, ks, vs, lens = _fp8_dev(w)
+    ma.kv_append_int8(kc, vc, ks, vs, lens, w.k_new.to(DEV), w.v_new.to(DEV))
+    o, l = ma.attn_decode_int8kv(w.q.to(DEV), kc, vc, ks, vs, lens, w.scale, want_lse=True)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(9)
+    heads = [(int(b), int(h)) for b, h in zip(g.integers(0, 32, 16), g.integers(0, 32, 16))]
+    heads += [(int(np.argmax(w.lens)), 7)]
+    Or, Lr = oracle.decode_int8kv(w.q, kc.cpu().numpy(), vc.cpu().numpy(), w.k_scale, w.v_scale,
+                                  lens.cpu().numpy(), w.scale, heads=heads)
+    check_attn(torch.stack([o[b, h, 0] for b, h in heads]), torch.stack([l[b, h] for b, h in heads]),
+               Or, Lr, torch.bfloat16, "int8 decode sampled heads")
+
+
+# ---- lazy-rescale regression: the reference rises inside a 32-key block -------------------------
+
+def _rising(B=2, Hq=8, Hkv=2, T=320, D=64, seed=31):
+    """Q all ones; K rows constant per token.  Score steps of sqrt(D)·log2(e) log2 units sit in
+    the second 16-key half of a 32-key block while its first half still carries the old
+    reference's weights: 0 up to token 47, 1 for tokens 48..63 (block 1), 1 for 224..239 and 2
+    for 240..255 (block 7; these last keys dominate the result, so a weight of the first half
+    kept against the old reference shows in O).  V is N(0,1).  Returns float32 q, k, v and the
+    scale."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.ones(B, Hq, 1, D)
+    k = torch.zeros(B, Hkv, T, D)
+    k[:, :, 48:64] = 1.0
+    k[:, :, 224:240] = 1.0
+    k[:, :, 240:256] = 2.0
+    v = torch.randn(B, Hkv, T, D, generator=g)
+    return q, k, v, 1.0 / math.sqrt(D)
+
+
+def test_decode_rescale_inside_block_bf16_and_paged(ma):
+    q, k, v, scale = _rising()
+    B = q.shape[0]
+    lens = torch.full((B,), 300, dtype=torch.int32)
+    Or, Lr = oracle.decode(q, k, v, lens, scale)
+    kb, vb, qb = k.to(torch.bfloat16), v.to(torch.bfloat16), q.to(torch.bfloat16)
+    o, l = ma.attn_decode(qb.to(DEV), kb.to(DEV), vb.to(DEV), lens.to(DEV), scale, want_lse=True)
+    torch.cuda.synchronize()
+    check_attn(o, l, Or, Lr, torch.bfloat16, "bf16 decode, reference raised inside a block")
+    d = W.Decode(qb, kb, vb, kb[:, :, :1].contiguous(), vb[:, :, :1].contiguous(), lens, scale)
+    pg = W.to_paged(d, 16, seed=2)
+    kp, vp, bt = _paged_dev(pg)
+    o, l = ma.attn_decode_paged(qb.to(DEV), kp, vp, bt, lens.to(DEV), scale, want_lse=True)
+    torch.cuda.synchronize()
+    check_attn(o, l, Or, Lr, torch.bfloat16, "paged decode, reference raised inside a block")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_decode_rescale_inside_block_8bit(ma, fmt):
+    q, k, v, scale = _rising(D=128)
+    B, Hkv, T, D = k.shape
+    lens = torch.full((B,), 300, dtype=torch.int32)
+    vs = torch.full((B, Hkv), 1.0 / 16)
+    ks = torch.ones(B, Hkv)
+    if fmt == "fp8":      # K values 0, 1, 2 and V / (1/16) are E4M3-exact after the cast
+        kc = k.to(torch.float8_e4m3fn).view(torch.uint8)
+        vc = (v * 16).to(torch.float8_e4m3fn).view(torch.uint8)
+        kd, vd = oracle.dequantize_e4m3(kc, 1.0), oracle.dequantize_e4m3(vc, 1.0 / 16)
+        fn = ma.attn_decode_fp8kv
+    else:
+        kc = k.to(torch.int8)
+        vc = torch.round(v * 16).clamp(-127, 127).to(torch.int8)
+        kd, vd = oracle.dequantize_int8(kc, 1.0), oracle.dequantize_int8(vc, 1.0 / 16)
+        fn = ma.attn_decode_int8kv
+    Or, Lr = oracle.decode(q, kd, vd, lens, scale)
+    o, l = fn(q.to(torch.bfloat16).to(DEV), kc.contiguous().to(DEV), vc.contiguous().to(DEV), ks.to(DEV),
+              vs.to(DEV), lens.to(DEV), scale, want_lse=True)
+    torch.cuda.synchronize()
+    check_attn(o, l, Or, Lr, torch.bfloat16, f"{fmt} decode, reference raised inside a block")

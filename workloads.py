@@ -293,6 +293,32 @@ def make_decode_fp8(B, H_q, H_kv, D, len_lo, len_hi, *, T_max=None, seed=0, scal
     return DecodeFp8(q, kc, vc, ks, vs, kn, vn, lens.to(torch.int32), float(scale), name)
 
 
+def make_decode_int8(B, H_q, H_kv, D, len_lo, len_hi, *, T_max=None, seed=0, scale=None, lens=None,
+                     name="") -> DecodeFp8:
+    """Symmetric INT8 caches: codes round(N(0,1) * 32) clamped to +-127 (int8), scales 2^U{-10..-6}
+    per (b, KV head) (dequantised values about N(0,1) * 2^-5 .. 2^-1, the FP8 cache's range), new
+    tokens N(0,1) * 32 * their head's scale in bf16 (so they quantise into the bulk of the code
+    range), Q N(0,1) bf16.  Draw order as make_decode_fp8.  Returned in a DecodeFp8 record (the
+    caches hold int8 codes)."""
+    g = _gen(seed)
+    if lens is None:
+        lens = torch.randint(len_lo, len_hi + 1, (B,), generator=g, dtype=torch.int64)
+    lens = torch.as_tensor(lens, dtype=torch.int64)
+    if T_max is None:
+        T_max = round_up(len_hi + 1, 64)
+    codes = lambda: torch.round(torch.randn(B, H_kv, T_max, D, generator=g) * 32).clamp(-127, 127).to(torch.int8)
+    kc = codes().contiguous()
+    vc = codes().contiguous()
+    ks = torch.exp2(torch.randint(-10, -5, (B, H_kv), generator=g).float()).contiguous()
+    vs = torch.exp2(torch.randint(-10, -5, (B, H_kv), generator=g).float()).contiguous()
+    kn = (torch.randn(B, H_kv, 1, D, generator=g) * 32 * ks[:, :, None, None]).to(torch.bfloat16).contiguous()
+    vn = (torch.randn(B, H_kv, 1, D, generator=g) * 32 * vs[:, :, None, None]).to(torch.bfloat16).contiguous()
+    q = torch.randn(B, H_q, 1, D, generator=g).to(torch.bfloat16).contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return DecodeFp8(q, kc, vc, ks, vs, kn, vn, lens.to(torch.int32), float(scale), name)
+
+
 def make_gqa_prefill(B, H_q, H_kv, Tq, Tk, D, dtype=torch.bfloat16, *, valid=None, amp=1.0, seed=0,
                      scale=None, name="") -> Prefill:
     """Q [B, H_q, Tq, D] and K/V [B, H_kv, Tk, D] (grouped-query layout), drawn Q, K, V."""
@@ -419,3 +445,9 @@ def gqa_causal_prefill_8192_fp8(seed=0) -> PrefillFp8:
     """The causal GQA prompt pass (B1, H_q 32 / H_kv 8, D128, 8,192 tokens) with E4M3 inputs."""
     return make_prefill_fp8(1, 32, 8, 8192, 8192, 128, seed=seed,
                             name="E4M3 causal GQA prefill B1 Hq32 Hkv8 D128, 8192-token prompt")
+
+
+def gqa_decode_b32_int8(seed=0) -> DecodeFp8:
+    """The GQA decode workload (B32, H_q 32 / H_kv 8, D128, len U[512, 8192]) with an INT8 cache."""
+    return make_decode_int8(32, 32, 8, 128, 512, 8192, seed=seed,
+                            name="INT8-cache GQA decode B32 Hq32 Hkv8 D128, len U[512,8192] + 1 appended")
