@@ -251,10 +251,12 @@ def paged_section(torch, ma, W, dev):
     return res
 
 
-def fp8_section(torch, ma, W, dev):
+def fp8_section(torch, ma, W, dev, int8=False):
     """The decode workload with an E4M3 cache (attn_decode_fp8kv; per-(sequence, KV head) scales),
-    timed on its own after the append; bytes: one byte per cached K and V element, plus q and o."""
-    w = W.gqa_decode_b32_fp8()
+    or an INT8 cache (attn_decode_int8kv), timed on its own after the append; bytes: one byte per
+    cached K and V element, plus q and o."""
+    w = W.gqa_decode_b32_int8() if int8 else W.gqa_decode_b32_fp8()
+    decode_fn = ma.attn_decode_int8kv if int8 else ma.attn_decode_fp8kv
     kc, vc, ks, vs = w.k_cache.to(dev), w.v_cache.to(dev), w.k_scale.to(dev), w.v_scale.to(dev)
     lens = (w.lens + 1).to(dev)
     q = w.q.to(dev)
@@ -263,8 +265,8 @@ def fp8_section(torch, ma, W, dev):
     B, Hq, _, D = q.shape
     Hkv, Tm = kc.shape[1], kc.shape[2]
     ws = torch.empty(ma.attn_decode_workspace_bytes(B, Hq, Hkv, Tm, D), dtype=torch.uint8, device=dev)
-    t = _time_call(torch, lambda: ma.attn_decode_fp8kv(q, kc, vc, ks, vs, lens, w.scale, out=o, lse=lse,
-                                                       workspace=ws, want_lse=True), n=20)
+    t = _time_call(torch, lambda: decode_fn(q, kc, vc, ks, vs, lens, w.scale, out=o, lse=lse,
+                                            workspace=ws, want_lse=True), n=20)
     nbytes = int((w.lens + 1).sum()) * 2 * Hkv * D + 2 * q.numel() * 2
     return {"workload": w.name, "us": round(t * 1e6, 2), "gbps": round(nbytes / t / 1e9, 1),
             "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBPS, 4), "algorithmic_bytes": nbytes}
@@ -488,6 +490,7 @@ def main():
         out["paged_decode"] = paged_section(torch, ma, W, dev)
         out["causal_gqa_prefill"] = causal_section(torch, ma, W, dev)
         out["fp8_kv_decode"] = fp8_section(torch, ma, W, dev)
+        out["int8_kv_decode"] = fp8_section(torch, ma, W, dev, int8=True)
         out["fp8_prefill"] = fp8_prefill_section(torch, ma, W, dev)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(pf, args.cpu_seconds)
