@@ -591,7 +591,9 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
         // next chunk already in flight (at the check after slot CP+1, chunk 1's
         // stage A of pairs CP, CP+1 and stage B of pair CP).  Final O = acc / l and
         // LSE = (mc + log2 l)·ln 2 hold for any reference, so only rounding
-        // changes.
+        // changes.  Order: check(0) comes before any PV of chunk 0, and check(1)
+        // after all of them and before any PV of chunk 1, so the scaled O holds
+        // exactly the weights taken against the old reference.
         auto check = [&](int k2) {
             bool over = false;
 #pragma unroll
@@ -674,8 +676,8 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
         } else {
             // D=128, one query block: 16 slots.  QK(u+1) is one chain of 8 MFMAs
             // (slots 0-5, 7, 9); PV(u,0) in 6, 8, 10, 11 once chunk 0 is packed
-            // (slot 5); PV(u,1) in 12-15 once chunk 1 is packed (slot 9);
-            // softmax in 0-9.  FP8: QK(u+1) is a chain of two E4M3 MFMAs (slots 0, 4).
+            // (slot 5); PV(u,1) in 12-15 once chunk 1 is packed (slot 9) and checked
+            // (after slot 11, when every PV of chunk 0 has been issued); softmax in 0-9.  FP8: QK(u+1) is a chain of two E4M3 MFMAs (slots 0, 4).
 #pragma unroll
             for (int sl = 0; sl < 16; ++sl) {
                 if (sl == 1) { rd_v(0); rd_v(1); }
@@ -706,7 +708,7 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
                 if (sl < NPP + 2) softmax_slot(sl);
                 fence();
                 if (sl == CP + 1) check(0);
-                if (sl == NPP + 1) check(1);
+                if (sl == 11) check(1);
             }
         }
 
