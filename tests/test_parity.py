@@ -863,20 +863,23 @@ def test_decode_rescale_inside_block_8bit(ma, fmt):
     check_attn(o, l, Or, Lr, torch.bfloat16, f"{fmt} decode, reference raised inside a block")
 
 
+@pytest.mark.parametrize("half", [0, 1])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("fp8", [False, True])
-def test_prefill_rescale_inside_step(ma, D, fp8):
+def test_prefill_rescale_inside_step(ma, D, fp8, half):
     """The lazy reference rising at the second 16-key half of a 32-key block while the first half
     still carries the old reference's weights (the rescale then has to cover every PV product of
     the first half).  Q all ones; K rows constant per key: 0, except a for keys 48..63 (a = 0.5 at
     D = 64, 0.375 at D = 128: steps of 5.8 and 6.1 log2 units, a lane's chunk sum of ~440 and
     ~560, just past the 2^8 trigger, so the old-reference weights of the first half matter);
-    V N(0,1)."""
+    V N(0,1).  half = 0 puts the step at keys 32..47 instead (the first half of block 1): the
+    check of the first half then also redoes the second half's softmax stages already begun."""
     B, H, Tq, Tk = 1, 2, 64, 200
     g = torch.Generator().manual_seed(D)
     q = torch.ones(B, H, Tq, D)
     k = torch.zeros(B, H, Tk, D)
-    k[:, :, 48:64] = 0.5 if D == 64 else 0.375
+    lo = 48 if half else 32
+    k[:, :, lo:64] = 0.5 if D == 64 else 0.375
     v = torch.randn(B, H, Tk, D, generator=g)
     scale = 1.0 / math.sqrt(D)
     Or, Lr = oracle.prefill(q, k, v, None, False, scale)
@@ -891,4 +894,4 @@ def test_prefill_rescale_inside_step(ma, D, fp8):
         o, l = ma.attn_prefill(q.to(torch.bfloat16).to(DEV), k.to(torch.bfloat16).to(DEV),
                                v.to(torch.bfloat16).to(DEV), None, False, scale)
     torch.cuda.synchronize()
-    check_attn(o, l, Or, Lr, torch.bfloat16, f"prefill rescale inside a step D={D} fp8={fp8}")
+    check_attn(o, l, Or, Lr, torch.bfloat16, f"prefill rescale inside a step D={D} fp8={fp8} half={half}")
