@@ -31,10 +31,10 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import decode, prefill, _f64
+from .attention import decode, prefill, prefill_varlen, _f64
 
 __all__ = ["E4M3_MAX", "e4m3_values", "quantize_e4m3", "dequantize_e4m3", "kv_append_fp8", "decode_fp8kv",
-           "prefill_fp8"]
+           "prefill_fp8", "prefill_varlen_fp8"]
 
 E4M3_MAX = 448.0
 
@@ -134,3 +134,23 @@ def prefill_fp8(q, k, v, q_scale, k_scale, v_scale, key_padding_mask=None, causa
     kd = dequantize_e4m3(k, _f64(k_scale)[:, :, None, None])
     vd = dequantize_e4m3(v, _f64(v_scale)[:, :, None, None])
     return prefill(qd, kd, vd, key_padding_mask, causal, scale, rows)
+
+
+def prefill_varlen_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, causal=False, scale=None):
+    """``prefill_varlen`` on dequantised E4M3 inputs.
+
+    q uint8 [total_q, H_q, D], k and v uint8 [total_k, H_kv, D] (packed sequences as in
+    ``attention_varlen``); q_scale [B, H_q], k_scale and v_scale [B, H_kv], one per (sequence,
+    head).  Returns O [total_q, H_q, D] and LSE [H_q, total_q] as ``prefill_varlen``.
+    """
+    cq = np.asarray(_f64(cu_seqlens_q), dtype=np.int64)
+    ck = np.asarray(_f64(cu_seqlens_k), dtype=np.int64)
+    qs, ks, vs = _f64(q_scale), _f64(k_scale), _f64(v_scale)
+    B = cq.size - 1
+    # per-row scales: row t of sequence b takes that sequence's (b, head) scale
+    bq = np.repeat(np.arange(B), np.diff(cq))
+    bk = np.repeat(np.arange(B), np.diff(ck))
+    qd = dequantize_e4m3(q, qs[bq][:, :, None])
+    kd = dequantize_e4m3(k, ks[bk][:, :, None])
+    vd = dequantize_e4m3(v, vs[bk][:, :, None])
+    return prefill_varlen(qd, kd, vd, cq, ck, causal, scale)

@@ -828,3 +828,32 @@ def test_kv_append_int8_writes_only_the_quantised_slot():
             assert np.all(err <= sc[b][:, None] * 0.5 + 1e-7)
         other = [i for i in range(T) if i != t]
         assert np.array_equal(kc2[b, :, other], kc[b, :, other]) and np.array_equal(vc2[b, :, other], vc[b, :, other])
+
+
+def test_prefill_varlen_fp8_equals_dense_per_sequence():
+    # each packed sequence equals the dense FP8 prefill of that sequence alone (its own scales)
+    r = _rng(320)
+    lq, lk = [5, 0, 7, 3], [6, 4, 7, 0]
+    Hkv, G, D = 2, 2, 8
+    cq, ck = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q8 = _e4m3_codes(r, (cq[-1], Hkv * G, D))
+    k8, v8 = _e4m3_codes(r, (ck[-1], Hkv, D)), _e4m3_codes(r, (ck[-1], Hkv, D))
+    qs, ks, vs = r.uniform(0.01, 0.1, (4, Hkv * G)), r.uniform(0.01, 0.1, (4, Hkv)), r.uniform(0.5, 2, (4, Hkv))
+    for causal in (False, True):
+        O, L = oracle.prefill_varlen_fp8(q8, k8, v8, qs, ks, vs, cq, ck, causal, 0.6)
+        for b in range(4):
+            if lq[b] == 0:
+                continue
+            tq = q8[cq[b]:cq[b + 1]].transpose(1, 0, 2)[None]
+            tk, tv = k8[ck[b]:ck[b + 1]].transpose(1, 0, 2)[None], v8[ck[b]:ck[b + 1]].transpose(1, 0, 2)[None]
+            Od, Ld = oracle.prefill_fp8(tq, tk, tv, qs[b:b + 1], ks[b:b + 1], vs[b:b + 1], None, causal, 0.6)
+            assert np.allclose(O[cq[b]:cq[b + 1]], Od[0].transpose(1, 0, 2), atol=1e-12, rtol=0)
+            Lv = L[:, cq[b]:cq[b + 1]]
+            assert np.array_equal(np.isneginf(Lv), np.isneginf(Ld[0]))
+            assert np.allclose(Lv[np.isfinite(Lv)], Ld[0][np.isfinite(Ld[0])], atol=1e-12, rtol=0)
+        # a sequence's scales touch that sequence only
+        qs2 = qs.copy()
+        qs2[2] *= 3
+        O2, L2 = oracle.prefill_varlen_fp8(q8, k8, v8, qs2, ks, vs, cq, ck, causal, 0.6)
+        other = np.r_[0:cq[2], cq[3]:cq[-1]]
+        assert np.array_equal(O2[other], O[other]) and not np.allclose(O2[cq[2]:cq[3]], O[cq[2]:cq[3]])
