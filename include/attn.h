@@ -116,7 +116,8 @@ int attn_fwd_lse(const void* q, const void* k, const void* v,
  *       rows past it are not written); 0 <= max_seqlen_q <= total_q
  * bf16 only (ATTN_ERR_UNSUPPORTED otherwise); H·D <= 2^22, total_k·H·D < 2^30
  * and total_q·H·D < 2^31 (else ATTN_ERR_SHAPE); the other rules as
- * attn_fwd_masked.  total_q = 0 or max_seqlen_q = 0 is a no-op.
+ * attn_fwd_masked.  total_q = 0 or max_seqlen_q = 0 is a no-op; with total_k = 0 (no keys:
+ * every row gets O = 0, LSE = -inf) k and v may be NULL.
  */
 int attn_fwd_varlen(const void* q, const void* k, const void* v,
                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
@@ -356,6 +357,22 @@ int attn_prefill_fp8(const void* q, const void* k, const void* v,
                      const uint8_t* key_padding_mask, void* o, float* lse,
                      int B, int H_q, int H_kv, int Tq, int Tk, int D, int causal,
                      float scale, void* stream);
+
+/*
+ * attn_prefill_varlen_fp8 — attn_prefill_varlen on E4M3 inputs, with the LSE: the packed call a
+ * ring-attention hop makes (sglang PR 49078 analysis, section "1. aiter.py"), in the FP8 form
+ * that analysis finds without an LSE output.  Layouts as attn_prefill_varlen with uint8 codes
+ * for q [total_q, H_q, D] and k, v [total_k, H_kv, D]; q_scale [B, H_q], k_scale and v_scale
+ * [B, H_kv] float32, one per (sequence, head), as attn_prefill_fp8; o [total_q, H_q, D] bf16,
+ * lse [H_q, total_q] float32 or NULL.  Size limits and errors as attn_prefill_varlen;
+ * total_q = 0 or max_seqlen_q = 0 is a no-op.
+ */
+int attn_prefill_varlen_fp8(const void* q, const void* k, const void* v,
+                            const float* q_scale, const float* k_scale, const float* v_scale,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            void* o, float* lse, int B, int H_q, int H_kv,
+                            int total_q, int total_k, int max_seqlen_q, int D, int causal,
+                            float scale, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(int status);

@@ -32,7 +32,7 @@ STATUS = {
 EXPORTS = ("attn_fwd_masked", "attn_fwd_lse", "attn_fwd_varlen", "attn_merge_lse", "kv_append",
            "attn_decode", "attn_decode_workspace_bytes", "kv_append_paged", "attn_decode_paged",
            "attn_prefill", "attn_prefill_varlen", "kv_append_fp8", "attn_decode_fp8kv", "attn_prefill_fp8",
-           "kv_append_int8", "attn_decode_int8kv", "attn_status_string")
+           "kv_append_int8", "attn_decode_int8kv", "attn_prefill_varlen_fp8", "attn_status_string")
 
 _lib = None
 
@@ -66,6 +66,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_decode_fp8kv.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, S, P]
     lib.kv_append_int8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
     lib.attn_decode_int8kv.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, S, P]
+    lib.attn_prefill_varlen_fp8.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
     lib.attn_prefill_fp8.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
     lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, S, P]
     lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -75,7 +76,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("attn_fwd_masked", "attn_fwd_lse", "attn_fwd_varlen", "attn_merge_lse", "kv_append",
                  "attn_decode", "kv_append_paged", "attn_decode_paged", "attn_prefill", "attn_prefill_varlen",
                  "kv_append_fp8", "attn_decode_fp8kv", "attn_prefill_fp8", "kv_append_int8",
-                 "attn_decode_int8kv"):
+                 "attn_decode_int8kv", "attn_prefill_varlen_fp8"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -560,4 +561,41 @@ def attn_prefill_fp8(q, k, v, q_scale, k_scale, v_scale, key_padding_mask=None, 
         _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(key_padding_mask),
         _ptr(out), _ptr(lse if want_lse else None), B, Hq, Hkv, Tq, Tk, D, 1 if causal else 0, float(scale),
         _stream(q.device)))
+    return (out, lse) if want_lse else out
+
+
+def attn_prefill_varlen_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                            causal=False, scale=None, out=None, lse=None, want_lse: bool = True):
+    """attn_prefill_varlen on E4M3 codes: q uint8 [total_q, H_q, D], k/v uint8 [total_k, H_kv, D]
+    (or torch.float8_e4m3fn), per-(sequence, head) float32 scales q_scale [B, H_q], k_scale /
+    v_scale [B, H_kv].  Returns O bf16 [total_q, H_q, D] (and the LSE [H_q, total_q])."""
+    q, k, v = (t.view(torch.uint8) if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn else t
+               for t in (q, k, v))
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale"),
+                 (cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
+        _dev(t, n)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or q.dtype != torch.uint8 or k.dtype != torch.uint8 \
+            or v.dtype != torch.uint8:
+        raise ValueError("q, k, v must be E4M3 codes [total, H, D]")
+    total_q, Hq, D = q.shape
+    total_k, Hkv, _ = k.shape
+    if k.shape[2] != D or v.shape != k.shape:
+        raise ValueError("k/v must be [total_k, H_kv, D] with q's D")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32 or cu_seqlens_q.dim() != 1 \
+            or cu_seqlens_k.shape != cu_seqlens_q.shape:
+        raise ValueError("cu_seqlens_q / cu_seqlens_k must be int32 [B + 1]")
+    B = cu_seqlens_q.numel() - 1
+    for t, n, shp in ((q_scale, "q_scale", (B, Hq)), (k_scale, "k_scale", (B, Hkv)), (v_scale, "v_scale", (B, Hkv))):
+        if t.shape != shp or t.dtype != torch.float32:
+            raise ValueError(f"{n} must be float32 {list(shp)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((total_q, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    _check("attn_prefill_varlen_fp8", load().attn_prefill_varlen_fp8(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(cu_seqlens_q),
+        _ptr(cu_seqlens_k), _ptr(out), _ptr(lse if want_lse else None), B, Hq, Hkv, total_q, total_k,
+        int(max_seqlen_q), D, 1 if causal else 0, float(scale), _stream(q.device)))
     return (out, lse) if want_lse else out

@@ -57,7 +57,8 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* cu
                   const int32_t* cu_seqlens_k, void* o, float* lse, int B, int H, int H_kv,
                   int total_q, int total_k, int max_seqlen_q, int D, bool causal, float scale,
                   int dtype, void* stream) {
-    if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL;
+    // with no keys at all (total_k = 0) k and v are never read and may be null
+    if (!q || !o || !cu_seqlens_q || !cu_seqlens_k || (total_k > 0 && (!k || !v))) return ATTN_ERR_NULL;
     if (!dtype_ok(dtype) || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
     if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0 || total_q < 0 || total_k < 0 ||
@@ -318,6 +319,45 @@ int attn_prefill_fp8(const void* q, const void* k, const void* v, const float* q
     FwdArgs a{q, k, v, key_padding_mask, o, lse, B, H_q, Tq, Tk, D, scale, stream};
     a.H_kv = H_kv;
     a.causal = causal != 0;
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    return finish(D == 64 ? launch_fwd_fp8_d64(a) : launch_fwd_fp8_d128(a));
+}
+
+int attn_prefill_varlen_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                            const float* k_scale, const float* v_scale, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, void* o, float* lse, int B, int H_q, int H_kv,
+                            int total_q, int total_k, int max_seqlen_q, int D, int causal, float scale,
+                            void* stream) {
+    // with no keys at all (total_k = 0) k and v are never read and may be null
+    if (!q || !q_scale || !k_scale || !v_scale || !o || !cu_seqlens_q || !cu_seqlens_k ||
+        (total_k > 0 && (!k || !v)))
+        return ATTN_ERR_NULL;
+    if (!head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+    if (B < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 ||
+        max_seqlen_q > total_q)
+        return ATTN_ERR_SHAPE;
+    // as the bf16 packed call: one packed row is H·D codes, and tile offsets of 64 rows fit the
+    // 32-bit buffer offset (the O rows are bf16, so the same element bounds hold)
+    if ((long long)H_q * D > (1ll << 22) || (long long)total_q * H_q * D > (1ll << 31) - 1 ||
+        (long long)total_k * H_kv * D > (1ll << 30) - 1 ||
+        (long long)B * H_q * ((max_seqlen_q + 127) / 128) > (1ll << 31) - 64)
+        return ATTN_ERR_SHAPE;
+    if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
+    if (o == q || o == k || o == v || (lse && ((void*)lse == q || (void*)lse == k || (void*)lse == v ||
+                                               (void*)lse == o)))
+        return ATTN_ERR_ALIAS;
+    if (total_q == 0 || max_seqlen_q == 0) return ATTN_OK;      // no query rows: nothing to write
+    FwdArgs a{q, k, v, nullptr, o, lse, B, H_q, max_seqlen_q, 0, D, scale, stream};
+    a.H_kv = H_kv;
+    a.causal = causal != 0;
+    a.varlen = true;
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.total_q = total_q;
+    a.total_k = total_k;
     a.q_scale = q_scale;
     a.k_scale = k_scale;
     a.v_scale = v_scale;

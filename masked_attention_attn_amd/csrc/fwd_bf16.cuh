@@ -130,7 +130,7 @@ __device__ __forceinline__ f32x16 mfma_e4m3(i32x8 a, i32x8 b, f32x16 acc) {
 // sequences back to back at the offsets cu_q / cu_k (B+1 entries, clamped to
 // [0, total]); lse [H, total_q]; no mask; Tq = the longest sequence (grid).
 // Query head h reads KV head h / (H / H_kv).
-// FP8 (dense layout only): q, k, v are E4M3 codes; qsc [B, H], ksc and vsc [B, H_kv].
+// FP8: q, k, v are E4M3 codes (either layout); qsc [B, H], ksc and vsc [B, H_kv] (b = sequence).
 // CAUSAL: query i of a sequence sees keys j <= i + (Tk - Tq) only.  A workgroup's
 // key range ends at its last query's limit, the per-query limit is applied on
 // the key blocks that cross a wave's diagonal, and q-tiles run last-first
@@ -144,7 +144,6 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
                      const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                      int total_q, int total_k, const float* __restrict__ qsc,
                      const float* __restrict__ ksc, const float* __restrict__ vsc) {
-    static_assert(!(FP8 && VARLEN), "the FP8 variant takes the dense layout");
     using L = Lds<D, FP8>;
     using ET = Elem<FP8>;
     constexpr int ES = (int)sizeof(ET);   // bytes per Q/K/V element in HBM
@@ -846,12 +845,16 @@ hipError_t launch(const FwdArgs& a) {
     return a.lse ? launch_lse<D, true>(a) : launch_lse<D, false>(a);
 }
 
-// E4M3 inputs, dense layout (GQA, padding and causal as in the bf16 kernel).
+// E4M3 inputs, either layout (GQA, padding and causal as in the bf16 kernel).
+template <int D, bool WRITE_LSE>
+hipError_t launch_fp8_lse(const FwdArgs& a) {
+    if (a.varlen)
+        return a.causal ? launch_one<D, WRITE_LSE, true, true, true>(a) : launch_one<D, WRITE_LSE, true, false, true>(a);
+    return a.causal ? launch_one<D, WRITE_LSE, false, true, true>(a) : launch_one<D, WRITE_LSE, false, false, true>(a);
+}
 template <int D>
 hipError_t launch_fp8(const FwdArgs& a) {
-    if (a.lse)
-        return a.causal ? launch_one<D, true, false, true, true>(a) : launch_one<D, true, false, false, true>(a);
-    return a.causal ? launch_one<D, false, false, true, true>(a) : launch_one<D, false, false, false, true>(a);
+    return a.lse ? launch_fp8_lse<D, true>(a) : launch_fp8_lse<D, false>(a);
 }
 
 }  // namespace fwdk

@@ -235,6 +235,7 @@ def test_prefill_validation(lib):
     assert pv(mq=101) == 2
     assert pv(o=A) == 8
     assert pv(tq=0, mq=0) == 0
+    assert pv(k=0) == 1
 
 
 def test_fp8_validation(lib):
@@ -310,3 +311,24 @@ def test_int8_validation(lib):
     assert lib.kv_append_int8(A, B_, KS, VS, L, C, O, 2, 2, 16, 64, 5, None) == 3
     assert lib.kv_append_int8(A, B_, KS, VS, L, C, O, 2, 0, 16, 64, 1, None) == 2
     assert lib.kv_append_int8(A, A, KS, VS, L, C, O, 2, 2, 16, 64, 1, None) == 8
+
+
+def test_prefill_varlen_fp8_validation(lib):
+    QS, KS, VS, CQ, CK = 0x70000, 0x80000, 0x90000, 0xA0000, 0xB0000
+
+    def pv(**kw):
+        a = dict(q=A, k=B_, v=C, qs=QS, ks=KS, vs=VS, cq=CQ, ck=CK, o=O, lse=L, B=2, Hq=8, Hkv=2, tq=100, tk=90,
+                 mq=60, D=128, causal=1, scale=0.088)
+        a.update(kw)
+        return lib.attn_prefill_varlen_fp8(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["cq"], a["ck"],
+                                           a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["tq"], a["tk"], a["mq"],
+                                           a["D"], a["causal"], a["scale"], None)
+    assert pv(qs=0) == 1
+    assert pv(cq=0) == 1
+    assert pv(D=96) == 3
+    assert pv(Hq=8, Hkv=3) == 2
+    assert pv(mq=101) == 2
+    assert pv(scale=0.0) == 6
+    assert pv(q=A + 8) == 7
+    assert pv(o=A) == 8
+    assert pv(tq=0, mq=0) == 0

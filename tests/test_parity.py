@@ -895,3 +895,57 @@ def test_prefill_rescale_inside_step(ma, D, fp8, half):
                                v.to(torch.bfloat16).to(DEV), None, False, scale)
     torch.cuda.synchronize()
     check_attn(o, l, Or, Lr, torch.bfloat16, f"prefill rescale inside a step D={D} fp8={fp8} half={half}")
+
+
+# ---- packed (varlen) FP8 prefill ---------------------------------------------------------------
+
+VARLEN_FP8 = [
+    # lens_q, lens_k, H_q, H_kv, D, causal
+    ([300, 0, 513, 64], [300, 10, 513, 100], 4, 2, 64, True),
+    ([1, 257, 40], [1, 257, 600], 8, 2, 128, True),
+    ([700, 129], [700, 129], 2, 1, 64, False),
+    ([100, 300], [40, 300], 4, 4, 128, True),       # Tq > Tk in the first sequence
+    ([333], [0], 2, 2, 64, False),                  # no keys at all
+]
+
+
+def _fp8v_dev(w):
+    return tuple(t.to(DEV) for t in (w.q, w.k, w.v, w.q_scale, w.k_scale, w.v_scale, w.cu_q, w.cu_k))
+
+
+@pytest.mark.parametrize("case", VARLEN_FP8)
+def test_prefill_varlen_fp8(ma, case):
+    lq, lk, Hq, Hkv, D, causal = case
+    w = W.make_varlen_fp8(lq, lk, Hq, D, H_kv=Hkv, seed=len(lq) * 10 + Hq + D)
+    q, k, v, qs, ks, vs, cq, ck = _fp8v_dev(w)
+    o, l = ma.attn_prefill_varlen_fp8(q, k, v, qs, ks, vs, cq, ck, w.max_q, causal, w.scale)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.prefill_varlen_fp8(w.q, w.k, w.v, w.q_scale, w.k_scale, w.v_scale, w.cu_q, w.cu_k,
+                                       causal, w.scale)
+    check_attn(o, l.t(), Or, Lr.T, torch.bfloat16, f"packed fp8 prefill {case}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_varlen_fp8_bitwise_equals_dense(ma, D):
+    # one packed sequence is the dense [1, H, T, D] call on the same codes, bit for bit
+    w = W.make_varlen_fp8([700], [900], 8, D, H_kv=2, seed=D + 1)
+    q, k, v, qs, ks, vs, cq, ck = _fp8v_dev(w)
+    o1, l1 = ma.attn_prefill_varlen_fp8(q, k, v, qs, ks, vs, cq, ck, w.max_q, True, w.scale)
+    dense = lambda t: t.transpose(0, 1).unsqueeze(0).contiguous()
+    o2, l2 = ma.attn_prefill_fp8(dense(q), dense(k), dense(v), qs, ks, vs, None, True, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2[0].transpose(0, 1)) and torch.equal(l1, l2[0])
+
+
+def test_varlen_ring_hop_8192_fp8_sampled_rows(ma):
+    """The E4M3 packed ring hop (8,192 queries x 8,192 keys, H24 D128) on sampled rows."""
+    w = W.varlen_ring_hop_8192_fp8()
+    q, k, v, qs, ks, vs, cq, ck = _fp8v_dev(w)
+    o, l = ma.attn_prefill_varlen_fp8(q, k, v, qs, ks, vs, cq, ck, w.max_q, False, w.scale)
+    torch.cuda.synchronize()
+    rows = [0, 1, 255, 256, 4095, 8191] + list(range(11, 8192, 997))
+    dq = lambda t: t.transpose(0, 1).unsqueeze(0)
+    Or, Lr = oracle.prefill_fp8(dq(w.q), dq(w.k), dq(w.v), w.q_scale, w.k_scale, w.v_scale, None, False, w.scale,
+                                rows=rows)
+    check_attn(o[rows].transpose(0, 1).unsqueeze(0), l[:, rows].unsqueeze(0), Or, Lr, torch.bfloat16,
+               "packed fp8 ring hop sampled rows")

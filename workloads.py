@@ -245,6 +245,50 @@ def make_varlen(lens_q, lens_k, H, D, dtype=torch.bfloat16, *, H_kv=None, amp=1.
     return Varlen(q, k, v, cq, ck, max([int(n) for n in lens_q]), float(scale), name)
 
 
+@dataclass
+class VarlenFp8:
+    """Packed prefill inputs as E4M3 codes with float32 scales per (sequence, head)."""
+    q: torch.Tensor        # [total_q, H_q, D] uint8
+    k: torch.Tensor        # [total_k, H_kv, D] uint8
+    v: torch.Tensor
+    q_scale: torch.Tensor  # [B, H_q] float32
+    k_scale: torch.Tensor  # [B, H_kv] float32
+    v_scale: torch.Tensor
+    cu_q: torch.Tensor     # int32 [B + 1]
+    cu_k: torch.Tensor
+    max_q: int
+    scale: float
+    name: str = ""
+
+
+def make_varlen_fp8(lens_q, lens_k, H, D, *, H_kv=None, amp=1.0, seed=0, scale=None, name="") -> VarlenFp8:
+    """Packed E4M3 inputs whose dequantised values are about N(0, amp^2), with make_prefill_fp8's
+    recipe per (sequence, head): scale amp * 2^-e, e ~ U{2..6}, codes N(0,1) * 2^e cast to
+    float8_e4m3fn.  Draw order: Q, K, V scale exponents, then Q, K, V."""
+    H_kv = H if H_kv is None else H_kv
+    g = _gen(seed)
+    B = len(lens_q)
+    cq, ck = cu_from_lengths(lens_q), cu_from_lengths(lens_k)
+    tq, tk = int(cq[-1]), int(ck[-1])
+    eq = torch.randint(2, 7, (B, H), generator=g)
+    ek = torch.randint(2, 7, (B, H_kv), generator=g)
+    ev = torch.randint(2, 7, (B, H_kv), generator=g)
+    rq = torch.repeat_interleave(torch.arange(B), torch.as_tensor(lens_q, dtype=torch.int64))
+    rk = torch.repeat_interleave(torch.arange(B), torch.as_tensor(lens_k, dtype=torch.int64))
+
+    def codes(total, heads, e, rows):
+        x = torch.randn(total, heads, D, generator=g) * torch.exp2(e.float())[rows][:, :, None]
+        return x.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+
+    q = codes(tq, H, eq, rq)
+    k = codes(tk, H_kv, ek, rk)
+    v = codes(tk, H_kv, ev, rk)
+    sc = lambda e: (amp * torch.exp2(-e.float())).contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return VarlenFp8(q, k, v, sc(eq), sc(ek), sc(ev), cq, ck, max([int(n) for n in lens_q]), float(scale), name)
+
+
 def to_paged(dec: Decode, page_size: int, *, seed=1, spare_pages=3) -> Paged:
     """Scatter the contiguous caches of `dec` into shuffled physical pages.
 
@@ -451,3 +495,10 @@ def gqa_decode_b32_int8(seed=0) -> DecodeFp8:
     """The GQA decode workload (B32, H_q 32 / H_kv 8, D128, len U[512, 8192]) with an INT8 cache."""
     return make_decode_int8(32, 32, 8, 128, 512, 8192, seed=seed,
                             name="INT8-cache GQA decode B32 Hq32 Hkv8 D128, len U[512,8192] + 1 appended")
+
+
+def varlen_ring_hop_8192_fp8(seed=0) -> VarlenFp8:
+    """The packed ring hop (one sequence, 8,192 queries against an 8,192-key chunk, H24 D128) with
+    E4M3 inputs."""
+    return make_varlen_fp8([8192], [8192], 24, 128, seed=seed,
+                           name="E4M3 packed varlen ring hop H24 D128, 8192 queries x 8192-key chunk")
