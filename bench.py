@@ -273,8 +273,9 @@ def fp8_section(torch, ma, W, dev, int8=False):
 
 
 def fp8_prefill_section(torch, ma, W, dev):
-    """E4M3-input prefill with LSE (attn_prefill_fp8), each timed on its own: the P = 11,616 patch
-    shape (non-causal, padded keys) and the causal GQA 8,192-token prompt.  FLOP are algorithmic
+    """E4M3-input prefill with LSE, each timed on its own: the P = 11,616 patch shape (non-causal,
+    padded keys) and the causal GQA 8,192-token prompt (attn_prefill_fp8), and the packed ring hop
+    (attn_prefill_varlen_fp8).  FLOP are algorithmic
     as for the bf16 calls; frac_mfma is against the split fp8 / bf16 matrix-core bound."""
     res = {}
     for key, w, causal in (("p11616", W.patch_p11616_fp8(), False),
@@ -295,6 +296,19 @@ def fp8_prefill_section(torch, ma, W, dev):
                     "frac_mfma": round(flop / t / 1e12 / PEAK_FP8_PREFILL_TFLOPS, 4),
                     "peak_tflops": round(PEAK_FP8_PREFILL_TFLOPS, 1), "algorithmic_flop": flop}
         del q, k, v, o, lse
+    # the packed ring hop (attn_prefill_varlen_fp8)
+    w = W.varlen_ring_hop_8192_fp8()
+    q, k, v, qs, ks, vs, cq, ck = (t_.to(dev) for t_ in (w.q, w.k, w.v, w.q_scale, w.k_scale, w.v_scale, w.cu_q,
+                                                          w.cu_k))
+    tq, Hq, D = q.shape
+    o = torch.empty((tq, Hq, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Hq, tq), dtype=torch.float32, device=dev)
+    t = _time_call(torch, lambda: ma.attn_prefill_varlen_fp8(q, k, v, qs, ks, vs, cq, ck, w.max_q, False, w.scale,
+                                                             out=o, lse=lse))
+    flop = 4 * D * Hq * sum(a * b for a, b in zip(w.cu_q.diff().tolist(), w.cu_k.diff().tolist()))
+    res["ring_hop_8192"] = {"workload": w.name, "us": round(t * 1e6, 1), "tflops": round(flop / t / 1e12, 1),
+                            "frac_mfma": round(flop / t / 1e12 / PEAK_FP8_PREFILL_TFLOPS, 4),
+                            "peak_tflops": round(PEAK_FP8_PREFILL_TFLOPS, 1), "algorithmic_flop": flop}
     return res
 
 
