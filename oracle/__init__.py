@@ -11,8 +11,9 @@ from .attention import (  # noqa: F401
 )
 from .fp8 import (  # noqa: F401
     E4M3_MAX, e4m3_values, quantize_e4m3, dequantize_e4m3, kv_append_fp8, decode_fp8kv,
-    prefill_fp8, prefill_varlen_fp8,
+    prefill_fp8, prefill_varlen_fp8, kv_append_fp8_paged, decode_fp8kv_paged,
 )
 from .int8 import (  # noqa: F401
-    INT8_MAX, quantize_int8, dequantize_int8, kv_append_int8, decode_int8kv,
+    INT8_MAX, quantize_int8, dequantize_int8, kv_append_int8, decode_int8kv, kv_append_int8_paged,
+    decode_int8kv_paged,
 )

@@ -31,10 +31,11 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import decode, prefill, prefill_varlen, _f64
+from .attention import decode, prefill, prefill_varlen, gather_pages, kv_append_paged, _f64
 
 __all__ = ["E4M3_MAX", "e4m3_values", "quantize_e4m3", "dequantize_e4m3", "kv_append_fp8", "decode_fp8kv",
-           "prefill_fp8", "prefill_varlen_fp8"]
+           "prefill_fp8", "prefill_varlen_fp8",
+           "kv_append_fp8_paged", "decode_fp8kv_paged"]
 
 E4M3_MAX = 448.0
 
@@ -154,3 +155,32 @@ def prefill_varlen_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seql
     kd = dequantize_e4m3(k, ks[bk][:, :, None])
     vd = dequantize_e4m3(v, vs[bk][:, :, None])
     return prefill_varlen(qd, kd, vd, cq, ck, causal, scale)
+
+
+def kv_append_fp8_paged(k_pages, v_pages, k_scale, v_scale, block_table, lens, k_new, v_new):
+    """``kv_append_fp8`` into page pools [num_pages, H_kv, page_size, D] of codes: the new token's
+    codes (quantised with its (b, KV head) scales) are written at logical slot lens[b] through
+    the block table, as ``kv_append_paged``.  Returns copies of the pools and lens + 1."""
+    ks, vs = _f64(k_scale), _f64(v_scale)
+    kn = quantize_e4m3(_f64(k_new), ks[:, :, None, None])
+    vn = quantize_e4m3(_f64(v_new), vs[:, :, None, None])
+    kp = np.asarray(k_pages.detach().cpu().numpy() if hasattr(k_pages, "detach") else k_pages)
+    vp = np.asarray(v_pages.detach().cpu().numpy() if hasattr(v_pages, "detach") else v_pages)
+    return kv_append_paged(kp.astype(np.uint8), vp.astype(np.uint8), block_table, lens, kn, vn)
+
+
+def decode_fp8kv_paged(q, k_pages, v_pages, k_scale, v_scale, block_table, lens, scale=None, heads=None):
+    """``decode_fp8kv`` over page pools of codes: each sequence's first lens[b] codes are gathered
+    through its block-table row into a contiguous cache, which is then decoded as
+    ``decode_fp8kv`` (per-(sequence, KV head) scales)."""
+    lens = np.asarray(lens).astype(np.int64)
+    kp, vp = _f64(k_pages), _f64(v_pages)
+    B, H_kv, D = lens.size, kp.shape[1], kp.shape[3]
+    T = max(1, int(lens.max()) if lens.size else 1)
+    kc = np.zeros((B, H_kv, T, D), dtype=np.uint8)
+    vc = np.zeros((B, H_kv, T, D), dtype=np.uint8)
+    for b in range(B):
+        n = int(lens[b])
+        kc[b, :, :n] = gather_pages(kp, block_table, b, n).astype(np.uint8)
+        vc[b, :, :n] = gather_pages(vp, block_table, b, n).astype(np.uint8)
+    return decode_fp8kv(q, kc, vc, k_scale, v_scale, lens, scale, heads)

@@ -20,9 +20,10 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import decode, _f64
+from .attention import decode, gather_pages, kv_append_paged, _f64
 
-__all__ = ["INT8_MAX", "quantize_int8", "dequantize_int8", "kv_append_int8", "decode_int8kv"]
+__all__ = ["INT8_MAX", "quantize_int8", "dequantize_int8", "kv_append_int8", "decode_int8kv",
+           "kv_append_int8_paged", "decode_int8kv_paged"]
 
 INT8_MAX = 127
 
@@ -68,3 +69,32 @@ def decode_int8kv(q, k_cache, v_cache, k_scale, v_scale, lens, scale=None, heads
     kd = dequantize_int8(k_cache, _f64(k_scale)[:, :, None, None])
     vd = dequantize_int8(v_cache, _f64(v_scale)[:, :, None, None])
     return decode(q, kd, vd, lens, scale, heads)
+
+
+def kv_append_int8_paged(k_pages, v_pages, k_scale, v_scale, block_table, lens, k_new, v_new):
+    """``kv_append_int8`` into page pools [num_pages, H_kv, page_size, D] of codes: the new token's
+    codes (quantised with its (b, KV head) scales) are written at logical slot lens[b] through
+    the block table, as ``kv_append_paged``.  Returns copies of the pools and lens + 1."""
+    ks, vs = _f64(k_scale), _f64(v_scale)
+    kn = quantize_int8(_f64(k_new), ks[:, :, None, None])
+    vn = quantize_int8(_f64(v_new), vs[:, :, None, None])
+    kp = np.asarray(k_pages.detach().cpu().numpy() if hasattr(k_pages, "detach") else k_pages)
+    vp = np.asarray(v_pages.detach().cpu().numpy() if hasattr(v_pages, "detach") else v_pages)
+    return kv_append_paged(kp.astype(np.int8), vp.astype(np.int8), block_table, lens, kn, vn)
+
+
+def decode_int8kv_paged(q, k_pages, v_pages, k_scale, v_scale, block_table, lens, scale=None, heads=None):
+    """``decode_int8kv`` over page pools of codes: each sequence's first lens[b] codes are gathered
+    through its block-table row into a contiguous cache, which is then decoded as
+    ``decode_int8kv`` (per-(sequence, KV head) scales)."""
+    lens = np.asarray(lens).astype(np.int64)
+    kp, vp = _f64(k_pages), _f64(v_pages)
+    B, H_kv, D = lens.size, kp.shape[1], kp.shape[3]
+    T = max(1, int(lens.max()) if lens.size else 1)
+    kc = np.zeros((B, H_kv, T, D), dtype=np.int8)
+    vc = np.zeros((B, H_kv, T, D), dtype=np.int8)
+    for b in range(B):
+        n = int(lens[b])
+        kc[b, :, :n] = gather_pages(kp, block_table, b, n).astype(np.int8)
+        vc[b, :, :n] = gather_pages(vp, block_table, b, n).astype(np.int8)
+    return decode_int8kv(q, kc, vc, k_scale, v_scale, lens, scale, heads)

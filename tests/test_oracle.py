@@ -857,3 +857,43 @@ def test_prefill_varlen_fp8_equals_dense_per_sequence():
         O2, L2 = oracle.prefill_varlen_fp8(q8, k8, v8, qs2, ks, vs, cq, ck, causal, 0.6)
         other = np.r_[0:cq[2], cq[3]:cq[-1]]
         assert np.array_equal(O2[other], O[other]) and not np.allclose(O2[cq[2]:cq[3]], O[cq[2]:cq[3]])
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_paged_8bit_equals_contiguous(fmt):
+    # the paged 8-bit append + decode equal the contiguous ones on the same codes, through an
+    # identity table and through shuffled physical pages (a relabelling changes nothing)
+    r = _rng(330)
+    B, Hkv, G, D, ps, mp = 3, 2, 2, 8, 4, 5
+    T = ps * mp
+    if fmt == "fp8":
+        codes = lambda shp: _e4m3_codes(r, shp)
+        append, decode = oracle.kv_append_fp8, oracle.decode_fp8kv
+        append_p, decode_p = oracle.kv_append_fp8_paged, oracle.decode_fp8kv_paged
+    else:
+        codes = lambda shp: r.integers(-128, 128, shp).astype(np.int8)
+        append, decode = oracle.kv_append_int8, oracle.decode_int8kv
+        append_p, decode_p = oracle.kv_append_int8_paged, oracle.decode_int8kv_paged
+    kc, vc = codes((B, Hkv, T, D)), codes((B, Hkv, T, D))
+    ks, vs = r.uniform(0.01, 0.1, (B, Hkv)).astype(np.float32), r.uniform(0.01, 0.1, (B, Hkv)).astype(np.float32)
+    kn, vn = r.standard_normal((B, Hkv, 1, D)), r.standard_normal((B, Hkv, 1, D))
+    lens = np.array([0, 7, T - 1])
+    q = r.standard_normal((B, Hkv * G, 1, D))
+    ek, ev, el = append(kc, vc, ks, vs, lens, kn, vn)
+    O, L = decode(q, ek, ev, ks, vs, el, 0.5)
+    for shuffle in (False, True):
+        perm = r.permutation(B * mp + 2) if shuffle else np.arange(B * mp + 2)
+        bt = perm[:B * mp].reshape(B, mp)
+        kp, vp = codes((B * mp + 2, Hkv, ps, D)), codes((B * mp + 2, Hkv, ps, D))
+        for b in range(B):
+            for i in range(mp):
+                kp[bt[b, i]] = kc[b, :, i * ps:(i + 1) * ps]
+                vp[bt[b, i]] = vc[b, :, i * ps:(i + 1) * ps]
+        kp2, vp2, el2 = append_p(kp, vp, ks, vs, bt, lens, kn, vn)
+        assert el2.tolist() == el.tolist()
+        for b in range(B):
+            t = int(lens[b])
+            assert np.array_equal(kp2[bt[b, t // ps], :, t % ps], ek[b, :, t])
+            assert np.array_equal(vp2[bt[b, t // ps], :, t % ps], ev[b, :, t])
+        Op, Lp = decode_p(q, kp2, vp2, ks, vs, bt, el2, 0.5)
+        assert np.array_equal(Op, O) and np.array_equal(Lp, L)
