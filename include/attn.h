@@ -334,6 +334,39 @@ int attn_decode_int8kv(const void* q, const void* k_cache, const void* v_cache,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Paged 8-bit caches: the FP8 and INT8 calls above over page pools, the paged
+ * layout of attn_decode_paged (LLM inference memory accounting 2/10, sections
+ * "15. Paged KV Cache가 해결하는 것" and "18. KV Cache Quantization").
+ *   k_pages, v_pages  [num_pages, H_kv, page_size, D] codes (uint8 E4M3 or int8)
+ *   block_table, page_size, max_pages_per_seq  as attn_decode_paged (T_max =
+ *       max_pages_per_seq · page_size; the workspace is sized with that T_max)
+ *   k_scale, v_scale  [B, H_kv] float32, per (sequence, KV head), as the contiguous calls
+ * Quantisation, results and errors as the contiguous 8-bit calls; paging rules
+ * (page sizes, clamped table entries) as the bf16 paged calls.
+ */
+int kv_append_fp8_paged(void* k_pages, void* v_pages, const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, int32_t* cache_seqlens,
+                        const void* k_new, const void* v_new, int B, int H_kv, int num_pages,
+                        int page_size, int max_pages_per_seq, int D, int new_dtype, void* stream);
+
+int kv_append_int8_paged(void* k_pages, void* v_pages, const float* k_scale, const float* v_scale,
+                         const int32_t* block_table, int32_t* cache_seqlens,
+                         const void* k_new, const void* v_new, int B, int H_kv, int num_pages,
+                         int page_size, int max_pages_per_seq, int D, int new_dtype, void* stream);
+
+int attn_decode_fp8kv_paged(const void* q, const void* k_pages, const void* v_pages,
+                            const float* k_scale, const float* v_scale, const int32_t* block_table,
+                            const int32_t* cache_seqlens, void* o, float* lse, int B, int H_q,
+                            int H_kv, int num_pages, int page_size, int max_pages_per_seq, int D,
+                            float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+int attn_decode_int8kv_paged(const void* q, const void* k_pages, const void* v_pages,
+                             const float* k_scale, const float* v_scale, const int32_t* block_table,
+                             const int32_t* cache_seqlens, void* o, float* lse, int B, int H_q,
+                             int H_kv, int num_pages, int page_size, int max_pages_per_seq, int D,
+                             float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_prefill_fp8 — attn_prefill on E4M3 inputs, with the LSE.
  *
  * The aiter ring-attention analysis (sglang PR 49078 analysis, section

@@ -32,7 +32,8 @@ STATUS = {
 EXPORTS = ("attn_fwd_masked", "attn_fwd_lse", "attn_fwd_varlen", "attn_merge_lse", "kv_append",
            "attn_decode", "attn_decode_workspace_bytes", "kv_append_paged", "attn_decode_paged",
            "attn_prefill", "attn_prefill_varlen", "kv_append_fp8", "attn_decode_fp8kv", "attn_prefill_fp8",
-           "kv_append_int8", "attn_decode_int8kv", "attn_prefill_varlen_fp8", "attn_status_string")
+           "kv_append_int8", "attn_decode_int8kv", "attn_prefill_varlen_fp8", "kv_append_fp8_paged",
+           "kv_append_int8_paged", "attn_decode_fp8kv_paged", "attn_decode_int8kv_paged", "attn_status_string")
 
 _lib = None
 
@@ -67,6 +68,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kv_append_int8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
     lib.attn_decode_int8kv.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, S, P]
     lib.attn_prefill_varlen_fp8.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
+    for name in ("kv_append_fp8_paged", "kv_append_int8_paged"):
+        getattr(lib, name).argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    for name in ("attn_decode_fp8kv_paged", "attn_decode_int8kv_paged"):
+        getattr(lib, name).argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, S, P]
     lib.attn_prefill_fp8.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
     lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, S, P]
     lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -76,7 +81,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("attn_fwd_masked", "attn_fwd_lse", "attn_fwd_varlen", "attn_merge_lse", "kv_append",
                  "attn_decode", "kv_append_paged", "attn_decode_paged", "attn_prefill", "attn_prefill_varlen",
                  "kv_append_fp8", "attn_decode_fp8kv", "attn_prefill_fp8", "kv_append_int8",
-                 "attn_decode_int8kv", "attn_prefill_varlen_fp8"):
+                 "attn_decode_int8kv", "attn_prefill_varlen_fp8", "kv_append_fp8_paged", "kv_append_int8_paged",
+                 "attn_decode_fp8kv_paged", "attn_decode_int8kv_paged"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -599,3 +605,81 @@ def attn_prefill_varlen_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu
         _ptr(cu_seqlens_k), _ptr(out), _ptr(lse if want_lse else None), B, Hq, Hkv, total_q, total_k,
         int(max_seqlen_q), D, 1 if causal else 0, float(scale), _stream(q.device)))
     return (out, lse) if want_lse else out
+
+
+def _q8_paged_args(k_pages, v_pages, k_scale, v_scale, block_table, cache_seqlens, B, code_dtype):
+    num_pages, Hkv, ps, D, mp = _paged_args(k_pages, v_pages, block_table, cache_seqlens, B)
+    if k_pages.dtype != code_dtype or v_pages.dtype != code_dtype:
+        raise ValueError(f"k_pages / v_pages must hold {code_dtype} codes")
+    for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        _dev(t, n)
+        if t.shape != (B, Hkv) or t.dtype != torch.float32:
+            raise ValueError(f"{n} must be float32 [B, H_kv]")
+    return num_pages, Hkv, ps, D, mp
+
+
+def _q8_append_paged(fn, code_dtype, k_pages, v_pages, k_scale, v_scale, block_table, cache_seqlens, k_new, v_new):
+    _dev(k_new, "k_new")
+    _dev(v_new, "v_new")
+    B = k_new.shape[0]
+    num_pages, Hkv, ps, D, mp = _q8_paged_args(k_pages, v_pages, k_scale, v_scale, block_table, cache_seqlens, B,
+                                               code_dtype)
+    if k_new.shape != (B, Hkv, 1, D) or v_new.shape != (B, Hkv, 1, D) or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new / v_new must be [B, H_kv, 1, D] of one dtype")
+    _check(fn, getattr(load(), fn)(
+        _ptr(k_pages), _ptr(v_pages), _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(cache_seqlens),
+        _ptr(k_new), _ptr(v_new), B, Hkv, num_pages, ps, mp, D, _dtype_code(k_new), _stream(k_pages.device)))
+
+
+def _q8_decode_paged(fn, code_dtype, q, k_pages, v_pages, k_scale, v_scale, block_table, cache_seqlens, scale, out,
+                     lse, workspace, want_lse):
+    _dev(q, "q")
+    if q.dim() != 4 or q.shape[2] != 1 or q.dtype != torch.bfloat16:
+        raise ValueError("q must be bfloat16 [B, H_q, 1, D]")
+    B, Hq, _, D = q.shape
+    num_pages, Hkv, ps, Dk, mp = _q8_paged_args(k_pages, v_pages, k_scale, v_scale, block_table, cache_seqlens, B,
+                                                code_dtype)
+    if Dk != D:
+        raise ValueError("pool head_dim does not match q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, mp * ps, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(fn, getattr(load(), fn)(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(cache_seqlens),
+        _ptr(out), _ptr(lse if want_lse else None), B, Hq, Hkv, num_pages, ps, mp, D, float(scale), _ptr(workspace),
+        nbytes, _stream(q.device)))
+    return (out, lse) if want_lse else out
+
+
+def kv_append_fp8_paged(k_pages, v_pages, k_scale, v_scale, block_table, cache_seqlens, k_new, v_new):
+    """kv_append_fp8 into E4M3 page pools [num_pages, H_kv, page_size, D] (uint8) through block_table."""
+    _q8_append_paged("kv_append_fp8_paged", torch.uint8, k_pages, v_pages, k_scale, v_scale, block_table,
+                     cache_seqlens, k_new, v_new)
+
+
+def kv_append_int8_paged(k_pages, v_pages, k_scale, v_scale, block_table, cache_seqlens, k_new, v_new):
+    """kv_append_int8 into INT8 page pools [num_pages, H_kv, page_size, D] (int8) through block_table."""
+    _q8_append_paged("kv_append_int8_paged", torch.int8, k_pages, v_pages, k_scale, v_scale, block_table,
+                     cache_seqlens, k_new, v_new)
+
+
+def attn_decode_fp8kv_paged(q, k_pages, v_pages, k_scale, v_scale, block_table, cache_seqlens, scale=None, out=None,
+                            lse=None, workspace=None, want_lse: bool = False):
+    """attn_decode_fp8kv over E4M3 page pools through block_table [B, max_pages]."""
+    return _q8_decode_paged("attn_decode_fp8kv_paged", torch.uint8, q, k_pages, v_pages, k_scale, v_scale,
+                            block_table, cache_seqlens, scale, out, lse, workspace, want_lse)
+
+
+def attn_decode_int8kv_paged(q, k_pages, v_pages, k_scale, v_scale, block_table, cache_seqlens, scale=None, out=None,
+                             lse=None, workspace=None, want_lse: bool = False):
+    """attn_decode_int8kv over INT8 page pools through block_table [B, max_pages]."""
+    return _q8_decode_paged("attn_decode_int8kv_paged", torch.int8, q, k_pages, v_pages, k_scale, v_scale,
+                            block_table, cache_seqlens, scale, out, lse, workspace, want_lse)

@@ -218,6 +218,57 @@ static int paged_geometry(int B, int H_kv, int num_pages, int page_size, int max
     return ATTN_OK;
 }
 
+// 8-bit paged pools: shared checks of the append and decode calls.
+static int q8_append_paged(void* k_pages, void* v_pages, const float* k_scale, const float* v_scale,
+                           const int32_t* block_table, int32_t* cache_seqlens, const void* k_new,
+                           const void* v_new, int B, int H_kv, int num_pages, int page_size, int max_pages,
+                           int D, int new_dtype, void* stream, bool int8) {
+    if (!k_pages || !v_pages || !k_scale || !v_scale || !block_table || !cache_seqlens || !k_new || !v_new)
+        return ATTN_ERR_NULL;
+    if (!dtype_ok(new_dtype) || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+    if (B < 1 || H_kv < 1 || B > (1 << 30)) return ATTN_ERR_SHAPE;
+    int T_max = 0;
+    if (const int st = paged_geometry(B, H_kv, num_pages, page_size, max_pages, D, T_max)) return st;
+    if (!aligned16(k_pages) || !aligned16(v_pages) || !aligned16(k_new) || !aligned16(v_new))
+        return ATTN_ERR_ALIGN;
+    if (k_pages == v_pages || k_new == k_pages || v_new == v_pages) return ATTN_ERR_ALIAS;
+    AppendFp8Args a{k_pages, v_pages, k_scale, v_scale, cache_seqlens, k_new, v_new,
+                    new_dtype == ATTN_BF16, B, H_kv, T_max, D, stream};
+    a.int8 = int8;
+    a.block_table = block_table;
+    a.page_size = page_size;
+    a.max_pages = max_pages;
+    a.num_pages = num_pages;
+    return finish(launch_kv_append_fp8(a));
+}
+
+static int q8_decode_paged(const void* q, const void* k_pages, const void* v_pages, const float* k_scale,
+                           const float* v_scale, const int32_t* block_table, const int32_t* cache_seqlens,
+                           void* o, float* lse, int B, int H_q, int H_kv, int num_pages, int page_size,
+                           int max_pages, int D, float scale, void* workspace, size_t workspace_bytes,
+                           void* stream, bool int8) {
+    if (!q || !k_pages || !v_pages || !k_scale || !v_scale || !block_table || !cache_seqlens || !o)
+        return ATTN_ERR_NULL;
+    if (!head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
+    if (H_kv <= 0 || H_q <= 0 || H_q % H_kv != 0) return ATTN_ERR_SHAPE;
+    if (!fits(B, H_q, 1, D) || (long long)B * H_q > (1 << 30)) return ATTN_ERR_SHAPE;
+    int T_max = 0;
+    if (const int st = paged_geometry(B, H_kv, num_pages, page_size, max_pages, D, T_max)) return st;
+    if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
+    if (!workspace || workspace_bytes < decode_workspace_bytes(B, H_q, T_max, D)) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) || !aligned16(workspace))
+        return ATTN_ERR_ALIGN;
+    if (o == q || o == k_pages || o == v_pages) return ATTN_ERR_ALIAS;
+    DecodeFp8Args a{q, k_pages, v_pages, k_scale, v_scale, cache_seqlens, o, lse, B, H_q, H_kv, T_max, D,
+                    scale, workspace, stream};
+    a.int8 = int8;
+    a.block_table = block_table;
+    a.page_size = page_size;
+    a.max_pages = max_pages;
+    a.num_pages = num_pages;
+    return finish(launch_decode_fp8kv(a));
+}
+
 int kv_append_paged(void* k_pages, void* v_pages, const int32_t* block_table, int32_t* cache_seqlens,
                     const void* k_new, const void* v_new, int B, int H_kv, int num_pages,
                     int page_size, int max_pages_per_seq, int D, int dtype, void* stream) {
@@ -298,6 +349,42 @@ int attn_decode_int8kv(const void* q, const void* k_cache, const void* v_cache, 
                      workspace, workspace_bytes, stream, true);
 }
 
+
+int kv_append_fp8_paged(void* k_pages, void* v_pages, const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, int32_t* cache_seqlens, const void* k_new, const void* v_new,
+                        int B, int H_kv, int num_pages, int page_size, int max_pages_per_seq, int D,
+                        int new_dtype, void* stream) {
+    return q8_append_paged(k_pages, v_pages, k_scale, v_scale, block_table, cache_seqlens, k_new, v_new, B, H_kv,
+                           num_pages, page_size, max_pages_per_seq, D, new_dtype, stream, false);
+}
+
+int kv_append_int8_paged(void* k_pages, void* v_pages, const float* k_scale, const float* v_scale,
+                         const int32_t* block_table, int32_t* cache_seqlens, const void* k_new, const void* v_new,
+                         int B, int H_kv, int num_pages, int page_size, int max_pages_per_seq, int D,
+                         int new_dtype, void* stream) {
+    return q8_append_paged(k_pages, v_pages, k_scale, v_scale, block_table, cache_seqlens, k_new, v_new, B, H_kv,
+                           num_pages, page_size, max_pages_per_seq, D, new_dtype, stream, true);
+}
+
+int attn_decode_fp8kv_paged(const void* q, const void* k_pages, const void* v_pages, const float* k_scale,
+                            const float* v_scale, const int32_t* block_table, const int32_t* cache_seqlens,
+                            void* o, float* lse, int B, int H_q, int H_kv, int num_pages, int page_size,
+                            int max_pages_per_seq, int D, float scale, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    return q8_decode_paged(q, k_pages, v_pages, k_scale, v_scale, block_table, cache_seqlens, o, lse, B, H_q, H_kv,
+                           num_pages, page_size, max_pages_per_seq, D, scale, workspace, workspace_bytes, stream,
+                           false);
+}
+
+int attn_decode_int8kv_paged(const void* q, const void* k_pages, const void* v_pages, const float* k_scale,
+                             const float* v_scale, const int32_t* block_table, const int32_t* cache_seqlens,
+                             void* o, float* lse, int B, int H_q, int H_kv, int num_pages, int page_size,
+                             int max_pages_per_seq, int D, float scale, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    return q8_decode_paged(q, k_pages, v_pages, k_scale, v_scale, block_table, cache_seqlens, o, lse, B, H_q, H_kv,
+                           num_pages, page_size, max_pages_per_seq, D, scale, workspace, workspace_bytes, stream,
+                           true);
+}
 
 int attn_prefill_fp8(const void* q, const void* k, const void* v, const float* q_scale,
                      const float* k_scale, const float* v_scale, const uint8_t* key_padding_mask, void* o,

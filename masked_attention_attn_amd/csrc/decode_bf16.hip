@@ -245,7 +245,11 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
     for (int db = 0; db < DB; ++db) v_lane[db] = (uint32_t)((vrow * D + (((db * 4 + vc0) ^ vfv) * 8) + vin) * 2);
     // V of block j lands before the loads of the three blocks issued after it
     // (3 x (NCH + KSTEPS) loads, plus any Q loads and partial stores): waiting for
-    // at most that many outstanding makes slot j's V complete.
+    // at most that many outstanding makes slot j's V complete.  The same holds for the
+    // Q of an item, issued right after the V of its first block here (or of the
+    // wavefront's first block): at least NV_AFTER loads follow it by the time that
+    // block is computed, also at the first block of the range.  The compiler derives
+    // no wait for reading the Q slot after its buffer->LDS loads, so it is explicit.
     constexpr int NV_AFTER = (RV - 1) * (NCH + KSTEPS);
     static_assert(NV_AFTER <= 63, "vmcnt range");
 
@@ -254,6 +258,7 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
         const int col = hg * 32 + l32;
         const bool col_ok = col < G;
         if (need_q) {                    // first block of an item: Q from its LDS slot
+            wait_vmem_le<NV_AFTER>();    // the slot's buffer->LDS loads have landed
             // rows past the group's heads are not in the slot: read row 0 there, then zero
             const bf16* qrow = reinterpret_cast<const bf16*>(qslot(qs)) + (col_ok ? l32 : 0) * D;
 #pragma unroll

@@ -45,14 +45,19 @@ __device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff)
 
 // At D = 128 the K and V register rings alone fill 256 registers: one wavefront per SIMD,
 // with the accumulation registers as well (no spills).
-template <int D, bool INT8>
+// PAGED: kc / vc are page pools [num_pages, H_kv, 2^lps, D] of codes; token t of sequence b is
+// row t mod 2^lps of page bt[b * max_pages + (t >> lps)] (entries clamped to [0, num_pages)),
+// T_max = max_pages << lps.  V of a 32-token block is loaded as two 16-token halves, each
+// through the buffer range of its page; K by per-lane global loads from the page of each key.
+template <int D, bool INT8, bool PAGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, D == 128 ? 1 : 8)))
 void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc,
                        const uint8_t* __restrict__ vc, const float* __restrict__ kscale,
                        const float* __restrict__ vscale, const int32_t* __restrict__ lens,
                        float* __restrict__ ws_o, float* __restrict__ ws_ml,
                        int B, int H_q, int H_kv, int T_max, int G, int n_hg, int nsplit,
-                       int nwaves, int qb, float c) {
+                       int nwaves, int qb, float c, const int32_t* __restrict__ bt, int max_pages,
+                       int num_pages, int lps) {
     using Gm = Geo8<D, INT8>;
     constexpr int RB = Gm::RB, NV = Gm::NV, QCH = Gm::QCH, RV = Gm::RV, LK = Gm::LK;
     constexpr int KSTEPS = D / 16;     // MFMA k-steps of K·Qᵀ
@@ -93,6 +98,36 @@ void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc
         v_dst[i] = (uint32_t)(r * RB16 + (g0 ^ v_swz<D>(r)) * 16);
     }
     const __amdgpu_buffer_rsrc_t zrs = brsrc(kc, 0u);
+    constexpr int HNV = NV / 2;           // V loads per 16-row half of a block
+    static_assert(HNV * 2 == NV && HNV * 1024 == 16 * RB, "a V load lies inside one half");
+
+    // Paged: the V buffer ranges of the two 16-token halves of block (cursor) x, each inside
+    // one page (pages are powers of two >= 16 tokens, blocks start at multiples of 32), and
+    // the row offset of each half within its range.
+    auto page_halves = [&](const Cursor& x, __amdgpu_buffer_rsrc_t* vh, uint32_t* roff) {
+        const int t0 = x.s * kDecodeSplit + x.i * CK;
+        const int last = x.t_end - 1;
+        const int pi0 = t0 >> lps, pi1 = min(t0 + 16, last) >> lps;
+        const uint32_t rowb = (uint32_t)x.b * (uint32_t)max_pages * 4u;
+        int e0, e1;
+        sload2(bt, __builtin_amdgcn_readfirstlane(rowb + (uint32_t)pi0 * 4u),
+               __builtin_amdgcn_readfirstlane(rowb + (uint32_t)pi1 * 4u), e0, e1);
+        const int pe[2] = {e0, e1}, pidx[2] = {pi0, pi1};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            vh[h] = zrs;
+            roff[h] = 0u;
+            const int th = t0 + 16 * h;
+            if (th < x.t_end) {
+                const int page = min(max(pe[h], 0), num_pages - 1);
+                const int pstart = pidx[h] << lps;
+                const int rows = min(1 << lps, x.t_end - pstart);
+                const size_t head = (((size_t)page * H_kv + x.g) << lps) * D;
+                vh[h] = brsrc(vc + head, (uint32_t)rows * RB);
+                roff[h] = (uint32_t)(th - pstart) * RB;
+            }
+        }
+    };
 
     // ---- issue side: V (+ Q) cursor RV-1 blocks ahead of the compute, K cursor LK ahead
     Cursor icv = cursor_at(L, HG, n_hg, b0, a0 - before);
@@ -102,14 +137,27 @@ void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc
         const size_t head = ((size_t)x.b * H_kv + x.g) * (size_t)T_max * D;
         return brsrc(base + head, (uint32_t)x.t_end * RB);
     };
-    __amdgpu_buffer_rsrc_t vrs = item_rsrc(icv, vc), krs = item_rsrc(ick, kc);
+    __amdgpu_buffer_rsrc_t vrs = zrs, krs = zrs;
+    if constexpr (!PAGED) {
+        vrs = item_rsrc(icv, vc);
+        krs = item_rsrc(ick, kc);
+    }
     u32x4 vr[RV][NV];
     u32x2 kr[RV][KSTEPS];
     auto issue_v = [&](int s) {
         const bool live = nv < nblk;
-        const uint32_t row0 = (uint32_t)(icv.s * kDecodeSplit + icv.i * CK) * RB;
+        if constexpr (PAGED) {
+            __amdgpu_buffer_rsrc_t vh[2] = {zrs, zrs};
+            uint32_t roff[2] = {0u, 0u};
+            if (live) page_halves(icv, vh, roff);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) vr[s][i] = bload16(live ? vrs : zrs, row0 + v_off[i]);
+            for (int i = 0; i < NV; ++i)
+                vr[s][i] = bload16(vh[i / HNV], roff[i / HNV] + v_off[i] - (uint32_t)(i / HNV) * 16u * RB);
+        } else {
+            const uint32_t row0 = (uint32_t)(icv.s * kDecodeSplit + icv.i * CK) * RB;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) vr[s][i] = bload16(live ? vrs : zrs, row0 + v_off[i]);
+        }
         if (!live) return;
         if (icv.i == 0 || nv == 0) {     // the item's Q (also for a range that starts inside it)
             const int ncols = min(32, G - icv.hg * 32);
@@ -124,18 +172,44 @@ void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc
         advance(icv, L, HG, n_hg);
         if (icv.i == 0) {
             qs_issue = qs_issue == RV - 1 ? 0 : qs_issue + 1;
-            vrs = item_rsrc(icv, vc);
+            if constexpr (!PAGED) vrs = item_rsrc(icv, vc);
         }
     };
     auto issue_k = [&](int s) {
         const bool live = nk < nblk;
-        const uint32_t row0 = (uint32_t)(ick.s * kDecodeSplit + ick.i * CK) * RB;
+        if constexpr (PAGED) {
+            // one global load per k-step from a per-lane address: lane l reads key perm(l % 32)
+            // of the block from the page of its half; a key past the item's end (its score is
+            // masked) and a block past the wavefront's range read row 0 of a valid page
+            const uint8_t* src = kc;
+            if (live) {
+                const int t0 = ick.s * kDecodeSplit + ick.i * CK;
+                const int last = ick.t_end - 1;
+                const int pi0 = t0 >> lps, pi1 = min(t0 + 16, last) >> lps;
+                const uint32_t rowb = (uint32_t)ick.b * (uint32_t)max_pages * 4u;
+                int e0, e1;
+                sload2(bt, __builtin_amdgcn_readfirstlane(rowb + (uint32_t)pi0 * 4u),
+                       __builtin_amdgcn_readfirstlane(rowb + (uint32_t)pi1 * 4u), e0, e1);
+                const int key = swap_bits23(l32);
+                const int t = t0 + key <= last ? t0 + key : t0;       // t0 <= last: a live block
+                const bool h1 = t - t0 >= 16;
+                const int page = min(max(h1 ? e1 : e0, 0), num_pages - 1);
+                const int pstart = (h1 ? pi1 : pi0) << lps;
+                src = kc + ((((size_t)page * H_kv + ick.g) << lps) + (size_t)(t - pstart)) * D;
+            }
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) kr[s][kk] = bload8(live ? krs : zrs, row0 + k_off[kk]);
+            for (int kk = 0; kk < KSTEPS; ++kk)
+                kr[s][kk] = *reinterpret_cast<const u32x2*>(src + kk * 16 + hl * 8);
+        } else {
+            const uint32_t row0 = (uint32_t)(ick.s * kDecodeSplit + ick.i * CK) * RB;
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk) kr[s][kk] = bload8(live ? krs : zrs, row0 + k_off[kk]);
+        }
         if (!live) return;
         ++nk;
         advance(ick, L, HG, n_hg);
-        if (ick.i == 0) krs = item_rsrc(ick, kc);
+        if constexpr (!PAGED)
+            if (ick.i == 0) krs = item_rsrc(ick, kc);
     };
 #pragma unroll
     for (int s = 0; s < RV - 1; ++s) issue_v(s);
@@ -171,11 +245,20 @@ void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc
             vaddr[db] = tb + (uint32_t)((vrow * D + (((db * 4 + vc0) ^ vfv) * 8) + vin) * 2);
     }
 
+    // The Q of an item is loaded into its LDS slot right after the V of the item's first
+    // block here (or of the wavefront's first block).  By the time that block is computed,
+    // at least (RV - 1) x NV V loads and (LK + 1) x KSTEPS K loads follow it (the fewest
+    // at the range's first block), so waiting for at most that many outstanding (capped at
+    // the counter's 63) makes the slot complete.  The compiler derives no wait for reading
+    // the slot after its buffer->LDS loads, so it is explicit.
+    constexpr int NQ = (RV - 1) * NV + (LK + 1) * KSTEPS < 63 ? (RV - 1) * NV + (LK + 1) * KSTEPS : 63;
+
     auto compute = [&](int j, int s) {
         const int g = cc.g, hg = cc.hg;
         const int col = hg * 32 + l32;
         const bool col_ok = col < G;
         if (need_q) {                    // first block of an item: Q and the scales
+            wait_vmem_le<NQ>();          // the Q slot's buffer->LDS loads have landed
             const bf16* qrow = reinterpret_cast<const bf16*>(qslot(qs)) + (col_ok ? l32 : 0) * D;
 #pragma unroll
             for (int kk = 0; kk < KSTEPS; ++kk) {
@@ -311,14 +394,14 @@ void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc
     wait_vmem_le<0>();     // the Q loads into LDS land before the wavefront ends
 }
 
-template <int D, bool INT8>
+template <int D, bool INT8, bool PAGED>
 int resident_waves8(int lds_bytes) {
     static int cached_lds = -1, cached = 0;
     if (lds_bytes == cached_lds) return cached;
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_q8_kernel<D, INT8>, 64, lds_bytes) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_q8_kernel<D, INT8, PAGED>, 64, lds_bytes) != hipSuccess ||
         cus <= 0 || per_cu <= 0)
         return 256;
     cached = cus * per_cu;
@@ -326,10 +409,10 @@ int resident_waves8(int lds_bytes) {
     return cached;
 }
 
-template <int D, bool INT8>
+template <int D, bool INT8, bool PAGED>
 hipError_t launch8(const DecodeFp8Args& a) {
     static const hipError_t attr =
-        hipFuncSetAttribute((const void*)decode_q8_kernel<D, INT8>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        hipFuncSetAttribute((const void*)decode_q8_kernel<D, INT8, PAGED>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             Geo8<D, INT8>::RV * q_slot_bytes(32, D));
     if (attr != hipSuccess) return attr;
     const int G = a.H_q / a.H_kv;
@@ -337,13 +420,14 @@ hipError_t launch8(const DecodeFp8Args& a) {
     const int nsplit = decode_nsplit(a.T_max);
     const int qb = q_slot_bytes(G, D);
     const int lds = Geo8<D, INT8>::RV * qb;
-    const int nwaves = resident_waves8<D, INT8>(lds);
+    const int nwaves = resident_waves8<D, INT8, PAGED>(lds);
     float* ws_o = static_cast<float*>(a.workspace);
     float* ws_ml = ws_o + (size_t)a.B * a.H_q * nsplit * 2 * D;
-    hipLaunchKernelGGL((decode_q8_kernel<D, INT8>), dim3(nwaves), dim3(64), lds, (hipStream_t)a.stream,
+    const int lps = PAGED ? __builtin_ctz((unsigned)a.page_size) : 0;
+    hipLaunchKernelGGL((decode_q8_kernel<D, INT8, PAGED>), dim3(nwaves), dim3(64), lds, (hipStream_t)a.stream,
                        (const bf16*)a.q, (const uint8_t*)a.k_cache, (const uint8_t*)a.v_cache, a.k_scale,
                        a.v_scale, a.lens, ws_o, ws_ml, a.B, a.H_q, a.H_kv, a.T_max, G, n_hg, nsplit, nwaves, qb,
-                       a.scale * kLog2e);
+                       a.scale * kLog2e, a.block_table, a.max_pages, a.num_pages, lps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_bh = a.B * a.H_q;
@@ -354,9 +438,14 @@ hipError_t launch8(const DecodeFp8Args& a) {
 
 }  // namespace
 
+template <bool PAGED>
+hipError_t launch8_fmt(const DecodeFp8Args& a) {
+    if (a.int8) return a.D == 64 ? launch8<64, true, PAGED>(a) : launch8<128, true, PAGED>(a);
+    return a.D == 64 ? launch8<64, false, PAGED>(a) : launch8<128, false, PAGED>(a);
+}
+
 hipError_t launch_decode_fp8kv(const DecodeFp8Args& a) {
-    if (a.int8) return a.D == 64 ? launch8<64, true>(a) : launch8<128, true>(a);
-    return a.D == 64 ? launch8<64, false>(a) : launch8<128, false>(a);
+    return a.block_table ? launch8_fmt<true>(a) : launch8_fmt<false>(a);
 }
 
 }  // namespace mattn

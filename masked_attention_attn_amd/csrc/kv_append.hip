@@ -72,16 +72,29 @@ void kv_append_kernel(unsigned char* __restrict__ kc, unsigned char* __restrict_
 // one of the cache formats of LLM inference memory accounting 2/10, section
 // "18. KV Cache Quantization").  Four elements per thread become one dword of
 // codes (element i in byte i).
-template <bool INT8>
+// PAGED: the pools and slot mapping of kv_append_kernel's paged form.
+template <bool INT8, bool PAGED>
 __global__ __launch_bounds__(NT)
 void kv_append_q8_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
                           const float* __restrict__ ks, const float* __restrict__ vs,
                           int32_t* __restrict__ lens, const void* __restrict__ kn,
-                          const void* __restrict__ vn, int new_bf16, int H_kv, int T_max, int D) {
+                          const void* __restrict__ vn, int new_bf16, int H_kv, int T_max, int D,
+                          const int32_t* __restrict__ block_table, int page_size, int max_pages,
+                          int num_pages) {
     const int b = blockIdx.x;
     const int t = lens[b];
     const bool ok = t >= 0 && t < T_max;
     if (ok) {
+        size_t row0, head_rows;       // row of slot t in head 0, rows between heads
+        if constexpr (PAGED) {
+            const int e = block_table[(size_t)b * max_pages + t / page_size];
+            const int page = min(max(e, 0), num_pages - 1);
+            row0 = (size_t)page * H_kv * page_size + t % page_size;
+            head_rows = (size_t)page_size;
+        } else {
+            row0 = (size_t)b * H_kv * T_max + t;
+            head_rows = (size_t)T_max;
+        }
         const int quads = D / 4;
         const int total = 2 * H_kv * quads;          // K then V
         for (int idx = threadIdx.x; idx < total; idx += NT) {
@@ -112,7 +125,7 @@ void kv_append_q8_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
                 wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
                 wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], wd, true);
             }
-            uint8_t* dst = (which ? vc : kc) + (((size_t)b * H_kv + g) * T_max + t) * D + (size_t)qd * 4;
+            uint8_t* dst = (which ? vc : kc) + (row0 + g * head_rows) * D + (size_t)qd * 4;
             *reinterpret_cast<uint32_t*>(dst) = (uint32_t)wd;
         }
     }
@@ -123,10 +136,12 @@ void kv_append_q8_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
 }  // namespace
 
 hipError_t launch_kv_append_fp8(const AppendFp8Args& a) {
-    auto kern = a.int8 ? kv_append_q8_kernel<true> : kv_append_q8_kernel<false>;
+    auto kern = a.block_table ? (a.int8 ? kv_append_q8_kernel<true, true> : kv_append_q8_kernel<false, true>)
+                              : (a.int8 ? kv_append_q8_kernel<true, false> : kv_append_q8_kernel<false, false>);
     hipLaunchKernelGGL(kern, dim3(a.B), dim3(NT), 0, (hipStream_t)a.stream,
                        (uint8_t*)a.k_cache, (uint8_t*)a.v_cache, a.k_scale, a.v_scale, a.lens, a.k_new,
-                       a.v_new, a.new_bf16 ? 1 : 0, a.H_kv, a.T_max, a.D);
+                       a.v_new, a.new_bf16 ? 1 : 0, a.H_kv, a.T_max, a.D, a.block_table, a.page_size,
+                       a.max_pages, a.num_pages);
     return hipGetLastError();
 }
 

@@ -80,6 +80,9 @@ struct DecodeFp8Args {
     void* workspace;
     void* stream;
     bool int8 = false;
+    // paged pools, as in DecodeArgs
+    const int32_t* block_table = nullptr;
+    int page_size = 0, max_pages = 0, num_pages = 0;
 };
 
 struct AppendFp8Args {
@@ -91,6 +94,9 @@ struct AppendFp8Args {
     int B, H_kv, T_max, D;
     void* stream;
     bool int8 = false;            // symmetric INT8 codes instead of E4M3
+    // paged pools, as in AppendArgs
+    const int32_t* block_table = nullptr;
+    int page_size = 0, max_pages = 0, num_pages = 0;
 };
 
 hipError_t launch_fwd_bf16_d64(const FwdArgs& a);

@@ -949,3 +949,100 @@ def test_varlen_ring_hop_8192_fp8_sampled_rows(ma):
                                 rows=rows)
     check_attn(o[rows].transpose(0, 1).unsqueeze(0), l[:, rows].unsqueeze(0), Or, Lr, torch.bfloat16,
                "packed fp8 ring hop sampled rows")
+
+
+# ---- paged 8-bit caches ------------------------------------------------------------------------
+
+PAGED8_CASES = [
+    # (B, Hq, Hkv, D, len_lo, len_hi, T_max), page_size
+    ((3, 8, 2, 128, 1, 700, 768), 16),
+    ((4, 8, 8, 64, 0, 600, 640), 64),
+    ((2, 32, 8, 128, 500, 1100, 1152), 32),
+    ((5, 40, 1, 64, 1, 1500, 1536), 512),
+]
+
+
+def _q8_calls(ma, fmt):
+    if fmt == "fp8":
+        return (W.make_decode_fp8, ma.kv_append_fp8_paged, ma.attn_decode_fp8kv_paged, oracle.kv_append_fp8_paged,
+                oracle.decode_fp8kv_paged, ma.kv_append_fp8, ma.attn_decode_fp8kv)
+    return (W.make_decode_int8, ma.kv_append_int8_paged, ma.attn_decode_int8kv_paged, oracle.kv_append_int8_paged,
+            oracle.decode_int8kv_paged, ma.kv_append_int8, ma.attn_decode_int8kv)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("case", PAGED8_CASES)
+def test_paged_8bit_append_then_decode(ma, case, fmt):
+    (B, Hq, Hkv, D, lo, hi, Tm), ps = case
+    make, append, decode, o_append, o_decode, _, _ = _q8_calls(ma, fmt)
+    w = make(B, Hq, Hkv, D, lo, hi, T_max=Tm, seed=B * 100 + Hq + ps)
+    pg = W.to_paged(w, ps, seed=ps)
+    kp, vp, bt = _paged_dev(pg)
+    ks, vs, lens = w.k_scale.to(DEV), w.v_scale.to(DEV), w.lens.to(DEV)
+    append(kp, vp, ks, vs, bt, lens, w.k_new.to(DEV), w.v_new.to(DEV))
+    o, l = decode(w.q.to(DEV), kp, vp, ks, vs, bt, lens, w.scale, want_lse=True)
+    torch.cuda.synchronize()
+    ek, ev, el = o_append(pg.k_pages, pg.v_pages, w.k_scale, w.v_scale, pg.block_table.numpy(), w.lens.numpy(),
+                          w.k_new, w.v_new)
+    assert lens.cpu().tolist() == el.tolist()
+    assert np.array_equal(kp.cpu().numpy(), ek) and np.array_equal(vp.cpu().numpy(), ev)   # bytes, whole pools
+    Or, Lr = o_decode(w.q, ek, ev, w.k_scale, w.v_scale, pg.block_table, el, w.scale)
+    check_attn(o, l, Or, Lr, torch.bfloat16, f"paged {fmt} decode {case}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("ps", [16, 128])
+def test_paged_8bit_bitwise_equals_contiguous(ma, ps, fmt):
+    make, append, decode, _, _, c_append, c_decode = _q8_calls(ma, fmt)
+    w = make(5, 16, 4, 128, 0, 2500, T_max=2560, seed=ps + 7)
+    pg = W.to_paged(w, ps, seed=3)
+    kp, vp, bt = _paged_dev(pg)
+    kc, vc, ks, vs = w.k_cache.to(DEV), w.v_cache.to(DEV), w.k_scale.to(DEV), w.v_scale.to(DEV)
+    l1, l2 = w.lens.to(DEV), w.lens.to(DEV)
+    q, kn, vn = w.q.to(DEV), w.k_new.to(DEV), w.v_new.to(DEV)
+    append(kp, vp, ks, vs, bt, l1, kn, vn)
+    c_append(kc, vc, ks, vs, l2, kn, vn)
+    o1, s1 = decode(q, kp, vp, ks, vs, bt, l1, w.scale, want_lse=True)
+    o2, s2 = c_decode(q, kc, vc, ks, vs, l2, w.scale, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+# ---- repeated short-item decodes (the Q slot wait) ---------------------------------------------
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "int8"])
+def test_decode_short_items_repeated(ma, fmt):
+    """Many short items (lengths 1..300, 2 query heads per KV head) start an item every few blocks,
+    so an item's Q is read from its LDS slot soon after its buffer->LDS loads were issued.  Without a
+    wait for those loads a read could see the slot's previous item (about 1% of such decodes went
+    wrong); every one of 150 append + decode rounds must match the oracle."""
+    B, Hq, Hkv, D = 32, 8, 4, 64
+    if fmt == "bf16":
+        w = W.make_decode(B, Hq, Hkv, D, 1, 300, torch.bfloat16, T_max=320, seed=41)
+        ek, ev, el = oracle.kv_append(w.k_cache.float().numpy(), w.v_cache.float().numpy(), w.lens.numpy(),
+                                      w.k_new.float().numpy(), w.v_new.float().numpy())
+        Or, Lr = oracle.decode(w.q, ek, ev, el, w.scale)
+    else:
+        make = W.make_decode_fp8 if fmt == "fp8" else W.make_decode_int8
+        w = make(B, Hq, Hkv, D, 1, 300, T_max=320, seed=41)
+        oapp = oracle.kv_append_fp8 if fmt == "fp8" else oracle.kv_append_int8
+        odec = oracle.decode_fp8kv if fmt == "fp8" else oracle.decode_int8kv
+        ek, ev, el = oapp(w.k_cache.numpy(), w.v_cache.numpy(), w.k_scale, w.v_scale, w.lens.numpy(), w.k_new, w.v_new)
+        Or, Lr = odec(w.q, ek, ev, w.k_scale, w.v_scale, el, w.scale)
+    q, kn, vn = w.q.to(DEV), w.k_new.to(DEV), w.v_new.to(DEV)
+    worst = 0.0
+    for it in range(150):
+        kc, vc, lens = w.k_cache.to(DEV), w.v_cache.to(DEV), w.lens.to(DEV)
+        if fmt == "bf16":
+            ma.kv_append(kc, vc, lens, kn, vn)
+            o, l = ma.attn_decode(q, kc, vc, lens, w.scale, want_lse=True)
+        else:
+            ks, vs = w.k_scale.to(DEV), w.v_scale.to(DEV)
+            (ma.kv_append_fp8 if fmt == "fp8" else ma.kv_append_int8)(kc, vc, ks, vs, lens, kn, vn)
+            o, l = (ma.attn_decode_fp8kv if fmt == "fp8" else ma.attn_decode_int8kv)(q, kc, vc, ks, vs, lens, w.scale,
+                                                                                     want_lse=True)
+        torch.cuda.synchronize()
+        worst = max(worst, float(np.max(np.abs(l.cpu().double().numpy() - Lr))))
+        if it == 0 or worst > 1e-3:
+            check_attn(o, l, Or, Lr, torch.bfloat16, f"{fmt} short-item decode, round {it}")
+    assert worst <= 1e-3, f"{fmt}: max |dLSE| over the rounds {worst:.3e}"
