@@ -227,8 +227,9 @@ def varlen_section(torch, ma, W, dev):
 
 def paged_section(torch, ma, W, dev):
     """The decode workload (B32, H_q 32 / H_kv 8, D128, len U[512, 8192] + 1) with its cache in a
-    shuffled page pool (attn_decode_paged), per page size, timed on its own; bytes as the
-    contiguous decode (K and V of every cached token, plus q and o)."""
+    shuffled page pool (attn_decode_paged), per page size, and with an E4M3 cache in 16-token
+    pages (attn_decode_fp8kv_paged), each timed on its own; bytes as the contiguous decodes (K
+    and V of every cached token, plus q and o)."""
     res = {}
     for ps in (16, 64):
         pg = W.gqa_decode_b32_paged(ps)
@@ -248,6 +249,21 @@ def paged_section(torch, ma, W, dev):
         res[f"page_{ps}"] = {"us": round(t * 1e6, 2), "gbps": round(nbytes / t / 1e9, 1),
                              "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBPS, 4)}
         del kp, vp, bt, lens, q, o, lse, ws
+    # the same workload with an E4M3 cache in 16-token pages (attn_decode_fp8kv_paged)
+    w = W.gqa_decode_b32_fp8()
+    pg = W.to_paged(w, 16)
+    kp, vp, bt = pg.k_pages.to(dev), pg.v_pages.to(dev), pg.block_table.to(dev)
+    ks, vs, lens, q = w.k_scale.to(dev), w.v_scale.to(dev), (w.lens + 1).to(dev), w.q.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    B, Hq, _, D = q.shape
+    Hkv = kp.shape[1]
+    ws = torch.empty(ma.attn_decode_workspace_bytes(B, Hq, Hkv, bt.shape[1] * 16, D), dtype=torch.uint8, device=dev)
+    t = _time_call(torch, lambda: ma.attn_decode_fp8kv_paged(q, kp, vp, ks, vs, bt, lens, w.scale, out=o, lse=lse,
+                                                             workspace=ws, want_lse=True), n=20)
+    nbytes = int((w.lens + 1).sum()) * 2 * Hkv * D + 2 * q.numel() * 2
+    res["fp8_page_16"] = {"us": round(t * 1e6, 2), "gbps": round(nbytes / t / 1e9, 1),
+                          "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBPS, 4)}
     return res
 
 
