@@ -237,7 +237,7 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar registers
     const int hl = lane >> 5;
     const int l32 = lane & 31;
     const int q0 = qt * BM + wave * QW;
@@ -356,18 +356,25 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
     // (t - t_first) % K_RING and V slot (t - t_first) % V_RING; kcur / vcur
     // track the slots of the current tile.
     auto kslot_b = [&](int sl) -> unsigned char* { return smem_raw + sl * L::K_TILE; };
+    // the same slots as LDS byte addresses (for the DMA's M0; scalar arithmetic only)
+    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) unsigned char*)smem_raw);
+    auto kslot_a = [&](int sl) -> uint32_t { return lds0 + (uint32_t)(sl * L::K_TILE); };
+    auto vslot_a = [&](int sl) -> uint32_t {
+        return lds0 + (uint32_t)(L::K_RING * L::K_TILE + sl * L::V_TILE);
+    };
     auto vslot_b = [&](int sl) -> unsigned char* { return smem_raw + L::K_RING * L::K_TILE + sl * L::V_TILE; };
     auto kslot = [&](int sl) -> const bf16* { return reinterpret_cast<const bf16*>(kslot_b(sl)); };
     auto vslot = [&](int sl) -> const bf16* { return reinterpret_cast<const bf16*>(vslot_b(sl)); };
     auto dma_k = [&](int t, int sl) {
 #pragma unroll
         for (int i = 0; i < CPW; ++i)
-            dma16(krs, kslot_b(sl) + (CPW * wave + i) * 1024, k_voff[i] + (uint32_t)t * TK * rsk * (uint32_t)ES, 0u);
+            dma16(krs, kslot_a(sl) + (uint32_t)((CPW * wave + i) * 1024), k_voff[i] + (uint32_t)t * TK * rsk * (uint32_t)ES, 0u);
     };
     auto dma_v = [&](int t, int sl) {
 #pragma unroll
         for (int i = 0; i < CPWV; ++i)
-            dma16(vrs, vslot_b(sl) + (CPWV * wave + i) * 1024, v_voff[i] + (uint32_t)t * TK * rsk * 2u, 0u);
+            dma16(vrs, vslot_a(sl) + (uint32_t)((CPWV * wave + i) * 1024), v_voff[i] + (uint32_t)t * TK * rsk * 2u, 0u);
     };
     // FP8 V: thread tid loads codes 16*vt_j .. +15 of tile row vt_r into registers a tile
     // ahead and stores them, as bf16, as chunks 2*vt_j and 2*vt_j + 1 of that row of a bf16
@@ -415,10 +422,11 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[db][nb][i] = 0.f;
     // mc: the reference the weights are taken against, 2^(S·c - mc), in log2
-    // units; always finite.  lsum: running sum of the weights.
-    float mc[NB], lsum[NB];
+    // units; always finite.  Kept negated (nmc = -mc), the addend of the fma that
+    // forms every exponent.  lsum: running sum of the weights.
+    float nmc[NB], lsum[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) { mc[nb] = 0.f; lsum[nb] = 0.f; }
+    for (int nb = 0; nb < NB; ++nb) { nmc[nb] = 0.f; lsum[nb] = 0.f; }
 
     // Sᵀ = K·Qᵀ for one key block (u) from a tile in LDS: element i of lane l
     // holds key (i/8)*16 + (l/32)*8 + i%8 of the block.
@@ -536,7 +544,7 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
                 for (int i = 1; i < 16; ++i) m = fmaxf(m, S[nb][i]);
                 // a causal row may have no key at all (then any finite reference serves)
                 m = pair_max(m);
-                mc[nb] = m == kNegInf ? 0.f : m * c;
+                nmc[nb] = m == kNegInf ? 0.f : -(m * c);
             }
             mc_set = true;
         }
@@ -565,8 +573,8 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
         auto pair_i = [&](int pp) { return (pp / (4 * NB)) * 8 + (pp % 4) * 2; };
         auto stA = [&](int pp) {
             const int nb = pair_nb(pp), i = pair_i(pp);
-            xs[pp][0] = __builtin_fmaf(S[nb][i], c, -mc[nb]);
-            xs[pp][1] = __builtin_fmaf(S[nb][i + 1], c, -mc[nb]);
+            xs[pp][0] = __builtin_fmaf(S[nb][i], c, nmc[nb]);
+            xs[pp][1] = __builtin_fmaf(S[nb][i + 1], c, nmc[nb]);
         };
         auto stB = [&](int pp) {
             ps[pp][0] = __builtin_amdgcn_exp2f(xs[pp][0]);
@@ -600,12 +608,15 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
             if (__ballot(over)) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    float m = S[nb][k2 * 8];
+                    // (highest index first: no partial max shared with the first-block
+                    // reference above, which the compiler would otherwise hoist into
+                    // the common path)
+                    float m = S[nb][k2 * 8 + 7];
 #pragma unroll
-                    for (int i = 1; i < 8; ++i) m = fmaxf(m, S[nb][k2 * 8 + i]);
-                    const float mn = fmaxf(mc[nb], pair_max(m) * c);
-                    const float alpha = __builtin_amdgcn_exp2f(mc[nb] - mn);
-                    mc[nb] = mn;
+                    for (int i = 6; i >= 0; --i) m = fmaxf(m, S[nb][k2 * 8 + i]);
+                    const float mn = fmaxf(-nmc[nb], pair_max(m) * c);
+                    const float alpha = __builtin_amdgcn_exp2f(-nmc[nb] - mn);
+                    nmc[nb] = -mn;
                     lsum[nb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < DB; ++db)
@@ -797,7 +808,7 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
                     *reinterpret_cast<u32x2*>(orow + db * 32 + g * 8 + hl * 4) = w;
                 }
             if (WRITE_LSE && hl == 0)
-                lse[l_row0 + (size_t)qi] = lt > 0.f ? (mc[nb] + __log2f(lt)) * kLn2 : kNegInf;
+                lse[l_row0 + (size_t)qi] = lt > 0.f ? (__log2f(lt) - nmc[nb]) * kLn2 : kNegInf;
         }
     }
 }

@@ -51,16 +51,16 @@ __device__ __forceinline__ i32x4_sgpr make_rsrc(const void* p, uint32_t bytes) {
     r[3] = 0x00020000;
     return r;
 }
-// 16 bytes per lane from a buffer straight into LDS at lds_base + 16*lane.
+// 16 bytes per lane from a buffer straight into LDS at lds_addr + 16*lane.
 // Written as inline assembly on purpose: the compiler cannot tell these LDS
 // writes apart from the operand reads of other ring slots and would put a
 // wait for every outstanding global load in front of the next LDS read.  The
 // calling kernel orders them itself (an explicit vmcnt wait, plus a barrier
 // where other waves read the data); loads the compiler does not see only make
 // its own vmcnt waits stricter, never too weak.
-__device__ __forceinline__ void dma16(i32x4_sgpr r, unsigned char* lds_base, uint32_t voff, uint32_t soff) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)lds_base));
+// lds_addr: LDS byte address of the 1 KiB destination (wave-uniform).
+__device__ __forceinline__ void dma16(i32x4_sgpr r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
     uint32_t saved;     // M0 is restored, so the compiler's view of it stays valid
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
                  "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
