@@ -9,7 +9,10 @@
 //
 // Memory-bound: each thread owns 8 consecutive elements of one row, reads
 // them once from every chunk with 16- or 32-byte vector loads and writes the
-// merged 8 once; the per-row LSEs are tiny and cached.  The partials are read
+// merged 8 once; the per-row LSEs are tiny and cached.  For up to four chunks
+// every load (LSEs and partial outputs) is issued before any is used, so a
+// thread waits for memory once instead of once per chunk plus once for the
+// LSEs; more chunks take a loop.  The partials are read
 // and the result written with non-temporal accesses: each byte is touched
 // once, and the output then does not linger in the caches for the next kernel
 // to write back (a decode after the merge ran 8% faster with them).
@@ -54,11 +57,48 @@ template <> struct Vec8<float> {
     }
 };
 
-template <typename T>
+// NF > 0: exactly NF chunks, all loads issued up front; NF = 0: any n, one chunk at a time.
+template <typename T, int NF>
 __global__ __launch_bounds__(NT)
 void merge_kernel(ChunkPtrs ptrs, int n, T* __restrict__ out, float* __restrict__ lse_out,
                   int rows, int D) {
     const int per_row = D / 8;
+    if constexpr (NF > 0) {
+        // rows * per_row < 2^32 here (checked by the launcher): 32-bit index arithmetic
+        const uint32_t idx = blockIdx.x * (uint32_t)NT + threadIdx.x;
+        const uint32_t row = idx / (uint32_t)per_row;
+        const uint32_t ch = idx - row * (uint32_t)per_row;
+        if (row >= (uint32_t)rows) return;
+        const size_t off = (size_t)row * D + (size_t)ch * 8;
+        float l[NF], x[NF][8];
+#pragma unroll
+        for (int i = 0; i < NF; ++i) l[i] = ptrs.lses[i][row];
+#pragma unroll
+        for (int i = 0; i < NF; ++i) Vec8<T>::load(static_cast<const T*>(ptrs.outs[i]) + off, x[i]);
+        // No branch on the LSEs (selects only), so the compiler cannot sink the output loads
+        // behind the LSE loads.
+        float M = l[0];
+#pragma unroll
+        for (int i = 1; i < NF; ++i) M = fmaxf(M, l[i]);
+        const bool empty = M == kNegInf;          // every chunk empty: out = 0, lse = -inf
+        const float Ms = empty ? 0.f : M;
+        float tot = 0.f;
+#pragma unroll
+        for (int i = 0; i < NF; ++i) tot += __expf(l[i] - Ms);
+        const float lse = empty ? kNegInf : Ms + __logf(tot);
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            const float w = empty ? 0.f : __expf(l[i] - lse);   // empty chunk: exp(-inf) = 0
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = __builtin_fmaf(w, x[i][j], acc[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = empty ? 0.f : acc[j];
+        Vec8<T>::store(out + off, acc);
+        if (lse_out && ch == 0) lse_out[row] = lse;
+        return;
+    }
     const long idx = (long)blockIdx.x * NT + threadIdx.x;
     const long row = idx / per_row;
     const int ch = (int)(idx - row * per_row);
@@ -96,7 +136,11 @@ hipError_t launch(const MergeArgs& a) {
     }
     const long threads = (long)a.rows * (a.D / 8);
     const long grid = (threads + NT - 1) / NT;
-    hipLaunchKernelGGL(merge_kernel<T>, dim3((unsigned)grid), dim3(NT), 0, (hipStream_t)a.stream,
+    const bool idx32 = grid * (long)NT <= 0xFFFFFFFFL;
+    const auto kern = !idx32 || a.n > 4 ? merge_kernel<T, 0>
+                    : a.n == 1 ? merge_kernel<T, 1> : a.n == 2 ? merge_kernel<T, 2>
+                    : a.n == 3 ? merge_kernel<T, 3> : merge_kernel<T, 4>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), 0, (hipStream_t)a.stream,
                        p, a.n, (T*)a.out, a.lse_out, a.rows, a.D);
     return hipGetLastError();
 }

@@ -172,7 +172,7 @@ def test_patch_p11616_sampled_rows(ma):
 # ---- merge ---------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("n", [1, 2, 3, 5])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 32])
 def test_merge_random_partials(ma, n, dtype):
     g = torch.Generator().manual_seed(n)
     B, H, T, D = 2, 3, 37, 128 if n % 2 else 64
