@@ -12,9 +12,9 @@
 // Work decomposition
 //   workgroup = 256 queries of one (batch, head): at D = 64 four wavefronts of
 //   64 queries (two 32-column blocks of the MFMA), at D = 128 eight
-//   wavefronts of 32 queries.  K/V are staged in LDS in tiles of TK keys (64
-//   at D = 64, 32 at D = 128) shared by the workgroup; the compute steps over
-//   blocks of 32 keys.
+//   wavefronts of 32 queries.  K/V are staged in LDS in tiles of TK = 64 keys
+//   shared by the workgroup; the compute steps over blocks of 32 keys (two per
+//   tile).
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, operands 8 bf16 per lane,
 // accumulator 16 fp32 per lane; lane l holds column l%32 of the result and
