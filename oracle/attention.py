@@ -16,7 +16,7 @@ is the slow, obviously-correct yardstick.
 Inputs are NumPy arrays (any float dtype; they are upcast to float64, which
 holds every bf16 and fp32 value exactly) or anything ``numpy.asarray`` takes.
 
-Readings of points the pages leave open (each is also listed in the design doc):
+Readings of points the pages leave open:
   * mask polarity: nonzero = padded = ignored, the key_padding_mask sense;
     the same page, section "출력은 달라졌는가", warns that SDPA's boolean mask
     means the opposite.

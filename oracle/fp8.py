@@ -8,7 +8,7 @@ metadata, and the attention kernel must dequantise on the fly (LLM inference
 memory accounting 2/10, section "18. KV Cache Quantization": lower-precision
 KV halves or quarters the bytes per token and brings scales and a dequant
 step with it).  The pages fix neither the 8-bit format nor the scale
-granularity; the readings taken here (also listed in the design doc):
+granularity; the readings taken here:
   * format: OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent bits with bias 7,
     3 mantissa bits, subnormals, no infinities, S.1111.111 = NaN, largest
     finite magnitude 448;

@@ -7,7 +7,7 @@ KV-cache quantisation keeps each cached K/V element in fewer bytes plus scale
 metadata and dequantises inside the attention kernel; INT8 is one of the
 formats the page lists (LLM inference memory accounting 2/10, section
 "18. KV Cache Quantization").  The page fixes neither the scale granularity
-nor the rounding; the readings taken here (also listed in the design doc):
+nor the rounding; the readings taken here:
   * symmetric INT8: code q stands for q * scale, with one float32 scale per
     (sequence, KV head) for K and one for V (the FP8 cache's granularity);
   * quantising x: y = x / scale in float32 (IEEE division), rounded to the
