@@ -470,7 +470,10 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
     };
 
     // bit i set: key u*CK + i of block u lies outside [first, last]
+    // blocks u_in0 .. u_in1 lie wholly inside [first, last]: nothing there is padded
+    const int u_in0 = (first + CK - 1) / CK, u_in1 = (last + 1) / CK - 1;
     auto edge_bits = [&](int u) -> uint32_t {
+        if (__builtin_expect(u >= u_in0 && u <= u_in1, 1)) return 0u;
         const int lo = first - u * CK, hi = last - u * CK;
         uint32_t m = 0u;
         if (lo > 0) m |= lo >= 32 ? ~0u : (1u << lo) - 1u;

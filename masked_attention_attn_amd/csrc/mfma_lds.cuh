@@ -61,12 +61,11 @@ __device__ __forceinline__ i32x4_sgpr make_rsrc(const void* p, uint32_t bytes) {
 // lds_addr: LDS byte address of the 1 KiB destination (wave-uniform).
 __device__ __forceinline__ void dma16(i32x4_sgpr r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
-    uint32_t saved;     // M0 is restored, so the compiler's view of it stays valid
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
-                 "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved)
+    // M0 is declared clobbered, so the compiler sets it again wherever it needs it.
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
                  : "s"(m0), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
-                 : "memory");
+                 : "memory", "m0");
 }
 // Buffer descriptor for the compiler's buffer-load builtins: `bytes` from p are
 // addressable, offsets past them read as zero without touching memory.
