@@ -469,11 +469,15 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
         }
     };
 
+    // Blocks u_in0 .. u_in0 + in_span lie wholly inside [first, last]; without interior
+    // holes nothing there is padded, and one unsigned compare recognises them (the range
+    // is empty when there are holes or no such block).
+    const int ui0 = (first + CK - 1) / CK, ui1 = (last + 1) / CK - 1;
+    const bool any_in = ui1 >= ui0 && !holes;
+    const int u_in0 = any_in ? ui0 : (1 << 30);
+    const uint32_t in_span = any_in ? (uint32_t)(ui1 - ui0) : 0u;
     // bit i set: key u*CK + i of block u lies outside [first, last]
-    // blocks u_in0 .. u_in1 lie wholly inside [first, last]: nothing there is padded
-    const int u_in0 = (first + CK - 1) / CK, u_in1 = (last + 1) / CK - 1;
     auto edge_bits = [&](int u) -> uint32_t {
-        if (__builtin_expect(u >= u_in0 && u <= u_in1, 1)) return 0u;
         const int lo = first - u * CK, hi = last - u * CK;
         uint32_t m = 0u;
         if (lo > 0) m |= lo >= 32 ? ~0u : (1u << lo) - 1u;
@@ -509,10 +513,13 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
     auto step = [&](int j, const int hf, f32x16 (&S)[NB], f32x16 (&Sn)[NB]) {
         const int u = u_first + j;
         const int T = u / HALVES;
-        uint32_t pm = edge_bits(u);                 // bit i: key u*32+i padded
-        if (holes) {
-            if (hf == 0) pm_tile = __ballot(padf) & TILE_BITS;
-            pm |= (uint32_t)(pm_tile >> (hf * 32));
+        uint32_t pm = 0u;                           // bit i: key u*32+i padded
+        if (__builtin_expect((uint32_t)(u - u_in0) > in_span, 0)) {   // an edge block, or holes
+            pm = edge_bits(u);
+            if (holes) {
+                if (hf == 0) pm_tile = __ballot(padf) & TILE_BITS;
+                pm |= (uint32_t)(pm_tile >> (hf * 32));
+            }
         }
         if (pm != 0u) {             // workgroup-uniform, rare: padded keys get -inf
             // element i of this lane is key (i/8)*16 + hl*8 + i%8 of the block
@@ -539,7 +546,7 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
                 }
             }
         }
-        if (!mc_set && pm != ~0u) {   // once: first block with an unpadded key
+        if (__builtin_expect(!mc_set, 0) && pm != ~0u) {   // once: first block with an unpadded key
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 float m = S[nb][0];
