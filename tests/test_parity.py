@@ -72,6 +72,8 @@ SHAPES = [
     (1, 2, 100, 77, 128, "suffix"),
     (2, 2, 130, 300, 128, "random"),
     (1, 1, 257, 33, 128, "none"),
+    (3, 2, 100, 256, 64, "aligned"),
+    (3, 1, 70, 256, 128, "aligned"),
 ]
 
 
@@ -97,6 +99,13 @@ def _mask(kind, B, Tk, seed):
                 b = a
             else:
                 b = int(torch.randint(a, Tk, (1,), generator=g))
+            m[bi, a:b + 1] = 0
+        return m
+    if kind == "aligned":
+        # valid runs that start and end on 32-key block edges ([32, 95], [64, 255]) and one
+        # too short to hold a whole block ([3, 30]): the edges of the interior-block test
+        m = torch.ones(B, Tk, dtype=torch.uint8)
+        for bi, (a, b) in enumerate([(32, 95), (64, Tk - 1), (3, 30)][:B]):
             m[bi, a:b + 1] = 0
         return m
     if kind == "holes":   # whole 64-key tiles padded in the middle plus a ragged tail
