@@ -484,11 +484,11 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
         if (hi < 31) m |= hi < 0 ? ~0u : ~((2u << hi) - 1u);
         return m;
     };
-    // With interior holes, lane j of padf / padf_nxt flags key j of the current /
-    // next LDS tile; the next tile's flags are loaded a tile ahead, so reading
-    // them never waits on the tile loads issued at the same time.
-    uint64_t pm_tile = 0;
-    int padf = 0, padf_nxt = 0;
+    // With interior holes, lane j of padf_nxt flags key j of the tile after the current
+    // one, loaded a tile ahead; at a tile end (after its wait for loads) the flags are
+    // gathered into the wave-uniform mask pm_next, which the next tile takes as pm_tile.
+    uint64_t pm_tile = 0, pm_next = 0;
+    int padf_nxt = 0;
     // Vᵀ operand (8 keys x one d per lane) of k-step k2 of half hf of the current V tile
     auto v_opnd = [&](int hf, int k2, int db) -> u32x4 {
         const bf16* base = vslot(vcur) + (hf * 32 + k2 * 16) * D + v_off(db);
@@ -512,12 +512,12 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
     i32x8 ka8[KS8];
     auto step = [&](int j, const int hf, f32x16 (&S)[NB], f32x16 (&Sn)[NB]) {
         const int u = u_first + j;
-        const int T = u / HALVES;
+        const int T = (int)((uint32_t)u / HALVES);   // u >= 0
         uint32_t pm = 0u;                           // bit i: key u*32+i padded
         if (__builtin_expect((uint32_t)(u - u_in0) > in_span, 0)) {   // an edge block, or holes
             pm = edge_bits(u);
             if (holes) {
-                if (hf == 0) pm_tile = __ballot(padf) & TILE_BITS;
+                if (hf == 0) pm_tile = pm_next;
                 pm |= (uint32_t)(pm_tile >> (hf * 32));
             }
         }
@@ -751,7 +751,7 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
                 for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = k_opnd(kblock(kcur == 2 ? 0 : kcur + 1, 0), kk);
             }
             if (holes) {
-                padf = padf_nxt;
+                pm_next = __ballot(padf_nxt) & TILE_BITS;
                 padf_nxt = pad_flag(min(T + 2, t_last));
             }
         }
@@ -768,11 +768,13 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
             if constexpr (FP8) vraw1 = vload(t_first + 1);
             else dma_v(t_first + 1, 1);
         }
+        int padf0 = 0;
         if (holes) {
-            padf = pad_flag(t_first);
+            padf0 = pad_flag(t_first);
             padf_nxt = pad_flag(min(t_first + 1, t_last));
         }
         wait_vmem();
+        if (holes) pm_next = __ballot(padf0) & TILE_BITS;
         if constexpr (FP8) {
             vstore(vraw, 0);
             if (t_first + 1 <= t_last) vstore(vraw1, 1);
