@@ -61,8 +61,10 @@ __device__ __forceinline__ i32x4_sgpr make_rsrc(const void* p, uint32_t bytes) {
 // lds_addr: LDS byte address of the 1 KiB destination (wave-uniform).
 __device__ __forceinline__ void dma16(i32x4_sgpr r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
-    // M0 is declared clobbered, so the compiler sets it again wherever it needs it.
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+    // M0 is declared clobbered, so the compiler sets it again wherever it needs it.  One
+    // wait state separates the scalar write of M0 from the load that reads it as the LDS
+    // address (a manual wait state of the CDNA ISA the compiler cannot insert into asm).
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :
                  : "s"(m0), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
                  : "memory", "m0");
