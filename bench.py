@@ -18,6 +18,11 @@ every cached token, plus q and o, over the attn_decode duration) and the
 merge's rate are reported beside it.  `cpu_baseline` times the float64 CPU
 oracle on a bounded sample of the prefill workload.
 
+Timing: HIP events on the launch stream around every call of every timed step (K >= 50
+by default), reported as the mean and the 10th / 50th / 90th percentiles per kernel.  The
+decodes timed on their own write a 512 MiB scratch buffer before each call, so the 256 MB
+last-level cache (MALL) holds none of the cache they read.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 Prints one JSON line.
 """
@@ -49,8 +54,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_p11616_traffic.json")
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--settle", type=float, default=0.5,
                    help="seconds of untimed steps before the warm-up (clock ramp)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -75,6 +80,18 @@ def calibrate_copy(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calibration_copy_bytes": n, "copies": 3}))
+
+
+LIB_SRCS = sorted(os.path.join(ROOT, "masked_attention_attn_amd", "csrc", f)
+                  for f in os.listdir(os.path.join(ROOT, "masked_attention_attn_amd", "csrc")))
+
+
+def file_sha(path):
+    h = hashlib.sha256()
+    with open(path, "rb") as f:
+        for chunk in iter(lambda: f.read(1 << 20), b""):
+            h.update(chunk)
+    return h.hexdigest()[:16]
 
 
 def src_hash(paths):
@@ -137,30 +154,91 @@ def cpu_model():
 
 
 SWEEP_P = (1944, 3952, 7776, 11616, 32122)   # the pages' patch counts, up to their OOM point
+FLUSH_BYTES = 512 * 2**20                     # > the 256 MB MALL
 
 
-def _time_call(torch, call, n=5, settle=0.3):
-    """Mean seconds per call over n calls, after `settle` seconds of untimed calls (the
-    clocks drop while the host prepares the next inputs and need ~30 ms of work to ramp)."""
+def pct(xs, f):
+    """The f-quantile of xs (nearest rank on the sorted values)."""
+    ys = sorted(xs)
+    return ys[min(len(ys) - 1, int(f * (len(ys) - 1) + 0.5))]
+
+
+def dist_us(us):
+    """mean / p10 / p50 / p90 of per-call durations in microseconds."""
+    return {"mean": round(sum(us) / len(us), 2), "p10": round(pct(us, 0.1), 2), "p50": round(pct(us, 0.5), 2),
+            "p90": round(pct(us, 0.9), 2), "n": len(us)}
+
+
+def _time_call(torch, call, n=50, settle=0.3, flush=None):
+    """Per-call durations (us) of n calls, each between two HIP events on the current stream,
+    after `settle` seconds of untimed calls (the clocks drop while the host prepares the next
+    inputs and need ~30 ms of work to ramp).  flush(), if given, runs before each timed call,
+    outside its events.  Returns (mean seconds per call, mean/p10/p50/p90 in us)."""
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < settle:
         for _ in range(3):
             call()
         torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(n):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in ev:
+        if flush is not None:
+            flush()
+        e0.record()
         call()
-    e1.record()
+        e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / n / 1e3
+    us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+    return sum(us) / len(us) / 1e6, dist_us(us)
+
+
+def make_flush(torch, dev):
+    """A fill of FLUSH_BYTES of scratch: afterwards the MALL holds none of a decode's cache."""
+    buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    state = {"i": 0}
+
+    def flush():
+        state["i"] = (state["i"] + 1) & 0xFF
+        buf.fill_(state["i"])
+    return flush
+
+
+def smi_clocks():
+    """Current clock levels as rocm-smi reports them (card 0), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        data = json.loads(r.stdout)
+    except Exception:
+        return None
+    card = next((v for k, v in data.items() if k.startswith("card")), None)
+    if not isinstance(card, dict):
+        return None
+    return {k: v for k, v in card.items() if "clock" in k.lower() or "clk" in k.lower()}
+
+
+def gpu_info(torch, dev, busy_step):
+    """Device name, CU count and memory, plus the clock levels read while the GPU runs
+    queued bench steps (so they are the clocks under this load, not idle ones)."""
+    p = torch.cuda.get_device_properties(dev)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "total_memory_bytes": int(p.total_memory)}
+    for _ in range(200):       # ~0.4 s of queued work
+        busy_step()
+    info["clocks_under_load"] = smi_clocks()
+    torch.cuda.synchronize()
+    return info
 
 
 def p_sweep(torch, ma, dev):
-    """Masked prefill with LSE, bf16, B1 H16 D64, last 16 keys padded, at each P:
-    the call-level extra device bytes (the O and LSE the caller provides; the library
-    allocates nothing, which the free-memory reading around the call confirms) next to the
-    score matrix a materialising path would hold, and the TFLOP/s."""
+    """Masked prefill with LSE, bf16, B1 H16 D64, last 16 keys padded, at each P: measured peak
+    extra device memory of one call, its time, and the score matrix a materialising path holds.
+
+    Around one call (O and LSE allocated by the caller, as a user would), after the inputs
+    are resident: torch's peak allocated and reserved bytes above the pre-call level
+    (reset_peak_memory_stats first), and the drop in the device's free memory (mem_get_info),
+    which would also show any allocation made outside torch, i.e. by the library.  The
+    library's own share is that drop minus torch's reserve growth.  The line fitted over P is
+    through the measured peak allocated bytes."""
     rows = []
     g = torch.Generator(device=dev)
     g.manual_seed(0)
@@ -170,32 +248,44 @@ def p_sweep(torch, ma, dev):
                    for _ in range(3))
         mask = torch.zeros(1, P, dtype=torch.uint8, device=dev)
         mask[0, P - 16:] = 1
-        before_out = torch.cuda.mem_get_info()[0]
+        ma.attn_fwd_lse(q, k, v, mask, D ** -0.5)      # code objects loaded, then the outputs freed
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats(dev)
+        base_alloc, base_res = torch.cuda.memory_allocated(dev), torch.cuda.memory_reserved(dev)
+        free0 = torch.cuda.mem_get_info(dev)[0]
         o = torch.empty_like(q)
         lse = torch.empty(1, H, P, dtype=torch.float32, device=dev)
-        extra = torch.cuda.mem_get_info()[0]
-        call = lambda: ma.attn_fwd_lse(q, k, v, mask, D ** -0.5, out=o, lse=lse)
-        call()
+        ma.attn_fwd_lse(q, k, v, mask, D ** -0.5, out=o, lse=lse)
         torch.cuda.synchronize()
-        free0 = torch.cuda.mem_get_info()[0]
-        t = _time_call(torch, call)
-        free1 = torch.cuda.mem_get_info()[0]
+        peak_alloc = torch.cuda.max_memory_allocated(dev) - base_alloc
+        peak_res = torch.cuda.max_memory_reserved(dev) - base_res
+        drop = free0 - torch.cuda.mem_get_info(dev)[0]
+        lib_bytes = drop - (torch.cuda.memory_reserved(dev) - base_res)
+        call = lambda: ma.attn_fwd_lse(q, k, v, mask, D ** -0.5, out=o, lse=lse)
+        t, d = _time_call(torch, call)
         flop = 4 * D * H * P * (P - 16)
-        rows.append({"P": P, "us": round(t * 1e6, 1), "tflops": round(flop / t / 1e12, 1),
-                     "call_extra_bytes": o.numel() * 2 + lse.numel() * 4,
-                     "allocator_view_extra_bytes": int(before_out - extra),
-                     "library_alloc_bytes_during_calls": int(free0 - free1),
+        rows.append({"P": P, "us": d, "tflops": round(flop / t / 1e12, 1),
+                     "measured_peak_allocated_bytes": int(peak_alloc),
+                     "measured_peak_reserved_bytes": int(peak_res),
+                     "measured_device_free_drop_bytes": int(drop),
+                     "library_allocated_bytes": int(lib_bytes),
+                     "o_plus_lse_bytes": o.numel() * 2 + lse.numel() * 4,
                      "score_matrix_bytes_avoided": H * P * P * 2})
         del q, k, v, mask, o, lse
-    # call-level bytes are linear in P: fit bytes = a*P + c
+        torch.cuda.empty_cache()
+    # measured peak bytes against P: least-squares line and its worst residual
     xs = [r["P"] for r in rows]
-    ys = [r["call_extra_bytes"] for r in rows]
+    ys = [r["measured_peak_allocated_bytes"] for r in rows]
     n = len(xs)
     mx, my = sum(xs) / n, sum(ys) / n
     a = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sum((x - mx) ** 2 for x in xs)
     c = my - a * mx
+    resid = max(abs(y - (a * x + c)) for x, y in zip(xs, ys))
     return {"workload": "masked prefill with LSE, bf16, B1 H16 D64, last 16 keys padded, N(0,1)*0.5",
-            "rows": rows, "linear_fit_bytes_per_P": round(a, 3), "linear_fit_intercept_bytes": round(c, 1)}
+            "rows": rows, "fit_measured_peak_bytes_per_P": round(a, 3),
+            "fit_measured_peak_intercept_bytes": round(c, 1), "fit_max_abs_residual_bytes": round(resid, 1),
+            "score_matrix_bytes_per_P_at_32122": 16 * 32122 * 2}
 
 
 def varlen_section(torch, ma, W, dev):
@@ -210,22 +300,22 @@ def varlen_section(torch, ma, W, dev):
         q, k, v, cq, ck = (t.to(dev) for t in (w.q, w.k, w.v, w.cu_q, w.cu_k))
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=dev)
-        t = _time_call(torch, lambda: ma.attn_fwd_varlen(q, k, v, cq, ck, w.max_q, w.scale, out=o, lse=lse))
+        t, d = _time_call(torch, lambda: ma.attn_fwd_varlen(q, k, v, cq, ck, w.max_q, w.scale, out=o, lse=lse))
         H, D = q.shape[1], q.shape[2]
         flop = 4 * D * H * sum(a * b for a, b in zip(w.lens_q, w.lens_k))
-        res[name] = {"workload": w.name, "us": round(t * 1e6, 1), "tflops": round(flop / t / 1e12, 1),
+        res[name] = {"workload": w.name, "us": d, "tflops": round(flop / t / 1e12, 1),
                      "frac_mfma": round(flop / t / 1e12 / PEAK_BF16_TFLOPS, 4), "algorithmic_flop": flop}
         del q, k, v, cq, ck, o, lse
     pd = W.patch_p1944()
     q, k, v, m = (t.to(dev) for t in (pd.q, pd.k, pd.v, pd.mask))
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    t = _time_call(torch, lambda: ma.attn_fwd_lse(q, k, v, m, pd.scale, out=o, lse=lse))
-    res["p1944_padded_masked_us"] = round(t * 1e6, 1)
+    t, d = _time_call(torch, lambda: ma.attn_fwd_lse(q, k, v, m, pd.scale, out=o, lse=lse))
+    res["p1944_padded_masked_us"] = d
     return res
 
 
-def paged_section(torch, ma, W, dev):
+def paged_section(torch, ma, W, dev, flush):
     """The decode workload (B32, H_q 32 / H_kv 8, D128, len U[512, 8192] + 1) with its cache in a
     shuffled page pool (attn_decode_paged), per page size, and with an E4M3 cache in 16-token
     pages (attn_decode_fp8kv_paged), each timed on its own; bytes as the contiguous decodes (K
@@ -243,10 +333,10 @@ def paged_section(torch, ma, W, dev):
         Hkv = kp.shape[1]
         ws = torch.empty(ma.attn_decode_workspace_bytes(B, Hq, Hkv, bt.shape[1] * ps, D), dtype=torch.uint8,
                          device=dev)
-        t = _time_call(torch, lambda: ma.attn_decode_paged(q, kp, vp, bt, lens, w.scale, out=o, lse=lse,
-                                                           workspace=ws, want_lse=True), n=20)
+        t, d = _time_call(torch, lambda: ma.attn_decode_paged(q, kp, vp, bt, lens, w.scale, out=o, lse=lse,
+                                                              workspace=ws, want_lse=True), flush=flush)
         nbytes = int((w.lens + 1).sum()) * 2 * Hkv * D * 2 + 2 * q.numel() * 2
-        res[f"page_{ps}"] = {"us": round(t * 1e6, 2), "gbps": round(nbytes / t / 1e9, 1),
+        res[f"page_{ps}"] = {"us": d, "gbps": round(nbytes / t / 1e9, 1),
                              "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBPS, 4)}
         del kp, vp, bt, lens, q, o, lse, ws
     # the same workload with an E4M3 cache in 16-token pages (attn_decode_fp8kv_paged)
@@ -259,15 +349,15 @@ def paged_section(torch, ma, W, dev):
     B, Hq, _, D = q.shape
     Hkv = kp.shape[1]
     ws = torch.empty(ma.attn_decode_workspace_bytes(B, Hq, Hkv, bt.shape[1] * 16, D), dtype=torch.uint8, device=dev)
-    t = _time_call(torch, lambda: ma.attn_decode_fp8kv_paged(q, kp, vp, ks, vs, bt, lens, w.scale, out=o, lse=lse,
-                                                             workspace=ws, want_lse=True), n=20)
+    t, d = _time_call(torch, lambda: ma.attn_decode_fp8kv_paged(q, kp, vp, ks, vs, bt, lens, w.scale, out=o,
+                                                                lse=lse, workspace=ws, want_lse=True), flush=flush)
     nbytes = int((w.lens + 1).sum()) * 2 * Hkv * D + 2 * q.numel() * 2
-    res["fp8_page_16"] = {"us": round(t * 1e6, 2), "gbps": round(nbytes / t / 1e9, 1),
+    res["fp8_page_16"] = {"us": d, "gbps": round(nbytes / t / 1e9, 1),
                           "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBPS, 4)}
     return res
 
 
-def fp8_section(torch, ma, W, dev, int8=False):
+def fp8_section(torch, ma, W, dev, flush, int8=False):
     """The decode workload with an E4M3 cache (attn_decode_fp8kv; per-(sequence, KV head) scales),
     or an INT8 cache (attn_decode_int8kv), timed on its own after the append; bytes: one byte per
     cached K and V element, plus q and o."""
@@ -281,10 +371,10 @@ def fp8_section(torch, ma, W, dev, int8=False):
     B, Hq, _, D = q.shape
     Hkv, Tm = kc.shape[1], kc.shape[2]
     ws = torch.empty(ma.attn_decode_workspace_bytes(B, Hq, Hkv, Tm, D), dtype=torch.uint8, device=dev)
-    t = _time_call(torch, lambda: decode_fn(q, kc, vc, ks, vs, lens, w.scale, out=o, lse=lse,
-                                            workspace=ws, want_lse=True), n=20)
+    t, d = _time_call(torch, lambda: decode_fn(q, kc, vc, ks, vs, lens, w.scale, out=o, lse=lse,
+                                               workspace=ws, want_lse=True), flush=flush)
     nbytes = int((w.lens + 1).sum()) * 2 * Hkv * D + 2 * q.numel() * 2
-    return {"workload": w.name, "us": round(t * 1e6, 2), "gbps": round(nbytes / t / 1e9, 1),
+    return {"workload": w.name, "us": d, "gbps": round(nbytes / t / 1e9, 1),
             "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBPS, 4), "algorithmic_bytes": nbytes}
 
 
@@ -302,13 +392,13 @@ def fp8_prefill_section(torch, ma, W, dev):
         B, Hq, T, D = q.shape
         o = torch.empty((B, Hq, T, D), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
-        t = _time_call(torch, lambda: ma.attn_prefill_fp8(q, k, v, qs, ks, vs, m, causal, w.scale, out=o, lse=lse))
+        t, d = _time_call(torch, lambda: ma.attn_prefill_fp8(q, k, v, qs, ks, vs, m, causal, w.scale, out=o, lse=lse))
         if causal:
             flop = 4 * D * Hq * B * T * (T + 1) // 2
         else:
             n_valid = [int((w.mask[b] == 0).sum()) if w.mask is not None else T for b in range(B)]
             flop = 4 * D * Hq * T * sum(n_valid)
-        res[key] = {"workload": w.name, "us": round(t * 1e6, 1), "tflops": round(flop / t / 1e12, 1),
+        res[key] = {"workload": w.name, "us": d, "tflops": round(flop / t / 1e12, 1),
                     "frac_mfma": round(flop / t / 1e12 / PEAK_FP8_PREFILL_TFLOPS, 4),
                     "peak_tflops": round(PEAK_FP8_PREFILL_TFLOPS, 1), "algorithmic_flop": flop}
         del q, k, v, o, lse
@@ -319,10 +409,10 @@ def fp8_prefill_section(torch, ma, W, dev):
     tq, Hq, D = q.shape
     o = torch.empty((tq, Hq, D), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((Hq, tq), dtype=torch.float32, device=dev)
-    t = _time_call(torch, lambda: ma.attn_prefill_varlen_fp8(q, k, v, qs, ks, vs, cq, ck, w.max_q, False, w.scale,
-                                                             out=o, lse=lse))
+    t, d = _time_call(torch, lambda: ma.attn_prefill_varlen_fp8(q, k, v, qs, ks, vs, cq, ck, w.max_q, False,
+                                                                w.scale, out=o, lse=lse))
     flop = 4 * D * Hq * sum(a * b for a, b in zip(w.cu_q.diff().tolist(), w.cu_k.diff().tolist()))
-    res["ring_hop_8192"] = {"workload": w.name, "us": round(t * 1e6, 1), "tflops": round(flop / t / 1e12, 1),
+    res["ring_hop_8192"] = {"workload": w.name, "us": d, "tflops": round(flop / t / 1e12, 1),
                             "frac_mfma": round(flop / t / 1e12 / PEAK_FP8_PREFILL_TFLOPS, 4),
                             "peak_tflops": round(PEAK_FP8_PREFILL_TFLOPS, 1), "algorithmic_flop": flop}
     return res
@@ -337,19 +427,20 @@ def causal_section(torch, ma, W, dev):
     q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    t = _time_call(torch, lambda: ma.attn_prefill(q, k, v, None, True, w.scale, out=o, lse=lse))
+    t, d = _time_call(torch, lambda: ma.attn_prefill(q, k, v, None, True, w.scale, out=o, lse=lse))
     B, Hq, T, D = q.shape
     flop = 4 * D * Hq * B * T * (T + 1) // 2
-    res["prompt_8192"] = {"workload": w.name, "us": round(t * 1e6, 1), "tflops": round(flop / t / 1e12, 1),
+    res["prompt_8192"] = {"workload": w.name, "us": d, "tflops": round(flop / t / 1e12, 1),
                           "frac_mfma": round(flop / t / 1e12 / PEAK_BF16_TFLOPS, 4), "algorithmic_flop": flop}
     del q, k, v, o, lse
     w = W.gqa_causal_prompts_packed()
     q, k, v, cq, ck = (t_.to(dev) for t_ in (w.q, w.k, w.v, w.cu_q, w.cu_k))
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=dev)
-    t = _time_call(torch, lambda: ma.attn_prefill_varlen(q, k, v, cq, ck, w.max_q, True, w.scale, out=o, lse=lse))
+    t, d = _time_call(torch, lambda: ma.attn_prefill_varlen(q, k, v, cq, ck, w.max_q, True, w.scale, out=o,
+                                                            lse=lse))
     flop = 4 * 128 * 32 * sum(n * (n + 1) // 2 for n in w.lens_q)
-    res["packed_prompts"] = {"workload": w.name, "us": round(t * 1e6, 1), "tflops": round(flop / t / 1e12, 1),
+    res["packed_prompts"] = {"workload": w.name, "us": d, "tflops": round(flop / t / 1e12, 1),
                              "frac_mfma": round(flop / t / 1e12 / PEAK_BF16_TFLOPS, 4), "algorithmic_flop": flop}
     return res
 
@@ -439,13 +530,14 @@ def main():
     wall = time.perf_counter() - t0
     free_after = torch.cuda.mem_get_info()[0]
 
-    def span(a, b):
-        return sum(events[s][a].elapsed_time(events[s][b]) for s in range(args.steps)) / args.steps / 1e3
+    def spans(a, b):
+        return [events[s_][a].elapsed_time(events[s_][b]) * 1e3 for s_ in range(args.steps)]   # us per step
 
-    t_prefill, t_chunks, t_merge, t_append, t_decode = (span(0, 1), span(1, 2), span(2, 3), span(3, 4),
-                                                        span(4, 5))
-    per_step = sorted(events[s][0].elapsed_time(events[s][1]) * 1e3 for s in range(args.steps))
-    pct = lambda f: round(per_step[min(len(per_step) - 1, int(f * (len(per_step) - 1) + 0.5))], 2)
+    d_prefill, d_chunks, d_merge, d_append, d_decode = (spans(0, 1), spans(1, 2), spans(2, 3), spans(3, 4),
+                                                        spans(4, 5))
+    mean_s = lambda us: sum(us) / len(us) / 1e6
+    t_prefill, t_chunks, t_merge, t_append, t_decode = (mean_s(d) for d in (d_prefill, d_chunks, d_merge,
+                                                                              d_append, d_decode))
     # ---- algorithmic work
     B, H, P, D = pf.q.shape
     n_valid = int((pf.mask[0] == 0).sum())
@@ -459,6 +551,16 @@ def main():
     decode_bytes = kv_bytes + q5.numel() * 2 + o5.numel() * 2
     decode_gbps = decode_bytes / t_decode / 1e9
     traffic = measured_traffic()
+
+    # ---- the decode on its own, with the MALL flushed before every call
+    flush = make_flush(torch, dev)
+    lens_ready = (lens0 + 1).to(torch.int32)
+    t_dec_flushed, d_dec_flushed = _time_call(
+        torch, lambda: ma.attn_decode(q5, kc, vc, lens_ready, dc.scale, out=o5, lse=l5, workspace=ws, want_lse=True),
+        flush=flush)
+
+    # ---- device identity and clocks under this load (outside the timed region)
+    gpu = gpu_info(torch, dev, step)
 
     prefill_extra = o3.numel() * o3.element_size() + l3.numel() * 4
     out = {
@@ -487,7 +589,7 @@ def main():
             "achieved": round(tf_prefill, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf_prefill / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
             "algorithmic_flop_per_launch": flop_prefill, "avg_launch_us": round(t_prefill * 1e6, 2),
-            "launch_us_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+            "launch_us": dist_us(d_prefill),
             "exps_per_launch": H * P * n_valid,
             "exp_rate_Gexp_per_s": round(H * P * n_valid / t_prefill / 1e9, 1),
         },
@@ -496,31 +598,39 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(decode_gbps, 1), "peak": PEAK_HBM_GBPS,
                          "unit": "GB/s", "frac": round(decode_gbps / PEAK_HBM_GBPS, 4),
                          "algorithmic_bytes_per_launch": decode_bytes},
-            "attn_decode_us": round(t_decode * 1e6, 2), "kv_append_us": round(t_append * 1e6, 2),
+            "attn_decode_us": dist_us(d_decode), "kv_append_us": dist_us(d_append),
+            "standalone_mall_flushed": {"us": d_dec_flushed,
+                                        "gbps": round(decode_bytes / t_dec_flushed / 1e9, 1),
+                                        "frac_hbm": round(decode_bytes / t_dec_flushed / 1e9 / PEAK_HBM_GBPS, 4)},
             "cached_tokens": int(lens_after.sum().item()),
         },
         "chunked": {
-            "fwd_lse_x2_us": round(t_chunks * 1e6, 2),
+            "fwd_lse_x2_us": dist_us(d_chunks),
             "tflops": round(flop_chunks / t_chunks / 1e12, 2),
             "frac_mfma": round(flop_chunks / t_chunks / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "merge_us": round(t_merge * 1e6, 2),
+            "merge_us": dist_us(d_merge),
             "merge_gbps": round(merge_bytes / t_merge / 1e9, 1),
+            "merge_frac_hbm": round(merge_bytes / t_merge / 1e9 / PEAK_HBM_GBPS, 4),
         },
         "memory": {
-            "library_device_allocations_bytes": int(free_before - free_after),
+            "device_free_drop_across_timed_steps_bytes": int(free_before - free_after),
             "prefill_call_extra_bytes": int(prefill_extra),
             "prefill_call_extra_GB": round(prefill_extra / 1e9, 4),
             "avoided_score_matrix_bytes": H * P * P * 2,
             "decode_workspace_bytes": int(ws.numel()),
         },
+        "library": {"path": os.path.relpath(ma.LIB_PATH, ROOT), "sha256_16": file_sha(ma.LIB_PATH),
+                    "kernel_sources_sha256_16": src_hash(LIB_SRCS),
+                    "prefill_kernel_sources_sha256_16": src_hash(PREFILL_SRCS)},
+        "gpu": gpu,
     }
     if not args.no_sweep:
         out["p_sweep"] = p_sweep(torch, ma, dev)
         out["varlen"] = varlen_section(torch, ma, W, dev)
-        out["paged_decode"] = paged_section(torch, ma, W, dev)
+        out["paged_decode"] = paged_section(torch, ma, W, dev, flush)
         out["causal_gqa_prefill"] = causal_section(torch, ma, W, dev)
-        out["fp8_kv_decode"] = fp8_section(torch, ma, W, dev)
-        out["int8_kv_decode"] = fp8_section(torch, ma, W, dev, int8=True)
+        out["fp8_kv_decode"] = fp8_section(torch, ma, W, dev, flush)
+        out["int8_kv_decode"] = fp8_section(torch, ma, W, dev, flush, int8=True)
         out["fp8_prefill"] = fp8_prefill_section(torch, ma, W, dev)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(pf, args.cpu_seconds)

@@ -14,7 +14,8 @@
  *     float32, the mask (uint8) and cache lengths (int32).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *   - Head dimension D must be 64 or 128.
- *   - Outputs must not alias inputs.
+ *   - No output may share a byte with an input or with another output (byte
+ *     ranges from the stated shapes; in-place use is refused, ATTN_ERR_ALIAS).
  *   - Return value: an attn_status.  Argument checks happen on the host
  *     before anything is enqueued; a failed check enqueues nothing.  A
  *     launch failure reported by hipGetLastError maps to ATTN_ERR_LAUNCH.
@@ -47,7 +48,7 @@ typedef enum {
     ATTN_ERR_LAUNCH = 5,       /* hipGetLastError reported a failure after enqueueing */
     ATTN_ERR_VALUE = 6,        /* scale is not a finite positive number */
     ATTN_ERR_ALIGN = 7,        /* a tensor pointer is not 16-byte aligned */
-    ATTN_ERR_ALIAS = 8         /* an output pointer equals an input pointer */
+    ATTN_ERR_ALIAS = 8         /* an output's bytes overlap an input or another output */
 } attn_status;
 
 /*
@@ -279,8 +280,8 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
 /*
  * FP8 (E4M3) KV cache.  KV-cache quantisation stores each cached element in
  * fewer bytes plus scale metadata and dequantises inside the attention kernel
- * (blog.ruahverce.com, LLM inference memory accounting 2/10, section "18. KV
- * Cache Quantization").  Layout and conventions of the two FP8 calls:
+ * (blog.ruahverce.com, LLM inference memory accounting 2/10, section
+ * "18. KV Quantization은 Byte와 Kernel을 함께 바꾼다").  Layout and conventions of the two FP8 calls:
  *   k_cache, v_cache  [B, H_kv, T_max, D] uint8: OCP E4M3 codes (1 sign, 4
  *       exponent bits with bias 7, 3 mantissa bits, subnormals, largest
  *       magnitude 448, S.1111.111 = NaN; no infinities)
@@ -313,7 +314,7 @@ int attn_decode_fp8kv(const void* q, const void* k_cache, const void* v_cache,
 /*
  * INT8 KV cache: the two FP8 calls above with symmetric INT8 codes, another of
  * the cache formats LLM inference memory accounting 2/10 lists (section
- * "18. KV Cache Quantization").
+ * "18. KV Quantization은 Byte와 Kernel을 함께 바꾼다").
  *   k_cache, v_cache  [B, H_kv, T_max, D] int8: code q stands for q x scale
  *   k_scale, v_scale  as for the FP8 cache
  * kv_append_int8 writes code = clamp(rint(x / scale), -127, 127): an IEEE
@@ -336,7 +337,8 @@ int attn_decode_int8kv(const void* q, const void* k_cache, const void* v_cache,
 /*
  * Paged 8-bit caches: the FP8 and INT8 calls above over page pools, the paged
  * layout of attn_decode_paged (LLM inference memory accounting 2/10, sections
- * "15. Paged KV Cache가 해결하는 것" and "18. KV Cache Quantization").
+ * "15. Paged KV Cache가 해결하는 것" and
+ * "18. KV Quantization은 Byte와 Kernel을 함께 바꾼다").
  *   k_pages, v_pages  [num_pages, H_kv, page_size, D] codes (uint8 E4M3 or int8)
  *   block_table, page_size, max_pages_per_seq  as attn_decode_paged (T_max =
  *       max_pages_per_seq · page_size; the workspace is sized with that T_max)

@@ -17,8 +17,8 @@ from typing import Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# MATTN_LIB may point at another build of the same library (A/B comparisons).
-LIB_PATH = os.environ.get("MATTN_LIB") or os.path.join(_HERE, "libmasked_attn.so")
+# The in-tree build; nothing can redirect the binding to another library.
+LIB_PATH = os.path.join(_HERE, "libmasked_attn.so")
 
 ATTN_F32 = 0
 ATTN_BF16 = 1

@@ -4,6 +4,7 @@
 // call enqueues nothing.
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 #include "attn.h"
 #include "launch.h"
@@ -29,6 +30,28 @@ bool fits(long long a, long long b, long long c, long long d) {
 
 int finish(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
 
+// A tensor's byte range, for the aliasing rule: no output may share a byte with an input
+// or with another output (a null pointer or an empty range overlaps nothing).
+struct Span {
+    const void* p;
+    long long n;
+};
+bool overlap(Span a, Span b) {
+    if (!a.p || !b.p || a.n <= 0 || b.n <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + (uintptr_t)b.n && b0 < a0 + (uintptr_t)a.n;
+}
+// true if some output overlaps an input or another output
+bool aliased(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+    for (auto o = outs.begin(); o != outs.end(); ++o) {
+        for (const Span& i : ins)
+            if (overlap(*o, i)) return true;
+        for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlap(*o, *o2)) return true;
+    }
+    return false;
+}
+
 int fwd_common(const void* q, const void* k, const void* v, const uint8_t* mask, void* o,
                float* lse, bool need_lse, int B, int H, int H_kv, int Tq, int Tk, int D,
                bool causal, float scale, int dtype, void* stream) {
@@ -42,8 +65,13 @@ int fwd_common(const void* q, const void* k, const void* v, const uint8_t* mask,
         return ATTN_ERR_SHAPE;
     if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
-    if (o == k || o == v || (lse && ((void*)lse == q || (void*)lse == k || (void*)lse == v || (void*)lse == o)))
-        return ATTN_ERR_ALIAS;
+    {
+        const long long es = elem_bytes(dtype);
+        const Span sq{q, (long long)B * H * Tq * D * es}, sk{k, (long long)B * H_kv * Tk * D * es},
+            sv{v, (long long)B * H_kv * Tk * D * es}, sm{mask, mask ? (long long)B * Tk : 0};
+        if (aliased({Span{o, sq.n}, Span{lse, lse ? (long long)B * H * Tq * 4 : 0}}, {sq, sk, sv, sm}))
+            return ATTN_ERR_ALIAS;
+    }
     // the bf16 kernel addresses one head's K/V through a 32-bit buffer range
     if (dtype == ATTN_BF16 && (long long)Tk * D * 2 > (1ll << 31) - 1) return ATTN_ERR_SHAPE;
     FwdArgs a{q, k, v, mask, o, lse, B, H, Tq, Tk, D, scale, stream};
@@ -71,9 +99,13 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* cu
         return ATTN_ERR_SHAPE;
     if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
-    if (o == q || o == k || o == v || (lse && ((void*)lse == q || (void*)lse == k || (void*)lse == v ||
-                                               (void*)lse == o)))
-        return ATTN_ERR_ALIAS;
+    {
+        const Span sq{q, (long long)total_q * H * D * 2}, sk{k, (long long)total_k * H_kv * D * 2},
+            sv{v, (long long)total_k * H_kv * D * 2}, scq{cu_seqlens_q, (long long)(B + 1) * 4},
+            sck{cu_seqlens_k, (long long)(B + 1) * 4};
+        if (aliased({Span{o, sq.n}, Span{lse, lse ? (long long)H * total_q * 4 : 0}}, {sq, sk, sv, scq, sck}))
+            return ATTN_ERR_ALIAS;
+    }
     if (total_q == 0 || max_seqlen_q == 0) return ATTN_OK;      // no query rows: nothing to write
     FwdArgs a{q, k, v, nullptr, o, lse, B, H, max_seqlen_q, 0, D, scale, stream};
     a.H_kv = H_kv;
@@ -95,7 +127,13 @@ int q8_append(void* k_cache, void* v_cache, const float* k_scale, const float* v
     if (!fits(B, H_kv, T_max, D) || B > (1 << 30)) return ATTN_ERR_SHAPE;
     if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
         return ATTN_ERR_ALIGN;
-    if (k_cache == v_cache || k_new == k_cache || v_new == v_cache) return ATTN_ERR_ALIAS;
+    {
+        const long long cb = (long long)B * H_kv * T_max * D, nb = (long long)B * H_kv * D * elem_bytes(new_dtype);
+        const long long sb = (long long)B * H_kv * 4;
+        if (aliased({Span{k_cache, cb}, Span{v_cache, cb}, Span{cache_seqlens, (long long)B * 4}},
+                    {Span{k_new, nb}, Span{v_new, nb}, Span{k_scale, sb}, Span{v_scale, sb}}))
+            return ATTN_ERR_ALIAS;
+    }
     AppendFp8Args a{k_cache, v_cache, k_scale, v_scale, cache_seqlens, k_new, v_new,
                     new_dtype == ATTN_BF16, B, H_kv, T_max, D, stream};
     a.int8 = int8;
@@ -117,7 +155,15 @@ int q8_decode(const void* q, const void* k_cache, const void* v_cache, const flo
     if (!workspace || workspace_bytes < decode_workspace_bytes(B, H_q, T_max, D)) return ATTN_ERR_WORKSPACE;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(workspace))
         return ATTN_ERR_ALIGN;
-    if (o == q || o == k_cache || o == v_cache) return ATTN_ERR_ALIAS;
+    {
+        const long long qb = (long long)B * H_q * D * 2, cb = (long long)B * H_kv * T_max * D;
+        const long long sb = (long long)B * H_kv * 4;
+        if (aliased({Span{o, qb}, Span{lse, lse ? (long long)B * H_q * 4 : 0},
+                     Span{workspace, (long long)workspace_bytes}},
+                    {Span{q, qb}, Span{k_cache, cb}, Span{v_cache, cb}, Span{k_scale, sb}, Span{v_scale, sb},
+                     Span{cache_seqlens, (long long)B * 4}}))
+            return ATTN_ERR_ALIAS;
+    }
     DecodeFp8Args a{q, k_cache, v_cache, k_scale, v_scale, cache_seqlens, o, lse, B, H_q, H_kv, T_max, D,
                     scale, workspace, stream};
     a.int8 = int8;
@@ -177,7 +223,9 @@ int attn_merge_lse(int n_chunks, const void* const* outs, const float* const* ls
     for (int i = 0; i < n_chunks; ++i) {
         if (!outs[i] || !lses[i]) return ATTN_ERR_NULL;
         if (!aligned16(outs[i])) return ATTN_ERR_ALIGN;
-        if (outs[i] == out || (lse_out && lses[i] == lse_out)) return ATTN_ERR_ALIAS;
+        const long long ob = (long long)B * H * T * D * elem_bytes(dtype), lb = (long long)B * H * T * 4;
+        if (aliased({Span{out, ob}, Span{lse_out, lse_out ? lb : 0}}, {Span{outs[i], ob}, Span{lses[i], lb}}))
+            return ATTN_ERR_ALIAS;
         a.outs[i] = outs[i];
         a.lses[i] = lses[i];
     }
@@ -196,7 +244,13 @@ int kv_append(void* k_cache, void* v_cache, int32_t* cache_seqlens, const void* 
     if (!fits(B, H_kv, T_max, D) || B > (1 << 30)) return ATTN_ERR_SHAPE;
     if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
         return ATTN_ERR_ALIGN;
-    if (k_cache == v_cache || k_new == k_cache || v_new == v_cache) return ATTN_ERR_ALIAS;
+    {
+        const long long cb = (long long)B * H_kv * T_max * D * elem_bytes(dtype);
+        const long long nb = (long long)B * H_kv * D * elem_bytes(dtype);
+        if (aliased({Span{k_cache, cb}, Span{v_cache, cb}, Span{cache_seqlens, (long long)B * 4}},
+                    {Span{k_new, nb}, Span{v_new, nb}}))
+            return ATTN_ERR_ALIAS;
+    }
     AppendArgs a{k_cache, v_cache, cache_seqlens, k_new, v_new, B, H_kv, T_max, D,
                  elem_bytes(dtype), stream};
     return finish(launch_kv_append(a));
@@ -231,7 +285,14 @@ static int q8_append_paged(void* k_pages, void* v_pages, const float* k_scale, c
     if (const int st = paged_geometry(B, H_kv, num_pages, page_size, max_pages, D, T_max)) return st;
     if (!aligned16(k_pages) || !aligned16(v_pages) || !aligned16(k_new) || !aligned16(v_new))
         return ATTN_ERR_ALIGN;
-    if (k_pages == v_pages || k_new == k_pages || v_new == v_pages) return ATTN_ERR_ALIAS;
+    {
+        const long long pb = (long long)num_pages * H_kv * page_size * D;
+        const long long nb = (long long)B * H_kv * D * elem_bytes(new_dtype), sb = (long long)B * H_kv * 4;
+        if (aliased({Span{k_pages, pb}, Span{v_pages, pb}, Span{cache_seqlens, (long long)B * 4}},
+                    {Span{k_new, nb}, Span{v_new, nb}, Span{k_scale, sb}, Span{v_scale, sb},
+                     Span{block_table, (long long)B * max_pages * 4}}))
+            return ATTN_ERR_ALIAS;
+    }
     AppendFp8Args a{k_pages, v_pages, k_scale, v_scale, cache_seqlens, k_new, v_new,
                     new_dtype == ATTN_BF16, B, H_kv, T_max, D, stream};
     a.int8 = int8;
@@ -258,7 +319,15 @@ static int q8_decode_paged(const void* q, const void* k_pages, const void* v_pag
     if (!workspace || workspace_bytes < decode_workspace_bytes(B, H_q, T_max, D)) return ATTN_ERR_WORKSPACE;
     if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) || !aligned16(workspace))
         return ATTN_ERR_ALIGN;
-    if (o == q || o == k_pages || o == v_pages) return ATTN_ERR_ALIAS;
+    {
+        const long long qb = (long long)B * H_q * D * 2, pb = (long long)num_pages * H_kv * page_size * D;
+        const long long sb = (long long)B * H_kv * 4;
+        if (aliased({Span{o, qb}, Span{lse, lse ? (long long)B * H_q * 4 : 0},
+                     Span{workspace, (long long)workspace_bytes}},
+                    {Span{q, qb}, Span{k_pages, pb}, Span{v_pages, pb}, Span{k_scale, sb}, Span{v_scale, sb},
+                     Span{block_table, (long long)B * max_pages * 4}, Span{cache_seqlens, (long long)B * 4}}))
+            return ATTN_ERR_ALIAS;
+    }
     DecodeFp8Args a{q, k_pages, v_pages, k_scale, v_scale, cache_seqlens, o, lse, B, H_q, H_kv, T_max, D,
                     scale, workspace, stream};
     a.int8 = int8;
@@ -280,7 +349,13 @@ int kv_append_paged(void* k_pages, void* v_pages, const int32_t* block_table, in
         return st;
     if (!aligned16(k_pages) || !aligned16(v_pages) || !aligned16(k_new) || !aligned16(v_new))
         return ATTN_ERR_ALIGN;
-    if (k_pages == v_pages || k_new == k_pages || v_new == v_pages) return ATTN_ERR_ALIAS;
+    {
+        const long long pb = (long long)num_pages * H_kv * page_size * D * elem_bytes(dtype);
+        const long long nb = (long long)B * H_kv * D * elem_bytes(dtype);
+        if (aliased({Span{k_pages, pb}, Span{v_pages, pb}, Span{cache_seqlens, (long long)B * 4}},
+                    {Span{k_new, nb}, Span{v_new, nb}, Span{block_table, (long long)B * max_pages_per_seq * 4}}))
+            return ATTN_ERR_ALIAS;
+    }
     AppendArgs a{k_pages, v_pages, cache_seqlens, k_new, v_new, B, H_kv, T_max, D,
                  elem_bytes(dtype), stream};
     a.block_table = block_table;
@@ -309,7 +384,14 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
     if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) ||
         !aligned16(workspace))
         return ATTN_ERR_ALIGN;
-    if (o == q || o == k_pages || o == v_pages) return ATTN_ERR_ALIAS;
+    {
+        const long long qb = (long long)B * H_q * D * 2, pb = (long long)num_pages * H_kv * page_size * D * 2;
+        if (aliased({Span{o, qb}, Span{lse, lse ? (long long)B * H_q * 4 : 0},
+                     Span{workspace, (long long)workspace_bytes}},
+                    {Span{q, qb}, Span{k_pages, pb}, Span{v_pages, pb},
+                     Span{block_table, (long long)B * max_pages_per_seq * 4}, Span{cache_seqlens, (long long)B * 4}}))
+            return ATTN_ERR_ALIAS;
+    }
     DecodeArgs a{q, k_pages, v_pages, cache_seqlens, o, lse, B, H_q, H_kv, T_max, D, scale,
                  workspace, stream};
     a.block_table = block_table;
@@ -400,9 +482,14 @@ int attn_prefill_fp8(const void* q, const void* k, const void* v, const float* q
     if ((long long)Tk * D > (1ll << 31) - 1) return ATTN_ERR_SHAPE;
     if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
-    if (o == q || o == k || o == v || (lse && ((void*)lse == q || (void*)lse == k || (void*)lse == v ||
-                                               (void*)lse == o)))
-        return ATTN_ERR_ALIAS;
+    {
+        const long long qb = (long long)B * H_q * Tq * D, kb = (long long)B * H_kv * Tk * D;
+        if (aliased({Span{o, qb * 2}, Span{lse, lse ? (long long)B * H_q * Tq * 4 : 0}},
+                    {Span{q, qb}, Span{k, kb}, Span{v, kb}, Span{q_scale, (long long)B * H_q * 4},
+                     Span{k_scale, (long long)B * H_kv * 4}, Span{v_scale, (long long)B * H_kv * 4},
+                     Span{key_padding_mask, key_padding_mask ? (long long)B * Tk : 0}}))
+            return ATTN_ERR_ALIAS;
+    }
     FwdArgs a{q, k, v, key_padding_mask, o, lse, B, H_q, Tq, Tk, D, scale, stream};
     a.H_kv = H_kv;
     a.causal = causal != 0;
@@ -433,9 +520,14 @@ int attn_prefill_varlen_fp8(const void* q, const void* k, const void* v, const f
         return ATTN_ERR_SHAPE;
     if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
-    if (o == q || o == k || o == v || (lse && ((void*)lse == q || (void*)lse == k || (void*)lse == v ||
-                                               (void*)lse == o)))
-        return ATTN_ERR_ALIAS;
+    {
+        const long long qb = (long long)total_q * H_q * D, kb = (long long)total_k * H_kv * D;
+        if (aliased({Span{o, qb * 2}, Span{lse, lse ? (long long)H_q * total_q * 4 : 0}},
+                    {Span{q, qb}, Span{k, kb}, Span{v, kb}, Span{q_scale, (long long)B * H_q * 4},
+                     Span{k_scale, (long long)B * H_kv * 4}, Span{v_scale, (long long)B * H_kv * 4},
+                     Span{cu_seqlens_q, (long long)(B + 1) * 4}, Span{cu_seqlens_k, (long long)(B + 1) * 4}}))
+            return ATTN_ERR_ALIAS;
+    }
     if (total_q == 0 || max_seqlen_q == 0) return ATTN_OK;      // no query rows: nothing to write
     FwdArgs a{q, k, v, nullptr, o, lse, B, H_q, max_seqlen_q, 0, D, scale, stream};
     a.H_kv = H_kv;
@@ -472,7 +564,14 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
         !aligned16(workspace))
         return ATTN_ERR_ALIGN;
-    if (o == q || o == k_cache || o == v_cache) return ATTN_ERR_ALIAS;
+    {
+        const long long es = elem_bytes(dtype);
+        const long long qb = (long long)B * H_q * D * es, cb = (long long)B * H_kv * T_max * D * es;
+        if (aliased({Span{o, qb}, Span{lse, lse ? (long long)B * H_q * 4 : 0},
+                     Span{workspace, (long long)workspace_bytes}},
+                    {Span{q, qb}, Span{k_cache, cb}, Span{v_cache, cb}, Span{cache_seqlens, (long long)B * 4}}))
+            return ATTN_ERR_ALIAS;
+    }
     // the bf16 kernel addresses one (sequence, KV head) through a 32-bit buffer range
     if (dtype == ATTN_BF16 && (long long)T_max * D * 2 > (1ll << 31) - 1) return ATTN_ERR_SHAPE;
     DecodeArgs a{q, k_cache, v_cache, cache_seqlens, o, lse, B, H_q, H_kv, T_max, D, scale,
@@ -490,7 +589,7 @@ const char* attn_status_string(int status) {
         case ATTN_ERR_LAUNCH: return "kernel launch failed";
         case ATTN_ERR_VALUE: return "scale must be finite and > 0";
         case ATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
-        case ATTN_ERR_ALIAS: return "an output aliases an input";
+        case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
         default: return "unknown status";
     }
 }

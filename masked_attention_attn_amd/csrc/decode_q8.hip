@@ -3,7 +3,8 @@
 //
 // KV-cache quantisation stores each cached element in fewer bytes plus scale
 // metadata, and the attention kernel dequantises on the fly (blog.ruahverce.com,
-// LLM inference memory accounting 2/10, section "18. KV Cache Quantization").
+// LLM inference memory accounting 2/10, section
+// "18. KV Quantization은 Byte와 Kernel을 함께 바꾼다").
 // Here the cache holds OCP E4M3 codes (or INT8 integers) with one float32 scale
 // per (sequence, KV head) for K and one for V: a cached element is code value x
 // scale.  Every E4M3 value and every integer in [-128, 127] is exact in bf16, so

@@ -70,8 +70,8 @@ void kv_append_kernel(unsigned char* __restrict__ kc, unsigned char* __restrict_
 // E4M3(clamp(y, -448, 448)) (round to nearest, ties to even), INT8 codes as
 // clamp(rint(y), -127, 127) (nearest integer, ties to even; symmetric INT8 is
 // one of the cache formats of LLM inference memory accounting 2/10, section
-// "18. KV Cache Quantization").  Four elements per thread become one dword of
-// codes (element i in byte i).
+// "18. KV Quantization은 Byte와 Kernel을 함께 바꾼다").  Four elements per thread become one
+// dword of codes (element i in byte i).
 // PAGED: the pools and slot mapping of kv_append_kernel's paged form.
 template <bool INT8, bool PAGED>
 __global__ __launch_bounds__(NT)

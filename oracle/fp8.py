@@ -5,7 +5,7 @@ imports it and it shares no code with the HIP path.
 
 KV-cache quantisation stores each cached K/V element in fewer bytes plus scale
 metadata, and the attention kernel must dequantise on the fly (LLM inference
-memory accounting 2/10, section "18. KV Cache Quantization": lower-precision
+memory accounting 2/10, section "18. KV Quantization은 Byte와 Kernel을 함께 바꾼다": lower-precision
 KV halves or quarters the bytes per token and brings scales and a dequant
 step with it).  The pages fix neither the 8-bit format nor the scale
 granularity; the readings taken here:

@@ -6,7 +6,7 @@ imports it and it shares no code with the HIP path.
 KV-cache quantisation keeps each cached K/V element in fewer bytes plus scale
 metadata and dequantises inside the attention kernel; INT8 is one of the
 formats the page lists (LLM inference memory accounting 2/10, section
-"18. KV Cache Quantization").  The page fixes neither the scale granularity
+"18. KV Quantization은 Byte와 Kernel을 함께 바꾼다").  The page fixes neither the scale granularity
 nor the rounding; the readings taken here:
   * symmetric INT8: code q stands for q * scale, with one float32 scale per
     (sequence, KV head) for K and one for V (the FP8 cache's granularity);

@@ -40,6 +40,34 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+# Every HIP runtime routine the library may import: kernel registration and launch, error
+# query, device and occupancy queries, the kernel LDS attribute, and the address of a
+# file-scope device array.  No allocation, free, copy, memset or synchronisation.
+ALLOWED_HIP_IMPORTS = {
+    "__hipPopCallConfiguration", "__hipPushCallConfiguration", "__hipRegisterFatBinary",
+    "__hipRegisterFunction", "__hipUnregisterFatBinary", "__hipRegisterVar", "hipDeviceGetAttribute",
+    "hipFuncSetAttribute", "hipGetDevice", "hipGetLastError", "hipLaunchKernel",
+    "hipOccupancyMaxActiveBlocksPerMultiprocessor", "hipGetSymbolAddress",
+}
+
+
+def test_library_imports_no_allocation_or_sync(lib):
+    """The calls allocate no device memory and never synchronise: the shared library does not
+    even import hipMalloc*, hipFree*, hipMemset*, hipMemcpy* or any synchronisation routine."""
+    import shutil
+    import subprocess
+    import masked_attention_attn_amd as ma
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", ma.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    hip = {line.split()[-1].split("@")[0] for line in out.splitlines() if "hip" in line.lower()}
+    assert hip, "expected HIP runtime imports"
+    assert hip <= ALLOWED_HIP_IMPORTS, sorted(hip - ALLOWED_HIP_IMPORTS)
+    assert not any(("alloc" in n.lower() or "free" in n.lower() or "sync" in n.lower()) for n in hip)
+
+
 def test_status_strings(lib):
     for code in range(9):
         s = lib.attn_status_string(code).decode()
@@ -80,6 +108,17 @@ def test_fwd_validation(lib):
     assert lib.attn_fwd_lse(A, B_, C, 0, O, A, 1, 2, 8, 8, 64, 0.125, 1, None) == 8
 
 
+def test_alias_rule_covers_byte_ranges(lib):
+    # an output that shares any byte with an input or with another output is refused:
+    # in place (o == q), partial overlaps, LSE inside O, and a mask inside O
+    n = 1 * 2 * 8 * 64 * 2            # bytes of q and o at B1 H2 T8 D64 bf16
+    assert fwd(lib, o=A) == 8
+    assert fwd(lib, o=A + n - 16) == 8
+    assert fwd(lib, m=O + 64) == 8
+    assert lib.attn_fwd_lse(A, B_, C, 0, O, O + n - 16, 1, 2, 8, 8, 64, 0.125, 1, None) == 8
+    assert lib.attn_fwd_lse(A, B_, C, 0, O, B_ + 16, 1, 2, 8, 8, 64, 0.125, 1, None) == 8
+
+
 def test_merge_validation(lib):
     P = ctypes.c_void_p
     outs = (P * 2)(A, B_)
@@ -91,6 +130,8 @@ def test_merge_validation(lib):
     assert lib.attn_merge_lse(2, bad, lses, O, 0, 1, 2, 8, 64, 1, None) == 1
     assert lib.attn_merge_lse(2, outs, lses, A, 0, 1, 2, 8, 64, 1, None) == 8
     assert lib.attn_merge_lse(2, outs, lses, O, L, 1, 2, 8, 64, 1, None) == 8
+    assert lib.attn_merge_lse(2, outs, lses, A + 1024, 0, 1, 2, 8, 64, 1, None) == 8   # inside outs[0]
+    assert lib.attn_merge_lse(2, outs, lses, O, O + 512, 1, 2, 8, 64, 1, None) == 8    # lse inside out
     assert lib.attn_merge_lse(2, outs, lses, O, 0, 1, 2, 8, 100, 1, None) == 3
     assert lib.attn_merge_lse(2, outs, lses, O + 4, 0, 1, 2, 8, 64, 1, None) == 7
     assert lib.attn_merge_lse(2, outs, lses, O, 0, 1, 0, 8, 64, 1, None) == 2
@@ -102,6 +143,8 @@ def test_append_validation(lib):
     assert lib.kv_append(A, B_, O, C, L, 2, 2, 0, 64, 1, None) == 2
     assert lib.kv_append(A, A, O, C, L, 2, 2, 16, 64, 1, None) == 8
     assert lib.kv_append(A + 2, B_, O, C, L, 2, 2, 16, 64, 1, None) == 7
+    assert lib.kv_append(A, B_, O, A + 4096, L, 2, 2, 16, 64, 1, None) == 8    # k_new inside k_cache
+    assert lib.kv_append(A, B_, A + 64, C, L, 2, 2, 16, 64, 1, None) == 8      # lengths inside k_cache
 
 
 def test_decode_validation(lib):
@@ -123,6 +166,8 @@ def test_decode_validation(lib):
     assert dec(ws=0) == 4
     assert dec(wsb=ws - 1) == 4
     assert dec(o=A) == 8
+    assert dec(ws=O + 256) == 8            # workspace overlapping the output
+    assert dec(o=B_ + 4096) == 8           # output inside the K cache
     assert dec(q=A + 1) == 7
     assert lib.attn_decode_workspace_bytes(4, 6, 4, 1000, 128) == 0
     assert lib.attn_decode_workspace_bytes(0, 8, 2, 1000, 128) == 0
@@ -257,6 +302,8 @@ def test_fp8_validation(lib):
     assert dec(wsb=ws - 1) == 4
     assert dec(k=B_ + 8) == 7
     assert dec(o=A) == 8
+    assert dec(ws=O + 256) == 8            # workspace overlapping the output
+    assert dec(o=B_ + 4096) == 8           # output inside the K cache
     assert lib.kv_append_fp8(A, B_, KS, 0, L, C, O, 2, 2, 16, 64, 1, None) == 1
     assert lib.kv_append_fp8(A, B_, KS, VS, L, C, O, 2, 2, 16, 64, 7, None) == 3
     assert lib.kv_append_fp8(A, B_, KS, VS, L, C, O, 2, 2, 0, 64, 1, None) == 2

@@ -156,6 +156,14 @@ def _randn(g, shape, amp, dtype):
     return x.to(dtype).contiguous()
 
 
+def _uniform_scales(seed: int, shape, lo=0.01, hi=2.0) -> torch.Tensor:
+    """Float32 scale factors U[lo, hi) from a generator of their own (seed + 7919), so that
+    asking for them leaves every other draw of a workload unchanged.  Unlike powers of two,
+    their products with the softmax scale and with each other round in float32."""
+    g = _gen(seed + 7919)
+    return (lo + (hi - lo) * torch.rand(*shape, generator=g)).float().contiguous()
+
+
 def mask_from_valid_lengths(valid: Sequence[int], Tk: int) -> torch.Tensor:
     """uint8 [B, Tk]; keys at index >= valid[b] are marked padded (1)."""
     idx = torch.arange(Tk)
@@ -261,10 +269,12 @@ class VarlenFp8:
     name: str = ""
 
 
-def make_varlen_fp8(lens_q, lens_k, H, D, *, H_kv=None, amp=1.0, seed=0, scale=None, name="") -> VarlenFp8:
+def make_varlen_fp8(lens_q, lens_k, H, D, *, H_kv=None, amp=1.0, seed=0, scale=None, name="",
+                    scales="pow2") -> VarlenFp8:
     """Packed E4M3 inputs whose dequantised values are about N(0, amp^2), with make_prefill_fp8's
     recipe per (sequence, head): scale amp * 2^-e, e ~ U{2..6}, codes N(0,1) * 2^e cast to
-    float8_e4m3fn.  Draw order: Q, K, V scale exponents, then Q, K, V."""
+    float8_e4m3fn.  Draw order: Q, K, V scale exponents, then Q, K, V.  scales="uniform" as
+    make_prefill_fp8."""
     H_kv = H if H_kv is None else H_kv
     g = _gen(seed)
     B = len(lens_q)
@@ -284,9 +294,14 @@ def make_varlen_fp8(lens_q, lens_k, H, D, *, H_kv=None, amp=1.0, seed=0, scale=N
     k = codes(tk, H_kv, ek, rk)
     v = codes(tk, H_kv, ev, rk)
     sc = lambda e: (amp * torch.exp2(-e.float())).contiguous()
+    qs, ks, vs = sc(eq), sc(ek), sc(ev)
+    if scales == "uniform":
+        uq = _uniform_scales(seed, (B, H))
+        uk, uv = _uniform_scales(seed + 1, (2, B, H_kv))
+        qs, ks, vs = (qs * uq).contiguous(), (ks * uk).contiguous(), (vs * uv).contiguous()
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    return VarlenFp8(q, k, v, sc(eq), sc(ek), sc(ev), cq, ck, max([int(n) for n in lens_q]), float(scale), name)
+    return VarlenFp8(q, k, v, qs, ks, vs, cq, ck, max([int(n) for n in lens_q]), float(scale), name)
 
 
 def to_paged(dec: Decode, page_size: int, *, seed=1, spare_pages=3) -> Paged:
@@ -314,11 +329,12 @@ def to_paged(dec: Decode, page_size: int, *, seed=1, spare_pages=3) -> Paged:
 
 
 def make_decode_fp8(B, H_q, H_kv, D, len_lo, len_hi, *, T_max=None, seed=0, scale=None, lens=None,
-                    name="") -> DecodeFp8:
+                    name="", scales="pow2") -> DecodeFp8:
     """E4M3 caches drawn as N(0,1) cast to float8_e4m3fn (round to nearest even), scales
-    2^U{-6..-2} per (b, KV head), new tokens N(0,1) times their head's scale in bf16 (so they
-    quantise into the bulk of the code range), Q N(0,1) bf16.  Draw order: lengths, K cache,
-    V cache, K scale exponents, V scale exponents, k_new, v_new, Q."""
+    2^U{-6..-2} per (b, KV head) (scales="uniform": U[0.01, 2) instead, from their own
+    generator), new tokens N(0,1) times their head's scale in bf16 (so they quantise into the
+    bulk of the code range), Q N(0,1) bf16.  Draw order: lengths, K cache, V cache, K scale
+    exponents, V scale exponents, k_new, v_new, Q."""
     g = _gen(seed)
     if lens is None:
         lens = torch.randint(len_lo, len_hi + 1, (B,), generator=g, dtype=torch.int64)
@@ -329,6 +345,8 @@ def make_decode_fp8(B, H_q, H_kv, D, len_lo, len_hi, *, T_max=None, seed=0, scal
     vc = torch.randn(B, H_kv, T_max, D, generator=g).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
     ks = torch.exp2(torch.randint(-6, -1, (B, H_kv), generator=g).float()).contiguous()
     vs = torch.exp2(torch.randint(-6, -1, (B, H_kv), generator=g).float()).contiguous()
+    if scales == "uniform":
+        ks, vs = _uniform_scales(seed, (2, B, H_kv))
     kn = (torch.randn(B, H_kv, 1, D, generator=g) * ks[:, :, None, None]).to(torch.bfloat16).contiguous()
     vn = (torch.randn(B, H_kv, 1, D, generator=g) * vs[:, :, None, None]).to(torch.bfloat16).contiguous()
     q = torch.randn(B, H_q, 1, D, generator=g).to(torch.bfloat16).contiguous()
@@ -338,9 +356,10 @@ def make_decode_fp8(B, H_q, H_kv, D, len_lo, len_hi, *, T_max=None, seed=0, scal
 
 
 def make_decode_int8(B, H_q, H_kv, D, len_lo, len_hi, *, T_max=None, seed=0, scale=None, lens=None,
-                     name="") -> DecodeFp8:
+                     name="", scales="pow2") -> DecodeFp8:
     """Symmetric INT8 caches: codes round(N(0,1) * 32) clamped to +-127 (int8), scales 2^U{-10..-6}
-    per (b, KV head) (dequantised values about N(0,1) * 2^-5 .. 2^-1, the FP8 cache's range), new
+    per (b, KV head) (dequantised values about N(0,1) * 2^-5 .. 2^-1, the FP8 cache's range;
+    scales="uniform": 2^-5 * U[0.01, 2) instead, from their own generator), new
     tokens N(0,1) * 32 * their head's scale in bf16 (so they quantise into the bulk of the code
     range), Q N(0,1) bf16.  Draw order as make_decode_fp8.  Returned in a DecodeFp8 record (the
     caches hold int8 codes)."""
@@ -355,6 +374,8 @@ def make_decode_int8(B, H_q, H_kv, D, len_lo, len_hi, *, T_max=None, seed=0, sca
     vc = codes().contiguous()
     ks = torch.exp2(torch.randint(-10, -5, (B, H_kv), generator=g).float()).contiguous()
     vs = torch.exp2(torch.randint(-10, -5, (B, H_kv), generator=g).float()).contiguous()
+    if scales == "uniform":
+        ks, vs = _uniform_scales(seed, (2, B, H_kv)) * 2.0 ** -5
     kn = (torch.randn(B, H_kv, 1, D, generator=g) * 32 * ks[:, :, None, None]).to(torch.bfloat16).contiguous()
     vn = (torch.randn(B, H_kv, 1, D, generator=g) * 32 * vs[:, :, None, None]).to(torch.bfloat16).contiguous()
     q = torch.randn(B, H_q, 1, D, generator=g).to(torch.bfloat16).contiguous()
@@ -377,11 +398,12 @@ def make_gqa_prefill(B, H_q, H_kv, Tq, Tk, D, dtype=torch.bfloat16, *, valid=Non
 
 
 def make_prefill_fp8(B, H_q, H_kv, Tq, Tk, D, *, valid=None, amp=1.0, seed=0, scale=None,
-                     name="") -> PrefillFp8:
+                     name="", scales="pow2") -> PrefillFp8:
     """E4M3 prefill inputs whose dequantised values are about N(0, amp^2): each (b, head) of Q, K
     and V gets a scale amp * 2^-e with e ~ U{2..6}, and its codes are N(0,1) * 2^e cast to
     float8_e4m3fn (round to nearest even; |N * 2^e| stays far below 448).  Draw order: Q, K, V
-    scale exponents, then Q, K, V."""
+    scale exponents, then Q, K, V.  scales="uniform": each scale also carries a factor
+    U[0.01, 2) from its own generator (values about N(0, (amp u)^2))."""
     g = _gen(seed)
     eq = torch.randint(2, 7, (B, H_q), generator=g)
     ek = torch.randint(2, 7, (B, H_kv), generator=g)
@@ -395,10 +417,15 @@ def make_prefill_fp8(B, H_q, H_kv, Tq, Tk, D, *, valid=None, amp=1.0, seed=0, sc
     k = codes((B, H_kv, Tk, D), ek)
     v = codes((B, H_kv, Tk, D), ev)
     sc = lambda e: (amp * torch.exp2(-e.float())).contiguous()
+    qs, ks, vs = sc(eq), sc(ek), sc(ev)
+    if scales == "uniform":
+        uq = _uniform_scales(seed, (B, H_q))
+        uk, uv = _uniform_scales(seed + 1, (2, B, H_kv))
+        qs, ks, vs = (qs * uq).contiguous(), (ks * uk).contiguous(), (vs * uv).contiguous()
     mask = mask_from_valid_lengths(valid, Tk) if valid is not None else None
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    return PrefillFp8(q, k, v, sc(eq), sc(ek), sc(ev), mask, float(scale), name)
+    return PrefillFp8(q, k, v, qs, ks, vs, mask, float(scale), name)
 
 
 # ---- the five named workloads -------------------------------------------------
