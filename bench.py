@@ -20,7 +20,7 @@ oracle on a bounded sample of the prefill workload.
 
 Timing: HIP events on the launch stream around every call of every timed step (K >= 50
 by default), reported as the mean and the 10th / 50th / 90th percentiles per kernel.  The
-decodes timed on their own write a 512 MiB scratch buffer before each call, so the 256 MB
+decodes timed on their own read a 512 MiB scratch buffer before each call, so the 256 MB
 last-level cache (MALL) holds none of the cache they read.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -192,13 +192,13 @@ def _time_call(torch, call, n=50, settle=0.3, flush=None):
 
 
 def make_flush(torch, dev):
-    """A fill of FLUSH_BYTES of scratch: afterwards the MALL holds none of a decode's cache."""
-    buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
-    state = {"i": 0}
+    """A read of FLUSH_BYTES of scratch (a sum over it): afterwards the MALL holds none of a
+    decode's cache.  A read, not a write: written lines would stay dirty in the MALL and their
+    write-back would run during the next timed call."""
+    buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
 
     def flush():
-        state["i"] = (state["i"] + 1) & 0xFF
-        buf.fill_(state["i"])
+        buf.sum()
     return flush
 
 

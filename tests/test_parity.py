@@ -695,13 +695,26 @@ def test_prefill_fp8(ma, case):
     check_attn(o, l, Or, Lr, torch.bfloat16, f"fp8 prefill {case}")
 
 
+def v_units(codes, v_scale, packed=False):
+    """The largest per-(sequence, KV head) RMS of the dequantised V values (at least 1): the
+    unit of the O bar for inputs spread wider than N(0, 1).  O is a convex combination of V
+    rows, so its bf16 roundings scale with |V| (as in test_fwd_peaky_scores); LSE keeps its bar.
+    codes: uint8 E4M3 [B, H_kv, T, D] (packed: [T, H_kv, D], one sequence)."""
+    x = codes.view(torch.float8_e4m3fn).float()
+    if packed:
+        x = x.transpose(0, 1).unsqueeze(0)
+    rms = x.pow(2).mean(dim=(2, 3)).sqrt() * v_scale[: x.shape[0]]
+    return max(1.0, float(rms.max()))
+
+
 @pytest.mark.parametrize("case", [PREFILL_FP8[i] for i in (2, 3, 6, 7, 9)])
 def test_prefill_fp8_uniform_scales(ma, case):
     B, Hq, Hkv, Tq, Tk, D, causal, valid = case
     w = W.make_prefill_fp8(B, Hq, Hkv, Tq, Tk, D, valid=valid, seed=Tq + Hq + D + 1, scales="uniform")
     o, l = _fp8_prefill(ma, w, causal)
     Or, Lr = oracle.prefill_fp8(w.q, w.k, w.v, w.q_scale, w.k_scale, w.v_scale, w.mask, causal, w.scale)
-    check_attn(o, l, Or, Lr, torch.bfloat16, f"fp8 prefill, uniform scales {case}")
+    check_attn(o, l, Or, Lr, torch.bfloat16, f"fp8 prefill, uniform scales {case}",
+               o_tol=2e-2 * v_units(w.v, w.v_scale))
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -928,7 +941,10 @@ def test_prefill_varlen_fp8_uniform_scales(ma, case):
     torch.cuda.synchronize()
     Or, Lr = oracle.prefill_varlen_fp8(w.q, w.k, w.v, w.q_scale, w.k_scale, w.v_scale, w.cu_q, w.cu_k,
                                        causal, w.scale)
-    check_attn(o, l.t(), Or, Lr.T, torch.bfloat16, f"packed fp8 prefill, uniform scales {case}")
+    unit = max(v_units(w.v[int(w.cu_k[b]):int(w.cu_k[b + 1])], w.v_scale[b:b + 1], packed=True)
+               for b in range(len(lk)) if lk[b] > 0)
+    check_attn(o, l.t(), Or, Lr.T, torch.bfloat16, f"packed fp8 prefill, uniform scales {case}",
+               o_tol=2e-2 * unit)
 
 
 @pytest.mark.parametrize("D", [64, 128])
