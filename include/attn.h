@@ -48,7 +48,8 @@ typedef enum {
     ATTN_ERR_LAUNCH = 5,       /* hipGetLastError reported a failure after enqueueing */
     ATTN_ERR_VALUE = 6,        /* scale is not a finite positive number */
     ATTN_ERR_ALIGN = 7,        /* a tensor pointer is not 16-byte aligned */
-    ATTN_ERR_ALIAS = 8         /* an output's bytes overlap an input or another output */
+    ATTN_ERR_ALIAS = 8,        /* an output's bytes overlap an input or another output */
+    ATTN_ERR_SCRATCH = 9       /* attn_decode_noalloc: more scratch needed than its static buffer */
 } attn_status;
 
 /*
@@ -234,6 +235,30 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
 /* Bytes of workspace attn_decode needs for these sizes (0 on invalid sizes).
  * attn_decode_paged needs the same with T_max = max_pages_per_seq · page_size. */
 size_t attn_decode_workspace_bytes(int B, int H_q, int H_kv, int T_max, int D);
+
+/*
+ * attn_decode_noalloc — attn_decode for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, checks and results as attn_decode, without the workspace: the partial
+ * results live in a static device buffer of ATTN_DECODE_NOALLOC_SCRATCH_BYTES inside the
+ * library (one per GPU the library runs on, held until the process ends).  The call
+ * allocates nothing, takes the buffer's device address once per device on its first call
+ * there (hipGetSymbolAddress), and then only enqueues the attn_decode kernels.
+ *   Limit: attn_decode_workspace_bytes(B, H_q, H_kv, T_max, D) must not exceed
+ *       ATTN_DECODE_NOALLOC_SCRATCH_BYTES, else ATTN_ERR_SCRATCH (nothing enqueued).  At
+ *       D = 128 that is B·H_q·ceil(T_max / 1024) <= 32,263 (e.g. 32 sequences x 32 query
+ *       heads up to T_max = 31,744).
+ *   Every call on one GPU shares that GPU's buffer, which keeps the last call's contents
+ *   (nothing in it needs clearing: every slot a call reads, the same call writes first).
+ *   Calls that overlap in time on one GPU (different streams, no ordering) race on it;
+ *   order them on one stream.
+ */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* cache_seqlens, void* o, float* lse,
+                        int B, int H_q, int H_kv, int T_max, int D,
+                        float scale, int dtype, void* stream);
 
 /*
  * Paged KV cache.  A sequence's logical KV blocks live in non-contiguous

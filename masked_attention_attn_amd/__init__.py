@@ -8,5 +8,5 @@ from ._lib import (  # noqa: F401
     attn_decode, attn_decode_workspace_bytes, attn_fwd_lse, attn_fwd_masked, attn_fwd_varlen,
     attn_decode_fp8kv, attn_decode_paged, attn_merge_lse, attn_prefill, attn_prefill_fp8, attn_prefill_varlen, kv_append, kv_append_fp8, kv_append_int8, kv_append_paged, load,
     attn_decode_int8kv, attn_prefill_varlen_fp8, kv_append_fp8_paged, kv_append_int8_paged,
-    attn_decode_fp8kv_paged, attn_decode_int8kv_paged,
+    attn_decode_fp8kv_paged, attn_decode_int8kv_paged, attn_decode_noalloc, DECODE_NOALLOC_SCRATCH_BYTES,
 )

@@ -26,14 +26,14 @@ ATTN_BF16 = 1
 STATUS = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
     4: "ATTN_ERR_WORKSPACE", 5: "ATTN_ERR_LAUNCH", 6: "ATTN_ERR_VALUE", 7: "ATTN_ERR_ALIGN",
-    8: "ATTN_ERR_ALIAS",
+    8: "ATTN_ERR_ALIAS", 9: "ATTN_ERR_SCRATCH",
 }
 
 EXPORTS = ("attn_fwd_masked", "attn_fwd_lse", "attn_fwd_varlen", "attn_merge_lse", "kv_append",
            "attn_decode", "attn_decode_workspace_bytes", "kv_append_paged", "attn_decode_paged",
            "attn_prefill", "attn_prefill_varlen", "kv_append_fp8", "attn_decode_fp8kv", "attn_prefill_fp8",
            "kv_append_int8", "attn_decode_int8kv", "attn_prefill_varlen_fp8", "kv_append_fp8_paged",
-           "kv_append_int8_paged", "attn_decode_fp8kv_paged", "attn_decode_int8kv_paged", "attn_status_string")
+           "kv_append_int8_paged", "attn_decode_fp8kv_paged", "attn_decode_int8kv_paged", "attn_status_string", "attn_decode_noalloc")
 
 _lib = None
 
@@ -60,6 +60,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_merge_lse.argtypes = [I, ctypes.POINTER(P), ctypes.POINTER(P), P, P, I, I, I, I, I, P]
     lib.kv_append.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
     lib.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, P, S, P]
+    lib.attn_decode_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, P]
     lib.attn_prefill.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
     lib.attn_prefill_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P]
     lib.kv_append_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
@@ -79,7 +80,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_status_string.argtypes = [I]
     lib.attn_status_string.restype = ctypes.c_char_p
     for name in ("attn_fwd_masked", "attn_fwd_lse", "attn_fwd_varlen", "attn_merge_lse", "kv_append",
-                 "attn_decode", "kv_append_paged", "attn_decode_paged", "attn_prefill", "attn_prefill_varlen",
+                 "attn_decode", "attn_decode_noalloc", "kv_append_paged", "attn_decode_paged", "attn_prefill", "attn_prefill_varlen",
                  "kv_append_fp8", "attn_decode_fp8kv", "attn_prefill_fp8", "kv_append_int8",
                  "attn_decode_int8kv", "attn_prefill_varlen_fp8", "kv_append_fp8_paged", "kv_append_int8_paged",
                  "attn_decode_fp8kv_paged", "attn_decode_int8kv_paged"):
@@ -295,6 +296,41 @@ def attn_decode(q, k_cache, v_cache, cache_seqlens, scale=None, out=None, lse=No
                                              _ptr(out), _ptr(lse if want_lse else None), B, Hq, Hkv, Tmax, D,
                                              float(scale), code, _ptr(workspace), nbytes, _stream(q.device)))
     return (out, lse) if want_lse else out
+
+
+# Capacity of the library's static scratch behind attn_decode_noalloc (ATTN_DECODE_NOALLOC_SCRATCH_BYTES).
+DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, cache_seqlens, out, lse=None, scale=None):
+    """attn_decode without a workspace: the library's static device scratch holds the partial
+    results, and the C call allocates nothing.  The caller passes the outputs (out [B, H_q, 1, D],
+    lse [B, H_q] float32 or None).  Sizes whose workspace would exceed the static buffer raise
+    AttnError (ATTN_ERR_SCRATCH)."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (cache_seqlens, "cache_seqlens"),
+                 (out, "out")):
+        _dev(t, n)
+    B, Hq, one, D = q.shape
+    if one != 1:
+        raise ValueError("q must be [B, H_q, 1, D]")
+    _, Hkv, Tmax, Dk = k_cache.shape
+    if k_cache.shape[0] != B or Dk != D or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shapes do not match q")
+    if cache_seqlens.shape != (B,) or cache_seqlens.dtype != torch.int32:
+        raise ValueError("cache_seqlens must be int32 [B]")
+    code = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or out.dtype != q.dtype or out.shape != q.shape:
+        raise TypeError("q, caches and out must share a dtype, out the shape of q")
+    if lse is not None:
+        _dev(lse, "lse")
+        if lse.shape != (B, Hq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [B, H_q]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check("attn_decode_noalloc", load().attn_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens), _ptr(out), _ptr(lse), B, Hq, Hkv, Tmax, D,
+        float(scale), code, _stream(q.device)))
+    return (out, lse) if lse is not None else out
 
 
 def _paged_args(k_pages, v_pages, block_table, cache_seqlens, B):

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <initializer_list>
+#include <mutex>
 
 #include "attn.h"
 #include "launch.h"
@@ -549,20 +550,25 @@ size_t attn_decode_workspace_bytes(int B, int H_q, int H_kv, int T_max, int D) {
     return decode_workspace_bytes(B, H_q, T_max, D);
 }
 
-int attn_decode(const void* q, const void* k_cache, const void* v_cache,
-                const int32_t* cache_seqlens, void* o, float* lse, int B, int H_q, int H_kv,
-                int T_max, int D, float scale, int dtype, void* workspace,
-                size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The argument checks of attn_decode and attn_decode_noalloc.  caller_ws = false skips the
+// workspace checks (the no-allocation call brings its own).
+int decode_checks(const void* q, const void* k_cache, const void* v_cache, const int32_t* cache_seqlens,
+                  void* o, float* lse, int B, int H_q, int H_kv, int T_max, int D, float scale, int dtype,
+                  bool caller_ws, void* workspace, size_t workspace_bytes) {
     if (!q || !k_cache || !v_cache || !cache_seqlens || !o) return ATTN_ERR_NULL;
     if (!dtype_ok(dtype) || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED;
     if (H_kv <= 0 || H_q <= 0 || H_q % H_kv != 0) return ATTN_ERR_SHAPE;
     if (!fits(B, H_kv, T_max, D) || !fits(B, H_q, 1, D) || (long long)B * H_q > (1 << 30))
         return ATTN_ERR_SHAPE;
     if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_VALUE;
-    if (!workspace || workspace_bytes < decode_workspace_bytes(B, H_q, T_max, D))
+    if (caller_ws && (!workspace || workspace_bytes < decode_workspace_bytes(B, H_q, T_max, D)))
         return ATTN_ERR_WORKSPACE;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
-        !aligned16(workspace))
+        (workspace && !aligned16(workspace)))
         return ATTN_ERR_ALIGN;
     {
         const long long es = elem_bytes(dtype);
@@ -574,8 +580,66 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
     }
     // the bf16 kernel addresses one (sequence, KV head) through a 32-bit buffer range
     if (dtype == ATTN_BF16 && (long long)T_max * D * 2 > (1ll << 31) - 1) return ATTN_ERR_SHAPE;
+    return ATTN_OK;
+}
+
+// Scratch of attn_decode_noalloc: the decode's partial results (the workspace of attn_decode)
+// in a file-scope device array, one copy per GPU that the library runs on, held until the
+// process ends.  Host code never uses the array's name as an address: each device's address
+// comes from hipGetSymbolAddress, taken once with that device current.
+constexpr size_t kNoallocScratchBytes = ATTN_DECODE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void* scratch_addr[kMaxDevices];
+hipError_t scratch_err[kMaxDevices];
+
+// This device's address of `scratch`, or null (then *err says why).
+void* scratch_on_current_device(hipError_t* err) {
+    int dev = -1;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::call_once(scratch_once[dev], [dev] {
+        void* p = nullptr;
+        scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        scratch_addr[dev] = scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    *err = scratch_err[dev];
+    return scratch_addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* cache_seqlens, void* o, float* lse, int B, int H_q, int H_kv,
+                int T_max, int D, float scale, int dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    if (const int st = decode_checks(q, k_cache, v_cache, cache_seqlens, o, lse, B, H_q, H_kv, T_max, D, scale,
+                                     dtype, true, workspace, workspace_bytes))
+        return st;
     DecodeArgs a{q, k_cache, v_cache, cache_seqlens, o, lse, B, H_q, H_kv, T_max, D, scale,
                  workspace, stream};
+    return finish(dtype == ATTN_BF16 ? launch_decode_bf16(a) : launch_decode_f32(a));
+}
+
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* cache_seqlens, void* o, float* lse, int B, int H_q, int H_kv,
+                        int T_max, int D, float scale, int dtype, void* stream) {
+    if (const int st = decode_checks(q, k_cache, v_cache, cache_seqlens, o, lse, B, H_q, H_kv, T_max, D, scale,
+                                     dtype, false, nullptr, 0))
+        return st;
+    if (decode_workspace_bytes(B, H_q, T_max, D) > kNoallocScratchBytes) return ATTN_ERR_SCRATCH;
+    hipError_t err;
+    void* ws = scratch_on_current_device(&err);
+    if (!ws) return ATTN_ERR_LAUNCH;
+    DecodeArgs a{q, k_cache, v_cache, cache_seqlens, o, lse, B, H_q, H_kv, T_max, D, scale, ws, stream};
     return finish(dtype == ATTN_BF16 ? launch_decode_bf16(a) : launch_decode_f32(a));
 }
 
@@ -590,6 +654,7 @@ const char* attn_status_string(int status) {
         case ATTN_ERR_VALUE: return "scale must be finite and > 0";
         case ATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
         case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
+        case ATTN_ERR_SCRATCH: return "the problem needs more scratch than the static no-allocation buffer holds";
         default: return "unknown status";
     }
 }

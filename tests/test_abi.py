@@ -69,7 +69,7 @@ def test_library_imports_no_allocation_or_sync(lib):
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         s = lib.attn_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.attn_status_string(99).decode() == "unknown status"
