@@ -46,26 +46,28 @@ EXTRA = {
 }
 
 
-def _compile(src: str, build_dir: str = BUILD, include_first=None) -> str:
+def _compile(src: str, build_dir: str = BUILD, include_first=None, extra=()) -> str:
     obj = os.path.join(build_dir, os.path.basename(src).replace(".hip", ".o"))
     inc = ["-I", include_first] if include_first else []
-    cmd = [HIPCC, *inc, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
+    cmd = [HIPCC, *inc, *FLAGS, *EXTRA.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = True, out: str = LIB, build_dir: str = BUILD, csrc: str = CSRC) -> str:
-    """Compile csrc/*.hip into `out` (default: the in-tree library)."""
+def build(verbose: bool = True, out: str = LIB, build_dir: str = BUILD, csrc: str = CSRC, extra=(),
+          link_extra=()) -> str:
+    """Compile csrc/*.hip into `out` (default: the in-tree library).  `extra` flags go to every
+    compile, `link_extra` to the link (the debug build with host sanitizers uses both)."""
     os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(csrc, "*.hip")))
 
     workers = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(lambda f: _compile(f, build_dir), srcs))
+        objs = list(ex.map(lambda f: _compile(f, build_dir, extra=extra), srcs))
     tmp = out + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

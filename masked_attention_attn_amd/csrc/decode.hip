@@ -219,6 +219,10 @@ hipError_t launch(const DecodeArgs& a) {
     float* ws_o = static_cast<float*>(a.workspace);
     float* ws_ml = ws_o + parts * D;
     const int G = a.H_q / a.H_kv;
+    ATTN_CHECK(G >= 1 && G * a.H_kv == a.H_q, "query heads group onto KV heads");
+    ATTN_CHECK(parts * (D + 2) * sizeof(float) <= decode_workspace_bytes(a.B, a.H_q, a.T_max, D),
+               "split partials fit the workspace");
+    ATTN_CHECK((long long)a.B * a.H_kv * G <= kMaxGrid && (long long)a.B * a.H_q <= kMaxGrid, "grid size");
     if (G % 8 == 0) launch_split<T, D, 8>(a, ws_o, ws_ml, nsplit);
     else if (G % 4 == 0) launch_split<T, D, 4>(a, ws_o, ws_ml, nsplit);
     else if (G % 2 == 0) launch_split<T, D, 2>(a, ws_o, ws_ml, nsplit);

@@ -407,16 +407,27 @@ int resident_waves(int lds_bytes) {
 
 template <int D, bool PAGED>
 hipError_t launch(const DecodeArgs& a) {
-    // the largest dynamic LDS any call uses: RV full 32-head Q slots
-    static const hipError_t attr =
-        hipFuncSetAttribute((const void*)decode_stream_kernel<D, PAGED>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            Geo<D>::RV * q_slot_bytes(32, D));
-    if (attr != hipSuccess) return attr;
     const int G = a.H_q / a.H_kv;
     const int n_hg = (G + 31) / 32;
     const int nsplit = decode_nsplit(a.T_max);
     const int qb = q_slot_bytes(G, D);
     const int lds = Geo<D>::RV * qb;
+    ATTN_CHECK(G >= 1 && G * a.H_kv == a.H_q, "query heads group onto KV heads");
+    ATTN_CHECK(lds + Geo<D>::RV * Geo<D>::BLK <= kLdsBytesPerCu, "V ring and Q slots fit a CU");
+    ATTN_CHECK(nsplit >= 1 && (long long)nsplit * kDecodeSplit >= a.T_max, "splits cover the cache");
+    ATTN_CHECK((size_t)a.B * a.H_q * nsplit * 2 * (D + 2) * sizeof(float) <=
+                   decode_workspace_bytes(a.B, a.H_q, a.T_max, D),
+               "partials and (reference, sum) pairs fit the workspace");
+    ATTN_CHECK(PAGED || (long long)a.T_max * D * 2 < (1ll << 31), "a (sequence, KV head) fits a 32-bit range");
+    ATTN_CHECK(!PAGED || (a.page_size >= 16 && (a.page_size & (a.page_size - 1)) == 0 &&
+                          (long long)a.max_pages * a.page_size == a.T_max),
+               "pages are powers of two of at least 16 tokens");
+    ATTN_CHECK((long long)a.B * a.H_q / 4 + 1 <= kMaxGrid, "combine grid size");
+    // the largest dynamic LDS any call uses: RV full 32-head Q slots
+    static const hipError_t attr =
+        hipFuncSetAttribute((const void*)decode_stream_kernel<D, PAGED>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            Geo<D>::RV * q_slot_bytes(32, D));
+    if (attr != hipSuccess) return attr;
     const int nwaves = resident_waves<D, PAGED>(lds);
     float* ws_o = static_cast<float*>(a.workspace);
     float* ws_ml = ws_o + (size_t)a.B * a.H_q * nsplit * 2 * D;

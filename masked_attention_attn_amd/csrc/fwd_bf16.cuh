@@ -830,24 +830,35 @@ hipError_t launch_one(const FwdArgs& a) {
     using L = Lds<D, FP8>;
     using ET = Elem<FP8>;
     auto kern = fwd_bf16_kernel<D, WRITE_LSE, VARLEN, CAUSAL, FP8>;
-    // LDS above 64 KiB must be opted into once per kernel (thread-safe static init).
-    static const hipError_t attr =
-        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
-    if (attr != hipSuccess) return attr;
     constexpr int BM = kBM<D>;
     const int n_qt = (a.Tq + BM - 1) / BM;       // varlen: Tq = the longest sequence
     const int total = a.B * a.H * n_qt;
     int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
     int nparts = 1, tpp = 0;
+    const int H_kv = a.H_kv > 0 ? a.H_kv : a.H;
     if (VARLEN) {   // chunk parts dealt to the XCDs in turn (see the kernel)
-        const int H_kv = a.H_kv > 0 ? a.H_kv : a.H;
         const int chunks = a.B * H_kv, S = (a.H / H_kv) * n_qt;
         int g = kNumXcd, x = chunks;
         while (x % g) g /= 2;                     // gcd(chunks, 8): 8 is a power of two
         nparts = kNumXcd / g;
         tpp = (S + nparts - 1) / nparts;
         grid = chunks * nparts * tpp;             // chunks * nparts is a multiple of 8
+        ATTN_CHECK((long long)nparts * tpp >= S && chunks * nparts % kNumXcd == 0, "parts cover every tile");
+    } else {
+        ATTN_CHECK(grid % kNumXcd == 0 && grid >= total, "the XCD swizzle covers every tile");
     }
+    ATTN_CHECK(L::BYTES <= kLdsBytesPerCu, "LDS tile rings fit a CU");
+    ATTN_CHECK(n_qt >= 1 && (long long)n_qt * BM >= a.Tq, "q-tiles cover every query row");
+    ATTN_CHECK(grid >= 1 && grid <= kMaxGrid, "grid size");
+    ATTN_CHECK(H_kv >= 1 && a.H % H_kv == 0, "query heads group onto KV heads");
+    // per-lane tile offsets are 32-bit: rows past the last one (up to a tile) times the row stride
+    ATTN_CHECK(((VARLEN ? (long long)a.total_k : a.Tk) + L::TK) * (VARLEN ? (long long)H_kv * a.D : a.D) *
+                       (long long)sizeof(ET) < (1ll << 32),
+               "K/V tile offsets fit 32 bits");
+    // LDS above 64 KiB must be opted into once per kernel (thread-safe static init).
+    static const hipError_t attr =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
+    if (attr != hipSuccess) return attr;
     const float c = a.scale * kLog2e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * Cfg<D>::NWAVE), L::BYTES, (hipStream_t)a.stream,
                        (const ET*)a.q, (const ET*)a.k, (const ET*)a.v, a.mask,

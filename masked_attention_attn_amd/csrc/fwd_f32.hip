@@ -120,6 +120,8 @@ hipError_t launch_one(const FwdArgs& a) {
     const int n_qt = (a.Tq + QPB - 1) / QPB;
     const int total = a.B * a.H * n_qt;
     const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
+    ATTN_CHECK(n_qt >= 1 && (long long)n_qt * QPB >= a.Tq, "query blocks cover every row");
+    ATTN_CHECK(grid >= total && grid <= kMaxGrid && grid % kNumXcd == 0, "grid size");
     hipLaunchKernelGGL((fwd_f32_kernel<D, WRITE_LSE>), dim3(grid), dim3(NT), 0, (hipStream_t)a.stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, a.mask,
                        (float*)a.o, a.lse, a.H, a.Tq, a.Tk, a.scale * kLog2e, n_qt, total);

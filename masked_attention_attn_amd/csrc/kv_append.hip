@@ -136,6 +136,8 @@ void kv_append_q8_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
 }  // namespace
 
 hipError_t launch_kv_append_fp8(const AppendFp8Args& a) {
+    ATTN_CHECK(a.B >= 1 && a.B <= kMaxGrid && a.D % 16 == 0, "one workgroup per sequence, whole 16-code rows");
+    ATTN_CHECK(!a.block_table || (long long)a.max_pages * a.page_size == a.T_max, "paged capacity");
     auto kern = a.block_table ? (a.int8 ? kv_append_q8_kernel<true, true> : kv_append_q8_kernel<false, true>)
                               : (a.int8 ? kv_append_q8_kernel<true, false> : kv_append_q8_kernel<false, false>);
     hipLaunchKernelGGL(kern, dim3(a.B), dim3(NT), 0, (hipStream_t)a.stream,
@@ -147,6 +149,8 @@ hipError_t launch_kv_append_fp8(const AppendFp8Args& a) {
 
 hipError_t launch_kv_append(const AppendArgs& a) {
     const int row_bytes = a.D * a.elem_bytes;
+    ATTN_CHECK(a.B >= 1 && a.B <= kMaxGrid && row_bytes % 16 == 0, "one workgroup per sequence, 16-byte rows");
+    ATTN_CHECK(!a.block_table || (long long)a.max_pages * a.page_size == a.T_max, "paged capacity");
     if (a.block_table)
         hipLaunchKernelGGL(kv_append_kernel<true>, dim3(a.B), dim3(NT), 0, (hipStream_t)a.stream,
                            (unsigned char*)a.k_cache, (unsigned char*)a.v_cache, a.lens,

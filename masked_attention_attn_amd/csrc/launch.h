@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "debug_checks.h"
+
 namespace mattn {
 
 struct FwdArgs {

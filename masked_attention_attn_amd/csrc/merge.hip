@@ -137,6 +137,8 @@ hipError_t launch(const MergeArgs& a) {
     const long threads = (long)a.rows * (a.D / 8);
     const long grid = (threads + NT - 1) / NT;
     const bool idx32 = grid * (long)NT <= 0xFFFFFFFFL;
+    ATTN_CHECK(a.n >= 1 && a.n <= kMaxMergeChunks && a.D % 8 == 0, "chunk count and row width");
+    ATTN_CHECK(grid >= 1 && grid <= 0xFFFFFFFFL && grid * (long)NT >= threads, "grid covers every row");
     const auto kern = !idx32 || a.n > 4 ? merge_kernel<T, 0>
                     : a.n == 1 ? merge_kernel<T, 1> : a.n == 2 ? merge_kernel<T, 2>
                     : a.n == 3 ? merge_kernel<T, 3> : merge_kernel<T, 4>;
