@@ -101,12 +101,12 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
         v_voff[ch] = (uint32_t)(r * RB + (p ^ v_swz<D>(r)) * 16);
     }
     const __amdgpu_buffer_rsrc_t zrs = brsrc(kc, 0u);
-    constexpr uint32_t kOob = 0x7FFFFFF0u;      // past every buffer range: reads zero
+    const i32x4_sgpr z4 = make_rsrc(kc, 0u);    // the same empty range, for the buffer->LDS loads
 
     // Paged: the buffer ranges of the two 16-token halves of block (cursor) x, each
     // inside one page (pages are powers of two >= 16 tokens, blocks start at
     // multiples of 32): kh/vh and the row offset of the half within its range.
-    auto page_halves = [&](const Cursor& x, __amdgpu_buffer_rsrc_t* kh, __amdgpu_buffer_rsrc_t* vh,
+    auto page_halves = [&](const Cursor& x, __amdgpu_buffer_rsrc_t* kh, i32x4_sgpr* vh,
                            uint32_t* roff) {
         const int t0 = x.s * kDecodeSplit + x.i * CK;
         const int last = x.t_end - 1;
@@ -119,7 +119,7 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             if (kh) kh[h] = zrs;
-            if (vh) vh[h] = zrs;
+            if (vh) vh[h] = z4;
             roff[h] = 0u;
             const int th = t0 + 16 * h;
             if (th < x.t_end) {
@@ -128,7 +128,7 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
                 const int rows = min(1 << lps, x.t_end - pstart);
                 const size_t head = (((size_t)page * H_kv + x.g) << lps) * D;
                 if (kh) kh[h] = brsrc(kc + head, (uint32_t)rows * RB);
-                if (vh) vh[h] = brsrc(vc + head, (uint32_t)rows * RB);
+                if (vh) vh[h] = make_rsrc(vc + head, (uint32_t)rows * RB);
                 roff[h] = (uint32_t)(th - pstart) * RB;
             }
         }
@@ -138,44 +138,53 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
     Cursor icv = cursor_at(L, HG, n_hg, b0, a0 - before);
     Cursor ick = icv;
     int nv = 0, nk = 0, qs_issue = 0;
-    __amdgpu_buffer_rsrc_t vrs = zrs, krs = zrs;
+    __amdgpu_buffer_rsrc_t krs = zrs;
+    i32x4_sgpr vrs = z4;
     auto item_rsrc = [&](const Cursor& x, const bf16* base) {
         const size_t head = ((size_t)x.b * H_kv + x.g) * (size_t)T_max * D;
         return brsrc(base + head, (uint32_t)x.t_end * RB);
     };
+    auto item_rsrc4 = [&](const Cursor& x, const bf16* base) {
+        const size_t head = ((size_t)x.b * H_kv + x.g) * (size_t)T_max * D;
+        return make_rsrc(base + head, (uint32_t)x.t_end * RB);
+    };
     if constexpr (!PAGED) {
-        vrs = item_rsrc(icv, vc);
+        vrs = item_rsrc4(icv, vc);
         krs = item_rsrc(ick, kc);
     }
     auto issue_v = [&](int s) {
         const bool live = nv < nblk;
         unsigned char* dst = vslot(s);
         if constexpr (PAGED) {
-            __amdgpu_buffer_rsrc_t vh[2] = {zrs, zrs};
+            i32x4_sgpr vh[2] = {z4, z4};
             uint32_t roff[2] = {0u, 0u};
             if (live) page_halves(icv, nullptr, vh, roff);
 #pragma unroll
             for (int ch = 0; ch < NCH; ++ch)
-                lds_dma16(vh[ch / HCH], dst + ch * 1024, roff[ch / HCH] + v_voff[ch] - (ch / HCH) * 16u * RB);
+                lds_dma16(vh[ch / HCH], dst + ch * 1024, roff[ch / HCH] + v_voff[ch] - (ch / HCH) * 16u * RB,
+                          ch == NCH - 1);
         } else {
             const uint32_t row0 = (uint32_t)(icv.s * kDecodeSplit + icv.i * CK) * RB;
+            const i32x4_sgpr r = live ? vrs : z4;
 #pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) lds_dma16(live ? vrs : zrs, dst + ch * 1024, row0 + v_voff[ch]);
+            for (int ch = 0; ch < NCH; ++ch) lds_dma16(r, dst + ch * 1024, row0 + v_voff[ch], ch == NCH - 1);
         }
         if (!live) return;
         if (icv.i == 0 || nv == 0) {     // the item's Q (also for a range that starts inside it)
             const int ncols = min(32, G - icv.hg * 32);
-            const __amdgpu_buffer_rsrc_t qrs =
-                brsrc(q + ((size_t)icv.b * H_q + icv.g * G + icv.hg * 32) * D, (uint32_t)(ncols * RB));
+            const i32x4_sgpr qrs =
+                make_rsrc(q + ((size_t)icv.b * H_q + icv.g * G + icv.hg * 32) * D, (uint32_t)(ncols * RB));
 #pragma unroll
             for (int ch = 0; ch < QCH; ++ch)
-                if (ch * 1024 < ncols * RB) lds_dma16(qrs, qslot(qs_issue) + ch * 1024, (uint32_t)(ch * 1024 + lane * 16));
+                if (ch * 1024 < ncols * RB)
+                    lds_dma16(qrs, qslot(qs_issue) + ch * 1024, (uint32_t)(ch * 1024 + lane * 16),
+                              (ch + 1) * 1024 >= ncols * RB);
         }
         ++nv;
         advance(icv, L, HG, n_hg);
         if (icv.i == 0) {
             qs_issue = qs_issue == RV - 1 ? 0 : qs_issue + 1;
-            if constexpr (!PAGED) vrs = item_rsrc(icv, vc);
+            if constexpr (!PAGED) vrs = item_rsrc4(icv, vc);
         }
     };
     u32x4 kr[RV][KSTEPS];
@@ -243,14 +252,22 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
     uint32_t v_lane[DB];           // this lane's byte offset of row block db in a V slot
 #pragma unroll
     for (int db = 0; db < DB; ++db) v_lane[db] = (uint32_t)((vrow * D + (((db * 4 + vc0) ^ vfv) * 8) + vin) * 2);
-    // V of block j lands before the loads of the three blocks issued after it
-    // (3 x (NCH + KSTEPS) loads, plus any Q loads and partial stores): waiting for
-    // at most that many outstanding makes slot j's V complete.  The same holds for the
-    // Q of an item, issued right after the V of its first block here (or of the
-    // wavefront's first block): at least NV_AFTER loads follow it by the time that
-    // block is computed, also at the first block of the range.  The compiler derives
-    // no wait for reading the Q slot after its buffer->LDS loads, so it is explicit.
-    constexpr int NV_AFTER = (RV - 1) * (NCH + KSTEPS);
+    // The slot waits.  Loop iteration i issues, in this program order: V of block
+    // i + RV - 1 (NCH buffer->LDS loads, then the QCH loads of the item's Q if that block
+    // starts an item), K of block i + LK (KSTEPS loads), then computes block i.  The
+    // buffer->LDS loads are asm statements with a memory clobber and the waits too, so the
+    // compiler moves no load across either: the count below is a property of this source.
+    // Between the V (and Q) loads of block j and the wait in front of computing j come at
+    // least the V loads of the RV - 1 blocks after j and the K loads of LK + 1 blocks (the
+    // fewest at the first block of a range, where the prologue has issued K of blocks
+    // 0 .. LK - 1 only): NV_AFTER loads, plus any Q loads and partial stores.  Loads return
+    // in issue order, so while block j's V or Q is outstanding so are all the loads after
+    // it, and at most NV_AFTER outstanding means they have landed.
+    constexpr int V_LOADS_AFTER = (RV - 1) * NCH;       // V of blocks j+1 .. j+RV-1
+    constexpr int K_LOADS_AFTER = (LK + 1) * KSTEPS;    // K of (at least) LK + 1 blocks
+    constexpr int NV_AFTER = V_LOADS_AFTER + K_LOADS_AFTER;
+    static_assert(RV == 4 && LK == 2 && NCH == BLK / 1024 && KSTEPS == D / 16, "the counted geometry");
+    static_assert(LK + 1 <= RV, "K of LK + 1 blocks is issued before block j is computed");
     static_assert(NV_AFTER <= 63, "vmcnt range");
 
     auto compute = [&](int j, int s) {

@@ -203,9 +203,21 @@ __device__ __forceinline__ void advance(Cursor& c, const Lens& L, int HG, int n_
     }
 }
 
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds_chunk, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_chunk, 16, voff,
-                                             0, 0, 0);
+// One 1 KiB buffer->LDS load: lane i's 16 bytes at byte offset voff of the buffer land at
+// lds_chunk + 16 i.  Asm statements, volatile, so they keep their order among themselves; the
+// last load of a group also carries a memory clobber (dma16), so no load the compiler issues
+// later in program order is moved in front of the group, and the slot waits (asm with a memory
+// clobber too) keep every load of the program order before them: the loads between a group
+// and a counted vmcnt wait are exactly those of the program order, which the decode kernels'
+// slot waits count.
+// last: the group's final load, which carries the memory clobber; the earlier ones of the group
+// (last = false) are ordered by it and by their own volatility.
+__device__ __forceinline__ void lds_dma16(const i32x4_sgpr& r, const unsigned char* lds_chunk, uint32_t voff,
+                                          bool last = true) {
+    const uint32_t a =
+        (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const unsigned char*)lds_chunk);
+    if (last) dma16(r, a, voff, 0u);
+    else dma16_nb(r, a, voff);
 }
 
 // The transposing LDS reads of one V block's operands (2 k-steps x DB row blocks x

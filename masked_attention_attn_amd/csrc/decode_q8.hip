@@ -162,12 +162,13 @@ void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc
         if (!live) return;
         if (icv.i == 0 || nv == 0) {     // the item's Q (also for a range that starts inside it)
             const int ncols = min(32, G - icv.hg * 32);
-            const __amdgpu_buffer_rsrc_t qrs =
-                brsrc(q + ((size_t)icv.b * H_q + icv.g * G + icv.hg * 32) * D, (uint32_t)(ncols * RB16));
+            const i32x4_sgpr qrs =
+                make_rsrc(q + ((size_t)icv.b * H_q + icv.g * G + icv.hg * 32) * D, (uint32_t)(ncols * RB16));
 #pragma unroll
             for (int ch = 0; ch < QCH; ++ch)
                 if (ch * 1024 < ncols * RB16)
-                    lds_dma16(qrs, qslot(qs_issue) + ch * 1024, (uint32_t)(ch * 1024 + lane * 16));
+                    lds_dma16(qrs, qslot(qs_issue) + ch * 1024, (uint32_t)(ch * 1024 + lane * 16),
+                              (ch + 1) * 1024 >= ncols * RB16);
         }
         ++nv;
         advance(icv, L, HG, n_hg);
@@ -246,13 +247,18 @@ void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc
             vaddr[db] = tb + (uint32_t)((vrow * D + (((db * 4 + vc0) ^ vfv) * 8) + vin) * 2);
     }
 
-    // The Q of an item is loaded into its LDS slot right after the V of the item's first
-    // block here (or of the wavefront's first block).  By the time that block is computed,
-    // at least (RV - 1) x NV V loads and (LK + 1) x KSTEPS K loads follow it (the fewest
-    // at the range's first block), so waiting for at most that many outstanding (capped at
-    // the counter's 63) makes the slot complete.  The compiler derives no wait for reading
-    // the slot after its buffer->LDS loads, so it is explicit.
-    constexpr int NQ = (RV - 1) * NV + (LK + 1) * KSTEPS < 63 ? (RV - 1) * NV + (LK + 1) * KSTEPS : 63;
+    // The Q slot wait.  Loop iteration i issues, in this program order: V of block
+    // i + RV - 1 (NV register loads, then the QCH buffer->LDS loads of the item's Q if that
+    // block starts an item), K of block i + LK (KSTEPS loads), then computes block i.  The Q
+    // loads are asm statements with a memory clobber and so is the wait: the compiler moves
+    // no load across them, and the count below is a property of this source.  Between an
+    // item's Q loads and the wait in front of its first block come at least the V loads of
+    // the RV - 1 blocks after it and the K loads of LK + 1 blocks (the fewest at the first
+    // block of a range): Q_LOADS_AFTER.  Loads return in issue order, so at most that many
+    // outstanding (capped at the counter's 63, which only waits longer) means Q has landed.
+    constexpr int Q_LOADS_AFTER = (RV - 1) * NV + (LK + 1) * KSTEPS;
+    static_assert(LK + 1 <= RV && NV == Gm::BLK / 1024 && KSTEPS == D / 16, "the counted geometry");
+    constexpr int NQ = Q_LOADS_AFTER < 63 ? Q_LOADS_AFTER : 63;
 
     auto compute = [&](int j, int s) {
         const int g = cc.g, hg = cc.hg;

@@ -69,6 +69,17 @@ __device__ __forceinline__ void dma16(i32x4_sgpr r, uint32_t lds_addr, uint32_t 
                  : "s"(m0), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
                  : "memory", "m0");
 }
+// dma16 without the compiler memory barrier: the asm statement stays in order with the other
+// asm statements (volatile), while the compiler may still move its own memory operations
+// across it.  A group of these loads closed by one dma16 keeps every later load behind the
+// whole group.
+__device__ __forceinline__ void dma16_nb(i32x4_sgpr r, uint32_t lds_addr, uint32_t voff) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(r)
+                 : "m0");
+}
 // Buffer descriptor for the compiler's buffer-load builtins: `bytes` from p are
 // addressable, offsets past them read as zero without touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* p, uint32_t bytes) {
