@@ -109,7 +109,11 @@ struct Lds {
     static constexpr int RBV = D * 2;             // bytes per V row (bf16 either way)
     static constexpr int K_TILE = TK * RBK;       // bytes
     static constexpr int V_TILE = TK * RBV;
-    static constexpr int K_RING = 3, V_RING = 2;
+    // bf16: tiles are loaded two tiles ahead (K one tile earlier still, for the operand reads
+    // one step ahead), so a ring of four K and three V tiles; E4M3 (V through registers): one
+    // tile ahead, three K and two V.
+    static constexpr int K_RING = FP8 ? 3 : 4, V_RING = FP8 ? 2 : 3;
+    static constexpr int AHEAD = FP8 ? 1 : 2;     // tiles a load is issued ahead of its first use
     static constexpr int BYTES = K_RING * K_TILE + V_RING * V_TILE;
 };
 
@@ -394,7 +398,7 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
     };
     u32x4 vraw = {};     // FP8: codes of the V tile two ahead of the current one
     int kcur = 0, vcur = 0;
-    static_assert(L::K_RING == 3 && L::V_RING == 2, "slot arithmetic below");
+    static_assert(L::K_RING == L::AHEAD + 2 && L::V_RING == L::AHEAD + 1, "slot arithmetic below");
     // Per-lane LDS offsets of the operand reads.
     //  K (A of K·Qᵀ): row hf*32 + l%32, chunk (kk*2 + hl) ^ k_swz(l % 32).
     const int kx = hl ^ k_swz<D>(l32);
@@ -569,7 +573,7 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
         // K rows of block u+2, read here for the next step: at D = 64 (two blocks
         // per tile) that block is in tile T+1, published since the end of tile
         // T-1; at D = 128 it is tile T+2, read after this step's tile-end barrier.
-        const int knext = kcur == 2 ? 0 : kcur + 1;
+        const int knext = kcur == L::K_RING - 1 ? 0 : kcur + 1;
         u32x4 va[DB], va1[DB];
         u32x4 pw[NB][PSTEPS];
         float cs[NB][PSTEPS];
@@ -732,27 +736,41 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
             }
         }
 
-        // ---- end of an LDS tile: publish the tiles loaded during this one, then
-        // start loading the next (K tile T+3 and V tile T+2 land by T+1's end).
+        // ---- end of an LDS tile: publish the tiles loaded during the previous one, then
+        // start loading the next batch.
+        //  bf16: K tile T+4 and V tile T+3 (into the slots tile T leaves), always issued (a
+        //  tile past the last reads zeros through the buffer range), so every batch is
+        //  CPW + CPWV loads and waiting for at most one batch outstanding means the batch
+        //  issued at the end of tile T-1 may still be in flight while the one from T-2
+        //  (K_{T+2}, V_{T+1}: read during tile T+1) has landed.  The loads are asm with a
+        //  memory clobber and so is the wait, so this count is a property of the source;
+        //  any loads the compiler adds after a batch (the hole flags) only make it stricter.
+        //  The look-ahead offsets of tiles past the last may exceed 32 bits and wrap; the
+        //  wrapped offset is still range-checked by the buffer load and the slot is never read.
+        //  E4M3: K tile T+3 and the V codes of T+3 (registers), one tile ahead, waiting for all.
+        //  The hole flags are ordinary loads the compiler waits for with a full count, so they
+        //  are gathered (and the next one issued) before the batch, not behind it.
         if (hf == HALVES - 1) {
-            wait_vmem();            // this wave's part of K_{T+2} and V_{T+1} has landed
-            __syncthreads();
-            if (T + 3 <= t_last) dma_k(T + 3, kcur);     // into the slot tile T leaves
-            if constexpr (FP8) {
-                if (T + 2 <= t_last) vstore(vraw, vcur);   // codes loaded during tile T-1
-                if (T + 3 <= t_last) vraw = vload(T + 3);
-            } else {
-                if (T + 2 <= t_last) dma_v(T + 2, vcur);
-            }
-            kcur = knext;
-            vcur ^= 1;
-            if constexpr (HALVES == 1 && !FP8) {    // K of block u+2 = tile T+2, just published
-#pragma unroll
-                for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = k_opnd(kblock(kcur == 2 ? 0 : kcur + 1, 0), kk);
-            }
+            if constexpr (FP8) wait_vmem();     // this wave's part of K_{T+2} and V_{T+1} has landed
+            else wait_vmem_le<CPW + CPWV>();    // all but the newest batch (K_{T+3}, V_{T+2})
             if (holes) {
                 pm_next = __ballot(padf_nxt) & TILE_BITS;
                 padf_nxt = pad_flag(min(T + 2, t_last));
+            }
+            __syncthreads();
+            if constexpr (FP8) {
+                if (T + 3 <= t_last) dma_k(T + 3, kcur);     // into the slot tile T leaves
+                if (T + 2 <= t_last) vstore(vraw, vcur);   // codes loaded during tile T-1
+                if (T + 3 <= t_last) vraw = vload(T + 3);
+            } else {
+                dma_k(T + 4, kcur);
+                dma_v(T + 3, vcur);
+            }
+            kcur = knext;
+            vcur = vcur == L::V_RING - 1 ? 0 : vcur + 1;
+            if constexpr (HALVES == 1 && !FP8) {    // K of block u+2 = tile T+2, just published
+#pragma unroll
+                for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = k_opnd(kblock(kcur == L::K_RING - 1 ? 0 : kcur + 1, 0), kk);
             }
         }
     };
@@ -780,9 +798,17 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
             if (t_first + 1 <= t_last) vstore(vraw1, 1);
         }
         __syncthreads();
-        if (t_first + 2 <= t_last) {     // waited for at the end of tile t_first
+        if constexpr (FP8) {
+            if (t_first + 2 <= t_last) {     // waited for at the end of tile t_first
+                dma_k(t_first + 2, 2);
+                vraw = vload(t_first + 2);
+            }
+        } else {
+            // the batch of "tile t_first - 1" (K_{t+3}, V_{t+2}) and K_{t+2}, all issued: the
+            // ring then holds K tiles t .. t+3 and V tiles t .. t+2
             dma_k(t_first + 2, 2);
-            if constexpr (FP8) vraw = vload(t_first + 2);
+            dma_k(t_first + 3, 3);
+            dma_v(t_first + 2, 2);
         }
         qk_full(sA);
         if constexpr (FP8) {
@@ -802,6 +828,8 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
         if (j < nsteps) step(j, 0, sA, sB);
     }
 
+    // the look-ahead batches (tiles past the last) land before the workgroup can end
+    wait_vmem();
     // ---- epilogue: O = acc / l, LSE = (m·c + log2 l)·ln 2
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
