@@ -68,6 +68,10 @@ def parse():
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run 3 plain device-to-device copies of MIB MiB (reference kernel "
                         "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    p.add_argument("--api-calls", type=int, default=0, metavar="N",
+                   help="only call every entry point of the step (and the allocation-free decode) N "
+                        "times on preallocated buffers, between two device synchronisations, and "
+                        "exit: the window a HIP runtime trace inspects for allocations and syncs")
     return p.parse_args()
 
 
@@ -202,18 +206,39 @@ def make_flush(torch, dev):
     return flush
 
 
-def smi_clocks():
-    """Current clock levels as rocm-smi reports them (card 0), or None."""
-    import subprocess
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        data = json.loads(r.stdout)
-    except Exception:
+def smi_clocks(props=None):
+    """Current sclk / mclk levels (the lines marked current in the amdgpu driver's pp_dpm_sclk and
+    pp_dpm_mclk files) of the card whose PCI bus matches the device, else of the only AMD card
+    listed; None where sysfs does not show them.  Read from sysfs, no child process: under a
+    profiler that preloads itself into every process, a started tool would initialise the GPU."""
+    import glob
+    bus = getattr(props, "pci_bus_id", None)
+    cards = []
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            with open(os.path.join(dev, "vendor")) as f:
+                if f.read().strip() != "0x1002":
+                    continue
+        except OSError:
+            continue
+        addr = os.path.basename(os.path.realpath(dev))      # e.g. 0000:75:00.0
+        if dev not in cards:
+            cards.append((dev, addr))
+    if bus is not None:
+        match = [c for c in cards if int(c[1].split(":")[1], 16) == int(bus)]
+    else:
+        match = cards if len(cards) == 1 else []
+    if not match:
         return None
-    card = next((v for k, v in data.items() if k.startswith("card")), None)
-    if not isinstance(card, dict):
-        return None
-    return {k: v for k, v in card.items() if "clock" in k.lower() or "clk" in k.lower()}
+    out = {"pci": match[0][1]}
+    for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+        try:
+            with open(os.path.join(match[0][0], name)) as f:
+                cur = [ln.strip() for ln in f if ln.strip().endswith("*")]
+            out[name] = cur[0] if cur else None
+        except OSError:
+            out[name] = None
+    return out
 
 
 def gpu_info(torch, dev, busy_step):
@@ -224,7 +249,7 @@ def gpu_info(torch, dev, busy_step):
             "total_memory_bytes": int(p.total_memory)}
     for _ in range(200):       # ~0.4 s of queued work
         busy_step()
-    info["clocks_under_load"] = smi_clocks()
+    info["clocks_under_load"] = smi_clocks(p)
     torch.cuda.synchronize()
     return info
 
@@ -492,6 +517,27 @@ def main():
 
     stream = torch.cuda.current_stream()
     n_ev = 6
+
+    if args.api_calls:
+        # Warm-up (the library's one-time set-up: kernel attributes, occupancy query, the
+        # static scratch's address), then the window: nothing but entry-point calls on
+        # buffers allocated above, between two device synchronisations.
+        def calls():
+            ma.attn_fwd_lse(q3, k3, v3, m3, pf.scale, out=o3, lse=l3)
+            for i in range(2):
+                ma.attn_fwd_lse(q4, k4[i], v4[i], None, ch.scale, out=o4[i], lse=l4[i])
+            ma.attn_merge_lse(o4, l4, out=om4, lse_out=lm4)
+            ma.kv_append(kc, vc, lens, kn, vn)
+            ma.attn_decode(q5, kc, vc, lens, dc.scale, out=o5, lse=l5, workspace=ws, want_lse=True)
+            ma.attn_decode_noalloc(q5, kc, vc, lens, o5, l5, scale=dc.scale)
+        calls()
+        torch.cuda.synchronize()
+        for _ in range(args.api_calls):
+            calls()
+        torch.cuda.synchronize()
+        print(json.dumps({"api_call_window": {"iterations": args.api_calls,
+                                              "entry_points_per_iteration": 7}}))
+        return
 
     def step(ev=None):
         lens.copy_(lens0)
