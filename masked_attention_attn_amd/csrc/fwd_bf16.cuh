@@ -90,10 +90,13 @@ constexpr int CK = 32;          // keys per compute step
 // four waves of 64 queries (the K operand of a key block serves two query
 // blocks).  D = 128: eight waves of 32 queries, which keeps a wave's live
 // state (output 4x16, scores 2x16, Q 8x4, operands) within the 256 VGPRs of
-// two waves per SIMD; a workgroup covers 256 queries either way.
+// two waves per SIMD; a workgroup covers 256 queries either way.  WG_PER_CU is
+// the launch bound's resident workgroups per CU: two at D = 64 make the compiler
+// fit a wave in 256 registers (two waves per SIMD) instead of spreading it over
+// 304 with accumulation registers (one wave per SIMD).
 template <int D> struct Cfg;
-template <> struct Cfg<64> { static constexpr int NWAVE = 4, NB = 2; };
-template <> struct Cfg<128> { static constexpr int NWAVE = 8, NB = 1; };
+template <> struct Cfg<64> { static constexpr int NWAVE = 4, NB = 2, WG_PER_CU = 2; };
+template <> struct Cfg<128> { static constexpr int NWAVE = 8, NB = 1, WG_PER_CU = 1; };
 template <int D> constexpr int kBM = Cfg<D>::NWAVE * Cfg<D>::NB * 32;   // queries per workgroup
 constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
 constexpr float kRescaleSum = 256.0f;   // 2^TAU: a lane's chunk sum above this forces a rescale
@@ -140,7 +143,7 @@ __device__ __forceinline__ f32x16 mfma_e4m3(i32x8 a, i32x8 b, f32x16 acc) {
 // the key blocks that cross a wave's diagonal, and q-tiles run last-first
 // (the longest first, for the balance of the grid).
 template <int D, bool WRITE_LSE, bool VARLEN, bool CAUSAL, bool FP8>
-__global__ __launch_bounds__(64 * Cfg<D>::NWAVE, 1)
+__global__ __launch_bounds__(64 * Cfg<D>::NWAVE, Cfg<D>::WG_PER_CU)
 void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restrict__ k,
                      const Elem<FP8>* __restrict__ v, const uint8_t* __restrict__ mask,
                      bf16* __restrict__ o, float* __restrict__ lse,
