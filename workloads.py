@@ -156,6 +156,18 @@ def _randn(g, shape, amp, dtype):
     return x.to(dtype).contiguous()
 
 
+def randn_device(shape, seed: int, device, dtype=torch.bfloat16, amp=1.0) -> torch.Tensor:
+    """Seeded N(0, amp^2) values drawn on `device` in float32, then cast (round to nearest even),
+    for inputs of billions of elements that the host would take minutes to draw.  The same
+    tensor serves both sides: the caller copies it to the host for the oracle."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    if amp != 1.0:
+        x.mul_(amp)
+    return x.to(dtype)
+
+
 def _uniform_scales(seed: int, shape, lo=0.01, hi=2.0) -> torch.Tensor:
     """Float32 scale factors U[lo, hi) from a generator of their own (seed + 7919), so that
     asking for them leaves every other draw of a workload unchanged.  Unlike powers of two,
