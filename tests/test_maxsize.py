@@ -3,9 +3,10 @@
 The bf16 prefill addresses one (b, KV head)'s K and V through a 32-bit buffer range and the
 boundary accepts Tk·D·2 bytes up to 2^31 - 1; the decode kernels do the same for one
 (sequence, KV head) of the cache (T_max·D·2 bytes for bf16, T_max·D for the 8-bit caches).
-At those sizes the kernels' per-lane tile offsets, look-ahead included, pass 2^31, the last
-blocks sit at the very end of the range, and a sequence of the decode is cut into ~8,200
-(bf16) or ~16,400 (E4M3) splits whose parts the combine merges over hundreds of rounds.
+The packed calls accept total_k·H_kv·D elements up to 2^30 - 1, with a sequence's rows strided
+by H_kv·D.  At those sizes the kernels' per-lane tile offsets, look-ahead included, pass 2^31,
+the last blocks sit at the very end of the range, and a sequence of the decode is cut into
+~8,200 (bf16) or ~16,400 (E4M3) splits whose parts the combine merges over hundreds of rounds.
 
 Inputs are seeded normal draws made on the GPU by the workload module (billions of values);
 the same tensors are copied to the host for the oracle.  Every output row of the prefill and
@@ -104,3 +105,46 @@ def test_fp8_decode_largest_cache(ma):
     o, l = o.cpu(), l.cpu()
     check_attn(torch.stack([o[b, h, 0] for b, h in heads]), torch.stack([l[b, h] for b, h in heads]),
                Or, Lr, torch.bfloat16, f"E4M3 decode T_max={T_max} D={D}, heads {heads}")
+
+
+def test_varlen_gqa_largest_packed_keys(ma):
+    # packed K/V of total_k * H_kv * D elements, the largest the packed calls accept
+    Hq, Hkv = 16, 8
+    total_k = (2**30 - 1) // (Hkv * D)          # 1,048,575 rows of 8 KV heads
+    lens_k = [total_k // 2, total_k - total_k // 2]
+    lens_q = [24, 17]
+    cu_q, cu_k = W.cu_from_lengths(lens_q), W.cu_from_lengths(lens_k)
+    q = W.randn_device((sum(lens_q), Hq, D), 401, DEV)
+    k = W.randn_device((total_k, Hkv, D), 402, DEV)
+    v = W.randn_device((total_k, Hkv, D), 403, DEV)
+    scale = 1.0 / np.sqrt(D)
+    o, l = ma.attn_prefill_varlen(q, k, v, cu_q.to(DEV), cu_k.to(DEV), max(lens_q), True, scale)
+    torch.cuda.synchronize()
+    o, l = o.cpu(), l.cpu()
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    del q, k, v
+    torch.cuda.empty_cache()
+    Or, Lr = oracle.prefill_varlen(qc, kc, vc, cu_q, cu_k, True, scale)
+    check_attn(o, l, Or, Lr, torch.bfloat16, f"packed causal GQA prefill, total_k={total_k}")
+
+
+def test_fp8_prefill_largest_key_range(ma):
+    Hq, Hkv, Tq, Tk = 2, 1, 24, T_MAX_8BIT
+    q = W.randn_device((1, Hq, Tq, D), 501, DEV, torch.float8_e4m3fn).view(torch.uint8)
+    k = W.randn_device((1, Hkv, Tk, D), 502, DEV, torch.float8_e4m3fn).view(torch.uint8)
+    v = W.randn_device((1, Hkv, Tk, D), 503, DEV, torch.float8_e4m3fn).view(torch.uint8)
+    qs = torch.tensor([[0.5, 0.25]], dtype=torch.float32)
+    ks = torch.tensor([[0.375]], dtype=torch.float32)
+    vs = torch.tensor([[1.25]], dtype=torch.float32)
+    mask = torch.zeros((1, Tk), dtype=torch.uint8)
+    mask[0, :64] = 1
+    mask[0, Tk - 100:] = 1
+    scale = 1.0 / np.sqrt(D)
+    o, l = ma.attn_prefill_fp8(q, k, v, qs.to(DEV), ks.to(DEV), vs.to(DEV), mask.to(DEV), False, scale)
+    torch.cuda.synchronize()
+    o, l = o.cpu(), l.cpu()
+    qc, kc, vc = q.cpu().numpy(), k.cpu().numpy(), v.cpu().numpy()
+    del q, k, v
+    torch.cuda.empty_cache()
+    Or, Lr = oracle.prefill_fp8(qc, kc, vc, qs, ks, vs, mask, False, scale)
+    check_attn(o, l, Or, Lr, torch.bfloat16, f"E4M3 prefill Tk={Tk} D={D}")
