@@ -42,10 +42,11 @@
 // issue order is fixed slot by slot, turns S_u into P_u while issuing the
 // matrix-core work S_{u+1} = K_{u+1}·Qᵀ and O += V_uᵀ·P_u: the exp / convert
 // / sum vector work of one block overlaps the MFMAs of two.  The K operands
-// of S_{u+1} are read from LDS during step u-1.  K tiles live in a ring of
-// three LDS buffers (tile T+1 is readable during tile T while tile T+2 is
-// being stored), V tiles in a ring of two; the buffer resources' range check
-// returns zeros past Tk, so no lane branches.
+// of S_{u+1} are read from LDS during step u-1.  bf16: K tiles live in a ring
+// of four LDS buffers and V tiles in a ring of three, loaded two tiles ahead
+// (tile T+1 is readable during tile T while tiles T+2 and T+3 are being
+// stored); E4M3: three K buffers of codes and two V buffers, one tile ahead.
+// The buffer resources' range check returns zeros past Tk, so no lane branches.
 // Padding (a rare, workgroup-uniform case) is applied before the fixed block,
 // so the common path has no per-element masking.  One pass over the mask
 // finds the sequence's first and last unpadded keys and whether any padded
