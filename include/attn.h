@@ -13,6 +13,10 @@
  *     operands of one call share it, except LSE arrays, which are always
  *     float32, the mask (uint8) and cache lengths (int32).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every kernel of a call goes to that stream, so calls may be captured into
+ *     a HIP graph.  The first call of an entry point on a device does one-time
+ *     set-up (kernel attributes, an occupancy query, the static scratch's
+ *     address); make that first call outside a capture.
  *   - Head dimension D must be 64 or 128.
  *   - No output may share a byte with an input or with another output (byte
  *     ranges from the stated shapes; in-place use is refused, ATTN_ERR_ALIAS).
