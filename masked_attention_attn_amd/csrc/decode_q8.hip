@@ -32,10 +32,16 @@ template <int D, bool INT8> struct Geo8 {
     static constexpr int RB = D;                   // bytes per cache row (one byte per element)
     static constexpr int BLK = CK * RB;            // bytes of one K (or V) block
     static constexpr int NV = BLK / 1024;          // 1 KiB V loads per block (16 bytes per lane)
-    // V register ring (look-ahead RV - 1 blocks); the INT8 conversion needs more temporaries,
-    // and at D = 128 a ring of 7 keeps the excess in accumulation registers (8 spills to memory)
-    static constexpr int RV = (INT8 && D == 128) ? 7 : 8;
-    static constexpr int LK = 4;                   // K look-ahead in blocks
+    // V register ring (look-ahead RV - 1 blocks) and K look-ahead in blocks.  E4M3 at D = 128:
+    // rings of 3 and 2 blocks, so a wave fits 256 registers and two waves share a SIMD (one
+    // hides the other's conversion and softmax work; the bytes in flight per SIMD stay about
+    // those of one deep-ring wave).  INT8 at D = 128: its conversion needs more temporaries,
+    // which the small rings would spill, so one wave per SIMD with rings of 7 and 4 (8 would
+    // push the excess past the accumulation registers into memory).  D = 64: rings of 8 and 4.
+    static constexpr bool TWO_WAVES = D == 128 && !INT8;
+    static constexpr int RV = D == 128 ? (INT8 ? 7 : 3) : 8;
+    static constexpr int LK = TWO_WAVES ? 2 : 4;
+    static constexpr int WAVES_MIN = TWO_WAVES ? 2 : 1, WAVES_MAX = D == 128 ? WAVES_MIN : 8;
     static constexpr int QCH = 32 * D * 2 / 1024;  // 1 KiB loads of a full 32-head bf16 Q slot
 };
 
@@ -44,14 +50,18 @@ __device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff)
 }
 
 
-// At D = 128 the K and V register rings alone fill 256 registers: one wavefront per SIMD,
-// with the accumulation registers as well (no spills).
+// At D = 128 the INT8 instance's K and V register rings alone fill 256 registers: one
+// wavefront per SIMD, with the accumulation registers as well (no spills).  The E4M3 instance's
+// smaller rings fit 256 registers in all, for two wavefronts per SIMD (the contiguous one
+// keeps two 8-byte values in scratch memory, stored before the block loop and reloaded twice
+// per block in it; measured faster than one wavefront per SIMD all the same).
 // PAGED: kc / vc are page pools [num_pages, H_kv, 2^lps, D] of codes; token t of sequence b is
 // row t mod 2^lps of page bt[b * max_pages + (t >> lps)] (entries clamped to [0, num_pages)),
 // T_max = max_pages << lps.  V of a 32-token block is loaded as two 16-token halves, each
 // through the buffer range of its page; K by per-lane global loads from the page of each key.
 template <int D, bool INT8, bool PAGED>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, D == 128 ? 1 : 8)))
+__global__ __launch_bounds__(64)
+__attribute__((amdgpu_waves_per_eu(Geo8<D, INT8>::WAVES_MIN, Geo8<D, INT8>::WAVES_MAX)))
 void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc,
                        const uint8_t* __restrict__ vc, const float* __restrict__ kscale,
                        const float* __restrict__ vscale, const int32_t* __restrict__ lens,
