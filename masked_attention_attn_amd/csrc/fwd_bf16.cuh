@@ -683,6 +683,9 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
         };
 
         if constexpr (D == 64) {
+            // unfenced (bf16): the compiler's small-GEMM interleave of LDS reads and MFMAs
+            // measured ~0.6% faster than its default order at P = 11,616
+            if constexpr (!FP8) __builtin_amdgcn_iglp_opt(0);
             // 22 slots: 0-7 QK(u+1), 10-13 PV(u,0) (chunk 0 packed by slot 9),
             // 18-21 PV(u,1) (chunk 1 packed by slot 17); softmax in 0-17.  FP8: QK(u+1)
             // is two E4M3 MFMAs, in slots 0 and 2.
