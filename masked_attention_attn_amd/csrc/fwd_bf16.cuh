@@ -373,7 +373,6 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
     };
     auto vslot_b = [&](int sl) -> unsigned char* { return smem_raw + L::K_RING * L::K_TILE + sl * L::V_TILE; };
     auto kslot = [&](int sl) -> const bf16* { return reinterpret_cast<const bf16*>(kslot_b(sl)); };
-    auto vslot = [&](int sl) -> const bf16* { return reinterpret_cast<const bf16*>(vslot_b(sl)); };
     auto dma_k = [&](int t, int sl) {
 #pragma unroll
         for (int i = 0; i < CPW; ++i)
@@ -414,6 +413,11 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
     const int vc0 = 2 * (vg & 1) + ((vm & 3) >> 1);
     const int vin = (vm & 1) * 4;                    // element offset inside the 16-byte chunk
     auto v_off = [&](int db) { return vrow * D + (((db * 4 + vc0) ^ vfv) * 8) + vin; };
+    // LDS byte address of this lane's row block db in the current V slot, moved on with the
+    // slot at each tile end, so the reads of a step take their row offsets as immediates
+    uint32_t vaddr[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) vaddr[db] = vslot_a(0) + (uint32_t)(v_off(db) * 2);
 
     // Lane j reports whether key t*TK + j is padded or past Tk (lanes >= TK report 1).
     auto pad_flag = [&](int t) -> int {
@@ -499,9 +503,9 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
     int padf_nxt = 0;
     // Vᵀ operand (8 keys x one d per lane) of k-step k2 of half hf of the current V tile
     auto v_opnd = [&](int hf, int k2, int db) -> u32x4 {
-        const bf16* base = vslot(vcur) + (hf * 32 + k2 * 16) * D + v_off(db);
-        const u32x2 lo = ds_read_tr(base);
-        const u32x2 hi = ds_read_tr(base + 4 * D);
+        const uint32_t a = vaddr[db] + (uint32_t)((hf * 32 + k2 * 16) * D * 2);
+        const u32x2 lo = ds_read_tr_at(a);
+        const u32x2 hi = ds_read_tr_at(a + 4 * D * 2);
         return u32x4{lo[0], lo[1], hi[0], hi[1]};
     };
 
@@ -778,7 +782,11 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
                 dma_v(T + 3, vcur);
             }
             kcur = knext;
-            vcur = vcur == L::V_RING - 1 ? 0 : vcur + 1;
+            const bool vwrap = vcur == L::V_RING - 1;
+            vcur = vwrap ? 0 : vcur + 1;
+            const uint32_t vstep = vwrap ? (uint32_t)(-(L::V_RING - 1) * L::V_TILE) : (uint32_t)L::V_TILE;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) vaddr[db] += vstep;
             if constexpr (HALVES == 1 && !FP8) {    // K of block u+2 = tile T+2, just published
 #pragma unroll
                 for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = k_opnd(kblock(kcur == L::K_RING - 1 ? 0 : kcur + 1, 0), kk);

@@ -127,6 +127,13 @@ __device__ __forceinline__ u32x2 ds_read_tr(const bf16* p) {
     return __builtin_bit_cast(u32x2, r);
 }
 
+// The same read at LDS byte address a.
+__device__ __forceinline__ u32x2 ds_read_tr_at(uint32_t a) {
+    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf;
+    const v4bf r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) v4bf*)(uintptr_t)a);
+    return __builtin_bit_cast(u32x2, r);
+}
+
 // Wait until at most N of this wave's global loads (including LDS-direct ones)
 // are outstanding; also a compiler barrier for memory operations, so no LDS
 // read of the landed data is moved above it.
