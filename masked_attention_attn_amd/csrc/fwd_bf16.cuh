@@ -43,8 +43,8 @@
 // matrix-core work S_{u+1} = K_{u+1}·Qᵀ and O += V_uᵀ·P_u: the exp / convert
 // / sum vector work of one block overlaps the MFMAs of two.  The K operands
 // of S_{u+1} are read from LDS during step u-1.  bf16: K tiles live in a ring
-// of four LDS buffers and V tiles in a ring of three, loaded two tiles ahead
-// (tile T+1 is readable during tile T while tiles T+2 and T+3 are being
+// of five LDS buffers and V tiles in a ring of four, loaded three tiles ahead
+// (tile T+1 is readable during tile T while tiles T+2 .. T+4 are being
 // stored); E4M3: three K buffers of codes and two V buffers, one tile ahead.
 // The buffer resources' range check returns zeros past Tk, so no lane branches.
 // Padding (a rare, workgroup-uniform case) is applied before the fixed block,
@@ -113,11 +113,11 @@ struct Lds {
     static constexpr int RBV = D * 2;             // bytes per V row (bf16 either way)
     static constexpr int K_TILE = TK * RBK;       // bytes
     static constexpr int V_TILE = TK * RBV;
-    // bf16: tiles are loaded two tiles ahead (K one tile earlier still, for the operand reads
-    // one step ahead), so a ring of four K and three V tiles; E4M3 (V through registers): one
-    // tile ahead, three K and two V.
-    static constexpr int K_RING = FP8 ? 3 : 4, V_RING = FP8 ? 2 : 3;
-    static constexpr int AHEAD = FP8 ? 1 : 2;     // tiles a load is issued ahead of its first use
+    // bf16: tiles are loaded three tiles ahead (K one tile earlier still, for the operand reads
+    // one step ahead), so a ring of five K and four V tiles (72 KiB at D = 64, two workgroups
+    // per CU; 144 KiB at D = 128); E4M3 (V through registers): one tile ahead, three K and two V.
+    static constexpr int AHEAD = FP8 ? 1 : 3;     // tiles a load is issued ahead of its first use
+    static constexpr int K_RING = AHEAD + 2, V_RING = AHEAD + 1;
     static constexpr int BYTES = K_RING * K_TILE + V_RING * V_TILE;
 };
 
@@ -753,11 +753,11 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
 
         // ---- end of an LDS tile: publish the tiles loaded during the previous one, then
         // start loading the next batch.
-        //  bf16: K tile T+4 and V tile T+3 (into the slots tile T leaves), always issued (a
+        //  bf16: K tile T+5 and V tile T+4 (into the slots tile T leaves), always issued (a
         //  tile past the last reads zeros through the buffer range), so every batch is
-        //  CPW + CPWV loads and waiting for at most one batch outstanding means the batch
-        //  issued at the end of tile T-1 may still be in flight while the one from T-2
-        //  (K_{T+2}, V_{T+1}: read during tile T+1) has landed.  The loads are asm with a
+        //  CPW + CPWV loads and waiting for at most two batches outstanding means the batches
+        //  issued at the ends of tiles T-1 and T-2 may still be in flight while the one from
+        //  T-3 (K_{T+2}, V_{T+1}: read during tile T+1) has landed.  The loads are asm with a
         //  memory clobber and so is the wait, so this count is a property of the source;
         //  any loads the compiler adds after a batch (the hole flags) only make it stricter.
         //  The look-ahead offsets of tiles past the last may exceed 32 bits and wrap; the
@@ -767,7 +767,7 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
         //  are gathered (and the next one issued) before the batch, not behind it.
         if (hf == HALVES - 1) {
             if constexpr (FP8) wait_vmem();     // this wave's part of K_{T+2} and V_{T+1} has landed
-            else wait_vmem_le<CPW + CPWV>();    // all but the newest batch (K_{T+3}, V_{T+2})
+            else wait_vmem_le<(L::AHEAD - 1) * (CPW + CPWV)>();    // all but the two newest batches
             if (holes) {
                 pm_next = __ballot(padf_nxt) & TILE_BITS;
                 padf_nxt = pad_flag(min(T + 2, t_last));
@@ -778,8 +778,8 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
                 if (T + 2 <= t_last) vstore(vraw, vcur);   // codes loaded during tile T-1
                 if (T + 3 <= t_last) vraw = vload(T + 3);
             } else {
-                dma_k(T + 4, kcur);
-                dma_v(T + 3, vcur);
+                dma_k(T + L::AHEAD + 2, kcur);
+                dma_v(T + L::AHEAD + 1, vcur);
             }
             kcur = knext;
             const bool vwrap = vcur == L::V_RING - 1;
@@ -823,11 +823,14 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
                 vraw = vload(t_first + 2);
             }
         } else {
-            // the batch of "tile t_first - 1" (K_{t+3}, V_{t+2}) and K_{t+2}, all issued: the
-            // ring then holds K tiles t .. t+3 and V tiles t .. t+2
+            // K_{t+2}, then the batches of "tiles t_first - 2 and t_first - 1" (K_{t+3}, V_{t+2};
+            // K_{t+4}, V_{t+3}), in this order: the ring then holds K tiles t .. t+4 and V tiles
+            // t .. t+3, and the first tile end's wait (two batches outstanding) covers K_{t+2}
             dma_k(t_first + 2, 2);
             dma_k(t_first + 3, 3);
             dma_v(t_first + 2, 2);
+            dma_k(t_first + 4, 4);
+            dma_v(t_first + 3, 3);
         }
         qk_full(sA);
         if constexpr (FP8) {
