@@ -146,6 +146,30 @@ def test_fwd_fully_padded_sequence(ma, dtype):
 
 
 @pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("holes", [False, True])
+def test_fwd_visited_tile_counts(ma, D, holes):
+    """The bf16 kernels keep K and V tiles of 64 keys in LDS rings filled several tiles ahead;
+    the prologue and every tile end issue loads for tiles past the last visited one.  Visited
+    ranges of 1 to 7 tiles, starting at tile 0, 1 or 2 and ending on, just past or inside a
+    tile edge, with and without padded keys between the first and last unpadded ones."""
+    g = torch.Generator().manual_seed(D + holes)
+    for t0 in (0, 1, 2):
+        for n in range(1, 8):
+            for tail in (0, 1, 37):
+                first = 64 * t0 + (5 if t0 else 0)
+                last = max(first, 64 * (t0 + n - 1) + (63 if tail == 0 else tail - 1))
+                Tk = last + 1 + int(torch.randint(0, 3, (1,), generator=g))
+                m = torch.ones(1, Tk, dtype=torch.uint8)
+                m[0, first:last + 1] = 0
+                if holes and last - first > 4:
+                    m[0, first + 1:last:3] = 1
+                w = W.make_prefill(1, 2, 40, Tk, D, torch.bfloat16, mask=m, seed=1000 * t0 + 10 * n + tail)
+                o, l = run_fwd(ma, w)
+                Or, Lr = oracle.attention(w.q, w.k, w.v, w.mask, w.scale)
+                check_attn(o, l, Or, Lr, torch.bfloat16, f"D={D} keys [{first}, {last}] of {Tk} holes={holes}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("amp", [4.0, 8.0])
 def test_fwd_peaky_scores(ma, amp, D):
     """Large scores (Q, K, V ~ N(0, amp^2)): the reference rises often, exercising the lazy
