@@ -21,7 +21,10 @@
 // buffer->LDS loads into a ring of four slots three blocks ahead (each slot
 // its own LDS array), and each item's Q into an LDS slot with the V of its
 // first block.  The loads are compiler builtins, so the compiler derives the
-// waits for K and Q; only the V slot reads carry an explicit wait.  Buffer
+// waits for K and Q; only the V slot reads carry an explicit wait.  V arrives in
+// 1 KiB loads of whole cache lines, each line read once, so it uses the
+// non-temporal cache policy; the K operand loads read each line over four k-step
+// loads and keep the default.  Buffer
 // ranges end at the item's last token, so look-ahead past it reads zeros
 // without touching memory.  Softmax per head column: weights 2^(S·c - mc),
 // mc from the exact max of the item's first block here, raised only when a
@@ -161,13 +164,13 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
             if (live) page_halves(icv, nullptr, vh, roff);
 #pragma unroll
             for (int ch = 0; ch < NCH; ++ch)
-                lds_dma16(vh[ch / HCH], dst + ch * 1024, roff[ch / HCH] + v_voff[ch] - (ch / HCH) * 16u * RB,
+                lds_dma16<true>(vh[ch / HCH], dst + ch * 1024, roff[ch / HCH] + v_voff[ch] - (ch / HCH) * 16u * RB,
                           ch == NCH - 1);
         } else {
             const uint32_t row0 = (uint32_t)(icv.s * kDecodeSplit + icv.i * CK) * RB;
             const i32x4_sgpr r = live ? vrs : z4;
 #pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) lds_dma16(r, dst + ch * 1024, row0 + v_voff[ch], ch == NCH - 1);
+            for (int ch = 0; ch < NCH; ++ch) lds_dma16<true>(r, dst + ch * 1024, row0 + v_voff[ch], ch == NCH - 1);
         }
         if (!live) return;
         if (icv.i == 0 || nv == 0) {     // the item's Q (also for a range that starts inside it)

@@ -211,13 +211,20 @@ __device__ __forceinline__ void advance(Cursor& c, const Lens& L, int HG, int n_
 // and a counted vmcnt wait are exactly those of the program order, which the decode kernels'
 // slot waits count.
 // last: the group's final load, which carries the memory clobber; the earlier ones of the group
-// (last = false) are ordered by it and by their own volatility.
+// (last = false) are ordered by it and by their own volatility.  NT: the streaming cache policy
+// (the KV cache, read once per call); Q slots keep the default.
+template <bool NT = false>
 __device__ __forceinline__ void lds_dma16(const i32x4_sgpr& r, const unsigned char* lds_chunk, uint32_t voff,
                                           bool last = true) {
     const uint32_t a =
         (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const unsigned char*)lds_chunk);
-    if (last) dma16(r, a, voff, 0u);
-    else dma16_nb(r, a, voff);
+    if constexpr (NT) {
+        if (last) dma16_nt(r, a, voff);
+        else dma16_nb_nt(r, a, voff);
+    } else {
+        if (last) dma16(r, a, voff, 0u);
+        else dma16_nb(r, a, voff);
+    }
 }
 
 // The transposing LDS reads of one V block's operands (2 k-steps x DB row blocks x

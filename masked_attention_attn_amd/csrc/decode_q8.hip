@@ -22,7 +22,9 @@
 // blocks ahead.  At its block, V is converted and written to a bf16 LDS tile in
 // the bf16 kernel's swizzled layout and read back with the transposing LDS
 // read.  Every global load is a compiler builtin, so the compiler derives the
-// waits; each item's Q (bf16) reaches an LDS slot by buffer->LDS loads.
+// waits; each item's Q (bf16) reaches an LDS slot by buffer->LDS loads.  V rows
+// (whole lines, read once) use the non-temporal cache policy; the K operand loads,
+// which read each line over several k-steps, keep the default.
 #include "decode_common.cuh"
 
 namespace mattn {
@@ -163,11 +165,11 @@ void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc
             if (live) page_halves(icv, vh, roff);
 #pragma unroll
             for (int i = 0; i < NV; ++i)
-                vr[s][i] = bload16(vh[i / HNV], roff[i / HNV] + v_off[i] - (uint32_t)(i / HNV) * 16u * RB);
+                vr[s][i] = bload16_nt(vh[i / HNV], roff[i / HNV] + v_off[i] - (uint32_t)(i / HNV) * 16u * RB);
         } else {
             const uint32_t row0 = (uint32_t)(icv.s * kDecodeSplit + icv.i * CK) * RB;
 #pragma unroll
-            for (int i = 0; i < NV; ++i) vr[s][i] = bload16(live ? vrs : zrs, row0 + v_off[i]);
+            for (int i = 0; i < NV; ++i) vr[s][i] = bload16_nt(live ? vrs : zrs, row0 + v_off[i]);
         }
         if (!live) return;
         if (icv.i == 0 || nv == 0) {     // the item's Q (also for a range that starts inside it)
