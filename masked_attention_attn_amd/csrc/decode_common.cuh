@@ -293,31 +293,39 @@ void decode_stream_combine(const float* __restrict__ ws_o, const float* __restri
     const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (bh >= n_bh) return;
     const int b = bh / H_q;
-    const int len = seq_len(lens, b, T_max);
-    const int np = (len + kDecodeSplit - 1) / kDecodeSplit * 2;    // (split, part) slots
     const size_t base = (size_t)bh * nsplit * 2;
     const float* orow_ws = ws_o + base * D + lane * E;
+    // The first round's loads do not wait for the length: slots 0 .. min(PG, 2·nsplit) - 1 are
+    // this (b, head)'s own, so they are loaded together with it and the slots past the
+    // sequence's parts are masked once it has arrived (a slot never written is loaded, not used).
+    const int cap0 = min(PG, 2 * nsplit);
+    float m0 = kNegInf, l0 = 0.f, ov0[PG][E];
+    if (lane < cap0) {
+        m0 = ws_ml[(base + lane) * 2];
+        l0 = ws_ml[(base + lane) * 2 + 1];
+    }
+#pragma unroll
+    for (int i = 0; i < PG; ++i)
+#pragma unroll
+        for (int e = 0; e < E; ++e) ov0[i][e] = i < cap0 ? orow_ws[(size_t)i * D + e] : 0.f;
+    const int len = seq_len(lens, b, T_max);
+    const int np = (len + kDecodeSplit - 1) / kDecodeSplit * 2;    // (split, part) slots
     float M = kNegInf, lsum = 0.f;
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    for (int k0 = 0; k0 < np; k0 += PG) {
-        // one round: (m, l) of parts k0 .. k0+PG-1 in lanes 0..PG-1, and their O elements
-        const int k = k0 + lane;
-        const bool mine = lane < PG && k < np;
-        const float m = mine ? ws_ml[(base + k) * 2] : kNegInf;
-        const float l = mine ? ws_ml[(base + k) * 2 + 1] : 0.f;
-        float ov[PG][E];
-#pragma unroll
-        for (int i = 0; i < PG; ++i)
-#pragma unroll
-            for (int e = 0; e < E; ++e) ov[i][e] = k0 + i < np ? orow_ws[(size_t)(k0 + i) * D + e] : 0.f;
+    // merge parts k0 .. k0+PG-1: (m, l) of part k0 + lane in lanes 0..PG-1, ov[i] = O elements of part k0 + i
+    auto merge_round = [&](int k0, float m, float l, const float (&ov)[PG][E]) {
+        if (!(lane < PG && k0 + lane < np)) {
+            m = kNegInf;
+            l = 0.f;
+        }
         float mg = m;
 #pragma unroll
         for (int sh = 8; sh >= 1; sh >>= 1) mg = fmaxf(mg, __shfl_xor(mg, sh));
         mg = __shfl(mg, 0);
         const float Mn = fmaxf(M, mg);
-        if (Mn == kNegInf) continue;             // nothing present yet
+        if (Mn == kNegInf) return;               // nothing present yet
         const float alpha = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
         M = Mn;
 #pragma unroll
@@ -334,6 +342,19 @@ void decode_stream_combine(const float* __restrict__ ws_o, const float* __restri
 #pragma unroll
             for (int e = 0; e < E; ++e) acc[e] = wi != 0.f ? __builtin_fmaf(ov[i][e], wi, acc[e]) : acc[e];
         }
+    };
+    if (np > 0) merge_round(0, m0, l0, ov0);
+    for (int k0 = PG; k0 < np; k0 += PG) {
+        const int k = k0 + lane;
+        const bool mine = lane < PG && k < np;
+        const float m = mine ? ws_ml[(base + k) * 2] : kNegInf;
+        const float l = mine ? ws_ml[(base + k) * 2 + 1] : 0.f;
+        float ov[PG][E];
+#pragma unroll
+        for (int i = 0; i < PG; ++i)
+#pragma unroll
+            for (int e = 0; e < E; ++e) ov[i][e] = k0 + i < np ? orow_ws[(size_t)(k0 + i) * D + e] : 0.f;
+        merge_round(k0, m, l, ov);
     }
     bf16* orow = o + (size_t)bh * D + lane * E;
     if (M == kNegInf) {                          // no cached token
