@@ -43,6 +43,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E (published)
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 matrix peak (published)
+PEAK_FP32_VECTOR_TFLOPS = 157.3   # MI355X fp32 vector peak (published; packed fp32 FMA)
 # The E4M3 prefill runs Q·Kᵀ (half its FLOP) at the fp8 rate and P·V (the other half) at
 # the bf16 rate: its matrix-core bound is 1 / (0.5 / fp8 peak + 0.5 / bf16 peak).
 PEAK_FP8_PREFILL_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
@@ -311,6 +312,25 @@ def p_sweep(torch, ma, dev):
             "rows": rows, "fit_measured_peak_bytes_per_P": round(a, 3),
             "fit_measured_peak_intercept_bytes": round(c, 1), "fit_max_abs_residual_bytes": round(resid, 1),
             "score_matrix_bytes_per_P_at_32122": 16 * 32122 * 2}
+
+
+def fp32_section(torch, ma, W, dev):
+    """The fp32 masked forward with LSE (B1 H16 T512 D64, last 48 keys padded), timed on its own.
+    It runs on the vector ALU (fp32 fma, one product per instruction): against the published fp32
+    vector peak, whose figure counts packed fp32 FMAs, twice what unpacked instructions reach.
+    FLOP are algorithmic: 4·D·H·Tq·n_valid."""
+    w = W.fp32_masked_t512()
+    q, k, v, m = (t.to(dev) for t in (w.q, w.k, w.v, w.mask))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    t, d = _time_call(torch, lambda: ma.attn_fwd_lse(q, k, v, m, w.scale, out=o, lse=lse))
+    B, H, Tq, D = q.shape
+    n_valid = int((w.mask[0] == 0).sum())
+    flop = 4 * D * H * Tq * n_valid
+    return {"workload": "fp32 masked prefill with LSE, B1 H16 T512 D64, last 48 keys padded", "us": d,
+            "tflops": round(flop / t / 1e12, 2), "bound": "alu",
+            "frac_alu": round(flop / t / 1e12 / PEAK_FP32_VECTOR_TFLOPS, 4),
+            "peak_tflops": PEAK_FP32_VECTOR_TFLOPS, "algorithmic_flop": flop}
 
 
 def varlen_section(torch, ma, W, dev):
@@ -672,6 +692,7 @@ def main():
     }
     if not args.no_sweep:
         out["p_sweep"] = p_sweep(torch, ma, dev)
+        out["fp32_prefill"] = fp32_section(torch, ma, W, dev)
         out["varlen"] = varlen_section(torch, ma, W, dev)
         out["paged_decode"] = paged_section(torch, ma, W, dev, flush)
         out["causal_gqa_prefill"] = causal_section(torch, ma, W, dev)
