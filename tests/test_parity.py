@@ -189,6 +189,30 @@ def test_fp32_masked_t512(ma):
     check_attn(o, l, Or, Lr, torch.float32, "fp32 T512")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp32_key_split_merge(ma, D):
+    """The fp32 kernel splits a query block's keys over four wavefronts (key blocks w, w+4, ...)
+    and merges their states: key ranges where some wavefronts see only padded blocks or no block
+    at all, where the largest scores sit in one wavefront's blocks, and long ranges with several
+    blocks per wavefront."""
+    g = torch.Generator().manual_seed(D)
+    cases = []
+    for Tk in (31, 33, 97, 130, 1000):
+        m = torch.zeros(3, Tk, dtype=torch.uint8)
+        m[1, : Tk // 2] = 1                      # leading half padded
+        if Tk > 64:
+            m[2, 32:64] = 1                      # wavefront 1's first block wholly padded
+            m[2, 96:] = 1                        # and everything past the third block
+        cases.append(W.make_prefill(3, 2, 45, Tk, D, torch.float32, mask=m, seed=Tk + D))
+    w = W.make_prefill(1, 2, 70, 900, D, torch.float32, seed=7 + D)
+    w.k[0, :, 700:710] *= 8.0                    # peaky scores inside one wavefront's blocks
+    cases.append(w)
+    for w in cases:
+        o, l = run_fwd(ma, w)
+        Or, Lr = oracle.attention(w.q, w.k, w.v, w.mask, w.scale)
+        check_attn(o, l, Or, Lr, torch.float32, f"fp32 D={D} Tk={w.k.shape[2]}")
+
+
 def test_patch_p1944(ma):
     w = W.patch_p1944()
     o, l = run_fwd(ma, w)
