@@ -113,8 +113,9 @@ void decode_split_kernel(const T* __restrict__ q, const T* __restrict__ kc,
         for (int u = 0; u < UNROLL; ++u) {
             const int tt = t0 + lane / LG + u * NSLOT;
             valid[u] = tt < t_end;
-            kw[u] = valid[u] ? ldg128(kb + (size_t)tt * D) : zero4;
-            vw[u] = valid[u] ? ldg128(vb + (size_t)tt * D) : zero4;
+            // whole token rows of consecutive slots, each cache line read once: streaming loads
+            kw[u] = valid[u] ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (size_t)tt * D)) : zero4;
+            vw[u] = valid[u] ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + (size_t)tt * D)) : zero4;
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
