@@ -62,7 +62,7 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
                           const bf16* __restrict__ vc, const int32_t* __restrict__ lens,
                           float* __restrict__ ws_o, float* __restrict__ ws_ml,
                           int B, int H_q, int H_kv, int T_max, int G, int n_hg, int nsplit,
-                          int nwaves, int qb, float c,
+                          int nwaves, int qb, int ns, int sob, float c,
                           const int32_t* __restrict__ bt, int lps, int max_pages, int num_pages) {
     using Gm = Geo<D>;
     constexpr int RB = Gm::RB, BLK = Gm::BLK, NCH = Gm::NCH, QCH = Gm::QCH;
@@ -75,6 +75,7 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
     extern __shared__ __attribute__((aligned(16))) unsigned char qlds[];   // RV Q slots of qb bytes
     auto vslot = [&](int s) -> unsigned char* { return s == 0 ? vs0 : s == 1 ? vs1 : s == 2 ? vs2 : vs3; };
     auto qslot = [&](int s) -> unsigned char* { return qlds + s * qb; };
+    unsigned char* const stash = qlds + RV * qb;    // ns slots of sob bytes after the Q slots
 
     const int HG = H_kv * n_hg;
     const Lens L = load_lens(lens, B, T_max);
@@ -245,6 +246,12 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
     float mc = 0.f, lsum = 0.f;
     bool mc_set = false;
+    // Partials of items that ended inside the range, held until it ends.  At D = 64 two
+    // workgroups per SIMD fill the LDS with their V rings and Q slots, so no slot is ever
+    // free for them and the stash is compiled out.
+    constexpr bool STASH = D == 128;
+    Held held0{}, held1{};
+    int nheld = 0;
 
     // Vᵀ operand reads (as in the prefill kernel)
     const int vg = lane >> 4, vm = lane & 15;
@@ -362,7 +369,15 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
         // end of this wavefront's part of the item: write the partial
         if (cc.i == cc.nb - 1 || j == nblk - 1) {
             const float Lsum = pair_sum(lsum);
-            if (col_ok) {
+            if (STASH && j < nblk - 1 && nheld < ns) {
+                // the item ends inside the range: hold its partial until the range ends
+                stash_o<D, false>(stash + nheld * sob, oacc, 1.f, col_ok, l32, hl);
+                const Held h = make_held((uint32_t)(((cc.b * H_q + g * G + hg * 32) * nsplit + cc.s) * 2 + part),
+                                         min(32, G - hg * 32), part == 0, mc, Lsum);
+                if (nheld == 0) held0 = h;
+                else held1 = h;
+                ++nheld;
+            } else if (col_ok) {
                 // the group's (split, part) slots: head column col, slot (col*nsplit + s)*2 + part
                 const size_t slot = ((size_t)(cc.b * H_q + g * G + col) * nsplit + cc.s) * 2 + part;
                 float* orow = ws_o + slot * D;
@@ -405,24 +420,11 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
         }
     }
     wait_vmem_le<0>();     // the look-ahead's LDS loads land before the wavefront ends
-}
-
-// Wavefronts the split kernel runs at once (one round of the whole GPU) for
-// a given dynamic LDS size; the last query is cached.
-template <int D, bool PAGED>
-int resident_waves(int lds_bytes) {
-    static int cached_lds = -1, cached = 0;
-    if (lds_bytes == cached_lds) return cached;
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_stream_kernel<D, PAGED>, 64, lds_bytes) !=
-            hipSuccess ||
-        cus <= 0 || per_cu <= 0)
-        return 256;
-    cached = cus * per_cu;
-    cached_lds = lds_bytes;
-    return cached;
+    static_assert(kStashSlots == 2, "held0, held1");
+    if constexpr (STASH) {
+        if (nheld > 0) stash_flush<D>(stash, held0, nsplit, ws_o, ws_ml);
+        if (nheld > 1) stash_flush<D>(stash + sob, held1, nsplit, ws_o, ws_ml);
+    }
 }
 
 template <int D, bool PAGED>
@@ -431,9 +433,9 @@ hipError_t launch(const DecodeArgs& a) {
     const int n_hg = (G + 31) / 32;
     const int nsplit = decode_nsplit(a.T_max);
     const int qb = q_slot_bytes(G, D);
-    const int lds = Geo<D>::RV * qb;
+    const int lds0 = Geo<D>::RV * qb;
     ATTN_CHECK(G >= 1 && G * a.H_kv == a.H_q, "query heads group onto KV heads");
-    ATTN_CHECK(lds + Geo<D>::RV * Geo<D>::BLK <= kLdsBytesPerCu, "V ring and Q slots fit a CU");
+    ATTN_CHECK(lds0 + Geo<D>::RV * Geo<D>::BLK <= kLdsBytesPerCu, "V ring and Q slots fit a CU");
     ATTN_CHECK(nsplit >= 1 && (long long)nsplit * kDecodeSplit >= a.T_max, "splits cover the cache");
     ATTN_CHECK((size_t)a.B * a.H_q * nsplit * 2 * (D + 2) * sizeof(float) <=
                    decode_workspace_bytes(a.B, a.H_q, a.T_max, D),
@@ -443,18 +445,24 @@ hipError_t launch(const DecodeArgs& a) {
                           (long long)a.max_pages * a.page_size == a.T_max),
                "pages are powers of two of at least 16 tokens");
     ATTN_CHECK((long long)a.B * a.H_q / 4 + 1 <= kMaxGrid, "combine grid size");
-    // the largest dynamic LDS any call uses: RV full 32-head Q slots
+    // the largest dynamic LDS any call uses: RV full 32-head Q slots and the stash slots
+    static const int max_dyn = Geo<D>::RV * q_slot_bytes(32, D) + kStashSlots * stash_slot_bytes(32, D);
     static const hipError_t attr =
-        hipFuncSetAttribute((const void*)decode_stream_kernel<D, PAGED>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            Geo<D>::RV * q_slot_bytes(32, D));
+        hipFuncSetAttribute((const void*)decode_stream_kernel<D, PAGED>, hipFuncAttributeMaxDynamicSharedMemorySize, max_dyn);
     if (attr != hipSuccess) return attr;
-    const int nwaves = resident_waves<D, PAGED>(lds);
+    // one round of the whole GPU: the wavefronts resident at the Q slots' LDS, and as many
+    // stash slots as leave that count unchanged
+    const int cus = cu_count(), per_cu = blocks_per_cu<decode_stream_kernel<D, PAGED>>(lds0);
+    const int nwaves = cus > 0 && per_cu > 0 ? cus * per_cu : 256;
+    const int sob = stash_slot_bytes(G, D);
+    const int ns = D == 128 && per_cu > 0 ? stash_slots<decode_stream_kernel<D, PAGED>>(lds0, sob, max_dyn, per_cu) : 0;
+    const int lds = lds0 + ns * sob;
     float* ws_o = static_cast<float*>(a.workspace);
     float* ws_ml = ws_o + (size_t)a.B * a.H_q * nsplit * 2 * D;
     const int lps = PAGED ? __builtin_ctz((unsigned)a.page_size) : 0;
     hipLaunchKernelGGL((decode_stream_kernel<D, PAGED>), dim3(nwaves), dim3(64), lds, (hipStream_t)a.stream,
                        (const bf16*)a.q, (const bf16*)a.k_cache, (const bf16*)a.v_cache, a.lens, ws_o, ws_ml,
-                       a.B, a.H_q, a.H_kv, a.T_max, G, n_hg, nsplit, nwaves, qb, a.scale * kLog2e,
+                       a.B, a.H_q, a.H_kv, a.T_max, G, n_hg, nsplit, nwaves, qb, ns, sob, a.scale * kLog2e,
                        a.block_table, lps, a.max_pages, a.num_pages);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

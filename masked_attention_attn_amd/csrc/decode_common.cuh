@@ -16,6 +16,8 @@
 // merge (sglang PR 49078 analysis, "1. aiter.py").
 #pragma once
 
+#include <atomic>
+
 #include "common.cuh"
 #include "launch.h"
 #include "mfma_lds.cuh"
@@ -34,6 +36,104 @@ inline int q_slot_bytes(int G, int D) { return (min(G, 32) * D * 2 + 1023) / 102
 
 __device__ __forceinline__ int seq_len(const int32_t* lens, int b, int T_max) {
     return min(max(lens[b], 0), T_max);
+}
+
+// Partials of items that end inside a wavefront's range are held until the range ends and
+// written then: O in an LDS stash slot, (reference, sum) and where they go in registers.
+// The same partial stores issued while the wavefront still streams its range cost ~7% of
+// the decode's time (measured against a timing copy without them).  A wavefront holds at
+// most kStashSlots, as many as the LDS left over at the kernel's occupancy allows (the host
+// picks the count, possibly 0); items past that store at once.
+constexpr int kStashSlots = 2;
+// Bytes of one stash slot: the O rows of a group's columns (at most 32), D floats each.
+__host__ __device__ inline int stash_slot_bytes(int G, int D) { return min(G, 32) * D * 4; }
+
+// A held partial: the workspace slot of its column 0 (column c at slot0 + c·2·nsplit), its
+// column count, whether its empty part 1 must be marked, and this lane's (reference, sum).
+// All four live in vector registers: the stream loop has no scalar registers to spare.
+struct Held {
+    uint32_t slot0, nc_mark;     // nc_mark = column count | mark << 8
+    float m, l;
+};
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t x) {
+    uint32_t v;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "s"(x));
+    return v;
+}
+__device__ __forceinline__ Held make_held(uint32_t slot0, int ncols, bool mark, float m, float l) {
+    return Held{in_vgpr(slot0), in_vgpr((uint32_t)ncols | (mark ? 256u : 0u)), m, l};
+}
+
+// This lane's column of an item's O (the MFMA accumulator layout, times vs when SCALE) into a
+// stash slot: column c's D floats at float offset c·D.
+template <int D, bool SCALE>
+__device__ __forceinline__ void stash_o(unsigned char* slot, const f32x16* o, float vs, bool col_ok, int l32,
+                                        int hl) {
+    if (!col_ok) return;
+    float* row = reinterpret_cast<float*>(slot) + l32 * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            f32x4 v{o[db][4 * g4], o[db][4 * g4 + 1], o[db][4 * g4 + 2], o[db][4 * g4 + 3]};
+            if constexpr (SCALE) v = f32x4{v[0] * vs, v[1] * vs, v[2] * vs, v[3] * vs};
+            *reinterpret_cast<f32x4*>(row + db * 32 + g4 * 8 + hl * 4) = v;
+        }
+}
+
+// A held partial to the workspace: O rows from its stash slot (consecutive lanes, consecutive
+// 16 bytes of a row), (reference, sum) from the first half's lanes of its columns, the empty
+// marker of part 1 from the second half's.
+template <int D>
+__device__ __forceinline__ void stash_flush(const unsigned char* slot, const Held& h, int nsplit,
+                                            float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+    constexpr int QPC = D / 4;       // 16-byte chunks per column
+    const int lane = threadIdx.x & 63, l32 = lane & 31;
+    const size_t cstep = (size_t)nsplit * 2;
+    const int ncols = (int)(h.nc_mark & 255u);
+    for (int c = lane; c < ncols * QPC; c += 64) {
+        const int col = c / QPC, qc = c - col * QPC;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(slot + (size_t)(col * D + qc * 4) * 4);
+        *reinterpret_cast<f32x4*>(ws_o + (h.slot0 + col * cstep) * D + qc * 4) = v;
+    }
+    if (l32 < ncols) {
+        if (lane < 32) *reinterpret_cast<f32x2*>(ws_ml + (h.slot0 + l32 * cstep) * 2) = f32x2{h.m, h.l};
+        else if (h.nc_mark & 256u)
+            *reinterpret_cast<f32x2*>(ws_ml + (h.slot0 + 1 + l32 * cstep) * 2) = f32x2{kNegInf, 0.f};
+    }
+}
+
+// Workgroups of one wavefront of KERNEL resident per CU at a dynamic LDS size (0 if the query
+// fails), cached per kernel and size: each entry packs (size + 1, count) into one word.
+template <auto KERNEL>
+int blocks_per_cu(int lds_bytes) {
+    static std::atomic<uint64_t> tab[8];
+    const uint64_t key = (uint64_t)(uint32_t)(lds_bytes + 1) << 32;
+    for (auto& e : tab) {
+        const uint64_t v = e.load(std::memory_order_relaxed);
+        if ((v & ~0xffffffffull) == key) return (int)(uint32_t)v;
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KERNEL, 64, lds_bytes) != hipSuccess || per_cu < 0)
+        per_cu = 0;
+    tab[(uint32_t)lds_bytes % 8].store(key | (uint32_t)per_cu, std::memory_order_relaxed);
+    return per_cu;
+}
+inline int cu_count() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return cus;
+}
+// Stash slots for a launch of KERNEL: the most (up to kStashSlots, within max_dyn bytes of
+// dynamic LDS) that leave its resident workgroups per CU at per_cu.
+template <auto KERNEL>
+int stash_slots(int lds0, int slot_bytes, int max_dyn, int per_cu) {
+    for (int n = kStashSlots; n >= 1; --n) {
+        const int lds = lds0 + n * slot_bytes;
+        if (lds <= max_dyn && blocks_per_cu<KERNEL>(lds) == per_cu) return n;
+    }
+    return 0;
 }
 
 // inclusive prefix sum over the 64 lanes of the wavefront

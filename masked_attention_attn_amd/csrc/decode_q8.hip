@@ -69,7 +69,7 @@ void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc
                        const float* __restrict__ vscale, const int32_t* __restrict__ lens,
                        float* __restrict__ ws_o, float* __restrict__ ws_ml,
                        int B, int H_q, int H_kv, int T_max, int G, int n_hg, int nsplit,
-                       int nwaves, int qb, float c, const int32_t* __restrict__ bt, int max_pages,
+                       int nwaves, int qbn, float c, const int32_t* __restrict__ bt, int max_pages,
                        int num_pages, int lps) {
     using Gm = Geo8<D, INT8>;
     constexpr int RB = Gm::RB, NV = Gm::NV, QCH = Gm::QCH, RV = Gm::RV, LK = Gm::LK;
@@ -78,8 +78,19 @@ void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc
     constexpr int RB16 = D * 2;        // bytes per row of the bf16 V tile
     static_assert(LK >= 1 && LK < RV, "ring geometry");
     __shared__ __attribute__((aligned(16))) unsigned char vtile[CK * RB16];
+    // Partials of items that end inside the range are held until it ends (E4M3 only: the INT8
+    // kernel measured slower with the stash, ~89 against ~87 us on the decode workload with
+    // the caches flushed, its loop being bound by the code conversions rather than the stores).
+    // qbn: the Q slot bytes (a multiple of 1 KiB), plus the stash slots in its low bits; one
+    // argument, so the INT8 instances keep the argument list they had without a stash (with
+    // two more arguments their register allocation, and time, moved).
+    constexpr bool STASH = !INT8;
+    const int qb = STASH ? qbn & ~1023 : qbn;
+    const int ns = STASH ? qbn & 1023 : 0;
+    const int sob = stash_slot_bytes(G, D);
     extern __shared__ __attribute__((aligned(16))) unsigned char qlds[];   // RV Q slots of qb bytes
     auto qslot = [&](int s) -> unsigned char* { return qlds + s * qb; };
+    unsigned char* const stash = qlds + RV * qb;    // ns slots of sob bytes after the Q slots
 
     const int HG = H_kv * n_hg;
     const Lens L = load_lens(lens, B, T_max);
@@ -244,6 +255,8 @@ void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
     float mc = 0.f, lsum = 0.f;
     bool mc_set = false;
+    Held held0{}, held1{};        // the held partials
+    int nheld = 0;
 
     const int vg = lane >> 4, vm = lane & 15;
     const int vrow = (vg >> 1) * 8 + (vm >> 2);
@@ -370,7 +383,15 @@ void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc
         // end of this wavefront's part of the item: write the partial (O times the V scale)
         if (cc.i == cc.nb - 1 || j == nblk - 1) {
             const float Lsum = pair_sum(lsum);
-            if (col_ok) {
+            if (STASH && j < nblk - 1 && nheld < ns) {
+                // the item ends inside the range: hold its partial until the range ends
+                stash_o<D, true>(stash + nheld * sob, oacc, vsc, col_ok, l32, hl);
+                const Held h = make_held((uint32_t)(((cc.b * H_q + g * G + hg * 32) * nsplit + cc.s) * 2 + part),
+                                         min(32, G - hg * 32), part == 0, mc, Lsum);
+                if (nheld == 0) held0 = h;
+                else held1 = h;
+                ++nheld;
+            } else if (col_ok) {
                 const size_t slot = ((size_t)(cc.b * H_q + g * G + col) * nsplit + cc.s) * 2 + part;
                 float* orow = ws_o + slot * D;
 #pragma unroll
@@ -411,21 +432,11 @@ void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc
         }
     }
     wait_vmem_le<0>();     // the Q loads into LDS land before the wavefront ends
-}
-
-template <int D, bool INT8, bool PAGED>
-int resident_waves8(int lds_bytes) {
-    static int cached_lds = -1, cached = 0;
-    if (lds_bytes == cached_lds) return cached;
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_q8_kernel<D, INT8, PAGED>, 64, lds_bytes) != hipSuccess ||
-        cus <= 0 || per_cu <= 0)
-        return 256;
-    cached = cus * per_cu;
-    cached_lds = lds_bytes;
-    return cached;
+    static_assert(kStashSlots == 2, "held0, held1");
+    if constexpr (STASH) {
+        if (nheld > 0) stash_flush<D>(stash, held0, nsplit, ws_o, ws_ml);
+        if (nheld > 1) stash_flush<D>(stash + sob, held1, nsplit, ws_o, ws_ml);
+    }
 }
 
 template <int D, bool INT8, bool PAGED>
@@ -433,10 +444,10 @@ hipError_t launch8(const DecodeFp8Args& a) {
     const int G = a.H_q / a.H_kv;
     const int n_hg = (G + 31) / 32;
     const int nsplit = decode_nsplit(a.T_max);
-    const int qb = q_slot_bytes(G, D);
-    const int lds = Geo8<D, INT8>::RV * qb;
+    const int qb = q_slot_bytes(G, D);           // a multiple of 1 KiB: the stash count rides in its low bits
+    const int lds0 = Geo8<D, INT8>::RV * qb;
     ATTN_CHECK(G >= 1 && G * a.H_kv == a.H_q, "query heads group onto KV heads");
-    ATTN_CHECK(lds <= kLdsBytesPerCu, "Q slots fit a CU");
+    ATTN_CHECK(lds0 <= kLdsBytesPerCu, "Q slots fit a CU");
     ATTN_CHECK(nsplit >= 1 && (long long)nsplit * kDecodeSplit >= a.T_max, "splits cover the cache");
     ATTN_CHECK((size_t)a.B * a.H_q * nsplit * 2 * (D + 2) * sizeof(float) <=
                    decode_workspace_bytes(a.B, a.H_q, a.T_max, D),
@@ -445,17 +456,24 @@ hipError_t launch8(const DecodeFp8Args& a) {
     ATTN_CHECK(!PAGED || (a.page_size >= 16 && (a.page_size & (a.page_size - 1)) == 0 &&
                           (long long)a.max_pages * a.page_size == a.T_max),
                "pages are powers of two of at least 16 tokens");
+    // the largest dynamic LDS any call uses: RV full 32-head Q slots and the stash slots
+    static const int max_dyn = Geo8<D, INT8>::RV * q_slot_bytes(32, D) + kStashSlots * stash_slot_bytes(32, D);
     static const hipError_t attr =
-        hipFuncSetAttribute((const void*)decode_q8_kernel<D, INT8, PAGED>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            Geo8<D, INT8>::RV * q_slot_bytes(32, D));
+        hipFuncSetAttribute((const void*)decode_q8_kernel<D, INT8, PAGED>, hipFuncAttributeMaxDynamicSharedMemorySize, max_dyn);
     if (attr != hipSuccess) return attr;
-    const int nwaves = resident_waves8<D, INT8, PAGED>(lds);
+    // one round of the whole GPU: the wavefronts resident at the Q slots' LDS, and as many
+    // stash slots as leave that count unchanged
+    const int cus = cu_count(), per_cu = blocks_per_cu<decode_q8_kernel<D, INT8, PAGED>>(lds0);
+    const int nwaves = cus > 0 && per_cu > 0 ? cus * per_cu : 256;
+    const int sob = stash_slot_bytes(G, D);
+    const int ns = !INT8 && per_cu > 0 ? stash_slots<decode_q8_kernel<D, INT8, PAGED>>(lds0, sob, max_dyn, per_cu) : 0;
+    const int lds = lds0 + ns * sob;
     float* ws_o = static_cast<float*>(a.workspace);
     float* ws_ml = ws_o + (size_t)a.B * a.H_q * nsplit * 2 * D;
     const int lps = PAGED ? __builtin_ctz((unsigned)a.page_size) : 0;
     hipLaunchKernelGGL((decode_q8_kernel<D, INT8, PAGED>), dim3(nwaves), dim3(64), lds, (hipStream_t)a.stream,
                        (const bf16*)a.q, (const uint8_t*)a.k_cache, (const uint8_t*)a.v_cache, a.k_scale,
-                       a.v_scale, a.lens, ws_o, ws_ml, a.B, a.H_q, a.H_kv, a.T_max, G, n_hg, nsplit, nwaves, qb,
+                       a.v_scale, a.lens, ws_o, ws_ml, a.B, a.H_q, a.H_kv, a.T_max, G, n_hg, nsplit, nwaves, qb + ns,
                        a.scale * kLog2e, a.block_table, a.max_pages, a.num_pages, lps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -1116,3 +1116,53 @@ def test_decode_short_items_repeated(ma, fmt):
         if it == 0 or worst > 1e-3:
             check_attn(o, l, Or, Lr, torch.bfloat16, f"{fmt} short-item decode, round {it}")
     assert worst <= 1e-3, f"{fmt}: max |dLSE| over the rounds {worst:.3e}"
+
+
+# ---- partials held until a wavefront's range ends ----------------------------------------------
+
+# (B, Hq, Hkv, len_lo, len_hi, T_max) at D = 128 with at most 4 query heads per KV head: the bf16
+# and E4M3 decodes then have LDS left for two held partials per wavefront.  Lengths 1..80 make
+# items of 1..3 blocks, so a 32-block range ends ~15 items inside it (two held, the rest stored
+# at once); lengths 1,025..1,120 end one or two items inside most ranges (all held).
+HELD_CASES = [(24, 4, 4, 1, 80, 128), (24, 16, 4, 1, 80, 128), (6, 32, 8, 1024, 1119, 1152), (9, 8, 8, 1024, 1119, 1152)]
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("case", HELD_CASES)
+def test_decode_held_partials(ma, case, fmt, paged):
+    B, Hq, Hkv, lo, hi, Tm = case
+    D = 128
+    if fmt == "bf16":
+        w = W.make_decode(B, Hq, Hkv, D, lo, hi, torch.bfloat16, T_max=Tm, seed=B + Hq + hi)
+        ek, ev, el = oracle.kv_append(w.k_cache.float().numpy(), w.v_cache.float().numpy(), w.lens.numpy(),
+                                      w.k_new.float().numpy(), w.v_new.float().numpy())
+        Or, Lr = oracle.decode(w.q, ek, ev, el, w.scale)
+    else:
+        w = W.make_decode_fp8(B, Hq, Hkv, D, lo, hi, T_max=Tm, seed=B + Hq + hi)
+        ek, ev, el = oracle.kv_append_fp8(w.k_cache.numpy(), w.v_cache.numpy(), w.k_scale, w.v_scale,
+                                          w.lens.numpy(), w.k_new, w.v_new)
+        Or, Lr = oracle.decode_fp8kv(w.q, ek, ev, w.k_scale, w.v_scale, el, w.scale)
+    q, kn, vn, lens = w.q.to(DEV), w.k_new.to(DEV), w.v_new.to(DEV), w.lens.to(DEV)
+    if paged:
+        pg = W.to_paged(w, 16, seed=B)
+        kp, vp, bt = _paged_dev(pg)
+        if fmt == "bf16":
+            ma.kv_append_paged(kp, vp, bt, lens, kn, vn)
+            o, l = ma.attn_decode_paged(q, kp, vp, bt, lens, w.scale, want_lse=True)
+        else:
+            ks, vs = w.k_scale.to(DEV), w.v_scale.to(DEV)
+            ma.kv_append_fp8_paged(kp, vp, ks, vs, bt, lens, kn, vn)
+            o, l = ma.attn_decode_fp8kv_paged(q, kp, vp, ks, vs, bt, lens, w.scale, want_lse=True)
+    else:
+        kc, vc = w.k_cache.to(DEV), w.v_cache.to(DEV)
+        if fmt == "bf16":
+            ma.kv_append(kc, vc, lens, kn, vn)
+            o, l = ma.attn_decode(q, kc, vc, lens, w.scale, want_lse=True)
+        else:
+            ks, vs = w.k_scale.to(DEV), w.v_scale.to(DEV)
+            ma.kv_append_fp8(kc, vc, ks, vs, lens, kn, vn)
+            o, l = ma.attn_decode_fp8kv(q, kc, vc, ks, vs, lens, w.scale, want_lse=True)
+    torch.cuda.synchronize()
+    assert lens.cpu().tolist() == el.tolist()
+    check_attn(o, l, Or, Lr, torch.bfloat16, f"{fmt} decode with held partials {case} paged={paged}")
