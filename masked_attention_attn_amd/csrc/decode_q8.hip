@@ -452,6 +452,7 @@ hipError_t launch8(const DecodeFp8Args& a) {
     ATTN_CHECK((size_t)a.B * a.H_q * nsplit * 2 * (D + 2) * sizeof(float) <=
                    decode_workspace_bytes(a.B, a.H_q, a.T_max, D),
                "partials and (reference, sum) pairs fit the workspace");
+    ATTN_CHECK((long long)a.B * a.H_q * nsplit * 2 < (1ll << 31), "partial slot indices fit 31 bits (held partials)");
     ATTN_CHECK(PAGED || (long long)a.T_max * D < (1ll << 31), "a (sequence, KV head) fits a 32-bit range");
     ATTN_CHECK(!PAGED || (a.page_size >= 16 && (a.page_size & (a.page_size - 1)) == 0 &&
                           (long long)a.max_pages * a.page_size == a.T_max),
