@@ -29,7 +29,9 @@
 // without touching memory.  Softmax per head column: weights 2^(S·c - mc),
 // mc from the exact max of the item's first block here, raised only when a
 // lane's weights of one 32-key block sum past 2^8 (then l and O are rescaled
-// and the block's weights redone against the new reference).
+// and the block's weights redone against the new reference).  At D = 128 the
+// partials of items that end inside a wavefront's range are held (O in LDS left
+// over at the kernel's occupancy) and written after the range's last block.
 #include "decode_common.cuh"
 
 namespace mattn {

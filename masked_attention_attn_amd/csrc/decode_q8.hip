@@ -24,7 +24,8 @@
 // read.  Every global load is a compiler builtin, so the compiler derives the
 // waits; each item's Q (bf16) reaches an LDS slot by buffer->LDS loads.  V rows
 // (whole lines, read once) use the non-temporal cache policy; the K operand loads,
-// which read each line over several k-steps, keep the default.
+// which read each line over several k-steps, keep the default.  The E4M3 instances hold
+// the partials of items that end inside a range until it ends, as the bf16 kernel does.
 #include "decode_common.cuh"
 
 namespace mattn {
