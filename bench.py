@@ -69,11 +69,46 @@ def parse():
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run 3 plain device-to-device copies of MIB MiB (reference kernel "
                         "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    p.add_argument("--decode-calls", type=int, default=0, metavar="N",
+                   help="only run the decode workload on its bf16, E4M3 and INT8 caches N times each, "
+                        "each call after a 512 MiB read (MALL flushed), and exit: the window the "
+                        "decode counter profiles cover")
     p.add_argument("--api-calls", type=int, default=0, metavar="N",
                    help="only call every entry point of the step (and the allocation-free decode) N "
                         "times on preallocated buffers, between two device synchronisations, and "
                         "exit: the window a HIP runtime trace inspects for allocations and syncs")
     return p.parse_args()
+
+
+def decode_calls(n):
+    """The decode workload (B32, 32/8 heads, D128, 0.58 GB bf16 cache) on its bf16, E4M3 and INT8
+    caches, n calls each, each after a 512 MiB read so that the MALL holds none of the cache."""
+    import torch
+    import masked_attention_attn_amd as ma
+    import workloads as W
+    ma.load()
+    dev = torch.device("cuda:0")
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    for fmt in ("bf16", "fp8", "int8"):
+        w = {"bf16": W.gqa_decode_b32, "fp8": W.gqa_decode_b32_fp8, "int8": W.gqa_decode_b32_int8}[fmt]()
+        kc, vc, q = w.k_cache.to(dev), w.v_cache.to(dev), w.q.to(dev)
+        lens = (w.lens + 1).to(dev)
+        B, Hq, _, D = q.shape
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        ws = torch.empty(ma.attn_decode_workspace_bytes(B, Hq, kc.shape[1], kc.shape[2], D), dtype=torch.uint8,
+                         device=dev)
+        if fmt == "bf16":
+            call = lambda: ma.attn_decode(q, kc, vc, lens, w.scale, out=o, lse=lse, workspace=ws, want_lse=True)
+        else:
+            ks, vs = w.k_scale.to(dev), w.v_scale.to(dev)
+            fn = ma.attn_decode_fp8kv if fmt == "fp8" else ma.attn_decode_int8kv
+            call = lambda: fn(q, kc, vc, ks, vs, lens, w.scale, out=o, lse=lse, workspace=ws, want_lse=True)
+        for _ in range(n):
+            flush.sum()
+            call()
+        torch.cuda.synchronize()
+    print(json.dumps({"decode_calls": {"per_cache": n, "caches": ["bf16", "fp8", "int8"]}}))
 
 
 def calibrate_copy(mib):
@@ -499,6 +534,9 @@ def main():
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
+    if args.decode_calls:
+        decode_calls(args.decode_calls)
+        return
 
     import torch
     import masked_attention_attn_amd as ma

@@ -104,7 +104,8 @@ __device__ __forceinline__ void stash_flush(const unsigned char* slot, const Hel
 }
 
 // Workgroups of one wavefront of KERNEL resident per CU at a dynamic LDS size (0 if the query
-// fails), cached per kernel and size: each entry packs (size + 1, count) into one word.
+// fails), cached per kernel and size: each entry packs (size + 1, count) into one word, and a
+// new size takes the first free entry (once all eight are taken, the one its size picks).
 template <auto KERNEL>
 int blocks_per_cu(int lds_bytes) {
     static std::atomic<uint64_t> tab[8];
@@ -115,14 +116,27 @@ int blocks_per_cu(int lds_bytes) {
     }
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KERNEL, 64, lds_bytes) != hipSuccess || per_cu < 0)
-        per_cu = 0;
-    tab[(uint32_t)lds_bytes % 8].store(key | (uint32_t)per_cu, std::memory_order_relaxed);
+        return 0;
+    const uint64_t entry = key | (uint32_t)per_cu;
+    for (auto& e : tab) {
+        uint64_t empty = 0;
+        if (e.compare_exchange_strong(empty, entry, std::memory_order_relaxed)) return per_cu;
+    }
+    tab[((uint32_t)lds_bytes >> 10) % 8].store(entry, std::memory_order_relaxed);
     return per_cu;
 }
+// Compute units of the current device, read once per device.
 inline int cu_count() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return 0;
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 64) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+    if (dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
     return cus;
 }
 // Stash slots for a launch of KERNEL: the most (up to kStashSlots, within max_dyn bytes of
