@@ -627,7 +627,11 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
             bool over = false;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) over |= cs[nb][k2] > kRescaleSum;
-            if (__ballot(over)) {
+            // The rescale is rare: bf16 lays it out off the common path, which then falls
+            // through instead of branching over it (0.6-1.0% faster); the E4M3 step measured
+            // 0.7% slower so, and keeps the compiler's own layout.
+            const bool rescale = __ballot(over) != 0;
+            if (FP8 ? rescale : __builtin_expect(rescale, 0)) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     // (highest index first: no partial max shared with the first-block
