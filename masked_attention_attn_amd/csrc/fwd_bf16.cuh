@@ -532,15 +532,17 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
                 if (hf == 0) pm_tile = pm_next;
                 pm |= (uint32_t)(pm_tile >> (hf * 32));
             }
-        }
-        if (pm != 0u) {             // workgroup-uniform, rare: padded keys get -inf
-            // element i of this lane is key (i/8)*16 + hl*8 + i%8 of the block
-            const uint32_t pl = ((pm >> (hl * 8)) & 0xFFu) | (((pm >> (16 + hl * 8)) & 0xFFu) << 8);
+            // Inside the edge branch, so that a block wholly inside the unpadded range passes
+            // both tests with one branch not taken.
+            if (pm != 0u) {         // workgroup-uniform: padded keys get -inf
+                // element i of this lane is key (i/8)*16 + hl*8 + i%8 of the block
+                const uint32_t pl = ((pm >> (hl * 8)) & 0xFFu) | (((pm >> (16 + hl * 8)) & 0xFFu) << 8);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if ((pl >> i) & 1u) {
+                for (int i = 0; i < 16; ++i) {
+                    if ((pl >> i) & 1u) {
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) S[nb][i] = kNegInf;
+                        for (int nb = 0; nb < NB; ++nb) S[nb][i] = kNegInf;
+                    }
                 }
             }
         }
