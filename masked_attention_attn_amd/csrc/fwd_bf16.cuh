@@ -774,7 +774,7 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
         if (hf == HALVES - 1) {
             if constexpr (FP8) wait_vmem();     // this wave's part of K_{T+2} and V_{T+1} has landed
             else wait_vmem_le<(L::AHEAD - 1) * (CPW + CPWV)>();    // all but the two newest batches
-            if (holes) {
+            if (__builtin_expect(holes, 0)) {      // off the common path, which falls through
                 pm_next = __ballot(padf_nxt) & TILE_BITS;
                 padf_nxt = pad_flag(min(T + 2, t_last));
             }
