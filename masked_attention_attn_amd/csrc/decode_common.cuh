@@ -288,9 +288,16 @@ __device__ Cursor cursor_at(const Lens& L, int HG, int n_hg, int b, int lb) {
     c.hg = c.it - c.g * n_hg;
     return c;
 }
-// Next block in the global order.
+// Next block in the global order.  LIKELY marks staying inside the item as the expected case,
+// which lays the item change out off the common path (the INT8 decode measured 85 against
+// 88 us with it; the bf16 and E4M3 decodes neutral or slower, so they keep the default).
+template <bool LIKELY = false>
 __device__ __forceinline__ void advance(Cursor& c, const Lens& L, int HG, int n_hg) {
-    if (++c.i < c.nb) return;
+    if constexpr (LIKELY) {
+        if (__builtin_expect(++c.i < c.nb, 1)) return;
+    } else {
+        if (++c.i < c.nb) return;
+    }
     c.i = 0;
     if (++c.it < HG) {
         if (++c.hg == n_hg) {

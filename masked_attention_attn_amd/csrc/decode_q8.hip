@@ -195,7 +195,7 @@ void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc
                               (ch + 1) * 1024 >= ncols * RB16);
         }
         ++nv;
-        advance(icv, L, HG, n_hg);
+        advance<INT8>(icv, L, HG, n_hg);
         if (icv.i == 0) {
             qs_issue = qs_issue == RV - 1 ? 0 : qs_issue + 1;
             if constexpr (!PAGED) vrs = item_rsrc(icv, vc);
@@ -233,7 +233,7 @@ void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc
         }
         if (!live) return;
         ++nk;
-        advance(ick, L, HG, n_hg);
+        advance<INT8>(ick, L, HG, n_hg);
         if constexpr (!PAGED)
             if (ick.i == 0) krs = item_rsrc(ick, kc);
     };
@@ -416,7 +416,7 @@ void decode_q8_kernel(const bf16* __restrict__ q, const uint8_t* __restrict__ kc
             part = 0;
             qs = qs == RV - 1 ? 0 : qs + 1;
         }
-        advance(cc, L, HG, n_hg);
+        advance<INT8>(cc, L, HG, n_hg);
     };
 
     // block j sits in V slot j % RV and K slot j % RV; unrolled RV times so every slot
