@@ -512,7 +512,7 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
     // The reference mc is set from the exact row max of the first visited block
     // that holds an unpadded key (then every weight of that block is <= 1) and
     // raised only when a 16-key chunk's weights sum past 2^TAU in some lane.
-    bool mc_set = false;
+    int mc_set = 0;                 // wave-uniform (an SGPR, tested with one scalar compare)
 
     // One pipeline step for key block u = u_first + j: S holds its raw scores;
     // Sn receives block u+1's.  hf (the step's half within its LDS tile) is a
@@ -560,7 +560,7 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
                 }
             }
         }
-        if (__builtin_expect(!mc_set, 0) && pm != ~0u) {   // once: first block with an unpadded key
+        if (__builtin_expect(__builtin_amdgcn_readfirstlane(mc_set) == 0, 0) && pm != ~0u) {   // once: first block with an unpadded key
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 float m = S[nb][0];
@@ -570,7 +570,7 @@ void fwd_bf16_kernel(const Elem<FP8>* __restrict__ q, const Elem<FP8>* __restric
                 m = pair_max(m);
                 nmc[nb] = m == kNegInf ? 0.f : -(m * c);
             }
-            mc_set = true;
+            mc_set = 1;
         }
 
         // ---- fixed block, issued slot by slot: the MFMA stream is
